@@ -1,0 +1,125 @@
+"""Exact-arithmetic brute force of the same method, for tiny inputs.
+
+TEST INFRASTRUCTURE, like the rest of this folder: only tests, the smoke
+check and the benchmark's CPU-baseline leg may use it.
+
+It shares no arithmetic with the numpy oracle. Every value is a Python
+Fraction; fp32 and fp16 results are produced by an explicit
+round-to-nearest-even routine written here from the IEEE 754 definition (p
+significand bits, minimum normal exponent emin, gradual underflow), and the
+integer accumulation uses Python ints. The method's steps are the ones of the
+Cider README's kernel pipeline and quantization sections (per-token or
+per-group symmetric min-max codes, int32 accumulation, dequant as
+acc * s_act * s_weight rounded to fp16); the readings of the unstated details
+(scale = max|v| / qmax in fp32, ties to even, a zero group gets scale 0) are
+the same ones the numpy oracle documents.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+__all__ = ["round_binary", "f32", "f16", "rint_half_even", "quantize_row",
+           "dot", "dequant", "dequant_groups", "linear"]
+
+_INF = float("inf")
+
+
+def round_binary(v: Fraction, p: int, emin: int, emax: int):
+    """Round v to the nearest binary floating-point number with p significand
+    bits (hidden bit included), exponents in [emin, emax], subnormals below
+    2**emin; ties go to the even significand. Returns a Fraction, or +-inf
+    when the rounded magnitude reaches 2**(emax+1)."""
+    v = Fraction(v)
+    if v == 0:
+        return Fraction(0)
+    sign = -1 if v < 0 else 1
+    a = -v if v < 0 else v
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    # now 2**(e-1) < a < 2**(e+1); settle e with 2**e <= a < 2**(e+1)
+    if Fraction(2) ** e > a:
+        e -= 1
+    if Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, emin)                       # subnormal range shares emin's ulp
+    ulp = Fraction(2) ** (e - p + 1)
+    n = a / ulp
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    r = fl * ulp
+    if r >= Fraction(2) ** (emax + 1):
+        return sign * _INF
+    return sign * r
+
+
+def f32(v) -> Fraction:
+    return round_binary(Fraction(v), 24, -126, 127)
+
+
+def f16(v) -> Fraction:
+    return round_binary(Fraction(v), 11, -14, 15)
+
+
+def rint_half_even(v: Fraction) -> int:
+    fl = v.numerator // v.denominator
+    rem = v - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return fl
+
+
+def quantize_row(values, group_size: int, qmax: int):
+    """values: exact fp16 values of one row (floats or Fractions).
+    Returns (codes list[int], scales list[Fraction]) with one scale per group."""
+    vals = [Fraction(v) for v in values]
+    K = len(vals)
+    gs = K if group_size == 0 else group_size
+    assert K % gs == 0
+    codes, scales = [], []
+    for g in range(K // gs):
+        grp = vals[g * gs:(g + 1) * gs]
+        amax = max(abs(v) for v in grp)
+        s = f32(amax / qmax)
+        scales.append(s)
+        for v in grp:
+            if s == 0:
+                codes.append(0)
+            else:
+                c = rint_half_even(f32(v / s))
+                codes.append(max(-qmax, min(qmax, c)))
+    return codes, scales
+
+
+def dot(a, b) -> int:
+    return sum(int(x) * int(y) for x, y in zip(a, b))
+
+
+def dequant(acc: int, s_a: Fraction, s_w: Fraction) -> Fraction:
+    return f16(Fraction(acc) * s_a * s_w)
+
+
+def dequant_groups(accs, s_as, s_ws) -> Fraction:
+    return f16(sum(Fraction(c) * a * w for c, a, w in zip(accs, s_as, s_ws)))
+
+
+def linear(x_rows, w_codes, w_scales, group_size: int):
+    """x_rows: list of fp16-valued rows; w_codes: list of int code rows [N][K];
+    w_scales: per row, a list of G scales (Fractions). Returns
+    (y [M][N] Fractions, qa [M][K], sa [M][G])."""
+    K = len(x_rows[0]) if x_rows else 0
+    gs = K if group_size == 0 else group_size
+    qa, sa = [], []
+    for row in x_rows:
+        c, s = quantize_row(row, group_size, 127)
+        qa.append(c)
+        sa.append(s)
+    y = []
+    for m in range(len(x_rows)):
+        out = []
+        for n in range(len(w_codes)):
+            accs = [dot(qa[m][g * gs:(g + 1) * gs], w_codes[n][g * gs:(g + 1) * gs])
+                    for g in range(K // gs)]
+            out.append(dequant_groups(accs, sa[m], w_scales[n]))
+        y.append(out)
+    return y, qa, sa

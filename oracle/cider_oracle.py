@@ -1,0 +1,202 @@
+"""Plain, slow CPU oracle of Cider's online-quantized linear layer (W8A8 / W4A8).
+
+TEST INFRASTRUCTURE. Only the test suite, the package's smoke check and the
+CPU-baseline leg of the benchmark may import or run this module. The HIP
+library never calls it, shares no code with it, and must not fall back to it.
+
+What it computes, and where the pages say so (all citations are to the
+top-level Cider README, a community translation of the upstream README):
+
+* Section "模式" (Modes) table: W8A8 = symmetric INT8 weights with INT8
+  per-token activations; W4A8 = INT4 weights packed in uint8 with INT8
+  per-token activations.
+* Section "W8A8 量化粒度" (W8A8 quantization granularity) table: per-channel
+  (one scale per output channel) or per-group (one scale per 128 or per 64
+  elements).
+* Section "架构 / Metal Kernel 流水线" (kernel pipeline): prefill first turns
+  fp16 activations into int8 plus one scale per token, then runs an
+  INT8 x INT8 -> INT32 matmul whose store stage dequantizes to fp16; for
+  W4A8 the int4 weights are unpacked to int8 while the fragments are loaded.
+* Section "量化" (Quantization) table: weights symmetric INT8 (per-channel or
+  per-group gs=64/128) or symmetric INT4 with zero point 8 per column;
+  activations symmetric INT8 per token; INT32 accumulation; the output is
+  the int32 accumulator times the activation scale times the weight scale,
+  per element, in fp16.
+* Section "说明" (Notes): scales come from the min-max rule by default.
+
+Readings taken where the pages are silent (each is also listed in the design
+notes of the repository):
+
+* scale = max|v| / qmax over the row (or group), qmax = 127 for int8 and 7
+  for int4, computed in fp32 with one correctly rounded division; stored as
+  fp32.
+* code = clamp(round_half_even(v / scale), -qmax, qmax), with v / scale one
+  correctly rounded fp32 division. The fp32 precision of this decision is
+  the kernel's (the pages fix none); -128 is never produced.
+* a row or group whose max|v| is 0 gets scale 0 and all codes 0.
+* per-group (gs = 64 or 128) groups run along K and apply to the activation
+  and the weight alike: y = sum_g acc_g * s_a[m,g] * s_w[n,g].
+* int4: codes in [-7, 7] stored as nibble u = code + 8; two codes per byte,
+  the even K index in the low nibble; weight rows are [N, K/2] bytes.
+* dequant: the exact product acc * s_a * s_w (summed over groups for
+  per-group) rounded once to fp16 (round to nearest even). This is the plain
+  definition of the formula; it is evaluated in fp64, where acc * s_a is
+  exact (at most 52 significant bits) and only the last product and the
+  group sum round.
+
+Integer accumulation is done as an fp64 matmul of int8-valued arrays. Every
+product and partial sum is an integer of magnitude at most 127*127*K, which
+is below 2**53 for every K this module accepts, so each fp64 operation
+(whatever the BLAS blocking order or FMA use) is exact.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "QMAX_INT8", "QMAX_INT4", "quantize_rows", "quantize_act", "quantize_weight",
+    "pack_int4", "unpack_int4", "int_dot", "int_dot_groups", "dequant_per_channel",
+    "dequant_per_group", "w8a8_linear", "w4a8_linear", "num_groups",
+]
+
+QMAX_INT8 = 127
+QMAX_INT4 = 7
+_EXACT_K_LIMIT = (2 ** 53) // (127 * 127)
+
+
+def num_groups(K: int, group_size: int) -> int:
+    """G = 1 for per-row scales (group_size 0), else K / group_size."""
+    if group_size == 0:
+        return 1
+    if K % group_size:
+        raise ValueError(f"K={K} is not a multiple of group_size={group_size}")
+    return K // group_size
+
+
+def quantize_rows(X: np.ndarray, group_size: int, qmax: int):
+    """Symmetric min-max quantization of every row (or K-group of a row).
+
+    X: fp16 [R, K]. group_size 0 = one scale per row; otherwise one scale per
+    run of group_size consecutive K elements. Returns (q int8 [R, K],
+    s fp32 [R, G]).
+    """
+    X = np.asarray(X)
+    if X.dtype != np.float16 or X.ndim != 2:
+        raise TypeError("X must be a 2-D float16 array")
+    R, K = X.shape
+    G = num_groups(K, group_size)
+    gs = K if group_size == 0 else group_size
+    xg = X.astype(np.float32).reshape(R, G, gs)          # fp16 -> fp32 is exact
+    amax = np.abs(xg).max(axis=2) if K else np.zeros((R, G), np.float32)
+    s = (amax / np.float32(qmax)).astype(np.float32)      # one rounded fp32 division
+    zero = s == 0
+    r = xg / np.where(zero, np.float32(1), s)[:, :, None]  # one rounded fp32 division
+    q = np.clip(np.rint(r), -qmax, qmax)                   # rint: ties to even
+    q[zero] = 0
+    return q.reshape(R, K).astype(np.int8), s
+
+
+def quantize_act(x: np.ndarray, group_size: int = 0):
+    """Per-token (group_size 0) or per-group int8 activation quantization.
+
+    Returns (q int8 [M, K], s fp32 [M] for per-token, [M, K/gs] per-group)."""
+    q, s = quantize_rows(x, group_size, QMAX_INT8)
+    return q, (s[:, 0] if group_size == 0 else s)
+
+
+def quantize_weight(w: np.ndarray, bits: int = 8, group_size: int = 0):
+    """Weight quantization, offline (the README's low-level API section shows
+    the weight quantizers running in numpy before any kernel call).
+
+    bits 8: int8 [N, K] codes with fp32 scales [N] (group_size 0) or [N, K/gs].
+    bits 4: packed uint8 [N, K/2] (low nibble = even k) with fp32 scales [N].
+    """
+    if bits == 8:
+        q, s = quantize_rows(w, group_size, QMAX_INT8)
+        return q, (s[:, 0] if group_size == 0 else s)
+    if bits == 4:
+        if group_size != 0:
+            raise ValueError("int4 weights are per output channel only")
+        q, s = quantize_rows(w, 0, QMAX_INT4)
+        return pack_int4(q), s[:, 0]
+    raise ValueError("bits must be 8 or 4")
+
+
+def pack_int4(q: np.ndarray) -> np.ndarray:
+    """Codes in [-7, 7], [N, K] with K even -> uint8 [N, K/2].
+
+    Byte j of a row holds code 2j (plus 8) in its low nibble and code 2j+1
+    (plus 8) in its high nibble."""
+    q = np.asarray(q)
+    if q.shape[1] % 2:
+        raise ValueError("K must be even to pack int4")
+    if q.size and (q.min() < -QMAX_INT4 or q.max() > QMAX_INT4):
+        raise ValueError("int4 codes must lie in [-7, 7]")
+    u = (q.astype(np.int16) + 8).astype(np.uint8)
+    return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_int4(p: np.ndarray) -> np.ndarray:
+    """Inverse of pack_int4: uint8 [N, K/2] -> int8 codes [N, K]."""
+    p = np.asarray(p, dtype=np.uint8)
+    lo = (p & 0x0F).astype(np.int16) - 8
+    hi = (p >> 4).astype(np.int16) - 8
+    out = np.empty((p.shape[0], 2 * p.shape[1]), np.int16)
+    out[:, 0::2] = lo
+    out[:, 1::2] = hi
+    return out.astype(np.int8)
+
+
+def int_dot(qa: np.ndarray, qw: np.ndarray) -> np.ndarray:
+    """acc[m, n] = sum_k qa[m, k] * qw[n, k], exact, as int64 [M, N]."""
+    K = qa.shape[1]
+    if qw.shape[1] != K:
+        raise ValueError("K mismatch")
+    if K > _EXACT_K_LIMIT:
+        raise ValueError("K too large for an exact fp64 integer dot product")
+    return (qa.astype(np.float64) @ qw.astype(np.float64).T).astype(np.int64)
+
+
+def int_dot_groups(qa: np.ndarray, qw: np.ndarray, group_size: int) -> np.ndarray:
+    """Per-group exact dot products: acc[g, m, n] over k in group g, int64."""
+    K = qa.shape[1]
+    G = num_groups(K, group_size)
+    gs = K if group_size == 0 else group_size
+    return np.stack([int_dot(qa[:, g * gs:(g + 1) * gs], qw[:, g * gs:(g + 1) * gs])
+                     for g in range(G)])
+
+
+def dequant_per_channel(acc: np.ndarray, s_a: np.ndarray, s_w: np.ndarray) -> np.ndarray:
+    """y[m, n] = fp16(acc[m, n] * s_a[m] * s_w[n]); fp64 product, one fp16 rounding."""
+    t = acc.astype(np.float64) * s_a.astype(np.float64)[:, None]   # exact (<= 52 bits)
+    t = t * s_w.astype(np.float64)[None, :]
+    return t.astype(np.float16)
+
+
+def dequant_per_group(acc_g: np.ndarray, s_a: np.ndarray, s_w: np.ndarray) -> np.ndarray:
+    """y[m, n] = fp16(sum_g acc_g[g, m, n] * s_a[m, g] * s_w[n, g]) in fp64."""
+    G = acc_g.shape[0]
+    y = np.zeros(acc_g.shape[1:], np.float64)
+    for g in range(G):
+        t = acc_g[g].astype(np.float64) * s_a[:, g].astype(np.float64)[:, None]
+        y += t * s_w[:, g].astype(np.float64)[None, :]
+    return y.astype(np.float16)
+
+
+def w8a8_linear(x: np.ndarray, w_q: np.ndarray, s_w: np.ndarray, group_size: int = 0):
+    """The full online W8A8 linear: quantize x, integer matmul, dequant to fp16.
+
+    Returns (y fp16 [M, N], q_a int8 [M, K], s_a fp32)."""
+    q_a, s_a = quantize_act(x, group_size)
+    if group_size == 0:
+        y = dequant_per_channel(int_dot(q_a, w_q), s_a, s_w)
+    else:
+        y = dequant_per_group(int_dot_groups(q_a, w_q, group_size), s_a, s_w)
+    return y, q_a, s_a
+
+
+def w4a8_linear(x: np.ndarray, w_packed: np.ndarray, s_w: np.ndarray):
+    """W4A8: per-token int8 activations times unpacked int4 weights, per-channel."""
+    q_a, s_a = quantize_act(x, 0)
+    y = dequant_per_channel(int_dot(q_a, unpack_int4(w_packed)), s_a, s_w)
+    return y, q_a, s_a

@@ -1,0 +1,304 @@
+"""Checks that pin the CPU oracle to facts fixed outside itself.
+
+Each check takes an implementation namespace with the oracle's primitive
+functions (quantize_rows, pack_int4, unpack_int4, int_dot, int_dot_groups,
+dequant_per_channel, dequant_per_group) and raises AssertionError when the
+implementation disagrees with:
+
+* hand-derived worked examples stored under tests/golden/ (closed forms);
+* the exact-rational brute force in oracle/brute.py on tiny inputs;
+* invariants of the definition (2^k scaling, sign symmetry, range, K
+  permutation, gs = K reducing to per-channel);
+* the deterministic error bound of symmetric min-max quantization against the
+  unquantized fp64 product, and cosine floors on the synthetic workload.
+
+The same checks run against deliberately broken copies of the oracle in
+test_oracle_mutants.py, to show that each plausible mistake is caught.
+"""
+from __future__ import annotations
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+
+from oracle import brute
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _act(impl, x, gs):
+    q, s = impl.quantize_rows(x, gs, 127)
+    return q, s
+
+
+def _linear(impl, x, wq, sw2d, gs):
+    """Compose the primitives into the W8A8 linear; sw2d is [N, G]."""
+    qa, sa = impl.quantize_rows(x, gs, 127)
+    if gs == 0:
+        return impl.dequant_per_channel(impl.int_dot(qa, wq), sa[:, 0], sw2d[:, 0])
+    return impl.dequant_per_group(impl.int_dot_groups(qa, wq, gs), sa, sw2d)
+
+
+# --------------------------------------------------------------- golden files
+def check_golden_quant(impl):
+    for case in _load("quant_ties.json")["cases"]:
+        x = np.array([case["x"]], np.float16)
+        q, s = impl.quantize_rows(x, case["group_size"], case["qmax"])
+        assert q.tolist()[0] == case["q"], (case, q)
+        assert s.astype(np.float64).ravel().tolist() == case["s"], (case, s)
+
+
+def check_golden_division(impl):
+    """Rows where only a correctly rounded fp32 division by the scale (not a
+    multiplication by its rounded reciprocal) gives the right code."""
+    for case in _load("division_cases.json")["cases"]:
+        x = np.array([case["x"]], np.float16)
+        q, s = impl.quantize_rows(x, 0, 127)
+        assert q.tolist()[0] == case["q"], (case, q)
+        assert float(s[0, 0]) == case["s"], (case, s)
+
+
+def check_golden_int4(impl):
+    g = _load("int4_pack.json")
+    codes = np.array(g["codes"], np.int8)
+    packed = impl.pack_int4(codes)
+    assert packed.dtype == np.uint8 and packed.tolist() == g["packed"], packed
+    assert impl.unpack_int4(np.array(g["packed"], np.uint8)).tolist() == g["codes"]
+
+
+def check_golden_integer_gemm(impl):
+    g = _load("integer_gemm.json")
+    x = np.array(g["x"], np.float16)
+    w = np.array(g["w"], np.float16)
+    qa, sa = impl.quantize_rows(x, 0, 127)
+    qw, sw = impl.quantize_rows(w, 0, 127)
+    assert np.all(sa == 1) and np.all(sw == 1)
+    acc = impl.int_dot(qa, qw)
+    assert acc.tolist() == g["acc"], acc
+    y = impl.dequant_per_channel(acc, sa[:, 0], sw[:, 0])
+    assert y.astype(np.float64).tolist() == g["y"], y
+
+
+def check_closed_form_k10240(impl):
+    g = _load("closed_form_k10240.json")
+    K = g["K"]
+    x = np.full((2, K), g["x_value"], np.float16)
+    w = np.full((2, K), g["w_value"], np.float16)
+    w[1, K // 3] = g["w_special_value"]
+    qa, sa = impl.quantize_rows(x, 0, 127)
+    qw, sw = impl.quantize_rows(w, 0, 127)
+    assert np.all(qa == 127) and np.all(sa == np.float32(2.0 ** -20))
+    assert np.all(sw == np.float32(2.0 ** -10)) and qw[1, K // 3] == 1
+    acc = impl.int_dot(qa, qw)
+    assert acc[0, 0] == g["acc_all_127"] and acc[0, 1] == g["acc_one_code_1"], acc
+    y = impl.dequant_per_channel(acc, sa[:, 0], sw[:, 0])
+    assert float(y[0, 1]) == g["y_one_code_1"], y
+
+
+# --------------------------------------------------------------- brute force
+def _rand_fp16(rng, shape, kind):
+    if kind == "normal":
+        v = rng.standard_normal(shape) * 3
+    elif kind == "wide":
+        v = rng.standard_normal(shape) * np.exp2(rng.integers(-12, 12, size=shape))
+    elif kind == "ties":      # values that land on code midpoints when amax = 127
+        v = rng.integers(-254, 255, size=shape) / 2.0
+        v.flat[0] = 127.0
+    else:
+        v = rng.integers(-3, 4, size=shape).astype(np.float64)
+    return v.astype(np.float16)
+
+
+def check_brute_quant(impl, trials=60, seed=1):
+    rng = np.random.default_rng(seed)
+    for t in range(trials):
+        R = int(rng.integers(1, 5))
+        gs = [0, 2, 4][t % 3]
+        K = int(rng.integers(1, 3)) * 4
+        qmax = 127 if t % 4 else 7
+        x = _rand_fp16(rng, (R, K), ["normal", "wide", "ties", "small"][t % 4])
+        q, s = impl.quantize_rows(x, gs, qmax)
+        for r in range(R):
+            bq, bs = brute.quantize_row([float(v) for v in x[r]], gs, qmax)
+            assert q[r].tolist() == bq, (x[r], q[r], bq)
+            assert [Fraction(float(v)) for v in s[r]] == bs, (x[r], s[r], bs)
+
+
+def check_brute_linear(impl, trials=24, seed=2):
+    rng = np.random.default_rng(seed)
+    for t in range(trials):
+        M, N = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        gs = [0, 4, 8][t % 3]
+        K = 16 if gs else int(rng.integers(1, 9)) * 2
+        x = _rand_fp16(rng, (M, K), ["normal", "wide", "ties"][t % 3])
+        w = _rand_fp16(rng, (N, K), ["normal", "wide", "small"][t % 3])
+        qw, sw = impl.quantize_rows(w, gs, 127)
+        with np.errstate(over="ignore"):   # fp16 overflow to inf is the IEEE reading
+            y = _linear(impl, x, qw, sw, gs)
+        wcodes = qw.astype(int).tolist()
+        wsc = [[Fraction(float(v)) for v in row] for row in sw]
+        by, bqa, bsa = brute.linear([[float(v) for v in row] for row in x], wcodes, wsc, gs)
+        for m in range(M):
+            for n in range(N):
+                assert float(y[m, n]) == float(by[m][n]), (t, m, n, y[m, n], float(by[m][n]))
+        # the int32 accumulators, one group at a time
+        qa, _ = impl.quantize_rows(x, gs, 127)
+        accg = impl.int_dot_groups(qa, qw, gs)
+        g_sz = K if gs == 0 else gs
+        for g in range(accg.shape[0]):
+            for m in range(M):
+                for n in range(N):
+                    ref = brute.dot(bqa[m][g * g_sz:(g + 1) * g_sz], wcodes[n][g * g_sz:(g + 1) * g_sz])
+                    assert accg[g, m, n] == ref
+
+
+def check_brute_int4(impl, trials=20, seed=3):
+    rng = np.random.default_rng(seed)
+    for _ in range(trials):
+        N, K = int(rng.integers(1, 4)), int(rng.integers(1, 5)) * 2
+        w = _rand_fp16(rng, (N, K), "normal")
+        q, s = impl.quantize_rows(w, 0, 7)
+        p = impl.pack_int4(q)
+        for n in range(N):
+            bq, bs = brute.quantize_row([float(v) for v in w[n]], 0, 7)
+            assert q[n].tolist() == bq
+            by = [(bq[2 * j] + 8) | ((bq[2 * j + 1] + 8) << 4) for j in range(K // 2)]
+            assert p[n].tolist() == by
+        assert np.array_equal(impl.unpack_int4(p), q)
+
+
+# --------------------------------------------------------------- invariants
+def check_pow2_invariance(impl, seed=4):
+    """Scaling a row by 2^k (exactly representable) keeps the codes and
+    multiplies the scale by exactly 2^k."""
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((6, 256)) * 4).astype(np.float16)
+    x[:, 7] *= np.float16(16)
+    for gs in (0, 64, 128):
+        q0, s0 = impl.quantize_rows(x, gs, 127)
+        for k in range(-3, 9):
+            xs = (x.astype(np.float64) * 2.0 ** k).astype(np.float16)
+            exact = (xs.astype(np.float64) * 2.0 ** -k == x.astype(np.float64)).all(axis=1)
+            q1, s1 = impl.quantize_rows(xs, gs, 127)
+            for r in np.nonzero(exact)[0]:
+                assert np.array_equal(q1[r], q0[r]), (gs, k, r)
+                assert np.array_equal(s1[r], (s0[r].astype(np.float64) * 2.0 ** k).astype(np.float32))
+
+
+def check_sign_and_range(impl, seed=5):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((16, 128)) * 10).astype(np.float16)
+    for qmax in (127, 7):
+        for gs in (0, 64):
+            q, s = impl.quantize_rows(x, gs, qmax)
+            qn, sn = impl.quantize_rows(-x, gs, qmax)
+            assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+            assert np.abs(q.astype(int)).max() <= qmax
+            G = s.shape[1]
+            gsz = 128 // G
+            xr = np.abs(x.astype(np.float32)).reshape(16, G, gsz)
+            qr = q.reshape(16, G, gsz)
+            at = xr.argmax(axis=2)
+            picked = np.take_along_axis(qr, at[:, :, None], axis=2)[:, :, 0]
+            assert np.all(np.abs(picked.astype(int)) == qmax)
+    z = np.zeros((2, 64), np.float16)
+    q, s = impl.quantize_rows(z, 0, 127)
+    assert not q.any() and not s.any()
+
+
+def check_k_permutation(impl, seed=6):
+    rng = np.random.default_rng(seed)
+    qa = rng.integers(-127, 128, (5, 96)).astype(np.int8)
+    qw = rng.integers(-127, 128, (7, 96)).astype(np.int8)
+    perm = rng.permutation(96)
+    a = impl.int_dot(qa, qw)
+    assert np.array_equal(a, impl.int_dot(qa[:, perm], qw[:, perm]))
+    ref = qa.astype(np.int64) @ qw.astype(np.int64).T
+    assert np.array_equal(a, ref)
+    assert a.shape == (5, 7)
+
+
+def check_gs_equals_k(impl, seed=7):
+    """Per-group with one group spanning all of K is per-channel."""
+    rng = np.random.default_rng(seed)
+    for K in (64, 128):
+        x = (rng.standard_normal((9, K)) * 2).astype(np.float16)
+        w = (rng.standard_normal((11, K)) * 0.02).astype(np.float16)
+        qw, sw = impl.quantize_rows(w, 0, 127)
+        qwg, swg = impl.quantize_rows(w, K, 127)
+        assert np.array_equal(qw, qwg) and np.array_equal(sw, swg)
+        y0 = _linear(impl, x, qw, sw, 0)
+        y1 = _linear(impl, x, qwg, swg, K)
+        assert np.array_equal(y0.view(np.uint16), y1.view(np.uint16))
+
+
+def error_bound(x, w, qa, sa, qw, sw, gs_a, gs_w):
+    """Deterministic bound on |y - x W^T| for symmetric round-to-nearest codes.
+
+    With x = s_a*q_a + e_a and |e_a| <= (s_a/2)(1 + 2^-15) (the rint of a
+    correctly rounded quotient of magnitude <= 128), and likewise for W:
+    x W - (s_a q_a)(s_w q_w) = x e_w + e_a W - e_a e_w, and the fp16 rounding
+    of the output adds 2^-11 relative plus half the smallest subnormal."""
+    K = x.shape[1]
+    ga = K if gs_a == 0 else gs_a
+    gw = K if gs_w == 0 else gs_w
+    sa_k = np.repeat(sa.astype(np.float64), ga, axis=1)  # [M, K]
+    sw_k = np.repeat(sw.astype(np.float64), gw, axis=1)  # [N, K]
+    ax = np.abs(x.astype(np.float64))
+    aw = np.abs(w.astype(np.float64))
+    c = (1 + 2.0 ** -15) ** 2
+    bq = c * (ax @ (sw_k / 2).T + (sa_k / 2) @ aw.T + (sa_k / 2) @ (sw_k / 2).T)
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    return ref, bq + 2.0 ** -11 * (np.abs(ref) + bq) + 2.0 ** -24 + 1e-12 * (ax @ aw.T)
+
+
+def cosine(a, b):
+    a = a.astype(np.float64).ravel()
+    b = b.astype(np.float64).ravel()
+    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b) + 1e-12))
+
+
+def check_error_bound_and_cosine(impl, M=48, N=96, seed=0):
+    from w8a8_online_quantized_amd import inputs
+    for K, gs, floor in ((2560, 0, 0.997), (10240, 0, 0.997), (1024, 128, 0.999), (1024, 64, 0.999)):
+        x = inputs.activations(M, K, seed=seed)
+        w = inputs.weights(N, K, seed=seed)
+        qw, sw = impl.quantize_rows(w, gs, 127)
+        qa, sa = impl.quantize_rows(x, gs, 127)
+        y = _linear(impl, x, qw, sw, gs)
+        ref, bound = error_bound(x, w, qa, sa, qw, sw, gs, gs)
+        err = np.abs(y.astype(np.float64) - ref)
+        assert np.all(err <= bound), (K, gs, float((err - bound).max()))
+        cs = cosine(y, ref)
+        assert cs >= floor, (K, gs, cs)
+
+
+def check_int4_bound_and_cosine(impl, M=48, N=96, seed=0):
+    from w8a8_online_quantized_amd import inputs
+    K = 2560
+    x = inputs.activations(M, K, seed=seed)
+    w = inputs.weights(N, K, seed=seed)
+    q4, s4 = impl.quantize_rows(w, 0, 7)
+    qw = impl.unpack_int4(impl.pack_int4(q4))
+    qa, sa = impl.quantize_rows(x, 0, 127)
+    y = impl.dequant_per_channel(impl.int_dot(qa, qw), sa[:, 0], s4[:, 0])
+    ref, bound = error_bound(x, w, qa, sa, qw, s4, 0, 0)
+    err = np.abs(y.astype(np.float64) - ref)
+    assert np.all(err <= bound), float((err - bound).max())
+    assert cosine(y, ref) >= 0.98
+
+
+ALL_CHECKS = [
+    check_golden_quant, check_golden_division, check_golden_int4, check_golden_integer_gemm,
+    check_closed_form_k10240, check_brute_quant, check_brute_linear,
+    check_brute_int4, check_pow2_invariance, check_sign_and_range,
+    check_k_permutation, check_gs_equals_k, check_error_bound_and_cosine,
+    check_int4_bound_and_cosine,
+]

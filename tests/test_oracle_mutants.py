@@ -1,0 +1,126 @@
+"""Plant plausible mistakes in copies of the CPU oracle and check that the pins
+catch every one of them (CPU only; nothing here touches the GPU)."""
+import types
+
+import numpy as np
+import pytest
+
+from oracle import cider_oracle as O
+from tests import oracle_pins as pins
+
+
+def _impl(**over):
+    base = {name: getattr(O, name) for name in (
+        "quantize_rows", "pack_int4", "unpack_int4", "int_dot", "int_dot_groups",
+        "dequant_per_channel", "dequant_per_group")}
+    base.update(over)
+    ns = types.SimpleNamespace(**base)
+    return ns
+
+
+def _quant_variant(rounding="even", divisor_bias=0, reciprocal=False, clamp=None):
+    def q(X, group_size, qmax):
+        R, K = X.shape
+        G = O.num_groups(K, group_size)
+        gs = K if group_size == 0 else group_size
+        xg = X.astype(np.float32).reshape(R, G, gs)
+        amax = np.abs(xg).max(axis=2)
+        s = (amax / np.float32(qmax + divisor_bias)).astype(np.float32)
+        zero = s == 0
+        sd = np.where(zero, np.float32(1), s)[:, :, None]
+        r = xg * (np.float32(1) / sd) if reciprocal else xg / sd
+        t = np.floor(r + np.float32(0.5)) if rounding == "up" else np.rint(r)
+        lo, hi = clamp if clamp else (-qmax, qmax)
+        q = np.clip(t, lo, hi)
+        q[zero] = 0
+        return q.reshape(R, K).astype(np.int8), s
+    return q
+
+
+def _pack_swapped(q):
+    u = (q.astype(np.int16) + 8).astype(np.uint8)
+    return (u[:, 1::2] | (u[:, 0::2] << 4)).astype(np.uint8)
+
+
+def _unpack_zp7(p):
+    lo = (p & 0x0F).astype(np.int16) - 7
+    hi = (p >> 4).astype(np.int16) - 7
+    out = np.empty((p.shape[0], 2 * p.shape[1]), np.int16)
+    out[:, 0::2], out[:, 1::2] = lo, hi
+    return out.astype(np.int8)
+
+
+def _dot_fp32(qa, qw):
+    return (qa.astype(np.float32) @ qw.astype(np.float32).T).astype(np.int64)
+
+
+def _dot_transposed(qa, qw):
+    # right shapes only when M == N; otherwise the pins' shape checks fail
+    k = min(qa.shape[0], qw.shape[0])
+    out = O.int_dot(qa, qw)
+    out[:k, :k] = out[:k, :k].T
+    return out
+
+
+def _dequant_no_sw(acc, s_a, s_w):
+    return (acc.astype(np.float64) * s_a.astype(np.float64)[:, None]).astype(np.float16) * 0 + \
+        (acc.astype(np.float64) * s_a.astype(np.float64)[:, None] * float(np.mean(s_w))).astype(np.float16)
+
+
+def _dequant_sign(acc, s_a, s_w):
+    y = O.dequant_per_channel(acc, s_a, s_w)
+    y[..., -1] = -y[..., -1]
+    return y
+
+
+def _dequant_fp16_steps(acc, s_a, s_w):
+    t = acc.astype(np.float16) * s_a.astype(np.float16)[:, None]
+    return (t * s_w.astype(np.float16)[None, :]).astype(np.float16)
+
+
+def _pg_drop_last_group(acc_g, s_a, s_w):
+    return O.dequant_per_group(acc_g[:-1], s_a[:, :-1], s_w[:, :-1]) if acc_g.shape[0] > 1 \
+        else O.dequant_per_group(acc_g, s_a, s_w)
+
+
+def _pg_row_scale(acc_g, s_a, s_w):
+    sa = np.repeat(s_a[:, :1], s_a.shape[1], axis=1)
+    return O.dequant_per_group(acc_g, sa, s_w)
+
+
+def _groups_off_by_one(qa, qw, group_size):
+    out = O.int_dot_groups(qa, qw, group_size)
+    if out.shape[0] > 1:
+        out = np.roll(out, 1, axis=0)
+    return out
+
+
+MUTANTS = {
+    "round_half_up": _impl(quantize_rows=_quant_variant(rounding="up")),
+    "scale_over_128": _impl(quantize_rows=_quant_variant(divisor_bias=1)),
+    "reciprocal_multiply": _impl(quantize_rows=_quant_variant(reciprocal=True)),
+    "clamp_to_126": _impl(quantize_rows=_quant_variant(clamp=(-126, 126))),
+    "int4_nibbles_swapped": _impl(pack_int4=_pack_swapped),
+    "int4_zero_point_7": _impl(unpack_int4=_unpack_zp7),
+    "fp32_accumulation": _impl(int_dot=_dot_fp32),
+    "transposed_output": _impl(int_dot=_dot_transposed),
+    "dropped_weight_scale": _impl(dequant_per_channel=_dequant_no_sw),
+    "sign_flip_last_column": _impl(dequant_per_channel=_dequant_sign),
+    "fp16_dequant_steps": _impl(dequant_per_channel=_dequant_fp16_steps),
+    "per_group_drops_a_group": _impl(dequant_per_group=_pg_drop_last_group),
+    "per_group_row_scale": _impl(dequant_per_group=_pg_row_scale),
+    "per_group_misaligned": _impl(int_dot_groups=_groups_off_by_one),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    impl = MUTANTS[name]
+    caught = []
+    for check in pins.ALL_CHECKS:
+        try:
+            with np.errstate(all="ignore"):
+                check(impl)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(check.__name__)
+    assert caught, f"mutant {name} passed every pin"
