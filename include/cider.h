@@ -1,0 +1,131 @@
+/*
+ * cider.h - C ABI of the MI355X (gfx950) online-quantized W8A8 / W4A8 linear layer.
+ *
+ * The operation follows the top-level Cider README:
+ *   - section "架构 / Metal Kernel 流水线" (kernel pipeline): a prefill linear is
+ *     two device steps, fp16 activations -> int8 codes + one scale per token,
+ *     then an INT8 x INT8 -> INT32 matmul whose store stage applies the scales
+ *     and writes fp16; for W4A8 the int4 weights are unpacked to int8 while the
+ *     matmul loads its fragments;
+ *   - section "量化" (Quantization) table: symmetric INT8 weights (per output
+ *     channel or per group of 64/128), symmetric INT4 weights with zero point 8,
+ *     symmetric INT8 per-token activations, INT32 accumulation, and
+ *     C_fp16 = C_int32 * s_act * s_weight per element;
+ *   - section "W8A8 量化粒度" (quantization granularity) table: per-channel,
+ *     per-group gs = 128, per-group gs = 64;
+ *   - section "底层 API" (low-level API): weight quantizers return
+ *     (codes, scale); the linear takes (x, codes, scale).
+ *
+ * Readings of details the page leaves open (fixed here, identical in the CPU
+ * oracle that the tests compare against):
+ *   - scale = max|v| / qmax in fp32 (one correctly rounded division), qmax = 127
+ *     for int8 and 7 for int4; a group whose max|v| is 0 gets scale 0, codes 0;
+ *   - code = clamp(round_half_even(v / scale), -qmax, qmax) where v / scale is
+ *     one correctly rounded fp32 division; -128 never appears;
+ *   - per-group (group_size 64 or 128) groups run along K for the activation
+ *     AND the weight: y[m,n] = sum_g acc_g[m,n] * s_a[m,g] * s_w[n,g];
+ *   - int4: code c stored as nibble c + 8, byte j of a weight row holds code 2j
+ *     in its low nibble and code 2j+1 in its high nibble ([N, K/2] bytes);
+ *   - dequant: ((float)acc * s_a) * s_w in fp32 (per group: summed over groups
+ *     in fp32), rounded to nearest-even fp16. Outputs that overflow fp16 become
+ *     +-inf. Non-finite inputs give unspecified results.
+ *
+ * Conventions for every call below:
+ *   - All tensor arguments are DEVICE pointers to contiguous row-major arrays,
+ *     owned by the caller, and must be 16-byte aligned. The library never
+ *     allocates, frees, retains or synchronizes; it enqueues kernels on
+ *     `stream` (a hipStream_t; NULL = the legacy default stream) and returns.
+ *   - Arguments are validated before any HIP call is made. A bad argument
+ *     returns CIDER_ERROR_INVALID_VALUE and enqueues nothing; a device that is
+ *     not gfx950 returns CIDER_ERROR_NOT_SUPPORTED; a failed launch returns
+ *     CIDER_ERROR_LAUNCH. A kernel fault surfaces at the caller's next
+ *     synchronization, as usual in HIP.
+ *   - Zero-sized work (M == 0 or N == 0) returns CIDER_SUCCESS and launches
+ *     nothing; the pointers may then be NULL.
+ *   - K must be a positive multiple of 16 (of 32 for int4 weights) and at most
+ *     CIDER_MAX_K, which keeps |acc| = |sum of K products of codes| <= 127*127*K
+ *     below 2^31. Per-group calls need K % group_size == 0.
+ *   - Calls are reentrant; concurrent calls on different streams do not share
+ *     any library state (there is none beyond a cached device-architecture flag).
+ */
+#ifndef CIDER_H
+#define CIDER_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CIDER_MAX_K 133120 /* multiple of 128; 127*127*133120 < 2^31 */
+
+typedef enum {
+  CIDER_SUCCESS = 0,
+  CIDER_ERROR_INVALID_VALUE = 1,
+  CIDER_ERROR_NOT_SUPPORTED = 2,
+  CIDER_ERROR_LAUNCH = 3,
+} cider_status_t;
+
+/* 1 if the current HIP device is a gfx950 (MI355X-class) GPU, else 0.
+ * Mirrors the README's is_available() gate (section "条件编译"). */
+int cider_is_available(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char* cider_status_string(cider_status_t status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int cider_version(void);
+
+/* Online activation quantization (pipeline step "quantize_per_token").
+ *   x_f16   : fp16 [M, K] activations.
+ *   group_size : 0 = one scale per token (row); 64 or 128 = one scale per
+ *                run of group_size consecutive K elements of a row.
+ *   x_q     : int8 [M, K] codes (output).
+ *   x_scale : fp32 [M] (group_size 0) or [M, K/group_size] (output).
+ */
+cider_status_t cider_quant_act(const void* x_f16, int64_t M, int64_t K, int32_t group_size,
+                               int8_t* x_q, float* x_scale, void* stream);
+
+/* Weight quantization (the README runs it offline in numpy; here it is a
+ * device kernel with the same rule, not part of the timed linear).
+ *   w_f16   : fp16 [N, K] weights, row = output channel.
+ *   bits    : 8 or 4. bits 4 requires group_size 0 and K % 32 == 0.
+ *   w_q     : bits 8: int8 [N, K] codes; bits 4: uint8 [N, K/2] packed nibbles.
+ *   w_scale : fp32 [N] (group_size 0) or [N, K/group_size].
+ */
+cider_status_t cider_quant_weight(const void* w_f16, int64_t N, int64_t K, int32_t bits,
+                                  int32_t group_size, void* w_q, float* w_scale, void* stream);
+
+/* W8A8 GEMM with fused dequant (pipeline step "matmul_fused_dequant"):
+ *   y[m,n] = fp16( sum over groups of ((float)acc_g[m,n] * x_scale[m,g]) * w_scale[n,g] )
+ *   acc_g[m,n] = sum_{k in group g} x_q[m,k] * w_q[n,k] (exact int32).
+ *   x_q [M, K] int8, x_scale fp32 [M] or [M, K/gs]; w_q [N, K] int8,
+ *   w_scale fp32 [N] or [N, K/gs]; y_f16 fp16 [M, N] (output).
+ *   group_size must equal the one used to quantize both operands.
+ */
+cider_status_t cider_w8a8_gemm(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
+                               const float* w_scale, int64_t M, int64_t N, int64_t K,
+                               int32_t group_size, void* y_f16, void* stream);
+
+/* W4A8 GEMM with fused dequant: the int4 weights are unpacked to int8 codes
+ * (nibble - 8) inside the matmul's operand loads; per-channel scales only.
+ *   w_packed uint8 [N, K/2] (K % 32 == 0), w_scale fp32 [N]; the rest as above.
+ */
+cider_status_t cider_w4a8_gemm(const int8_t* x_q, const float* x_scale, const uint8_t* w_packed,
+                               const float* w_scale, int64_t M, int64_t N, int64_t K,
+                               void* y_f16, void* stream);
+
+/* Test hook: the same matmul main loops with an int32 store instead of the
+ * dequant, so the accumulators can be compared bit-exactly.
+ *   mode 0: w = int8 [N, K] codes; mode 1: w = packed int4 [N, K/2] (group_size 0).
+ *   acc: int32 [M, N] for group_size 0, else [K/group_size, M, N] (one slab per group).
+ */
+cider_status_t cider_gemm_acc_i32(int32_t mode, const int8_t* x_q, const void* w, int64_t M,
+                                  int64_t N, int64_t K, int32_t group_size, int32_t* acc,
+                                  void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CIDER_H */

@@ -1,0 +1,101 @@
+"""The C-ABI library loads, exports every symbol include/cider.h declares, and
+rejects bad arguments before touching HIP (no GPU needed)."""
+import ctypes
+
+import pytest
+
+from w8a8_online_quantized_amd import cider
+
+L = None
+
+
+def setup_module(_):
+    global L
+    L = cider.lib()
+
+
+def test_exports_every_header_symbol():
+    names = cider.header_entry_points()
+    assert set(names) == set(cider.SIGNATURES), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version():
+    for s in range(4):
+        assert L.cider_status_string(s)
+    assert b"unknown" in L.cider_status_string(99)
+    assert cider.cider_version() >= 100
+
+
+# A fake, 16-byte aligned, non-null device address: argument checks that fail
+# return before any HIP call, so it is never dereferenced.
+P = ctypes.c_void_p(1 << 20)
+MIS = ctypes.c_void_p((1 << 20) + 8)
+NULL = None
+INV = cider.CIDER_ERROR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("M,K,gs", [(-1, 64, 0), (4, 0, 0), (4, 8, 0), (4, 24, 0), (4, 96, 64),
+                                    (4, 128, 32), (4, 133120 + 128, 0)])
+def test_quant_act_rejects_bad_sizes(M, K, gs):
+    assert L.cider_quant_act(P, M, K, gs, P, P, NULL) == INV
+
+
+def test_quant_act_rejects_null_and_misaligned():
+    assert L.cider_quant_act(NULL, 4, 64, 0, P, P, NULL) == INV
+    assert L.cider_quant_act(P, 4, 64, 0, NULL, P, NULL) == INV
+    assert L.cider_quant_act(P, 4, 64, 0, P, NULL, NULL) == INV
+    assert L.cider_quant_act(MIS, 4, 64, 0, P, P, NULL) == INV
+    assert L.cider_quant_act(P, 4, 64, 0, MIS, P, NULL) == INV
+
+
+def test_empty_work_is_success_without_pointers():
+    assert L.cider_quant_act(NULL, 0, 64, 0, NULL, NULL, NULL) == 0
+    assert L.cider_quant_weight(NULL, 0, 64, 8, 0, NULL, NULL, NULL) == 0
+    assert L.cider_w8a8_gemm(NULL, NULL, NULL, NULL, 0, 16, 64, 0, NULL, NULL) == 0
+    assert L.cider_w8a8_gemm(NULL, NULL, NULL, NULL, 16, 0, 64, 0, NULL, NULL) == 0
+    assert L.cider_w4a8_gemm(NULL, NULL, NULL, NULL, 0, 16, 64, NULL, NULL) == 0
+    assert L.cider_gemm_acc_i32(0, NULL, NULL, 0, 4, 64, 0, NULL, NULL) == 0
+
+
+def test_quant_weight_rejects():
+    assert L.cider_quant_weight(P, 4, 64, 6, 0, P, P, NULL) == INV        # bits
+    assert L.cider_quant_weight(P, 4, 64, 4, 64, P, P, NULL) == INV       # int4 is per-channel
+    assert L.cider_quant_weight(P, 4, 48, 4, 0, P, P, NULL) == INV        # int4 needs K % 32
+    assert L.cider_quant_weight(P, 4, 192, 8, 128, P, P, NULL) == INV     # K % gs
+    assert L.cider_quant_weight(P, 4, 64, 8, 0, P, MIS, NULL) == INV
+
+
+def test_gemm_rejects():
+    g = L.cider_w8a8_gemm
+    assert g(P, P, P, P, -1, 4, 64, 0, P, NULL) == INV
+    assert g(P, P, P, P, 4, -1, 64, 0, P, NULL) == INV
+    assert g(P, P, P, P, 4, 4, 40, 0, P, NULL) == INV
+    assert g(P, P, P, P, 4, 4, 192, 128, P, NULL) == INV
+    assert g(P, P, P, P, 4, 4, 128, 100, P, NULL) == INV
+    assert g(P, P, P, P, 4, 4, 1 << 20, 0, P, NULL) == INV               # int32 range guard
+    assert g(NULL, P, P, P, 4, 4, 64, 0, P, NULL) == INV
+    assert g(P, P, P, P, 4, 4, 64, 0, NULL, NULL) == INV
+    assert g(P, P, P, MIS, 4, 4, 64, 0, P, NULL) == INV
+    h = L.cider_w4a8_gemm
+    assert h(P, P, P, P, 4, 4, 48, P, NULL) == INV
+    assert h(P, P, MIS, P, 4, 4, 64, P, NULL) == INV
+    a = L.cider_gemm_acc_i32
+    assert a(2, P, P, 4, 4, 64, 0, P, NULL) == INV
+    assert a(1, P, P, 4, 4, 64, 64, P, NULL) == INV
+    assert a(0, P, P, 4, 4, 64, 0, NULL, NULL) == INV
+
+
+def test_not_available_without_gpu():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    assert cider.cider_is_available() is False
+
+
+def test_max_k_constant_keeps_int32_range():
+    import re
+    with open(cider.HEADER_PATH) as f:
+        k = int(re.search(r"#define CIDER_MAX_K (\d+)", f.read()).group(1))
+    assert 127 * 127 * k < 2 ** 31 and k % 128 == 0

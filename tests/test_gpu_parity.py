@@ -1,0 +1,280 @@
+"""HIP path (through the C ABI) against the CPU oracle, element by element.
+
+Codes, scales, packed bytes and int32 accumulators must match bit for bit;
+fp16 outputs must satisfy |y - o| <= 1e-3*|o| + 2^-14 (per-channel, W4A8) or
+|y - o| <= 2e-3*|o| + e_sum + 2^-14 (per-group, e_sum = the fp32 summation
+error bound (G+3)*2^-24*sum_g|term_g|), where o is the oracle's exactly
+rounded output. Per-channel and W4A8 outputs are also held to at most one
+fp16 ulp from o (the kernel rounds two fp32 products, the oracle none).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from w8a8_online_quantized_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def cider():
+    from w8a8_online_quantized_amd import cider as c
+    if not c.cider_is_available():
+        pytest.fail("libcider reports no gfx950 device")
+    return c
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def ulp_distance(a, b):
+    """Distance in fp16 ulps (sign-magnitude ordering), for finite values."""
+    def key(x):
+        u = x.view(np.uint16).astype(np.int32)
+        return np.where(u & 0x8000, -(u & 0x7FFF), u & 0x7FFF)
+    return np.abs(key(a) - key(b))
+
+
+def assert_y_close(y, o, rtol, extra_atol=0.0, max_ulp=None, what=""):
+    y64, o64 = y.astype(np.float64), o.astype(np.float64)
+    tol = rtol * np.abs(o64) + 2.0 ** -14 + extra_atol
+    err = np.abs(y64 - o64)
+    bad = err > tol
+    assert not bad.any(), f"{what}: {int(bad.sum())} outputs out of tolerance, worst {float((err - tol).max())}"
+    if max_ulp is not None:
+        u = ulp_distance(y, o)
+        assert int(u.max()) <= max_ulp, f"{what}: max ulp distance {int(u.max())}"
+
+
+def pg_sum_bound(qa, sa, qw, sw, gs, rows):
+    """(G+3)*2^-24*sum_g |acc_g*s_a*s_w| for the sampled rows."""
+    accg = oracle.int_dot_groups(qa[rows], qw, gs).astype(np.float64)
+    terms = np.abs(accg) * sa[rows].T.astype(np.float64)[:, :, None] * sw.T.astype(np.float64)[:, None, :]
+    G = accg.shape[0]
+    return (G + 3) * 2.0 ** -24 * terms.sum(axis=0)
+
+
+# ------------------------------------------------------------------ quantization
+QUANT_SHAPES = [(1, 16, 0), (7, 48, 0), (37, 2560, 0), (130, 1040, 0), (5, 10240, 0), (3, 16384, 0),
+                (2, 20480, 0), (64, 256, 64), (33, 1024, 128), (9, 10240, 64), (4, 10240, 128),
+                (2, 32768, 128), (3, 17408, 64)]
+
+
+@pytest.mark.parametrize("M,K,gs", QUANT_SHAPES)
+def test_quant_act_bit_exact(M, K, gs):
+    c = cider()
+    x = inputs.activations(M, K, seed=M + K)
+    q, s = c.cider_quant_act(dev(x), gs)
+    qo, so = oracle.quantize_act(x, gs)
+    assert np.array_equal(host(q), qo)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+
+
+def test_quant_act_special_rows():
+    """Ties, division-sensitive rows, zero rows, subnormal and huge magnitudes."""
+    import json, os
+    c = cider()
+    golden = os.path.join(os.path.dirname(__file__), "golden")
+    rows = []
+    for case in json.load(open(os.path.join(golden, "quant_ties.json")))["cases"]:
+        if case["qmax"] == 127 and case["group_size"] == 0:
+            rows.append(case["x"])
+    for case in json.load(open(os.path.join(golden, "division_cases.json")))["cases"]:
+        rows.append(case["x"])
+    K = 64
+    X = np.zeros((len(rows) + 4, K), np.float16)
+    for i, r in enumerate(rows):
+        X[i, :len(r)] = r
+    rng = np.random.default_rng(5)
+    X[-4] = 0                                                   # all-zero row
+    X[-3] = (rng.standard_normal(K) * 2.0 ** -20).astype(np.float16)   # subnormal fp16
+    X[-2] = np.clip(rng.standard_normal(K) * 20000, -65504, 65504).astype(np.float16)  # near fp16 max
+    X[-1] = np.float16(-0.0)
+    q, s = c.cider_quant_act(dev(X), 0)
+    qo, so = oracle.quantize_act(X, 0)
+    assert np.array_equal(host(q), qo)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+
+
+def test_quant_act_all_fp16_magnitudes_against_division():
+    """Every finite fp16 value v with |v| <= A as an element of rows whose
+    largest magnitude is A, for several A (each row ends with A itself)."""
+    c = cider()
+    allv = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16)   # finite, non-negative
+    K = 1024
+    rows = []
+    for A in (np.float16(1.0), np.float16(3.0), np.float16(100.0), np.float16(60000.0),
+              np.float16(0.01), np.float16(2.095703125)):
+        vals = allv[allv <= A]
+        vals = np.concatenate([vals, -vals])
+        for i in range(0, len(vals), K - 1):
+            r = np.zeros(K, np.float16)
+            part = vals[i:i + K - 1]
+            r[:len(part)] = part
+            r[K - 1] = A
+            rows.append(r)
+    X = np.stack(rows)
+    q, s = c.cider_quant_act(dev(X), 0)
+    qo, so = oracle.quantize_act(X, 0)
+    assert np.array_equal(host(q), qo)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+
+
+@pytest.mark.parametrize("N,K,bits,gs", [(10, 64, 8, 0), (300, 2560, 8, 0), (129, 1024, 8, 64),
+                                         (64, 10240, 8, 128), (77, 2560, 4, 0), (5, 32, 4, 0),
+                                         (3, 20480, 4, 0)])
+def test_quant_weight_bit_exact(N, K, bits, gs):
+    c = cider()
+    w = inputs.weights(N, K, seed=N)
+    q, s = c.cider_quant_weight(dev(w), bits, gs)
+    qo, so = oracle.quantize_weight(w, bits, gs)
+    assert np.array_equal(host(q), qo)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+
+
+# ------------------------------------------------------------------ accumulators
+ACC_SHAPES = [(1, 1, 16), (3, 5, 48), (17, 33, 80), (64, 64, 64), (65, 63, 1040), (300, 520, 1040),
+              (129, 257, 2560), (600, 700, 512), (1030, 770, 320)]
+
+
+def _codes(rng, shape):
+    return rng.integers(-127, 128, size=shape).astype(np.int8)
+
+
+@pytest.mark.parametrize("M,N,K", ACC_SHAPES)
+def test_acc_i32_w8a8_bit_exact(M, N, K):
+    c = cider()
+    rng = np.random.default_rng(M * 7 + N)
+    qa, qw = _codes(rng, (M, K)), _codes(rng, (N, K))
+    acc = c.cider_gemm_acc_i32(0, dev(qa), dev(qw))
+    assert np.array_equal(host(acc), oracle.int_dot(qa, qw))
+
+
+def test_acc_i32_extreme_codes_k10240():
+    """All codes +-127 at K = 10240: |acc| reaches 127*127*10240 > 2^27."""
+    c = cider()
+    K = 10240
+    qa = np.full((70, K), 127, np.int8)
+    qa[1::2] = -127
+    qw = np.full((90, K), 127, np.int8)
+    qw[5, 17] = 1
+    acc = host(c.cider_gemm_acc_i32(0, dev(qa), dev(qw)))
+    ref = oracle.int_dot(qa, qw)
+    assert np.array_equal(acc, ref)
+    assert acc[0, 0] == 165160960 and acc[0, 5] == 165144958
+
+
+@pytest.mark.parametrize("M,N,K,gs", [(5, 7, 128, 64), (70, 130, 1024, 128), (300, 200, 1152, 64),
+                                      (520, 260, 640, 128)])
+def test_acc_i32_per_group_bit_exact(M, N, K, gs):
+    c = cider()
+    rng = np.random.default_rng(M + N + gs)
+    qa, qw = _codes(rng, (M, K)), _codes(rng, (N, K))
+    acc = c.cider_gemm_acc_i32(0, dev(qa), dev(qw), gs)
+    assert np.array_equal(host(acc), oracle.int_dot_groups(qa, qw, gs))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 3, 32), (20, 17, 96), (70, 130, 1056), (600, 300, 2560)])
+def test_acc_i32_w4a8_bit_exact(M, N, K):
+    c = cider()
+    rng = np.random.default_rng(M + N)
+    qa = _codes(rng, (M, K))
+    q4 = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    acc = c.cider_gemm_acc_i32(1, dev(qa), dev(oracle.pack_int4(q4)))
+    assert np.array_equal(host(acc), oracle.int_dot(qa, q4))
+
+
+# ------------------------------------------------------------------ fused outputs
+def _pc_case(M, N, K, seed=0):
+    x = inputs.activations(M, K, seed=seed)
+    w = inputs.weights(N, K, seed=seed)
+    return x, w
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 10240, 2560), (3, 5, 16), (33, 100, 1040), (128, 1024, 2560),
+                                   (300, 520, 1040), (700, 900, 2048), (64, 63, 10240)])
+def test_w8a8_per_channel_outputs(M, N, K):
+    c = cider()
+    x, w = _pc_case(M, N, K)
+    wq, sw = c.cider_quant_weight(dev(w), 8, 0)
+    xq, sa = c.cider_quant_act(dev(x), 0)
+    y = host(c.cider_w8a8_gemm(xq, sa, wq, sw, 0))
+    wqo, swo = oracle.quantize_weight(w)
+    yo, qo, _ = oracle.w8a8_linear(x, wqo, swo, 0)
+    assert np.array_equal(host(xq), qo)
+    assert_y_close(y, yo, 1e-3, max_ulp=1, what=f"pc {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K,gs", [(3, 5, 128, 64), (33, 100, 1024, 128), (130, 300, 1152, 64),
+                                      (520, 260, 2560, 128)])
+def test_w8a8_per_group_outputs(M, N, K, gs):
+    c = cider()
+    x, w = _pc_case(M, N, K, seed=1)
+    wq, sw = c.cider_quant_weight(dev(w), 8, gs)
+    xq, sa = c.cider_quant_act(dev(x), gs)
+    y = host(c.cider_w8a8_gemm(xq, sa, wq, sw, gs))
+    wqo, swo = oracle.quantize_weight(w, 8, gs)
+    yo, qo, sao = oracle.w8a8_linear(x, wqo, swo, gs)
+    rows = np.arange(M)
+    e = pg_sum_bound(qo, sao, wqo, swo, gs, rows)
+    assert_y_close(y, yo, 2e-3, extra_atol=e, what=f"pg{gs} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 77, 64), (5, 3, 32), (40, 100, 1056), (300, 520, 2560)])
+def test_w4a8_outputs(M, N, K):
+    c = cider()
+    x, w = _pc_case(M, N, K, seed=2)
+    wp, sw = c.cider_quant_weight(dev(w), 4, 0)
+    xq, sa = c.cider_quant_act(dev(x), 0)
+    y = host(c.cider_w4a8_gemm(xq, sa, wp, sw))
+    wpo, swo = oracle.quantize_weight(w, 4, 0)
+    assert np.array_equal(host(wp), wpo)
+    yo, _, _ = oracle.w4a8_linear(x, wpo, swo)
+    assert_y_close(y, yo, 1e-3, max_ulp=1, what=f"w4a8 {M}x{N}x{K}")
+    # the same product through the int8 kernel with unpacked codes: bit-identical
+    y8 = host(c.cider_w8a8_gemm(xq, sa, dev(oracle.unpack_int4(wpo)), sw, 0))
+    assert np.array_equal(y.view(np.uint16), y8.view(np.uint16))
+
+
+def test_deterministic_repeats():
+    c = cider()
+    x, w = _pc_case(1024, 2048, 2560, seed=3)
+    wq, sw = c.cider_quant_weight(dev(w), 8, 0)
+    xq, sa = c.cider_quant_act(dev(x), 0)
+    y0 = host(c.cider_w8a8_gemm(xq, sa, wq, sw, 0))
+    for _ in range(20):
+        y = c.cider_w8a8_gemm(xq, sa, wq, sw, 0)
+        assert np.array_equal(host(y).view(np.uint16), y0.view(np.uint16))
+
+
+def test_empty_inputs():
+    c = cider()
+    x = torch.empty((0, 64), dtype=torch.float16, device="cuda")
+    q, s = c.cider_quant_act(x, 0)
+    assert q.shape == (0, 64)
+    w = dev(inputs.weights(8, 64))
+    wq, sw = c.cider_quant_weight(w, 8, 0)
+    y = c.cider_w8a8_gemm(q, s, wq, sw, 0)
+    assert y.shape == (0, 8)
+    torch.cuda.synchronize()
+
+
+def test_stream_ordering_on_side_stream():
+    """Calls enqueue on the caller's stream and nothing else."""
+    c = cider()
+    x, w = _pc_case(256, 512, 1024, seed=4)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        xd, wd = dev(x), dev(w)
+        wq, sw = c.cider_quant_weight(wd, 8, 0)
+        y = c.w8a8_linear(xd, wq, sw, 0)
+    s.synchronize()
+    yo, _, _ = oracle.w8a8_linear(x, *oracle.quantize_weight(w), 0)
+    assert_y_close(y.cpu().numpy(), yo, 1e-3, max_ulp=1, what="side stream")

@@ -1,0 +1,211 @@
+"""Python binding of libcider (include/cider.h): argument marshalling only.
+
+Each function has the name of the C entry point it calls and takes torch
+tensors that already live on the GPU (PyTorch is used for device memory and
+the current stream, nothing else). Every step of the computation runs in the
+HIP kernels of libcider.so; if the library is missing, or the device is not a
+gfx950, the call raises instead of computing anything some other way.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libcider.so")
+HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "cider.h")
+
+CIDER_SUCCESS = 0
+CIDER_ERROR_INVALID_VALUE = 1
+CIDER_ERROR_NOT_SUPPORTED = 2
+CIDER_ERROR_LAUNCH = 3
+
+_c_i64, _c_i32, _c_p = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+
+# (restype, argtypes) of every entry point declared in include/cider.h
+SIGNATURES = {
+    "cider_is_available": (ctypes.c_int, []),
+    "cider_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "cider_version": (ctypes.c_int, []),
+    "cider_quant_act": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i32, _c_p, _c_p, _c_p]),
+    "cider_quant_weight": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_p]),
+    "cider_w8a8_gemm": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p]),
+    "cider_w4a8_gemm": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p]),
+    "cider_gemm_acc_i32": (ctypes.c_int, [_c_i32, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p]),
+}
+
+_lib = None
+
+
+class CiderError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def header_entry_points(path: str = HEADER_PATH):
+    """Names of the functions include/cider.h declares."""
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cider_[a-z0-9_]+)\s*\(", text)))
+
+
+def lib() -> ctypes.CDLL:
+    """Load libcider.so (built in-tree by w8a8_online_quantized_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m w8a8_online_quantized_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().cider_status_string(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != CIDER_SUCCESS:
+        raise CiderError(fn, status, status_string(status))
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, dtype, shape, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def cider_is_available() -> bool:
+    return bool(lib().cider_is_available())
+
+
+def cider_version() -> int:
+    return int(lib().cider_version())
+
+
+def _scale_shape(rows, K, group_size):
+    return (rows,) if group_size == 0 else (rows, K // group_size)
+
+
+def cider_quant_act(x, group_size: int = 0, x_q=None, x_scale=None, stream=None):
+    """fp16 [M, K] -> (int8 codes [M, K], fp32 scales [M] or [M, K/gs])."""
+    import torch
+    M, K = x.shape
+    _need(x, torch.float16, (M, K), "x")
+    if x_q is None:
+        x_q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if x_scale is None:
+        x_scale = torch.empty(_scale_shape(M, K, group_size), dtype=torch.float32, device=x.device)
+    _need(x_q, torch.int8, (M, K), "x_q")
+    _need(x_scale, torch.float32, _scale_shape(M, K, group_size), "x_scale")
+    _check("cider_quant_act", lib().cider_quant_act(_ptr(x), M, K, group_size, _ptr(x_q), _ptr(x_scale),
+                                                    _stream(stream)))
+    return x_q, x_scale
+
+
+def cider_quant_weight(w, bits: int = 8, group_size: int = 0, w_q=None, w_scale=None, stream=None):
+    """fp16 [N, K] -> (int8 [N, K] or packed uint8 [N, K/2], fp32 scales)."""
+    import torch
+    N, K = w.shape
+    _need(w, torch.float16, (N, K), "w")
+    qshape = (N, K) if bits == 8 else (N, K // 2)
+    qdtype = torch.int8 if bits == 8 else torch.uint8
+    if w_q is None:
+        w_q = torch.empty(qshape, dtype=qdtype, device=w.device)
+    if w_scale is None:
+        w_scale = torch.empty(_scale_shape(N, K, group_size), dtype=torch.float32, device=w.device)
+    _need(w_q, qdtype, qshape, "w_q")
+    _need(w_scale, torch.float32, _scale_shape(N, K, group_size), "w_scale")
+    _check("cider_quant_weight", lib().cider_quant_weight(_ptr(w), N, K, bits, group_size, _ptr(w_q),
+                                                          _ptr(w_scale), _stream(stream)))
+    return w_q, w_scale
+
+
+def cider_w8a8_gemm(x_q, x_scale, w_q, w_scale, group_size: int = 0, y=None, stream=None):
+    """int8 codes + scales -> fp16 y [M, N] (fused dequant)."""
+    import torch
+    M, K = x_q.shape
+    N = w_q.shape[0]
+    _need(x_q, torch.int8, (M, K), "x_q")
+    _need(w_q, torch.int8, (N, K), "w_q")
+    if group_size and K % group_size:
+        raise ValueError("K must be a multiple of group_size")
+    _need(x_scale, torch.float32, _scale_shape(M, K, group_size), "x_scale")
+    _need(w_scale, torch.float32, _scale_shape(N, K, group_size), "w_scale")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x_q.device)
+    _need(y, torch.float16, (M, N), "y")
+    _check("cider_w8a8_gemm", lib().cider_w8a8_gemm(_ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale),
+                                                    M, N, K, group_size, _ptr(y), _stream(stream)))
+    return y
+
+
+def cider_w4a8_gemm(x_q, x_scale, w_packed, w_scale, y=None, stream=None):
+    """int8 activation codes x packed int4 weights -> fp16 y [M, N]."""
+    import torch
+    M, K = x_q.shape
+    N = w_packed.shape[0]
+    _need(x_q, torch.int8, (M, K), "x_q")
+    _need(w_packed, torch.uint8, (N, K // 2), "w_packed")
+    _need(x_scale, torch.float32, (M,), "x_scale")
+    _need(w_scale, torch.float32, (N,), "w_scale")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x_q.device)
+    _need(y, torch.float16, (M, N), "y")
+    _check("cider_w4a8_gemm", lib().cider_w4a8_gemm(_ptr(x_q), _ptr(x_scale), _ptr(w_packed), _ptr(w_scale),
+                                                    M, N, K, _ptr(y), _stream(stream)))
+    return y
+
+
+def cider_gemm_acc_i32(mode: int, x_q, w, group_size: int = 0, acc=None, stream=None):
+    """int32 accumulators of the GEMM main loop: [M, N], or [G, M, N] per group."""
+    import torch
+    M, K = x_q.shape
+    N = w.shape[0]
+    _need(x_q, torch.int8, (M, K), "x_q")
+    if mode == 0:
+        _need(w, torch.int8, (N, K), "w")
+    else:
+        _need(w, torch.uint8, (N, K // 2), "w")
+    shape = (M, N) if group_size == 0 else (K // group_size, M, N)
+    if acc is None:
+        acc = torch.empty(shape, dtype=torch.int32, device=x_q.device)
+    _need(acc, torch.int32, shape, "acc")
+    _check("cider_gemm_acc_i32", lib().cider_gemm_acc_i32(mode, _ptr(x_q), _ptr(w), M, N, K, group_size,
+                                                          _ptr(acc), _stream(stream)))
+    return acc
+
+
+def w8a8_linear(x, w_q, w_scale, group_size: int = 0, stream=None):
+    """The README's per-channel / per-group linear: quantize x, then the fused GEMM."""
+    x_q, x_scale = cider_quant_act(x, group_size, stream=stream)
+    return cider_w8a8_gemm(x_q, x_scale, w_q, w_scale, group_size, stream=stream)
+
+
+def w4a8_linear(x, w_packed, w_scale, stream=None):
+    """The README's W4A8 linear: per-token int8 activations times packed int4 weights."""
+    x_q, x_scale = cider_quant_act(x, 0, stream=stream)
+    return cider_w4a8_gemm(x_q, x_scale, w_packed, w_scale, stream=stream)

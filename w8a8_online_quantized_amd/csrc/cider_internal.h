@@ -1,0 +1,35 @@
+// Internal declarations shared by the HIP translation units of libcider.
+// Nothing here is part of the public ABI (include/cider.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cider {
+
+// Launches the activation / weight quantization kernel.
+//   x: fp16 [R, K]; qmax 127 (int8 codes into q8 [R, K]) or 7 (packed int4
+//   codes into q4 [R, K/2]); s: fp32 [R, G].
+hipError_t launch_quant_rows(const void* x, int64_t R, int64_t K, int group_size, int qmax,
+                             void* q, float* s, hipStream_t stream);
+
+// Epilogue kinds of the GEMM kernels.
+enum Epilogue { kEpiF16 = 0, kEpiAccI32 = 1 };
+
+// Weight encodings of the GEMM kernels.
+enum WeightKind { kWeightI8 = 0, kWeightI4 = 1 };
+
+struct GemmArgs {
+  const int8_t* a;   // activation codes [M, K]
+  const float* sa;   // activation scales [M] or [M, G]
+  const void* w;     // weight codes [N, K] int8 or packed [N, K/2]
+  const float* sw;   // weight scales [N] or [N, G]
+  int64_t M, N, K;
+  int group_size;    // 0, 64, 128
+  void* y;           // fp16 [M, N]
+  int32_t* acc;      // int32 [M, N] or [G, M, N] (accumulator test hook)
+};
+
+hipError_t launch_gemm(const GemmArgs& args, WeightKind wk, Epilogue epi, hipStream_t stream);
+
+}  // namespace cider

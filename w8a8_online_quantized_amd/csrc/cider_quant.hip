@@ -1,0 +1,217 @@
+// Online symmetric quantization of fp16 rows to int8 (or packed int4) codes.
+//
+// Follows the Cider README, section "架构 / Metal Kernel 流水线" (the first
+// prefill step turns fp16 activations into int8 codes plus one scale per
+// token) and section "量化" (symmetric INT8 per-token activations; symmetric
+// INT8 or zero-point-8 INT4 weights). Per-group scales (section "W8A8 量化粒度",
+// gs = 64 / 128) use the same rule on each run of gs elements along K.
+//
+// Rule (one group = a row, or gs consecutive elements of a row):
+//   s = max|v| / qmax              (fp32, one correctly rounded division)
+//   q = clamp(rint(v / s), +-qmax) (v / s one correctly rounded fp32 division,
+//                                   rint = ties to even); s == 0 -> q = 0.
+//
+// HBM-bound: 2 bytes read, 1 (or 0.5) byte written per element. One wave owns
+// one row; each lane owns 16-byte chunks (8 fp16) at a 64-chunk stride, so a
+// wave load instruction covers 1 KiB of contiguous row. The row stays in
+// registers between the max pass and the code pass.
+//
+// The division v / s costs a ~10-instruction correctly rounded sequence; with
+// 8 elements per chunk it would make the kernel ALU-bound. Instead each code
+// is first formed from r = v * fl(1/s). |r - fl(v/s)| <= 3 * 2^-24 * 128 <
+// 2.3e-5, so when r is at least 2^-13 away from every half-integer both values
+// round to the same integer; only the rare remaining elements take the exact
+// division. The result is bit-identical to always dividing.
+#include "cider_internal.h"
+
+namespace cider {
+namespace {
+
+constexpr int kWaves = 4;                 // waves (rows) per workgroup
+constexpr float kNearHalf = 0.4998779296875f;   // 0.5 - 2^-13
+
+__device__ __forceinline__ uint32_t abs_max_bits(uint4 v) {
+  // fp16 magnitudes compare like their 15-bit patterns (finite inputs).
+  uint32_t m = 0;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a = w[i] & 0x7FFF7FFFu;
+    m = max(m, max(a & 0xFFFFu, a >> 16));
+  }
+  return m;
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)bits);
+}
+
+// Code of one element given the group scale s (> 0) and inv = fl(1/s).
+__device__ __forceinline__ int code_of(float v, float s, float inv, float qmax) {
+  const float r = v * inv;
+  float t = __builtin_rintf(r);
+  if (__builtin_fabsf(r - t) > kNearHalf) t = __builtin_rintf(v / s);
+  t = __builtin_fminf(__builtin_fmaxf(t, -qmax), qmax);
+  return (int)t;
+}
+
+// 8 codes of one 16-byte chunk (8 fp16 values).
+__device__ __forceinline__ void codes_of_chunk(uint4 v, float s, float inv, float qmax, int q[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    q[2 * i] = code_of(half_bits_to_float(w[i] & 0xFFFFu), s, inv, qmax);
+    q[2 * i + 1] = code_of(half_bits_to_float(w[i] >> 16), s, inv, qmax);
+  }
+}
+
+__device__ __forceinline__ void store_codes(void* q, int64_t row, int64_t K, int chunk, bool pack4,
+                                            const int c[8]) {
+  if (!pack4) {
+    uint2 o;
+    o.x = (c[0] & 0xFF) | ((c[1] & 0xFF) << 8) | ((c[2] & 0xFF) << 16) | ((uint32_t)(c[3] & 0xFF) << 24);
+    o.y = (c[4] & 0xFF) | ((c[5] & 0xFF) << 8) | ((c[6] & 0xFF) << 16) | ((uint32_t)(c[7] & 0xFF) << 24);
+    *reinterpret_cast<uint2*>(static_cast<int8_t*>(q) + row * K + (int64_t)chunk * 8) = o;
+  } else {
+    // nibble j holds code j + 8: low nibble of byte b = even k, high = odd k
+    uint32_t o = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o |= (uint32_t)(c[j] + 8) << (4 * j);
+    *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(q) + row * (K / 2) + (int64_t)chunk * 4) = o;
+  }
+}
+
+// One wave per row, row held in registers: CPL = 16-byte chunks per lane.
+// GS = 0 (one scale per row; the whole row, K <= 512 * CPL, is one segment)
+// or 64 / 128 (groups never straddle a segment, so long rows are split into
+// segments of kSegChunks chunks along gridDim.y).
+constexpr int kSegChunks = 64 * 32;
+
+template <int CPL, int GS>
+__global__ __launch_bounds__(64 * kWaves) void quant_rows_reg(const uint4* __restrict__ x, int64_t R,
+                                                              int64_t K, float qmax, bool pack4,
+                                                              void* __restrict__ q,
+                                                              float* __restrict__ s) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (row >= R) return;
+  const int C = (int)(K / 8);
+  const int c0 = (int)blockIdx.y * kSegChunks;          // first chunk of this segment
+  const int cend = min(C, c0 + kSegChunks);
+  const uint4* xr = x + row * C;
+
+  uint4 v[CPL];
+  uint32_t m[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = c0 + lane + 64 * i;
+    v[i] = c < cend ? xr[c] : make_uint4(0, 0, 0, 0);
+    m[i] = abs_max_bits(v[i]);
+  }
+
+  if constexpr (GS == 0) {
+    uint32_t a = 0;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) a = max(a, m[i]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) a = max(a, (uint32_t)__shfl_xor((int)a, off));
+    const float amax = half_bits_to_float(a);
+    const float sc = amax / qmax;
+    if (lane == 0) s[row] = sc;
+    const float inv = 1.0f / sc;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = c0 + lane + 64 * i;
+      if (c < cend) {
+        int cq[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (sc != 0.0f) codes_of_chunk(v[i], sc, inv, qmax, cq);
+        store_codes(q, row, K, c, pack4, cq);
+      }
+    }
+  } else {
+    constexpr int kCpg = GS / 8;   // chunks per group: 8 or 16 lanes
+    const int G = (int)(K / GS);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      uint32_t a = m[i];
+#pragma unroll
+      for (int off = kCpg / 2; off >= 1; off >>= 1) a = max(a, (uint32_t)__shfl_xor((int)a, off));
+      const int c = c0 + lane + 64 * i;
+      if (c < cend) {
+        const float amax = half_bits_to_float(a);
+        const float sc = amax / qmax;
+        if ((lane & (kCpg - 1)) == 0) s[row * G + c / kCpg] = sc;
+        const float inv = 1.0f / sc;
+        int cq[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (sc != 0.0f) codes_of_chunk(v[i], sc, inv, qmax, cq);
+        store_codes(q, row, K, c, pack4, cq);
+      }
+    }
+  }
+}
+
+// Rows longer than the register path holds (per-row scale only): one
+// workgroup per row reads the row twice, first for max|v|, then for codes.
+__global__ __launch_bounds__(256) void quant_rows_two_pass(const uint4* __restrict__ x, int64_t K,
+                                                           float qmax, bool pack4, void* __restrict__ q,
+                                                           float* __restrict__ s) {
+  __shared__ uint32_t red[4];
+  const int64_t row = blockIdx.x;
+  const int C = (int)(K / 8);
+  const uint4* xr = x + row * C;
+  uint32_t a = 0;
+  for (int c = threadIdx.x; c < C; c += 256) a = max(a, abs_max_bits(xr[c]));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) a = max(a, (uint32_t)__shfl_xor((int)a, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+  __syncthreads();
+  a = max(max(red[0], red[1]), max(red[2], red[3]));
+  const float sc = half_bits_to_float(a) / qmax;
+  if (threadIdx.x == 0) s[row] = sc;
+  const float inv = 1.0f / sc;
+  for (int c = threadIdx.x; c < C; c += 256) {
+    int cq[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (sc != 0.0f) codes_of_chunk(xr[c], sc, inv, qmax, cq);
+    store_codes(q, row, K, c, pack4, cq);
+  }
+}
+
+template <int GS>
+hipError_t launch_reg(int cpl, int segs, const uint4* x, int64_t R, int64_t K, float qmax, bool pack4,
+                      void* q, float* s, hipStream_t st) {
+  const dim3 grid((unsigned)((R + kWaves - 1) / kWaves), (unsigned)segs), block(64 * kWaves);
+  switch (cpl) {
+    case 1: quant_rows_reg<1, GS><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
+    case 2: quant_rows_reg<2, GS><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
+    case 4: quant_rows_reg<4, GS><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
+    case 8: quant_rows_reg<8, GS><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
+    case 16: quant_rows_reg<16, GS><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
+    default: quant_rows_reg<32, GS><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_rows(const void* x, int64_t R, int64_t K, int group_size, int qmax, void* q,
+                             float* s, hipStream_t stream) {
+  const uint4* xv = static_cast<const uint4*>(x);
+  const bool pack4 = qmax == 7;
+  const float fq = (float)qmax;
+  const int64_t C = K / 8;
+  if (group_size == 0 && C > kSegChunks) {
+    quant_rows_two_pass<<<dim3((unsigned)R), dim3(256), 0, stream>>>(xv, K, fq, pack4, q, s);
+    return hipGetLastError();
+  }
+  const int64_t segs = (C + kSegChunks - 1) / kSegChunks;
+  const int64_t per_seg = segs > 1 ? kSegChunks : C;
+  int cpl = 1;
+  while (64 * cpl < per_seg) cpl *= 2;
+  switch (group_size) {
+    case 0: return launch_reg<0>(cpl, 1, xv, R, K, fq, pack4, q, s, stream);
+    case 64: return launch_reg<64>(cpl, (int)segs, xv, R, K, fq, pack4, q, s, stream);
+    default: return launch_reg<128>(cpl, (int)segs, xv, R, K, fq, pack4, q, s, stream);
+  }
+}
+
+}  // namespace cider
