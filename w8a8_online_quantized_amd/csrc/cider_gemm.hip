@@ -153,6 +153,232 @@ struct Int4TileLoader {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Direct-to-LDS pipeline (per-channel and W4A8).
+//
+// Each stage moves BK codes of every tile row from global memory straight
+// into LDS with buffer_load_dwordx4 ... lds (one wave instruction fills one
+// contiguous KiB of LDS), NS stages deep, so the loads of stage k+NS-1 are in
+// flight while the MFMAs of stage k run. The buffer descriptor covers exactly
+// the valid rows of the tile; chunks past K get an out-of-range offset, so
+// every out-of-bounds element arrives as 0 without a branch. Stage order is
+// kept with s_waitcnt vmcnt (own loads) followed by s_barrier (everyone's).
+// ---------------------------------------------------------------------------
+
+// Physical 16-byte slot of logical chunk c in tile row r, for rows of RB bytes.
+// Both XOR patterns were chosen by measurement on gfx950 (64 LDS banks): with
+// them the fragment reads of 16 consecutive rows (one chunk per 16-lane group)
+// complete in 4 cycles per ds_read_b128 with no bank-conflict cycles, while
+// e.g. c ^ (r & 3) or c ^ (((r >> 1) ^ (r >> 3)) & 3) on 64-byte rows take 8.
+template <int RB>
+__device__ __forceinline__ int slot_of(int r, int c) {
+  if constexpr (RB == 64) return c ^ ((r >> 1) & 3);
+  else return c ^ (r & 7);
+}
+
+template <int RB>
+__device__ __forceinline__ int tile_off(int r, int c) { return r * RB + (slot_of<RB>(r, c) << 4); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // dword 3 = 0x00020000: raw buffer, 32-bit data format (gfx9 family)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Issue the DMA loads of one stage of a ROWS x RB-byte operand tile. Block j
+// of 1 KiB holds rows j*(1024/RB) ...; lane L writes LDS bytes L*16..L*16+15
+// of its block, i.e. physical slot L % (RB/16) of block row L / (RB/16).
+template <int ROWS, int RB, int NW>
+__device__ __forceinline__ void dma_stage(__amdgpu_buffer_rsrc_t rsrc, int8_t* lds, int wave, int lane,
+                                          uint32_t ld, int kb0, int kb_total) {
+  constexpr int kBlocks = ROWS * RB / 1024;
+  constexpr int kSlots = RB / 16;
+  constexpr int kRowsPerBlock = 1024 / RB;
+  static_assert(kBlocks % NW == 0, "1 KiB blocks must spread evenly over the waves");
+#pragma unroll
+  for (int i = 0; i < kBlocks / NW; ++i) {
+    const int j = wave + i * NW;
+    const int r = j * kRowsPerBlock + lane / kSlots;
+    const int p = lane % kSlots;
+    const int c = slot_of<RB>(r, p);          // the XOR swizzle is an involution
+    const int kb = kb0 + c * 16;
+    const uint32_t off = kb < kb_total ? (uint32_t)r * ld + (uint32_t)kb : 0x80000000u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + j * 1024), 16, off, 0, 0, 0);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4]=7 | lgkmcnt[11:8]=15 | vmcnt[5:4] at [15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int BM, int BN, int WGM, int WGN, int BK, int NS, int WK, int EPI>
+__global__ void __launch_bounds__(WGM * WGN * 64)
+gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, const void* __restrict__ Wv,
+                const float* __restrict__ SW, int M, int N, int K, _Float16* __restrict__ Y,
+                int32_t* __restrict__ ACC) {
+  constexpr int NW = WGM * WGN;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int TM = WTM / 16, TN = WTN / 16;
+  constexpr bool kI4 = WK == kWeightI4;
+  constexpr int RBA = BK;                     // activation bytes per row per stage
+  constexpr int RBW = kI4 ? BK / 2 : BK;      // weight bytes per row per stage
+  constexpr int kStageBytes = BM * RBA + BN * RBW;
+  constexpr int LPS = (BM * RBA + BN * RBW) / 1024 / NW;   // DMA instructions per wave per stage
+  static_assert(!kI4 || BK == 128, "int4 weights use 128-code stages (64-byte packed rows)");
+  static_assert(BK == 64 || BK == 128, "stage depth");
+  static_assert(TM * 16 == WTM && TN * 16 == WTN, "wave tile must be a multiple of 16");
+
+  __shared__ __attribute__((aligned(1024))) int8_t smem[NS * kStageBytes];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = (wave % WGM) * WTM, wn = (wave / WGM) * WTN;
+  const int l16 = lane & 15, l4 = lane >> 4;
+
+  // tile index: XCD-contiguous ranges, then groups of 8 tile-rows of M
+  const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
+  const int total = nbm * nbn;
+  int tile;
+  {
+    const int b = blockIdx.x, xcd = b & 7, idx = b >> 3;
+    const int per = total >> 3, rem = total & 7;
+    tile = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+  }
+  constexpr int kGroupM = 8;
+  const int group = tile / (kGroupM * nbn);
+  const int first_m = group * kGroupM;
+  const int gsz = min(nbm - first_m, kGroupM);
+  const int tm = first_m + (tile % (kGroupM * nbn)) % gsz;
+  const int tn = (tile % (kGroupM * nbn)) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const uint32_t lda = (uint32_t)K, ldw = kI4 ? (uint32_t)K / 2 : (uint32_t)K;
+  const int rows_a = min(BM, M - m0), rows_w = min(BN, N - n0);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (int64_t)m0 * K, (uint32_t)rows_a * lda);
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(static_cast<const int8_t*>(Wv) + (int64_t)n0 * ldw, (uint32_t)rows_w * ldw);
+
+  v4i acc[TN][TM];
+#pragma unroll
+  for (int a = 0; a < TN; ++a)
+#pragma unroll
+    for (int b = 0; b < TM; ++b) acc[a][b] = zero4();
+
+  const int KT = (K + BK - 1) / BK;
+  auto issue = [&](int kt) {
+    int8_t* st = smem + (kt % NS) * kStageBytes;
+    dma_stage<BM, RBA, NW>(ra, st, wave, lane, lda, kt * RBA, (int)lda);
+    dma_stage<BN, RBW, NW>(rw, st + BM * RBA, wave, lane, ldw, kt * RBW, (int)ldw);
+  };
+
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) issue(s);
+
+  for (int kt = 0; kt < KT; ++kt) {
+    wait_vmcnt<(NS - 2) * LPS>();
+    stage_barrier();
+    issue(kt + NS - 1);   // past the end: out-of-range offsets, zero fill, never read
+    const int8_t* sa_ = smem + (kt % NS) * kStageBytes;
+    const int8_t* sw_ = sa_ + BM * RBA;
+    if constexpr (!kI4) {
+#pragma unroll
+      for (int ks = 0; ks < BK / 64; ++ks) {
+        v4i wf[TN], af[TM];
+#pragma unroll
+        for (int a = 0; a < TN; ++a)
+          wf[a] = *reinterpret_cast<const v4i*>(sw_ + tile_off<RBW>(wn + 16 * a + l16, 4 * ks + l4));
+#pragma unroll
+        for (int b = 0; b < TM; ++b)
+          af[b] = *reinterpret_cast<const v4i*>(sa_ + tile_off<RBA>(wm + 16 * b + l16, 4 * ks + l4));
+#pragma unroll
+        for (int a = 0; a < TN; ++a)
+#pragma unroll
+          for (int b = 0; b < TM; ++b)
+            acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[a], af[b], acc[a][b], 0, 0, 0);
+      }
+    } else {
+      // lane group g holds packed chunk g of its weight row: codes 32g .. 32g+31;
+      // half h of it (8 bytes, 16 codes) pairs with activation chunk 2g + h.
+      v4i wraw[TN];
+#pragma unroll
+      for (int a = 0; a < TN; ++a)
+        wraw[a] = *reinterpret_cast<const v4i*>(sw_ + tile_off<RBW>(wn + 16 * a + l16, l4));
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        v4i wf[TN], af[TM];
+#pragma unroll
+        for (int a = 0; a < TN; ++a)
+          wf[a] = unpack_int4(h ? make_uint2((uint32_t)wraw[a].z, (uint32_t)wraw[a].w)
+                                : make_uint2((uint32_t)wraw[a].x, (uint32_t)wraw[a].y));
+#pragma unroll
+        for (int b = 0; b < TM; ++b)
+          af[b] = even_odd_bytes(
+              *reinterpret_cast<const v4i*>(sa_ + tile_off<RBA>(wm + 16 * b + l16, 2 * l4 + h)));
+#pragma unroll
+        for (int a = 0; a < TN; ++a)
+#pragma unroll
+          for (int b = 0; b < TM; ++b)
+            acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[a], af[b], acc[a][b], 0, 0, 0);
+      }
+    }
+  }
+  wait_vmcnt<0>();
+
+  // ---- epilogue: y = fp16(((float)acc * s_a[m]) * s_w[n]), or the raw int32
+  const bool vec_ok = (N & 3) == 0;
+#pragma unroll
+  for (int b = 0; b < TM; ++b) {
+    const int m = m0 + wm + 16 * b + l16;
+    if (m >= M) continue;
+    float sam = 0.0f;
+    if constexpr (EPI == kEpiF16) sam = SA[m];
+#pragma unroll
+    for (int a = 0; a < TN; ++a) {
+      const int n = n0 + wn + 16 * a + 4 * l4;
+      if (n >= N) continue;
+      if constexpr (EPI == kEpiAccI32) {
+        int32_t* dst = ACC + (int64_t)m * N + n;
+        if (vec_ok && n + 3 < N) {
+          *reinterpret_cast<v4i*>(dst) = acc[a][b];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) dst[r] = acc[a][b][r];
+        }
+      } else {
+        float sw[4];
+        if (vec_ok && n + 3 < N) {
+          const float4 s4 = *reinterpret_cast<const float4*>(SW + n);
+          sw[0] = s4.x; sw[1] = s4.y; sw[2] = s4.z; sw[3] = s4.w;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sw[r] = SW[min(n + r, N - 1)];
+        }
+        h4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = (_Float16)(((float)acc[a][b][r] * sam) * sw[r]);
+        _Float16* dst = Y + (int64_t)m * N + n;
+        if (vec_ok && n + 3 < N) {
+          *reinterpret_cast<h4*>(dst) = o;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) dst[r] = o[r];
+        }
+      }
+    }
+  }
+}
+
 // Block tile BM (activation rows) x BN (weight rows); WGM x WGN waves.
 template <int BM, int BN, int WGM, int WGN, int WK, int GS, int EPI>
 __global__ void __launch_bounds__(WGM * WGN * 64)
@@ -367,12 +593,34 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Per-channel and W4A8 tiles, chosen by M.
+template <int BM, int BN, int WGM, int WGN, int BK, int NS, int WK, int EPI>
+hipError_t launch_dma(const GemmArgs& g, hipStream_t st) {
+  const int64_t nbm = (g.M + BM - 1) / BM, nbn = (g.N + BN - 1) / BN;
+  const dim3 grid((unsigned)(nbm * nbn)), block(WGM * WGN * 64);
+  gemm_dma_kernel<BM, BN, WGM, WGN, BK, NS, WK, EPI><<<grid, block, 0, st>>>(
+      g.a, g.sa, g.w, g.sw, (int)g.M, (int)g.N, (int)g.K, static_cast<_Float16*>(g.y), g.acc);
+  return hipGetLastError();
+}
+
+// Per-channel and W4A8 tiles, chosen by M. Large M: 256 x 256 tiles, eight
+// waves of 128 (m) x 64 (n), two 64 KiB stages of 128 codes. Measured on
+// MI355X with random int8 data this shape ran fastest among the tested
+// 128/256 tile shapes, 64/128-code stages and 2-4 stage depths: the int8 MFMA
+// path is power-limited (the shader clock falls to ~1.5 GHz), so fewer LDS and
+// L2 bytes per MFMA matter more than occupancy. Wave tiles stay <= 128 x 64
+// (128 accumulator registers): 128 x 128 wave tiles made the register
+// allocator shuffle accumulators between MFMAs.
 template <int WK, int EPI>
 hipError_t launch_pc(const GemmArgs& g, hipStream_t st) {
-  if (g.M <= 64) return launch_cfg<64, 64, 1, 4, WK, 0, EPI>(g, st);
-  if (g.M <= 512) return launch_cfg<128, 128, 2, 2, WK, 0, EPI>(g, st);
-  return launch_cfg<256, 256, 2, 2, WK, 0, EPI>(g, st);
+  if constexpr (WK == kWeightI4) {
+    if (g.M <= 64) return launch_dma<64, 64, 1, 4, 128, 2, WK, EPI>(g, st);
+    if (g.M <= 512) return launch_dma<128, 128, 2, 2, 128, 2, WK, EPI>(g, st);
+    return launch_dma<128, 256, 2, 4, 128, 2, WK, EPI>(g, st);
+  } else {
+    if (g.M <= 64) return launch_dma<64, 64, 1, 4, 64, 3, WK, EPI>(g, st);
+    if (g.M <= 512) return launch_dma<128, 128, 2, 2, 64, 3, WK, EPI>(g, st);
+    return launch_dma<256, 256, 2, 4, 128, 2, WK, EPI>(g, st);
+  }
 }
 
 // Per-group tiles: the fp32 running sum doubles the accumulator registers, so
