@@ -60,7 +60,8 @@ def measured_traffic(sha: str):
 
 
 def cpu_baseline(M, N, K, budget_s=12.0):
-    """The CPU oracle (never tuned) on a bounded row sample of the workload."""
+    """The CPU oracle (never tuned) on the same workload for about budget_s
+    seconds of host time (whole 256-row chunks, wrapping over the rows)."""
     import numpy as np
     import oracle
     from w8a8_online_quantized_amd import inputs
@@ -74,16 +75,102 @@ def cpu_baseline(M, N, K, budget_s=12.0):
     x = inputs.activations(M, K, seed=0)
     rows_done, chunk = 0, 256
     t0 = time.perf_counter()
-    while rows_done < M and time.perf_counter() - t0 < budget_s:
-        xs = x[rows_done:rows_done + chunk]
+    while time.perf_counter() - t0 < budget_s:
+        start = rows_done % M
+        xs = x[start:start + chunk]
         oracle.w8a8_linear(xs, wq, sw, 0)
         rows_done += xs.shape[0]
     dt = time.perf_counter() - t0
     ops = 2.0 * rows_done * N * K
     return {"value": round(ops / dt / 1e12, 6), "unit": "TOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{rows_done} of {M} rows (chunks of {chunk}) of the same M={M},N={N},K={K} "
-                      f"per-channel linear: numpy quantize + exact fp64 integer matmul + fp64 dequant, "
-                      f"{dt:.1f} s"}
+            "sample": f"{rows_done} rows ({rows_done / M:.2f} passes over the M={M} rows, chunks of {chunk}) "
+                      f"of the same N={N}, K={K} per-channel linear: numpy quantize + exact fp64 integer "
+                      f"matmul + fp64 dequant, {dt:.1f} s"}
+
+
+def algorithmic(mode, M, N, K, gs):
+    """Integer ops and HBM bytes one GEMM launch must move, and the bytes of the
+    activation quantization (fp16 in, int8 + fp32 scales out)."""
+    G = 1 if gs == 0 else K // gs
+    wbytes = N * K // 2 if mode == "w4a8" else N * K
+    gemm_bytes = M * K + wbytes + 4 * M * G + 4 * N * G + 2 * M * N
+    quant_bytes = 2 * M * K + M * K + 4 * M * G
+    return 2.0 * M * N * K, gemm_bytes, quant_bytes
+
+
+def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_bytes=512 * 2 ** 20):
+    """Times `steps` passes of quant_act + GEMM for one workload, rotating over
+    enough buffer sets to keep the working set out of the 256 MB last-level
+    cache. Returns per-kernel average times from HIP events on the launch stream."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    x_h = torch.from_numpy(inputs.activations(M, K, seed=0))
+    w_h = torch.from_numpy(inputs.weights(N, K, seed=0))
+    ops, gemm_bytes, quant_bytes = algorithmic(mode, M, N, K, gs)
+    R = max(2, -(-min_set_bytes // (gemm_bytes + quant_bytes)))
+    bits = 4 if mode == "w4a8" else 8
+    w_dev = w_h.to(dev)
+    wq0, sw0 = cider.cider_quant_weight(w_dev, bits, gs)
+    del w_dev
+    sets = []
+    for _ in range(R):
+        x = x_h.to(dev)
+        xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+        sa = torch.empty((M,) if gs == 0 else (M, K // gs), dtype=torch.float32, device=dev)
+        y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        sets.append((x, xq, sa, wq0.clone(), sw0.clone(), y))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def gemm(xq, sa, wq, sw, y):
+        if mode == "w4a8":
+            cider.cider_w4a8_gemm(xq, sa, wq, sw, y, stream=stream)
+        else:
+            cider.cider_w8a8_gemm(xq, sa, wq, sw, gs, y, stream=stream)
+
+    for i in range(warmup):
+        x, xq, sa, wq, sw, y = sets[i % R]
+        cider.cider_quant_act(x, gs, xq, sa, stream=stream)
+        gemm(xq, sa, wq, sw, y)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        x, xq, sa, wq, sw, y = sets[i % R]
+        ev[i][0].record(stream)
+        cider.cider_quant_act(x, gs, xq, sa, stream=stream)
+        ev[i][1].record(stream)
+        gemm(xq, sa, wq, sw, y)
+        ev[i][2].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    g_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    del sets
+    torch.cuda.empty_cache()
+    return {"ms_per_step": total_ms / steps, "quant_ms": q_ms, "gemm_ms": g_ms, "ops": ops,
+            "gemm_bytes": gemm_bytes, "quant_bytes": quant_bytes, "sets": R}
+
+
+def roofline_of(ops, nbytes, ms):
+    """Bound by the roof the algorithmic work hits first at peak rates."""
+    t_mfma = ops / (PEAK_INT8_TOPS * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        a = ops / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(a, 3), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                "frac": round(a / PEAK_INT8_TOPS, 4)}
+    a = nbytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(a / PEAK_HBM_GBS, 4)}
+
+
+SWEEP = ([("w8a8_pc", M, 10240, 2560, 0) for M in (1, 128, 1024, 4096, 8192)] +
+         [("w8a8_pc", M, 2560, 10240, 0) for M in (1, 128, 1024, 4096, 8192)] +
+         [("w8a8_pg", M, 2560, 10240, gs) for gs in (128, 64) for M in (128, 1024, 4096)] +
+         [("w4a8", M, 10240, 2560, 0) for M in (1, 1024, 8192)])
 
 
 def main():
@@ -91,11 +178,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--M", type=int, default=4096)
-    ap.add_argument("--N", type=int, default=10240)
-    ap.add_argument("--K", type=int, default=2560)
-    ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0 = enough for 512 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time every per-channel / per-group / W4A8 configuration")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -105,7 +190,6 @@ def main():
               "(collectives and sharding are out of scope); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     from w8a8_online_quantized_amd import cider, inputs
 
@@ -113,64 +197,20 @@ def main():
         print("bench.py needs a gfx950 GPU and the built libcider.so", file=sys.stderr)
         sys.exit(3)
 
-    M, N, K = args.M, args.N, args.K
-    dev = torch.device("cuda:0")
-    x_h = torch.from_numpy(inputs.activations(M, K, seed=0))
-    w_h = torch.from_numpy(inputs.weights(N, K, seed=0))
-    set_bytes = M * K * 2 + M * K + N * K + 2 * M * N + 4 * (M + N)
-    R = args.sets or max(2, -(-512 * 2 ** 20 // set_bytes))
-    sets = []
-    for _ in range(R):
-        x = x_h.to(dev)
-        wq, sw = cider.cider_quant_weight(w_h.to(dev), 8, 0)
-        xq = torch.empty((M, K), dtype=torch.int8, device=dev)
-        sa = torch.empty((M,), dtype=torch.float32, device=dev)
-        y = torch.empty((M, N), dtype=torch.float16, device=dev)
-        sets.append((x, xq, sa, wq, sw, y))
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-
-    def step(i):
-        x, xq, sa, wq, sw, y = sets[i % R]
-        cider.cider_quant_act(x, 0, xq, sa, stream=stream)
-        cider.cider_w8a8_gemm(xq, sa, wq, sw, 0, y, stream=stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(args.steps):
-        x, xq, sa, wq, sw, y = sets[i % R]
-        ev[i][0].record(stream)
-        cider.cider_quant_act(x, 0, xq, sa, stream=stream)
-        ev[i][1].record(stream)
-        cider.cider_w8a8_gemm(xq, sa, wq, sw, 0, y, stream=stream)
-        ev[i][2].record(stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-
-    total_ms = start.elapsed_time(end)
-    ms_step = total_ms / args.steps
-    q_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    g_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    q_avg, g_avg = float(np.mean(q_ms)), float(np.mean(g_ms))
-    ops = 2.0 * M * N * K
-    value = ops / (ms_step * 1e-3) / 1e12
-    gemm_tops = ops / (g_avg * 1e-3) / 1e12
-    gemm_bytes = M * K + N * K + 4 * M + 4 * N + 2 * M * N
-    quant_bytes = 2 * M * K + M * K + 4 * M
+    M, N, K = 4096, 10240, 2560
+    r = measure(cider, torch, inputs, "w8a8_pc", M, N, K, 0, args.steps, args.warmup)
+    ops = r["ops"]
+    value = ops / (r["ms_per_step"] * 1e-3) / 1e12
+    gemm_tops = ops / (r["gemm_ms"] * 1e-3) / 1e12
 
     if args.calib_copy_mb:
         n = args.calib_copy_mb * 2 ** 20
-        a = torch.empty(n, dtype=torch.uint8, device=dev)
-        b = torch.empty(n, dtype=torch.uint8, device=dev)
+        a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+        b = torch.empty(n, dtype=torch.uint8, device="cuda:0")
         for _ in range(3):
             b.copy_(a)
         torch.cuda.synchronize()
+        del a, b
 
     sha = kernel_source_sha()
     out = {
@@ -180,7 +220,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": round(r["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(value / PAGES_M5PRO_TOPS, 3),
@@ -189,20 +229,31 @@ def main():
         "config": {"workload": f"w8a8 per-channel online-quantized linear, M={M} N={N} K={K}, "
                                f"quant_act + fused GEMM per step",
                    "M": M, "N": N, "K": K, "group_size": 0, "x_dtype": "fp16", "y_dtype": "fp16",
-                   "cold_cache_sets": R, "parallelism": "single GPU"},
+                   "cold_cache_sets": r["sets"], "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "cider_w8a8_gemm",
                      "achieved": round(gemm_tops, 3), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
                      "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
                      "traffic": measured_traffic(sha),
-                     "algorithmic_bytes": gemm_bytes, "algorithmic_ops": ops,
-                     "avg_launch_ms": round(g_avg, 5)},
-        "kernels": {"cider_quant_act": {"avg_ms": round(q_avg, 5),
-                                        "GB/s": round(quant_bytes / (q_avg * 1e-3) / 1e9, 1),
-                                        "hbm_frac": round(quant_bytes / (q_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-                    "cider_w8a8_gemm": {"avg_ms": round(g_avg, 5), "TOP/s": round(gemm_tops, 2)}},
+                     "algorithmic_bytes": r["gemm_bytes"], "algorithmic_ops": ops,
+                     "avg_launch_ms": round(r["gemm_ms"], 5)},
+        "kernels": {"cider_quant_act": {"avg_ms": round(r["quant_ms"], 5),
+                                        "GB/s": round(r["quant_bytes"] / (r["quant_ms"] * 1e-3) / 1e9, 1),
+                                        "hbm_frac": round(r["quant_bytes"] / (r["quant_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+                    "cider_w8a8_gemm": {"avg_ms": round(r["gemm_ms"], 5), "TOP/s": round(gemm_tops, 2)}},
         "baseline_context": f"Apple M5 Pro, README single-op table: 4.41 ms = {PAGES_M5PRO_TOPS:.1f} TOP/s",
         "kernel_source_sha": sha,
     }
+    if args.sweep:
+        rows = []
+        for mode, m, n, k, gs in SWEEP:
+            rr = measure(cider, torch, inputs, mode, m, n, k, gs, max(10, args.steps // 2), 3)
+            rows.append({"mode": mode, "M": m, "N": n, "K": k, "group_size": gs,
+                         "gemm_us": round(rr["gemm_ms"] * 1e3, 2), "quant_us": round(rr["quant_ms"] * 1e3, 2),
+                         "gemm_roofline": roofline_of(rr["ops"], rr["gemm_bytes"], rr["gemm_ms"]),
+                         "quant_GBs": round(rr["quant_bytes"] / (rr["quant_ms"] * 1e-3) / 1e9, 1),
+                         "linear_TOPs": round(rr["ops"] / (rr["ms_per_step"] * 1e-3) / 1e12, 2)})
+            print(json.dumps({"sweep_row": rows[-1]}), file=sys.stderr, flush=True)
+        out["sweep"] = rows
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(M, N, K)
     print(json.dumps(out), flush=True)

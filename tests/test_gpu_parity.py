@@ -278,3 +278,55 @@ def test_stream_ordering_on_side_stream():
     s.synchronize()
     yo, _, _ = oracle.w8a8_linear(x, *oracle.quantize_weight(w), 0)
     assert_y_close(y.cpu().numpy(), yo, 1e-3, max_ulp=1, what="side stream")
+
+
+# ------------------------------------------------------------------ skinny path (M <= 16)
+@pytest.mark.parametrize("M,N,K", [(1, 17, 16), (2, 33, 48), (3, 70, 256), (4, 130, 2560), (7, 100, 1040),
+                                   (16, 64, 2560), (1, 2560, 10240), (4, 9, 16384), (16, 40, 10240), (5, 3000, 320)])
+def test_skinny_acc_and_outputs_per_channel(M, N, K):
+    c = cider()
+    rng = np.random.default_rng(M * 31 + N)
+    qa, qw = _codes(rng, (M, K)), _codes(rng, (N, K))
+    acc = c.cider_gemm_acc_i32(0, dev(qa), dev(qw))
+    assert np.array_equal(host(acc), oracle.int_dot(qa, qw))
+    x, w = _pc_case(M, N, K, seed=5)
+    wq, sw = c.cider_quant_weight(dev(w), 8, 0)
+    xq, sa = c.cider_quant_act(dev(x), 0)
+    y = host(c.cider_w8a8_gemm(xq, sa, wq, sw, 0))
+    wqo, swo = oracle.quantize_weight(w)
+    yo, _, _ = oracle.w8a8_linear(x, wqo, swo, 0)
+    assert_y_close(y, yo, 1e-3, max_ulp=1, what=f"skinny pc {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K,gs", [(1, 17, 128, 64), (3, 40, 1024, 128), (16, 70, 2560, 64), (1, 2560, 10240, 128)])
+def test_skinny_per_group(M, N, K, gs):
+    c = cider()
+    rng = np.random.default_rng(M + gs)
+    qa, qw = _codes(rng, (M, K)), _codes(rng, (N, K))
+    acc = c.cider_gemm_acc_i32(0, dev(qa), dev(qw), gs)
+    assert np.array_equal(host(acc), oracle.int_dot_groups(qa, qw, gs))
+    x, w = _pc_case(M, N, K, seed=6)
+    wq, sw = c.cider_quant_weight(dev(w), 8, gs)
+    xq, sa = c.cider_quant_act(dev(x), gs)
+    y = host(c.cider_w8a8_gemm(xq, sa, wq, sw, gs))
+    wqo, swo = oracle.quantize_weight(w, 8, gs)
+    yo, qo, sao = oracle.w8a8_linear(x, wqo, swo, gs)
+    e = pg_sum_bound(qo, sao, wqo, swo, gs, np.arange(M))
+    assert_y_close(y, yo, 2e-3, extra_atol=e, what=f"skinny pg{gs} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 10240, 2560), (3, 40, 64), (4, 33, 96), (2, 7, 8192), (16, 50, 1056)])
+def test_skinny_w4a8(M, N, K):
+    c = cider()
+    rng = np.random.default_rng(M + N + 1)
+    qa = _codes(rng, (M, K))
+    q4 = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    acc = c.cider_gemm_acc_i32(1, dev(qa), dev(oracle.pack_int4(q4)))
+    assert np.array_equal(host(acc), oracle.int_dot(qa, q4))
+    x, w = _pc_case(M, N, K, seed=7)
+    wp, sw = c.cider_quant_weight(dev(w), 4, 0)
+    xq, sa = c.cider_quant_act(dev(x), 0)
+    y = host(c.cider_w4a8_gemm(xq, sa, wp, sw))
+    wpo, swo = oracle.quantize_weight(w, 4, 0)
+    yo, _, _ = oracle.w4a8_linear(x, wpo, swo)
+    assert_y_close(y, yo, 1e-3, max_ulp=1, what=f"skinny w4a8 {M}x{N}x{K}")

@@ -42,6 +42,7 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 
 constexpr int kBK = 64;   // K codes per pipeline stage
 
@@ -593,6 +594,482 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Skinny path, M <= 16 (decode-sized batches): the weight stream dominates, so
+// nothing is staged in LDS. A block owns 16 weight rows; its S waves split K
+// into units of U codes (unit u goes to wave u % S) and each wave feeds its
+// weight and activation fragments straight from buffer loads into
+// v_mfma_i32_16x16x64_i8 (activation rows >= M and chunks past K load as
+// zero). The S int32 partial sums are added through LDS in wave order, which
+// is exact; per-group partial fp32 sums are added in the same fixed order.
+// ---------------------------------------------------------------------------
+template <int S, int WK, int GS, int EPI>
+__global__ void __launch_bounds__(S * 64)
+gemm_skinny_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, const void* __restrict__ Wv,
+                   const float* __restrict__ SW, int M, int N, int K, _Float16* __restrict__ Y,
+                   int32_t* __restrict__ ACC) {
+  constexpr bool kI4 = WK == kWeightI4;
+  constexpr int U = GS == 128 ? 128 : 64;      // codes per unit: one group for per-group
+  constexpr int kMf = U / 64;                  // MFMAs per unit
+  constexpr int kBatch = 8;                    // units in flight per wave
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, l4 = lane >> 4;
+  const int n0 = blockIdx.x * 16;
+  const int rows_w = min(16, N - n0);
+  const uint32_t ldw = kI4 ? (uint32_t)K / 2 : (uint32_t)K;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (uint32_t)M * (uint32_t)K);
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(static_cast<const int8_t*>(Wv) + (int64_t)n0 * ldw, (uint32_t)rows_w * ldw);
+  const int KU = (K + U - 1) / U;
+  const int G = GS == 0 ? 1 : K / (GS == 0 ? 1 : GS);
+
+  v4i acc = zero4();
+  float facc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int base = wave; base < KU; base += kBatch * S) {
+    v4i wf[kBatch][kMf], xf[kBatch][kMf];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int u = base + i * S;
+#pragma unroll
+      for (int j = 0; j < kMf; ++j) {
+        const int k = u * U + 64 * j + 16 * l4;    // first code of this lane's chunk
+        const bool in = u < KU && k < K;
+        const uint32_t xo = in ? (uint32_t)l16 * (uint32_t)K + (uint32_t)k : 0x80000000u;
+        xf[i][j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 0);
+        if constexpr (kI4) {
+          const uint32_t wo = in ? (uint32_t)l16 * ldw + (uint32_t)k / 2 : 0x80000000u;
+          const v2i p = __builtin_amdgcn_raw_buffer_load_b64(rw, wo, 0, 0);
+          wf[i][j] = v4i{p.x, p.y, 0, 0};
+        } else {
+          const uint32_t wo = in ? (uint32_t)l16 * ldw + (uint32_t)k : 0x80000000u;
+          wf[i][j] = __builtin_amdgcn_raw_buffer_load_b128(rw, wo, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int u = base + i * S;
+      if (u >= KU) break;
+#pragma unroll
+      for (int j = 0; j < kMf; ++j) {
+        v4i w = wf[i][j], x = xf[i][j];
+        if constexpr (kI4) {
+          w = unpack_int4(make_uint2((uint32_t)w.x, (uint32_t)w.y));
+          x = even_odd_bytes(x);
+        }
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(w, x, acc, 0, 0, 0);
+      }
+      if constexpr (GS != 0) {
+        // one unit is one group: fold it into the fp32 sum and restart
+        if constexpr (EPI == kEpiAccI32) {
+          const int m = l16, n = n0 + 4 * l4;
+          if (m < M) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (n + r < N) ACC[((int64_t)u * M + m) * N + n + r] = acc[r];
+          }
+        } else {
+          const float sa = SA[(int64_t)min(l16, M - 1) * G + u];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float sw = SW[(int64_t)min(n0 + 4 * l4 + r, N - 1) * G + u];
+            facc[r] += ((float)acc[r] * sa) * sw;
+          }
+        }
+        acc = zero4();
+      }
+    }
+  }
+
+  // cross-wave sum in wave order, then the store stage
+  using red_t = typename std::conditional<GS == 0, int, float>::type;
+  __shared__ red_t red[S][4][64];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if constexpr (GS == 0) red[wave][r][lane] = acc[r];
+    else red[wave][r][lane] = facc[r];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const int m = l16;
+  if (m >= M) return;
+  const int n = n0 + 4 * l4;
+  red_t t[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    t[r] = red[0][r][lane];
+#pragma unroll
+    for (int w = 1; w < S; ++w) t[r] += red[w][r][lane];
+  }
+  if constexpr (GS == 0) {
+    if constexpr (EPI == kEpiAccI32) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n + r < N) ACC[(int64_t)m * N + n + r] = t[r];
+    } else {
+      const float sam = SA[m];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n + r < N) Y[(int64_t)m * N + n + r] = (_Float16)(((float)t[r] * sam) * SW[n + r]);
+    }
+  } else if constexpr (EPI == kEpiF16) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (n + r < N) Y[(int64_t)m * N + n + r] = (_Float16)t[r];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// GEMV path, M <= 4, per-channel and W4A8: a pure weight stream. A block owns
+// 8 weight rows; each wave instruction loads 8 rows x 128 contiguous bytes
+// (full cache lines), lane L taking 16 bytes of row L / 8. The block's four
+// waves take alternate 128-byte steps along each row. The M activation rows
+// are staged once in LDS (for W4A8 already in the even/odd code order the
+// unpacked nibbles come in), and v_dot4_i32_i8 accumulates exact int32 sums,
+// reduced across the 8 lanes of a row and then across the waves in order.
+// ---------------------------------------------------------------------------
+template <int MT, int WK, int EPI>
+__global__ void __launch_bounds__(256)
+gemm_gemv_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, const void* __restrict__ Wv,
+                 const float* __restrict__ SW, int M, int N, int K, _Float16* __restrict__ Y,
+                 int32_t* __restrict__ ACC) {
+  constexpr bool kI4 = WK == kWeightI4;
+  constexpr int kCodes = kI4 ? 256 : 128;     // codes per 128-byte weight step
+  constexpr int kBatch = 8;                   // steps in flight per wave
+  extern __shared__ __attribute__((aligned(16))) int8_t xs[];   // [MT][Kpad]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int Kpad = (K + kCodes - 1) / kCodes * kCodes;
+
+  // stage x (rows >= M and codes >= K as zero)
+  for (int i = threadIdx.x; i < MT * Kpad / 16; i += 256) {
+    const int m = i / (Kpad / 16), c = i % (Kpad / 16);
+    v4i v = zero4();
+    if (m < M && c * 16 < K) v = *reinterpret_cast<const v4i*>(X + (int64_t)m * K + c * 16);
+    if constexpr (kI4) v = even_odd_bytes(v);
+    *reinterpret_cast<v4i*>(xs + m * Kpad + c * 16) = v;
+  }
+  __syncthreads();
+
+  const int n0 = blockIdx.x * 8;
+  const int row = lane >> 3, sub = lane & 7;
+  const int rows_w = min(8, N - n0);
+  const uint32_t ldw = kI4 ? (uint32_t)K / 2 : (uint32_t)K;
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(static_cast<const int8_t*>(Wv) + (int64_t)n0 * ldw, (uint32_t)rows_w * ldw);
+  const int steps = Kpad / kCodes;
+  int acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = 0;
+
+  for (int base = wave; base < steps; base += 4 * kBatch) {
+    v4i wv[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int st = base + 4 * i;
+      const uint32_t kb = (uint32_t)st * 128 + 16 * sub;        // byte offset within the row
+      const bool in = st < steps && kb < ldw;
+      wv[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, in ? (uint32_t)row * ldw + kb : 0x80000000u, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int st = base + 4 * i;
+      if (st >= steps) break;
+      if constexpr (kI4) {
+        // 16 packed bytes = codes st*256 + 32*sub .. +31, in 2 x 16 unpacked bytes
+        const v4i lo = unpack_int4(make_uint2((uint32_t)wv[i].x, (uint32_t)wv[i].y));
+        const v4i hi = unpack_int4(make_uint2((uint32_t)wv[i].z, (uint32_t)wv[i].w));
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const int8_t* xp = xs + m * Kpad + st * 256 + 32 * sub;
+          const v4i x0 = *reinterpret_cast<const v4i*>(xp);
+          const v4i x1 = *reinterpret_cast<const v4i*>(xp + 16);
+          int a = acc[m];
+          a = __builtin_amdgcn_sdot4(lo.x, x0.x, a, false);
+          a = __builtin_amdgcn_sdot4(lo.y, x0.y, a, false);
+          a = __builtin_amdgcn_sdot4(lo.z, x0.z, a, false);
+          a = __builtin_amdgcn_sdot4(lo.w, x0.w, a, false);
+          a = __builtin_amdgcn_sdot4(hi.x, x1.x, a, false);
+          a = __builtin_amdgcn_sdot4(hi.y, x1.y, a, false);
+          a = __builtin_amdgcn_sdot4(hi.z, x1.z, a, false);
+          a = __builtin_amdgcn_sdot4(hi.w, x1.w, a, false);
+          acc[m] = a;
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const v4i x = *reinterpret_cast<const v4i*>(xs + m * Kpad + st * 128 + 16 * sub);
+          int a = acc[m];
+          a = __builtin_amdgcn_sdot4(wv[i].x, x.x, a, false);
+          a = __builtin_amdgcn_sdot4(wv[i].y, x.y, a, false);
+          a = __builtin_amdgcn_sdot4(wv[i].z, x.z, a, false);
+          a = __builtin_amdgcn_sdot4(wv[i].w, x.w, a, false);
+          acc[m] = a;
+        }
+      }
+    }
+  }
+  // sum the 8 lanes of each row (integer: order does not matter)
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) acc[m] += __shfl_xor(acc[m], off);
+  __shared__ int red[4][8][MT];
+  if (sub == 0) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) red[wave][row][m] = acc[m];
+  }
+  __syncthreads();
+  if (threadIdx.x >= 8 * MT) return;
+  const int r = threadIdx.x / MT, m = threadIdx.x % MT;
+  const int n = n0 + r;
+  if (m >= M || n >= N) return;
+  const int t = red[0][r][m] + red[1][r][m] + red[2][r][m] + red[3][r][m];
+  if constexpr (EPI == kEpiAccI32) ACC[(int64_t)m * N + n] = t;
+  else Y[(int64_t)m * N + n] = (_Float16)(((float)t * SA[m]) * SW[n]);
+}
+
+template <int MT, int WK, int EPI>
+hipError_t launch_gemv_m(const GemmArgs& g, hipStream_t st) {
+  constexpr int kCodes = WK == kWeightI4 ? 256 : 128;
+  const int64_t kpad = (g.K + kCodes - 1) / kCodes * kCodes;
+  const size_t lds = (size_t)MT * kpad;
+  const dim3 grid((unsigned)((g.N + 7) / 8)), block(256);
+  gemm_gemv_kernel<MT, WK, EPI><<<grid, block, lds, st>>>(g.a, g.sa, g.w, g.sw, (int)g.M, (int)g.N, (int)g.K,
+                                                         static_cast<_Float16*>(g.y), g.acc);
+  return hipGetLastError();
+}
+
+// M <= 4 with the staged activations fitting in LDS (<= 64 KiB).
+inline bool gemv_fits(const GemmArgs& g) {
+  const int64_t mt = g.M <= 1 ? 1 : (g.M <= 2 ? 2 : 4);
+  return g.M <= 4 && mt * (g.K + 255) / 256 * 256 <= 65536;
+}
+
+template <int WK, int EPI>
+hipError_t launch_gemv(const GemmArgs& g, hipStream_t st) {
+  if (g.M <= 1) return launch_gemv_m<1, WK, EPI>(g, st);
+  if (g.M <= 2) return launch_gemv_m<2, WK, EPI>(g, st);
+  return launch_gemv_m<4, WK, EPI>(g, st);
+}
+
+template <int S, int WK, int GS, int EPI>
+hipError_t launch_skinny_s(const GemmArgs& g, hipStream_t st) {
+  const dim3 grid((unsigned)((g.N + 15) / 16)), block(S * 64);
+  gemm_skinny_kernel<S, WK, GS, EPI><<<grid, block, 0, st>>>(g.a, g.sa, g.w, g.sw, (int)g.M, (int)g.N,
+                                                             (int)g.K, static_cast<_Float16*>(g.y), g.acc);
+  return hipGetLastError();
+}
+
+// K-split factor: enough waves in flight to stream the weights at HBM rate.
+template <int WK, int GS, int EPI>
+hipError_t launch_skinny(const GemmArgs& g, hipStream_t st) {
+  const int64_t blocks = (g.N + 15) / 16;
+  const int64_t units = (g.K + 63) / 64;
+  if (blocks >= 1024 || units < 16) return launch_skinny_s<4, WK, GS, EPI>(g, st);
+  if (blocks >= 384 || units < 64) return launch_skinny_s<8, WK, GS, EPI>(g, st);
+  return launch_skinny_s<16, WK, GS, EPI>(g, st);
+}
+
+// ---------------------------------------------------------------------------
+// Per-group variant of the direct-to-LDS pipeline (gs = 64 or 128 along K, for
+// both operands). Each 128-code stage also gathers the stage's group scales
+// into LDS with 4-byte DMA loads (lane L fetches the scale of tile row 64p+L),
+// so the scales arrive with the codes and are covered by the same vmcnt wait.
+// After the MFMAs of a group, every accumulator element is folded into an fp32
+// sum as ((float)acc * s_a[m,g]) * s_w[n,g] and the int32 accumulator restarts.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WGM, int WGN, int NS, int GS, int EPI>
+__global__ void __launch_bounds__(WGM * WGN * 64)
+gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, const int8_t* __restrict__ W,
+                   const float* __restrict__ SW, int M, int N, int K, _Float16* __restrict__ Y,
+                   int32_t* __restrict__ ACC) {
+  constexpr int BK = 128, RB = 128;
+  constexpr int NW = WGM * WGN;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int TM = WTM / 16, TN = WTN / 16;
+  constexpr int GPS = BK / GS;                           // groups per stage
+  constexpr int kCodeBytes = (BM + BN) * RB;
+  // 4-byte DMA instructions per stage and per wave (spares load nothing). The
+  // int32-accumulator variant has no scales (its scale pointers are null), so
+  // it issues none.
+  constexpr int kScaleInstr = EPI == kEpiAccI32 ? 0 : GPS * (BM + BN) / 64;
+  constexpr int kScalePer = (kScaleInstr + NW - 1) / NW;
+  constexpr int kScaleBytes = GPS * (BM + BN) * 4 + 256;  // + a landing pad for the spares
+  constexpr int kStageBytes = kCodeBytes + kScaleBytes;
+  static_assert((BM + BN) % 64 == 0, "scale DMA covers 64 rows per instruction");
+  constexpr int LPS = kCodeBytes / 1024 / NW + kScalePer;
+  static_assert(TM * 16 == WTM && TN * 16 == WTN, "wave tile must be a multiple of 16");
+
+  __shared__ __attribute__((aligned(1024))) int8_t smem[NS * kStageBytes];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = (wave % WGM) * WTM, wn = (wave / WGM) * WTN;
+  const int l16 = lane & 15, l4 = lane >> 4;
+
+  const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
+  const int total = nbm * nbn;
+  int tile;
+  {
+    const int b = blockIdx.x, xcd = b & 7, idx = b >> 3;
+    const int per = total >> 3, rem = total & 7;
+    tile = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+  }
+  constexpr int kGroupM = 8;
+  const int group = tile / (kGroupM * nbn);
+  const int first_m = group * kGroupM;
+  const int gsz = min(nbm - first_m, kGroupM);
+  const int tm = first_m + (tile % (kGroupM * nbn)) % gsz;
+  const int tn = (tile % (kGroupM * nbn)) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int G = K / GS;
+  const uint32_t ld = (uint32_t)K;
+  const int rows_a = min(BM, M - m0), rows_w = min(BN, N - n0);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (int64_t)m0 * K, (uint32_t)rows_a * ld);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (int64_t)n0 * K, (uint32_t)rows_w * ld);
+  // scale descriptors (never dereferenced by the int32-accumulator variant)
+  const __amdgpu_buffer_rsrc_t rsa =
+      make_rsrc(SA + (EPI == kEpiF16 ? (int64_t)m0 * G : 0), EPI == kEpiF16 ? (uint32_t)rows_a * G * 4 : 0u);
+  const __amdgpu_buffer_rsrc_t rsw =
+      make_rsrc(SW + (EPI == kEpiF16 ? (int64_t)n0 * G : 0), EPI == kEpiF16 ? (uint32_t)rows_w * G * 4 : 0u);
+
+  v4i acc[TN][TM];
+  float facc[TN][TM][4];
+#pragma unroll
+  for (int a = 0; a < TN; ++a)
+#pragma unroll
+    for (int b = 0; b < TM; ++b) {
+      acc[a][b] = zero4();
+#pragma unroll
+      for (int r = 0; r < 4; ++r) facc[a][b][r] = 0.0f;
+    }
+
+  const int KT = (K + BK - 1) / BK;
+  auto issue = [&](int kt) {
+    int8_t* st = smem + (kt % NS) * kStageBytes;
+    dma_stage<BM, RB, NW>(ra, st, wave, lane, ld, kt * RB, (int)ld);
+    dma_stage<BN, RB, NW>(rw, st + BM * RB, wave, lane, ld, kt * RB, (int)ld);
+#pragma unroll
+    for (int i = 0; i < kScalePer; ++i) {
+      const int j = wave + i * NW;
+      if (j >= kScaleInstr) {   // keeps every wave's vmcnt count equal
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(st + kCodeBytes + GPS * (BM + BN) * 4), 4,
+                                                 0x80000000u, 0, 0, 0);
+        continue;
+      }
+      const int gi = j / ((BM + BN) / 64), p = j % ((BM + BN) / 64);
+      const int g = kt * GPS + gi;
+      int8_t* dst = st + kCodeBytes + (gi * (BM + BN) + 64 * p) * 4;
+      if (p < BM / 64) {
+        const uint32_t off = g < G ? ((uint32_t)(64 * p + lane) * G + g) * 4 : 0x80000000u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)dst, 4, off, 0, 0, 0);
+      } else {
+        const uint32_t off = g < G ? ((uint32_t)(64 * (p - BM / 64) + lane) * G + g) * 4 : 0x80000000u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_void*)dst, 4, off, 0, 0, 0);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) issue(s);
+
+  for (int kt = 0; kt < KT; ++kt) {
+    wait_vmcnt<(NS - 2) * LPS>();
+    stage_barrier();
+    issue(kt + NS - 1);
+    const int8_t* sa_ = smem + (kt % NS) * kStageBytes;
+    const int8_t* sw_ = sa_ + BM * RB;
+    const float* sc = reinterpret_cast<const float*>(sa_ + kCodeBytes);
+#pragma unroll
+    for (int ks = 0; ks < BK / 64; ++ks) {
+      v4i wf[TN], af[TM];
+#pragma unroll
+      for (int a = 0; a < TN; ++a)
+        wf[a] = *reinterpret_cast<const v4i*>(sw_ + tile_off<RB>(wn + 16 * a + l16, 4 * ks + l4));
+#pragma unroll
+      for (int b = 0; b < TM; ++b)
+        af[b] = *reinterpret_cast<const v4i*>(sa_ + tile_off<RB>(wm + 16 * b + l16, 4 * ks + l4));
+#pragma unroll
+      for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int b = 0; b < TM; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[a], af[b], acc[a][b], 0, 0, 0);
+      if ((ks + 1) * 64 % GS == 0) {   // a group ends here
+        const int gi = (ks * 64) / GS;
+        const int g = kt * GPS + gi;
+        if (g < G) {
+          if constexpr (EPI == kEpiAccI32) {
+#pragma unroll
+            for (int a = 0; a < TN; ++a)
+#pragma unroll
+              for (int b = 0; b < TM; ++b) {
+                const int m = m0 + wm + 16 * b + l16, n = n0 + wn + 16 * a + 4 * l4;
+                if (m < M) {
+#pragma unroll
+                  for (int r = 0; r < 4; ++r)
+                    if (n + r < N) ACC[((int64_t)g * M + m) * N + n + r] = acc[a][b][r];
+                }
+              }
+          } else {
+            const float* gsc = sc + gi * (BM + BN);
+            float sam[TM];
+#pragma unroll
+            for (int b = 0; b < TM; ++b) sam[b] = gsc[wm + 16 * b + l16];
+#pragma unroll
+            for (int a = 0; a < TN; ++a) {
+              const float4 s4 = *reinterpret_cast<const float4*>(gsc + BM + wn + 16 * a + 4 * l4);
+              const float swn[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+              for (int b = 0; b < TM; ++b)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) facc[a][b][r] += ((float)acc[a][b][r] * sam[b]) * swn[r];
+            }
+          }
+        }
+#pragma unroll
+        for (int a = 0; a < TN; ++a)
+#pragma unroll
+          for (int b = 0; b < TM; ++b) acc[a][b] = zero4();
+      }
+    }
+  }
+  wait_vmcnt<0>();
+  if constexpr (EPI == kEpiF16) {
+    const bool vec_ok = (N & 3) == 0;
+#pragma unroll
+    for (int b = 0; b < TM; ++b) {
+      const int m = m0 + wm + 16 * b + l16;
+      if (m >= M) continue;
+#pragma unroll
+      for (int a = 0; a < TN; ++a) {
+        const int n = n0 + wn + 16 * a + 4 * l4;
+        if (n >= N) continue;
+        h4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = (_Float16)facc[a][b][r];
+        _Float16* dst = Y + (int64_t)m * N + n;
+        if (vec_ok && n + 3 < N) {
+          *reinterpret_cast<h4*>(dst) = o;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) dst[r] = o[r];
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN, int NS, int GS, int EPI>
+hipError_t launch_dma_pg(const GemmArgs& g, hipStream_t st) {
+  const int64_t nbm = (g.M + BM - 1) / BM, nbn = (g.N + BN - 1) / BN;
+  const dim3 grid((unsigned)(nbm * nbn)), block(WGM * WGN * 64);
+  gemm_dma_pg_kernel<BM, BN, WGM, WGN, NS, GS, EPI><<<grid, block, 0, st>>>(
+      g.a, g.sa, static_cast<const int8_t*>(g.w), g.sw, (int)g.M, (int)g.N, (int)g.K,
+      static_cast<_Float16*>(g.y), g.acc);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WGM, int WGN, int BK, int NS, int WK, int EPI>
 hipError_t launch_dma(const GemmArgs& g, hipStream_t st) {
   const int64_t nbm = (g.M + BM - 1) / BM, nbn = (g.N + BN - 1) / BN;
@@ -602,37 +1079,58 @@ hipError_t launch_dma(const GemmArgs& g, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Per-channel and W4A8 tiles, chosen by M. Large M: 256 x 256 tiles, eight
-// waves of 128 (m) x 64 (n), two 64 KiB stages of 128 codes. Measured on
-// MI355X with random int8 data this shape ran fastest among the tested
-// 128/256 tile shapes, 64/128-code stages and 2-4 stage depths: the int8 MFMA
-// path is power-limited (the shader clock falls to ~1.5 GHz), so fewer LDS and
-// L2 bytes per MFMA matter more than occupancy. Wave tiles stay <= 128 x 64
-// (128 accumulator registers): 128 x 128 wave tiles made the register
-// allocator shuffle accumulators between MFMAs.
+// Per-channel and W4A8 tiles. The largest tile that still gives every CU a
+// block is used: 256 x 256 (eight waves of 128 (m) x 64 (n), two 64 KiB
+// stages of 128 codes) when there are enough output tiles, then 128 x 256,
+// 128 x 128 and 64 x 128 (four waves). Measured on MI355X with random int8
+// data, 256 x 256 ran fastest among the tested 128/256 shapes, 64/128-code
+// stages and 2-4 stage depths: the int8 MFMA path is power-limited (the
+// shader clock falls to ~1.5 GHz), so fewer LDS and L2 bytes per MFMA matter
+// more than occupancy. Wave tiles stay <= 128 x 64 (128 accumulator
+// registers): 128 x 128 wave tiles made the register allocator shuffle
+// accumulators between MFMAs.
+inline int64_t tiles_of(const GemmArgs& g, int bm, int bn) {
+  return ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn);
+}
+
 template <int WK, int EPI>
 hipError_t launch_pc(const GemmArgs& g, hipStream_t st) {
+  constexpr int kFill = 224;   // blocks needed to keep most of the 256 CUs busy
   if constexpr (WK == kWeightI4) {
-    if (g.M <= 64) return launch_dma<64, 64, 1, 4, 128, 2, WK, EPI>(g, st);
-    if (g.M <= 512) return launch_dma<128, 128, 2, 2, 128, 2, WK, EPI>(g, st);
-    return launch_dma<128, 256, 2, 4, 128, 2, WK, EPI>(g, st);
+    if (tiles_of(g, 128, 256) >= kFill) return launch_dma<128, 256, 2, 4, 128, 2, WK, EPI>(g, st);
+    if (tiles_of(g, 128, 128) >= kFill) return launch_dma<128, 128, 2, 2, 128, 2, WK, EPI>(g, st);
+    return launch_dma<64, 64, 1, 4, 128, 2, WK, EPI>(g, st);
   } else {
-    if (g.M <= 64) return launch_dma<64, 64, 1, 4, 64, 3, WK, EPI>(g, st);
-    if (g.M <= 512) return launch_dma<128, 128, 2, 2, 64, 3, WK, EPI>(g, st);
-    return launch_dma<256, 256, 2, 4, 128, 2, WK, EPI>(g, st);
+    if (tiles_of(g, 256, 256) >= kFill) return launch_dma<256, 256, 2, 4, 128, 2, WK, EPI>(g, st);
+    if (tiles_of(g, 128, 256) >= kFill) return launch_dma<128, 256, 2, 4, 128, 2, WK, EPI>(g, st);
+    if (tiles_of(g, 128, 128) >= kFill) return launch_dma<128, 128, 2, 2, 64, 3, WK, EPI>(g, st);
+    if (tiles_of(g, 64, 128) >= kFill) return launch_dma<64, 128, 1, 4, 64, 3, WK, EPI>(g, st);
+    return launch_dma<64, 64, 1, 4, 64, 3, WK, EPI>(g, st);
   }
 }
 
-// Per-group tiles: the fp32 running sum doubles the accumulator registers, so
-// the wave tile stays at 64 x 64.
+// Per-group tiles: the fp32 running sums double the accumulator registers,
+// so wave tiles stay at 64 x 64 (64 int32 + 64 fp32 registers per lane).
 template <int GS, int EPI>
 hipError_t launch_pg(const GemmArgs& g, hipStream_t st) {
-  if (g.M <= 64) return launch_cfg<64, 64, 1, 4, kWeightI8, GS, EPI>(g, st);
-  return launch_cfg<128, 128, 2, 2, kWeightI8, GS, EPI>(g, st);
+  constexpr int kFill = 224;
+  if (tiles_of(g, 256, 128) >= kFill) return launch_dma_pg<256, 128, 4, 2, 2, GS, EPI>(g, st);
+  if (tiles_of(g, 128, 128) >= kFill) return launch_dma_pg<128, 128, 2, 2, 2, GS, EPI>(g, st);
+  return launch_dma_pg<64, 64, 1, 4, 2, GS, EPI>(g, st);
 }
 
 template <int EPI>
 hipError_t launch_epi(const GemmArgs& g, WeightKind wk, hipStream_t st) {
+  if (g.group_size == 0 && gemv_fits(g))
+    return wk == kWeightI4 ? launch_gemv<kWeightI4, EPI>(g, st) : launch_gemv<kWeightI8, EPI>(g, st);
+  if (g.M <= 16) {
+    if (wk == kWeightI4) return launch_skinny<kWeightI4, 0, EPI>(g, st);
+    switch (g.group_size) {
+      case 0: return launch_skinny<kWeightI8, 0, EPI>(g, st);
+      case 64: return launch_skinny<kWeightI8, 64, EPI>(g, st);
+      default: return launch_skinny<kWeightI8, 128, EPI>(g, st);
+    }
+  }
   if (wk == kWeightI4) return launch_pc<kWeightI4, EPI>(g, st);
   switch (g.group_size) {
     case 0: return launch_pc<kWeightI8, EPI>(g, st);
