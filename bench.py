@@ -167,6 +167,44 @@ def roofline_of(ops, nbytes, ms):
             "frac": round(a / PEAK_HBM_GBS, 4)}
 
 
+def measure_stack(cider, torch, inputs, steps, warmup, layers=28, M=1024, dims=(2048, 2048, 1024, 6144)):
+    """The chained linear stack (4 quantizations + 7 GEMMs per layer), distinct
+    random weights per layer (1.4 GB of int8 codes for 28 layers: larger than
+    the last-level cache, so every pass streams its weights from HBM)."""
+    hidden, q_dim, kv_dim, mlp_dim = dims
+    shapes = {"q": (q_dim, hidden), "k": (kv_dim, hidden), "v": (kv_dim, hidden), "o": (hidden, q_dim),
+              "gate": (mlp_dim, hidden), "up": (mlp_dim, hidden), "down": (hidden, mlp_dim)}
+    dev = torch.device("cuda:0")
+    Ls = []
+    for l in range(layers):
+        L = {}
+        for name, (n, k) in shapes.items():
+            w = torch.from_numpy(inputs.weights(n, k, seed=inputs.stack_weight_seed(l, name))).to(dev)
+            L[name] = cider.cider_quant_weight(w, 8, 0)
+            del w
+        Ls.append(L)
+    x = torch.from_numpy(inputs.activations(M, hidden, seed=0)).to(dev)
+    y, ws = cider.cider_stack_forward(x, Ls, dims)
+    for _ in range(warmup):
+        cider.cider_stack_forward(x, Ls, dims, workspace=ws, y=y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    e0.record(stream)
+    for _ in range(steps):
+        cider.cider_stack_forward(x, Ls, dims, workspace=ws, y=y, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    ops = 2.0 * M * layers * sum(n * k for n, k in shapes.values())
+    del Ls, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"{layers}-layer linear stack, seq {M}, hidden {hidden}, q {q_dim}, kv {kv_dim}, "
+                        f"mlp {mlp_dim}: {4 * layers} quantizations + {7 * layers} GEMMs per pass",
+            "ms_per_pass": round(ms, 4), "TOP/s": round(ops / (ms * 1e-3) / 1e12, 2), "ops_per_pass": ops,
+            "steps": steps}
+
+
 SWEEP = ([("w8a8_pc", M, 10240, 2560, 0) for M in (1, 128, 1024, 4096, 8192)] +
          [("w8a8_pc", M, 2560, 10240, 0) for M in (1, 128, 1024, 4096, 8192)] +
          [("w8a8_pg", M, 2560, 10240, gs) for gs in (128, 64) for M in (128, 1024, 4096)] +
@@ -181,6 +219,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="also time every per-channel / per-group / W4A8 configuration")
+    ap.add_argument("--stack", action="store_true",
+                    help="also time the 28-layer Qwen3-VL-2B-shaped linear stack at seq 1024")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -254,6 +294,8 @@ def main():
                          "linear_TOPs": round(rr["ops"] / (rr["ms_per_step"] * 1e-3) / 1e12, 2)})
             print(json.dumps({"sweep_row": rows[-1]}), file=sys.stderr, flush=True)
         out["sweep"] = rows
+    if args.stack:
+        out["stack"] = measure_stack(cider, torch, inputs, max(3, args.steps // 10), 1)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(M, N, K)
     print(json.dumps(out), flush=True)

@@ -124,6 +124,47 @@ cider_status_t cider_gemm_acc_i32(int32_t mode, const int8_t* x_q, const void* w
                                   int64_t N, int64_t K, int32_t group_size, int32_t* acc,
                                   void* stream);
 
+/* ---- Linear-stack driver ----------------------------------------------------
+ * The prefill linear layers of a decoder stack shaped like the Qwen3-VL-2B
+ * model of the README's end-to-end VLM section, chained so that each layer's
+ * inputs are produced by the previous GEMM. Per layer, with per-channel W8A8:
+ *   quant(h)    -> Q = h Wq^T, K = h Wk^T, V = h Wv^T   (one shared quant; the
+ *                  README's experimental SplitLinear page shares the input
+ *                  preparation of same-input projections the same way)
+ *   quant(Q)    -> O = Q Wo^T
+ *   quant(O)    -> G = O Wg^T, U = O Wu^T               (one shared quant)
+ *   quant(U)    -> h' = U Wd^T                          (the next layer's input)
+ * i.e. 4 activation quantizations and 7 GEMMs per layer. K, V and G are
+ * computed and kept in the workspace but not consumed (there is no attention
+ * or activation function: this is the linear-layer work of the stack only).
+ * Shapes: Wq [q_dim, hidden], Wk/Wv [kv_dim, hidden], Wo [hidden, q_dim],
+ * Wg/Wu [mlp_dim, hidden], Wd [hidden, mlp_dim]; all dims multiples of 16.
+ */
+typedef struct {
+  const int8_t* w[7]; /* int8 codes, order q, k, v, o, gate, up, down (device) */
+  const float* s[7];  /* per-output-channel fp32 scales, same order (device) */
+} cider_stack_layer_t;
+
+/* Workspace regions, in this order, each starting at a 256-byte aligned
+ * offset: 0 codes int8 [M, max(hidden, q_dim, mlp_dim)], 1 scales fp32 [M],
+ * 2 Q fp16 [M, q_dim], 3 K fp16 [M, kv_dim], 4 V fp16 [M, kv_dim],
+ * 5 O fp16 [M, hidden], 6 G fp16 [M, mlp_dim], 7 U fp16 [M, mlp_dim],
+ * 8 h fp16 [M, hidden] (layer output ping buffer).
+ * Writes the 9 byte offsets into `offsets` (may be NULL) and returns the total
+ * size in bytes (0 for invalid dims). Host-only, no HIP call. */
+int64_t cider_stack_workspace_layout(int64_t M, int64_t hidden, int64_t q_dim, int64_t kv_dim,
+                                     int64_t mlp_dim, int64_t* offsets);
+
+/* Runs n_layers layers on x_f16 [M, hidden]; the last layer's output goes to
+ * y_f16 [M, hidden]. `layers` is a HOST array of n_layers descriptors holding
+ * device pointers. `workspace` is a device buffer of at least
+ * cider_stack_workspace_layout(...) bytes; after the call its regions hold the
+ * last layer's intermediates. All work is enqueued on `stream`. */
+cider_status_t cider_stack_forward(const void* x_f16, int64_t M, int64_t hidden, int64_t q_dim,
+                                   int64_t kv_dim, int64_t mlp_dim, int32_t n_layers,
+                                   const cider_stack_layer_t* layers, void* workspace,
+                                   int64_t workspace_bytes, void* y_f16, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -99,3 +99,22 @@ def test_max_k_constant_keeps_int32_range():
     with open(cider.HEADER_PATH) as f:
         k = int(re.search(r"#define CIDER_MAX_K (\d+)", f.read()).group(1))
     assert 127 * 127 * k < 2 ** 31 and k % 128 == 0
+
+
+def test_stack_layout_and_validation():
+    import ctypes as ct
+    offs = (ct.c_int64 * 9)()
+    total = L.cider_stack_workspace_layout(64, 256, 256, 128, 512, offs)
+    sizes = [64 * 512, 4 * 64, 2 * 64 * 256, 2 * 64 * 128, 2 * 64 * 128, 2 * 64 * 256, 2 * 64 * 512,
+             2 * 64 * 512, 2 * 64 * 256]
+    o = list(offs)
+    assert o[0] == 0 and all(x % 256 == 0 for x in o)
+    for i in range(8):
+        assert o[i + 1] - o[i] >= sizes[i]
+    assert total >= o[8] + sizes[8]
+    assert L.cider_stack_workspace_layout(64, 250, 256, 128, 512, None) == 0
+    layers = (cider.StackLayer * 1)()
+    # null weight pointers are rejected before any HIP call
+    assert L.cider_stack_forward(P, 64, 256, 256, 128, 512, 1, ct.cast(layers, ct.c_void_p), P, total, P,
+                                 NULL) == INV
+    assert L.cider_stack_forward(P, 64, 256, 256, 128, 512, 0, NULL, NULL, 0, NULL, NULL) == 0

@@ -33,7 +33,19 @@ SIGNATURES = {
     "cider_w8a8_gemm": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p]),
     "cider_w4a8_gemm": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p]),
     "cider_gemm_acc_i32": (ctypes.c_int, [_c_i32, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p]),
+    "cider_stack_workspace_layout": (ctypes.c_int64, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                                      ctypes.POINTER(ctypes.c_int64)]),
+    "cider_stack_forward": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p,
+                                           _c_i64, _c_p, _c_p]),
 }
+
+STACK_PROJECTIONS = ("q", "k", "v", "o", "gate", "up", "down")
+STACK_REGIONS = ("codes", "scales", "q", "k", "v", "o", "gate", "up", "h")
+
+
+class StackLayer(ctypes.Structure):
+    """cider_stack_layer_t: device pointers of one layer's 7 weight matrices."""
+    _fields_ = [("w", ctypes.c_void_p * 7), ("s", ctypes.c_void_p * 7)]
 
 _lib = None
 
@@ -209,3 +221,43 @@ def w4a8_linear(x, w_packed, w_scale, stream=None):
     """The README's W4A8 linear: per-token int8 activations times packed int4 weights."""
     x_q, x_scale = cider_quant_act(x, 0, stream=stream)
     return cider_w4a8_gemm(x_q, x_scale, w_packed, w_scale, stream=stream)
+
+
+def cider_stack_workspace_layout(M: int, hidden: int, q_dim: int, kv_dim: int, mlp_dim: int):
+    """(total bytes, {region: byte offset}) of the stack driver's workspace."""
+    offs = (ctypes.c_int64 * 9)()
+    total = int(lib().cider_stack_workspace_layout(M, hidden, q_dim, kv_dim, mlp_dim, offs))
+    return total, dict(zip(STACK_REGIONS, list(offs)))
+
+
+def stack_region(workspace, offsets, name, M, hidden, q_dim, kv_dim, mlp_dim):
+    """A torch view of one workspace region (for checking intermediates)."""
+    import torch
+    dims = {"q": q_dim, "k": kv_dim, "v": kv_dim, "o": hidden, "gate": mlp_dim, "up": mlp_dim, "h": hidden}
+    n = dims[name]
+    start = offsets[name]
+    return workspace[start:start + 2 * M * n].view(torch.float16).view(M, n)
+
+
+def cider_stack_forward(x, layers, dims, workspace=None, y=None, stream=None):
+    """Runs the chained linear stack. `layers`: list of dicts {name: (codes, scales)}
+    for the seven projections; dims = (hidden, q_dim, kv_dim, mlp_dim)."""
+    import torch
+    hidden, q_dim, kv_dim, mlp_dim = dims
+    M = x.shape[0]
+    _need(x, torch.float16, (M, hidden), "x")
+    total, _ = cider_stack_workspace_layout(M, hidden, q_dim, kv_dim, mlp_dim)
+    if workspace is None:
+        workspace = torch.empty(total, dtype=torch.uint8, device=x.device)
+    if y is None:
+        y = torch.empty((M, hidden), dtype=torch.float16, device=x.device)
+    arr = (StackLayer * len(layers))()
+    for i, L in enumerate(layers):
+        for j, name in enumerate(STACK_PROJECTIONS):
+            wq, ws = L[name]
+            arr[i].w[j] = wq.data_ptr()
+            arr[i].s[j] = ws.data_ptr()
+    _check("cider_stack_forward", lib().cider_stack_forward(
+        _ptr(x), M, hidden, q_dim, kv_dim, mlp_dim, len(layers), ctypes.cast(arr, ctypes.c_void_p),
+        _ptr(workspace), workspace.numel(), _ptr(y), _stream(stream)))
+    return y, workspace

@@ -4,6 +4,7 @@
 // enqueued, also on a machine without a GPU.
 #include "../../include/cider.h"
 
+#include <algorithm>
 #include <atomic>
 #include <cstring>
 
@@ -151,6 +152,75 @@ cider_status_t cider_gemm_acc_i32(int32_t mode, const int8_t* x_q, const void* w
   if (!x_q || !w || !acc || !aligned16(x_q) || !aligned16(w) || !aligned16(acc)) return CIDER_ERROR_INVALID_VALUE;
   cider::GemmArgs g{x_q, nullptr, w, nullptr, M, N, K, group_size, nullptr, acc};
   return gemm_common(g, mode == 1 ? cider::kWeightI4 : cider::kWeightI8, cider::kEpiAccI32, stream);
+}
+
+int64_t cider_stack_workspace_layout(int64_t M, int64_t hidden, int64_t q_dim, int64_t kv_dim, int64_t mlp_dim,
+                                     int64_t* offsets) {
+  if (M < 0 || hidden <= 0 || q_dim <= 0 || kv_dim <= 0 || mlp_dim <= 0) return 0;
+  if (hidden % 16 || q_dim % 16 || kv_dim % 16 || mlp_dim % 16) return 0;
+  const int64_t kmax = std::max(hidden, std::max(q_dim, mlp_dim));
+  const int64_t sizes[9] = {M * kmax, 4 * M, 2 * M * q_dim, 2 * M * kv_dim, 2 * M * kv_dim,
+                            2 * M * hidden, 2 * M * mlp_dim, 2 * M * mlp_dim, 2 * M * hidden};
+  int64_t off = 0;
+  for (int i = 0; i < 9; ++i) {
+    if (offsets) offsets[i] = off;
+    off += (sizes[i] + 255) / 256 * 256;
+  }
+  return off;
+}
+
+cider_status_t cider_stack_forward(const void* x_f16, int64_t M, int64_t hidden, int64_t q_dim, int64_t kv_dim,
+                                   int64_t mlp_dim, int32_t n_layers, const cider_stack_layer_t* layers,
+                                   void* workspace, int64_t workspace_bytes, void* y_f16, void* stream) {
+  int64_t off[9];
+  const int64_t need = cider_stack_workspace_layout(M, hidden, q_dim, kv_dim, mlp_dim, off);
+  if (need == 0 || n_layers < 0 || M >= (int64_t(1) << 31)) return CIDER_ERROR_INVALID_VALUE;
+  if (std::max(hidden, std::max(q_dim, mlp_dim)) > CIDER_MAX_K) return CIDER_ERROR_INVALID_VALUE;
+  if (M == 0 || n_layers == 0) return CIDER_SUCCESS;
+  if (!x_f16 || !layers || !workspace || !y_f16 || workspace_bytes < need) return CIDER_ERROR_INVALID_VALUE;
+  if (!aligned16(x_f16) || !aligned16(workspace) || !aligned16(y_f16)) return CIDER_ERROR_INVALID_VALUE;
+  for (int32_t l = 0; l < n_layers; ++l)
+    for (int j = 0; j < 7; ++j)
+      if (!layers[l].w[j] || !layers[l].s[j] || !aligned16(layers[l].w[j]) || !aligned16(layers[l].s[j]))
+        return CIDER_ERROR_INVALID_VALUE;
+  if (!device_is_gfx950()) return CIDER_ERROR_NOT_SUPPORTED;
+
+  char* ws = static_cast<char*>(workspace);
+  int8_t* xq = reinterpret_cast<int8_t*>(ws + off[0]);
+  float* sa = reinterpret_cast<float*>(ws + off[1]);
+  void* q = ws + off[2];
+  void* k = ws + off[3];
+  void* v = ws + off[4];
+  void* o = ws + off[5];
+  void* g = ws + off[6];
+  void* u = ws + off[7];
+  void* h = ws + off[8];
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  auto quant = [&](const void* in, int64_t K) { return cider::launch_quant_rows(in, M, K, 0, 127, xq, sa, st); };
+  auto gemm = [&](const cider_stack_layer_t& L, int j, int64_t N, int64_t K, void* out) {
+    cider::GemmArgs a{xq, sa, L.w[j], L.s[j], M, N, K, 0, out, nullptr};
+    return cider::launch_gemm(a, cider::kWeightI8, cider::kEpiF16, st);
+  };
+  const void* in = x_f16;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const cider_stack_layer_t& L = layers[l];
+    void* out = l + 1 == n_layers ? y_f16 : h;
+    hipError_t e = quant(in, hidden);
+    if (e == hipSuccess) e = gemm(L, 0, q_dim, hidden, q);
+    if (e == hipSuccess) e = gemm(L, 1, kv_dim, hidden, k);
+    if (e == hipSuccess) e = gemm(L, 2, kv_dim, hidden, v);
+    if (e == hipSuccess) e = quant(q, q_dim);
+    if (e == hipSuccess) e = gemm(L, 3, hidden, q_dim, o);
+    if (e == hipSuccess) e = quant(o, hidden);
+    if (e == hipSuccess) e = gemm(L, 4, mlp_dim, hidden, g);
+    if (e == hipSuccess) e = gemm(L, 5, mlp_dim, hidden, u);
+    if (e == hipSuccess) e = quant(u, mlp_dim);
+    if (e == hipSuccess) e = gemm(L, 6, hidden, mlp_dim, out);
+    if (e != hipSuccess) return CIDER_ERROR_LAUNCH;
+    in = out;   // stream order: the next layer's first quant reads h before h is rewritten
+  }
+  return CIDER_SUCCESS;
 }
 
 }  // extern "C"
