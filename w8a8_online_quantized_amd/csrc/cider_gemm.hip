@@ -1,14 +1,14 @@
-// INT8 x INT8 -> INT32 GEMM with the dequant fused into the store stage, on
-// CDNA4 matrix cores (v_mfma_i32_16x16x64_i8).
+// INT8 x INT8 -> INT32 GEMMs with the dequant fused into the store stage, on
+// CDNA4 matrix cores (v_mfma_i32_16x16x64_i8) and, for tiny M, v_dot4_i32_i8.
 //
 // Follows the Cider README: section "架构 / Metal Kernel 流水线"
 // (matmul_fused_dequant: INT8 x INT8 -> INT32 -> FP16 with the scales applied
 // in the store stage; for W4A8 the int4 weights are unpacked to int8 in the
 // fragment load), section "量化" (INT32 accumulation; C_fp16 = C_int32 *
 // s_act * s_weight per element) and section "W8A8 量化粒度" (per-channel or
-// per-group gs = 128 / 64 weight scales). Section "架构 / Tile 配置" picks the
-// tile by M and dispatches with an L2-friendly block order; here the tile
-// table is sized for 64-wide waves and 256 CUs, and the block order is
+// per-group gs = 128 / 64 scales). Section "架构 / Tile 配置" picks the tile by
+// M and dispatches with an L2-friendly block order; here tiles are chosen by
+// output-tile count for 64-wide waves and 256 CUs, and the block order is
 // remapped so that each of the 8 XCDs (each with its own L2) works on a
 // contiguous patch of output tiles.
 //
@@ -19,20 +19,19 @@
 // r = 0..3 - four consecutive n of one output row - so the fp16 store is one
 // 8-byte write per 16x16 sub-tile.
 //
-// Pipeline: a block computes a BM x BN output tile; K advances 64 codes per
-// stage through two LDS buffers. Global->register loads of stage k+1 are in
-// flight while the waves run the MFMAs of stage k; one barrier per stage.
-// LDS rows are 64 bytes; 16-byte chunk c of row r sits at slot c ^ swz(r),
-// which keeps the 16-byte fragment reads of 8 (or 16) consecutive rows on
-// distinct banks.
-//
-// Per-group (gs = 64 / 128): int32 partial sums run for one group, then each
-// element adds ((float)acc * s_a[m,g]) * s_w[n,g] into an fp32 accumulator and
-// the int32 one restarts. W4A8: the packed weight tile stays packed in LDS
-// (32 bytes per row and stage); each lane unpacks its 8 bytes into 16 codes
-// (nibble - 8) whose K order is 0,2,4,6 | 1,3,5,7 | 8,10,.. | 9,11,..; the
-// activation chunks are byte-permuted into the same order when they are
-// staged, so the MFMA pairs every activation code with its weight code.
+// Kernels in this file:
+//   gemm_dma_kernel     per-channel / W4A8 / int32 test hook, M > 16: operands
+//                       stream global -> LDS by buffer-load DMA, NS stages deep
+//   gemm_dma_pg_kernel  per-group (gs 64 / 128), same pipeline plus group
+//                       scales gathered into LDS
+//   gemm_skinny_kernel  M <= 16: fragments buffer-loaded straight into MFMA
+//                       registers, K split across the block's waves
+//   gemm_gemv_kernel    M <= 4 per-channel / W4A8: full-cache-line weight
+//                       stream with v_dot4_i32_i8
+// W4A8 keeps the weights packed (in LDS or registers) and unpacks each lane's
+// bytes into codes (nibble - 8) in the order 0,2,4,6 | 1,3,5,7 | ...; the
+// activation bytes are permuted into the same order, so every MFMA / dot4
+// pairs each activation code with its weight code.
 #include <type_traits>
 
 #include "cider_internal.h"
@@ -43,15 +42,7 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
-
-constexpr int kBK = 64;   // K codes per pipeline stage
-
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
-__device__ __forceinline__ int lds_off(int row, int chunk) { return row * 64 + ((chunk ^ swz(row)) << 4); }
-
-// Packed int4 tile: 32 bytes per row = four 8-byte slots; slot t of row r sits
-// at t ^ swz4(r) so 16 consecutive rows read the same slot on distinct banks.
-__device__ __forceinline__ int swz4(int row) { return (row >> 2) & 3; }
+typedef int v16i __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ v4i zero4() { return v4i{0, 0, 0, 0}; }
 
@@ -81,79 +72,6 @@ __device__ __forceinline__ v4i unpack_int4(uint2 p) {
   return o;
 }
 
-// Global -> register -> LDS loader of an int8 [rows, K] tile slice of 64 K
-// codes: ROWS * 4 chunks of 16 bytes spread over NT threads.
-template <int ROWS, int NT, bool PERMUTE>
-struct Int8TileLoader {
-  static constexpr int kTotal = ROWS * 4;
-  static constexpr int kPer = (kTotal + NT - 1) / NT;
-  static_assert(kTotal % NT == 0 || kTotal < NT, "tile chunks must divide evenly");
-  v4i reg[kPer];
-
-  __device__ __forceinline__ void load(const int8_t* __restrict__ g, int64_t ld, int rows_valid,
-                                       int64_t k0, int64_t K, int tid) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int f = tid + i * NT;
-      const int r = f >> 2, c = f & 3;
-      if (f >= kTotal) break;
-      const int64_t k = k0 + c * 16;
-      if (r < rows_valid && k < K)
-        reg[i] = *reinterpret_cast<const v4i*>(g + (int64_t)r * ld + k);
-      else
-        reg[i] = zero4();
-    }
-  }
-  __device__ __forceinline__ void store(int8_t* lds, int tid) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int f = tid + i * NT;
-      const int r = f >> 2, c = f & 3;
-      if (f >= kTotal) break;
-      *reinterpret_cast<v4i*>(lds + lds_off(r, c)) = PERMUTE ? even_odd_bytes(reg[i]) : reg[i];
-    }
-  }
-};
-
-// Loader of a packed int4 [rows, K/2] tile slice (64 codes = 32 bytes per row).
-template <int ROWS, int NT>
-struct Int4TileLoader {
-  static constexpr int kTotal = ROWS * 2;
-  static constexpr int kPer = (kTotal + NT - 1) / NT;
-  static_assert(kTotal % NT == 0 || kTotal < NT, "tile chunks must divide evenly");
-  v4i reg[kPer];
-
-  __device__ __forceinline__ void load(const uint8_t* __restrict__ g, int64_t ld_bytes, int rows_valid,
-                                       int64_t k0, int64_t K, int tid) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int f = tid + i * NT;
-      const int r = f >> 1, c = f & 1;
-      if (f >= kTotal) break;
-      const int64_t k = k0 + c * 32;   // 16 packed bytes = 32 codes
-      if (r < rows_valid && k < K)
-        reg[i] = *reinterpret_cast<const v4i*>(g + (int64_t)r * ld_bytes + k / 2);
-      else
-        reg[i] = zero4();   // rows past N feed discarded outputs; K past the end meets zero activations
-    }
-  }
-  __device__ __forceinline__ void store(int8_t* lds, int tid) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int f = tid + i * NT;
-      const int r = f >> 1, c = f & 1;
-      if (f >= kTotal) break;
-      // chunk c = 8-byte slots 2c, 2c+1 -> physical slots (2c)^s, (2c+1)^s,
-      // which form the aligned pair starting at ((2c)^s) & ~1, swapped when s is odd.
-      const int s = swz4(r);
-      const int base = ((2 * c) ^ s) & ~1;
-      v4i v = reg[i];
-      if (s & 1) v = v4i{v.z, v.w, v.x, v.y};
-      *reinterpret_cast<v4i*>(lds + r * 32 + base * 8) = v;
-    }
-  }
-};
-
 // ---------------------------------------------------------------------------
 // Direct-to-LDS pipeline (per-channel and W4A8).
 //
@@ -168,13 +86,14 @@ struct Int4TileLoader {
 
 // Physical 16-byte slot of logical chunk c in tile row r, for rows of RB bytes.
 // Both XOR patterns were chosen by measurement on gfx950 (64 LDS banks): with
-// them the fragment reads of 16 consecutive rows (one chunk per 16-lane group)
-// complete in 4 cycles per ds_read_b128 with no bank-conflict cycles, while
-// e.g. c ^ (r & 3) or c ^ (((r >> 1) ^ (r >> 3)) & 3) on 64-byte rows take 8.
+// them the MFMA fragment reads (16 consecutive rows per 16-lane group for the
+// 16x16x64 shape, 32 rows per 32-lane group for 32x32x32) complete in 4
+// cycles per ds_read_b128 with no bank-conflict cycles, while e.g. c ^ (r & 3)
+// on 64-byte rows or c ^ (r & 7) on 128-byte rows take 8 for some of them.
 template <int RB>
 __device__ __forceinline__ int slot_of(int r, int c) {
   if constexpr (RB == 64) return c ^ ((r >> 1) & 3);
-  else return c ^ (r & 7);
+  else return c ^ ((r >> 1) & 7);
 }
 
 template <int RB>
@@ -222,28 +141,32 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WGM, int WGN, int BK, int NS, int WK, int EPI>
+template <int BM, int BN, int WGM, int WGN, int BK, int NS, int WK, int EPI, int MF = 16>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, const void* __restrict__ Wv,
                 const float* __restrict__ SW, int M, int N, int K, _Float16* __restrict__ Y,
                 int32_t* __restrict__ ACC) {
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
-  constexpr int TM = WTM / 16, TN = WTN / 16;
+  constexpr int TM = WTM / MF, TN = WTN / MF;
   constexpr bool kI4 = WK == kWeightI4;
+  static_assert(MF == 16, "16x16x64 MFMA tiles (32x32x32 measured ~4% slower on this kernel)");
+  using acc_t = typename std::conditional<MF == 16, v4i, v16i>::type;
+  constexpr int NR = MF == 16 ? 4 : 16;       // accumulator registers per tile
   constexpr int RBA = BK;                     // activation bytes per row per stage
   constexpr int RBW = kI4 ? BK / 2 : BK;      // weight bytes per row per stage
   constexpr int kStageBytes = BM * RBA + BN * RBW;
   constexpr int LPS = (BM * RBA + BN * RBW) / 1024 / NW;   // DMA instructions per wave per stage
   static_assert(!kI4 || BK == 128, "int4 weights use 128-code stages (64-byte packed rows)");
   static_assert(BK == 64 || BK == 128, "stage depth");
-  static_assert(TM * 16 == WTM && TN * 16 == WTN, "wave tile must be a multiple of 16");
+  static_assert(TM * MF == WTM && TN * MF == WTN, "wave tile must be a multiple of the MFMA tile");
 
   __shared__ __attribute__((aligned(1024))) int8_t smem[NS * kStageBytes];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = (wave % WGM) * WTM, wn = (wave / WGM) * WTN;
   const int l16 = lane & 15, l4 = lane >> 4;
+  const int l32 = lane & 31, l2 = lane >> 5;
 
   // tile index: XCD-contiguous ranges, then groups of 8 tile-rows of M
   const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
@@ -268,11 +191,13 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
   const __amdgpu_buffer_rsrc_t rw =
       make_rsrc(static_cast<const int8_t*>(Wv) + (int64_t)n0 * ldw, (uint32_t)rows_w * ldw);
 
-  v4i acc[TN][TM];
+  acc_t acc[TN][TM];
 #pragma unroll
   for (int a = 0; a < TN; ++a)
 #pragma unroll
-    for (int b = 0; b < TM; ++b) acc[a][b] = zero4();
+    for (int b = 0; b < TM; ++b)
+#pragma unroll
+      for (int r = 0; r < NR; ++r) acc[a][b][r] = 0;
 
   const int KT = (K + BK - 1) / BK;
   auto issue = [&](int kt) {
@@ -334,230 +259,33 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
   }
   wait_vmcnt<0>();
 
-  // ---- epilogue: y = fp16(((float)acc * s_a[m]) * s_w[n]), or the raw int32
+  // ---- epilogue: y = fp16(((float)acc * s_a[m]) * s_w[n]), or the raw int32.
+  // Lane l holds column m = l % MF of each tile and, per group q of 4 registers,
+  // the 4 consecutive rows n = 8q + 4(l/32) .. +3 (32x32) or 4(l/16) .. +3 (16x16).
   const bool vec_ok = (N & 3) == 0;
 #pragma unroll
   for (int b = 0; b < TM; ++b) {
-    const int m = m0 + wm + 16 * b + l16;
+    const int m = m0 + wm + MF * b + (MF == 16 ? l16 : l32);
     if (m >= M) continue;
     float sam = 0.0f;
     if constexpr (EPI == kEpiF16) sam = SA[m];
 #pragma unroll
     for (int a = 0; a < TN; ++a) {
-      const int n = n0 + wn + 16 * a + 4 * l4;
-      if (n >= N) continue;
-      if constexpr (EPI == kEpiAccI32) {
-        int32_t* dst = ACC + (int64_t)m * N + n;
-        if (vec_ok && n + 3 < N) {
-          *reinterpret_cast<v4i*>(dst) = acc[a][b];
-        } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (n + r < N) dst[r] = acc[a][b][r];
-        }
-      } else {
-        float sw[4];
-        if (vec_ok && n + 3 < N) {
-          const float4 s4 = *reinterpret_cast<const float4*>(SW + n);
-          sw[0] = s4.x; sw[1] = s4.y; sw[2] = s4.z; sw[3] = s4.w;
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sw[r] = SW[min(n + r, N - 1)];
-        }
-        h4 o;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = (_Float16)(((float)acc[a][b][r] * sam) * sw[r]);
-        _Float16* dst = Y + (int64_t)m * N + n;
-        if (vec_ok && n + 3 < N) {
-          *reinterpret_cast<h4*>(dst) = o;
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (n + r < N) dst[r] = o[r];
-        }
-      }
-    }
-  }
-}
-
-// Block tile BM (activation rows) x BN (weight rows); WGM x WGN waves.
-template <int BM, int BN, int WGM, int WGN, int WK, int GS, int EPI>
-__global__ void __launch_bounds__(WGM * WGN * 64)
-gemm_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, const void* __restrict__ Wv,
-            const float* __restrict__ SW, int M, int N, int64_t K, _Float16* __restrict__ Y,
-            int32_t* __restrict__ ACC) {
-  constexpr int NT = WGM * WGN * 64;
-  constexpr int WTM = BM / WGM, WTN = BN / WGN;     // wave tile (m rows, n rows)
-  constexpr int TM = WTM / 16, TN = WTN / 16;       // 16x16 sub-tiles per wave
-  constexpr bool kI4 = WK == kWeightI4;
-  constexpr int kWRowBytes = kI4 ? 32 : 64;        // LDS bytes per weight row per stage
-  static_assert(TM * 16 == WTM && TN * 16 == WTN, "wave tile must be a multiple of 16");
-
-  __shared__ __attribute__((aligned(16))) int8_t sA[2][BM * 64];
-  __shared__ __attribute__((aligned(16))) int8_t sW[2][BN * kWRowBytes];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = (wave % WGM) * WTM, wn = (wave / WGM) * WTN;
-  const int l16 = lane & 15, l4 = lane >> 4;
-
-  // ---- tile index: XCD-contiguous ranges, then groups of 8 tile-rows of M
-  const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
-  const int total = nbm * nbn;
-  int tile;
-  {
-    const int b = blockIdx.x, xcd = b & 7, idx = b >> 3;
-    const int per = total >> 3, rem = total & 7;
-    tile = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
-  }
-  constexpr int kGroupM = 8;
-  const int group = tile / (kGroupM * nbn);
-  const int first_m = group * kGroupM;
-  const int gsz = min(nbm - first_m, kGroupM);
-  const int tm = first_m + (tile % (kGroupM * nbn)) % gsz;
-  const int tn = (tile % (kGroupM * nbn)) / gsz;
-  const int m0 = tm * BM, n0 = tn * BN;
-
-  const int8_t* Ab = A + (int64_t)m0 * K;
-  const int rows_a = min(BM, M - m0), rows_w = min(BN, N - n0);
-
-  Int8TileLoader<BM, NT, kI4> la;
-  typename std::conditional<kI4, Int4TileLoader<BN, NT>, Int8TileLoader<BN, NT, false>>::type lw;
-  const int64_t w_ld = kI4 ? K / 2 : K;
-  const auto* Wb = static_cast<const typename std::conditional<kI4, uint8_t, int8_t>::type*>(Wv) +
-                   (int64_t)n0 * w_ld;
-
-  v4i acc[TN][TM];
-#pragma unroll
-  for (int a = 0; a < TN; ++a)
-#pragma unroll
-    for (int b = 0; b < TM; ++b) acc[a][b] = zero4();
-
-  constexpr int kG = GS == 0 ? 1 : GS;
-  float facc[GS == 0 ? 1 : TN][GS == 0 ? 1 : TM][GS == 0 ? 1 : 4];
-  if constexpr (GS != 0) {
-#pragma unroll
-    for (int a = 0; a < TN; ++a)
-#pragma unroll
-      for (int b = 0; b < TM; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) facc[a][b][r] = 0.0f;
-  }
-  const int G = GS == 0 ? 1 : (int)(K / kG);
-
-  const int KT = (int)((K + kBK - 1) / kBK);
-  la.load(Ab, K, rows_a, 0, K, tid);
-  lw.load(Wb, w_ld, rows_w, 0, K, tid);
-  la.store(sA[0], tid);
-  lw.store(sW[0], tid);
-  __syncthreads();
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < KT;
-    if (more) {
-      la.load(Ab, K, rows_a, (int64_t)(kt + 1) * kBK, K, tid);
-      lw.load(Wb, w_ld, rows_w, (int64_t)(kt + 1) * kBK, K, tid);
-    }
-    {
-      const int8_t* a_s = sA[cur];
-      const int8_t* w_s = sW[cur];
-      v4i wf[TN], af[TM];
-#pragma unroll
-      for (int a = 0; a < TN; ++a) {
-        const int row = wn + 16 * a + l16;
-        if constexpr (kI4) {
-          const uint2 p = *reinterpret_cast<const uint2*>(w_s + row * 32 + ((l4 ^ swz4(row)) << 3));
-          wf[a] = unpack_int4(p);
-        } else {
-          wf[a] = *reinterpret_cast<const v4i*>(w_s + lds_off(row, l4));
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < TM; ++b) af[b] = *reinterpret_cast<const v4i*>(a_s + lds_off(wm + 16 * b + l16, l4));
-#pragma unroll
-      for (int a = 0; a < TN; ++a)
-#pragma unroll
-        for (int b = 0; b < TM; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[a], af[b], acc[a][b], 0, 0, 0);
-    }
-    if constexpr (GS != 0) {
-      // a group ends after every GS/64 stages
-      if (((kt + 1) * kBK) % GS == 0) {
-        const int g = (kt + 1) * kBK / GS - 1;
+      for (int q = 0; q < NR / 4; ++q) {
+        const int n = n0 + wn + MF * a + (MF == 16 ? 4 * l4 : 8 * q + 4 * l2);
+        if (n >= N) continue;
         if constexpr (EPI == kEpiAccI32) {
-#pragma unroll
-          for (int a = 0; a < TN; ++a)
-#pragma unroll
-            for (int b = 0; b < TM; ++b) {
-              const int m = m0 + wm + 16 * b + l16;
-              const int n = n0 + wn + 16 * a + 4 * l4;
-              if (m < M) {
-                int32_t* dst = ACC + ((int64_t)g * M + m) * N;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                  if (n + r < N) dst[n + r] = acc[a][b][r];
-              }
-              acc[a][b] = zero4();
-            }
-        } else {
-          float sa[TM];
-#pragma unroll
-          for (int b = 0; b < TM; ++b) {
-            const int m = min(m0 + wm + 16 * b + l16, M - 1);
-            sa[b] = SA[(int64_t)m * G + g];
-          }
-#pragma unroll
-          for (int a = 0; a < TN; ++a) {
-            float sw[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int n = min(n0 + wn + 16 * a + 4 * l4 + r, N - 1);
-              sw[r] = SW[(int64_t)n * G + g];
-            }
-#pragma unroll
-            for (int b = 0; b < TM; ++b) {
-#pragma unroll
-              for (int r = 0; r < 4; ++r) facc[a][b][r] += ((float)acc[a][b][r] * sa[b]) * sw[r];
-              acc[a][b] = zero4();
-            }
-          }
-        }
-      }
-    }
-    if (more) {
-      la.store(sA[cur ^ 1], tid);
-      lw.store(sW[cur ^ 1], tid);
-    }
-    __syncthreads();
-  }
-
-  // ---- epilogue
-  const bool vec_ok = (N & 3) == 0;
-#pragma unroll
-  for (int b = 0; b < TM; ++b) {
-    const int m = m0 + wm + 16 * b + l16;
-    if (m >= M) continue;
-    float sam = 0.0f;
-    if constexpr (GS == 0 && EPI == kEpiF16) sam = SA[m];
-#pragma unroll
-    for (int a = 0; a < TN; ++a) {
-      const int n = n0 + wn + 16 * a + 4 * l4;
-      if (n >= N) continue;
-      if constexpr (EPI == kEpiAccI32) {
-        if constexpr (GS == 0) {
           int32_t* dst = ACC + (int64_t)m * N + n;
           if (vec_ok && n + 3 < N) {
-            *reinterpret_cast<v4i*>(dst) = acc[a][b];
+            *reinterpret_cast<v4i*>(dst) =
+                v4i{acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]};
           } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              if (n + r < N) dst[r] = acc[a][b][r];
+              if (n + r < N) dst[r] = acc[a][b][4 * q + r];
           }
-        }
-      } else {
-        h4 o;
-        if constexpr (GS == 0) {
+        } else {
           float sw[4];
           if (vec_ok && n + 3 < N) {
             const float4 s4 = *reinterpret_cast<const float4*>(SW + n);
@@ -566,32 +294,21 @@ gemm_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, const vo
 #pragma unroll
             for (int r = 0; r < 4; ++r) sw[r] = SW[min(n + r, N - 1)];
           }
+          h4 o;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = (_Float16)(((float)acc[a][b][r] * sam) * sw[r]);
-        } else {
+          for (int r = 0; r < 4; ++r) o[r] = (_Float16)(((float)acc[a][b][4 * q + r] * sam) * sw[r]);
+          _Float16* dst = Y + (int64_t)m * N + n;
+          if (vec_ok && n + 3 < N) {
+            *reinterpret_cast<h4*>(dst) = o;
+          } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = (_Float16)facc[a][b][r];
-        }
-        _Float16* dst = Y + (int64_t)m * N + n;
-        if (vec_ok && n + 3 < N) {
-          *reinterpret_cast<h4*>(dst) = o;
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (n + r < N) dst[r] = o[r];
+            for (int r = 0; r < 4; ++r)
+              if (n + r < N) dst[r] = o[r];
+          }
         }
       }
     }
   }
-}
-
-template <int BM, int BN, int WGM, int WGN, int WK, int GS, int EPI>
-hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
-  const int64_t nbm = (g.M + BM - 1) / BM, nbn = (g.N + BN - 1) / BN;
-  const dim3 grid((unsigned)(nbm * nbn)), block(WGM * WGN * 64);
-  gemm_kernel<BM, BN, WGM, WGN, WK, GS, EPI><<<grid, block, 0, st>>>(
-      g.a, g.sa, g.w, g.sw, (int)g.M, (int)g.N, g.K, static_cast<_Float16*>(g.y), g.acc);
-  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -1070,11 +787,11 @@ hipError_t launch_dma_pg(const GemmArgs& g, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WGM, int WGN, int BK, int NS, int WK, int EPI>
+template <int BM, int BN, int WGM, int WGN, int BK, int NS, int WK, int EPI, int MF = 16>
 hipError_t launch_dma(const GemmArgs& g, hipStream_t st) {
   const int64_t nbm = (g.M + BM - 1) / BM, nbn = (g.N + BN - 1) / BN;
   const dim3 grid((unsigned)(nbm * nbn)), block(WGM * WGN * 64);
-  gemm_dma_kernel<BM, BN, WGM, WGN, BK, NS, WK, EPI><<<grid, block, 0, st>>>(
+  gemm_dma_kernel<BM, BN, WGM, WGN, BK, NS, WK, EPI, MF><<<grid, block, 0, st>>>(
       g.a, g.sa, g.w, g.sw, (int)g.M, (int)g.N, (int)g.K, static_cast<_Float16*>(g.y), g.acc);
   return hipGetLastError();
 }
