@@ -42,9 +42,33 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
-typedef int v16i __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ v4i zero4() { return v4i{0, 0, 0, 0}; }
+
+// Per-channel dequant of one element: fp16(fp32(fp32(acc) * s_a) * s_w), each
+// product rounded to fp32 before the round-to-nearest-even fp16 conversion.
+// The empty asm pins the second product as an fp32 register value: without it
+// the backend fuses that multiply with the conversion into v_fma_mixlo_f16
+// (even with contraction off), whose result differs from the two-step
+// rounding in rare cases.
+__device__ __forceinline__ _Float16 dequant1(int32_t acc, float sa, float sw) {
+  float t = (float)acc * sa;
+  t = t * sw;
+  asm("" : "+v"(t));
+  return (_Float16)t;
+}
+
+// Four consecutive outputs of one row (the same rounding as dequant1).
+__device__ __forceinline__ h4 dequant4(v4i acc, float sa, float4 sw) {
+  float4 t;
+  t.x = ((float)acc.x * sa) * sw.x;
+  t.y = ((float)acc.y * sa) * sw.y;
+  t.z = ((float)acc.z * sa) * sw.z;
+  t.w = ((float)acc.w * sa) * sw.w;
+  asm("" : "+v"(t.x), "+v"(t.y), "+v"(t.z), "+v"(t.w));
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  return __builtin_convertvector(f4{t.x, t.y, t.z, t.w}, h4);
+}
 
 // Reorder 16 activation codes (4 dwords, K order 0..15) into the order the
 // unpacked int4 weights come in: 0,2,4,6 | 1,3,5,7 | 8,10,12,14 | 9,11,13,15.
@@ -106,25 +130,42 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// DMA instructions each wave issues per stage for a ROWS x RB-byte tile.
+template <int ROWS, int RB, int NW>
+constexpr int dma_per_wave() {
+  static_assert(ROWS * RB % 1024 == 0, "a stage tile is a whole number of 1 KiB blocks");
+  return (ROWS * RB / 1024 + NW - 1) / NW;
+}
+
 // Issue the DMA loads of one stage of a ROWS x RB-byte operand tile. Block j
 // of 1 KiB holds rows j*(1024/RB) ...; lane L writes LDS bytes L*16..L*16+15
-// of its block, i.e. physical slot L % (RB/16) of block row L / (RB/16).
+// of its block, i.e. physical slot L % (RB/16) of block row L / (RB/16). When
+// the blocks do not split evenly over the NW waves, a wave with no block left
+// issues a zero-fill load (out-of-range offset) into the 1 KiB `pad`, so that
+// every wave issues the same number of DMA instructions per stage and one
+// s_waitcnt vmcnt count fits all waves. `wave` must be wave-uniform.
 template <int ROWS, int RB, int NW>
-__device__ __forceinline__ void dma_stage(__amdgpu_buffer_rsrc_t rsrc, int8_t* lds, int wave, int lane,
-                                          uint32_t ld, int kb0, int kb_total) {
+__device__ __forceinline__ void dma_stage(__amdgpu_buffer_rsrc_t rsrc, int8_t* lds, int8_t* pad, int wave,
+                                          int lane, uint32_t ld, int kb0, int kb_total) {
   constexpr int kBlocks = ROWS * RB / 1024;
   constexpr int kSlots = RB / 16;
   constexpr int kRowsPerBlock = 1024 / RB;
-  static_assert(kBlocks % NW == 0, "1 KiB blocks must spread evenly over the waves");
 #pragma unroll
-  for (int i = 0; i < kBlocks / NW; ++i) {
+  for (int i = 0; i < dma_per_wave<ROWS, RB, NW>(); ++i) {
     const int j = wave + i * NW;
     const int r = j * kRowsPerBlock + lane / kSlots;
     const int p = lane % kSlots;
     const int c = slot_of<RB>(r, p);          // the XOR swizzle is an involution
     const int kb = kb0 + c * 16;
-    const uint32_t off = kb < kb_total ? (uint32_t)r * ld + (uint32_t)kb : 0x80000000u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + j * 1024), 16, off, 0, 0, 0);
+    uint32_t off = kb < kb_total ? (uint32_t)r * ld + (uint32_t)kb : 0x80000000u;
+    int8_t* dst = lds + j * 1024;
+    if constexpr (kBlocks % NW != 0) {
+      if (j >= kBlocks) {
+        off = 0x80000000u;
+        dst = pad;
+      }
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, off, 0, 0, 0);
   }
 }
 
@@ -141,32 +182,37 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WGM, int WGN, int BK, int NS, int WK, int EPI, int MF = 16>
+template <int BM, int BN, int WGM, int WGN, int BK, int NS, int WK, int EPI>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, const void* __restrict__ Wv,
                 const float* __restrict__ SW, int M, int N, int K, _Float16* __restrict__ Y,
                 int32_t* __restrict__ ACC) {
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
-  constexpr int TM = WTM / MF, TN = WTN / MF;
+  constexpr int TM = WTM / 16, TN = WTN / 16;
   constexpr bool kI4 = WK == kWeightI4;
-  static_assert(MF == 16, "16x16x64 MFMA tiles (32x32x32 measured ~4% slower on this kernel)");
-  using acc_t = typename std::conditional<MF == 16, v4i, v16i>::type;
-  constexpr int NR = MF == 16 ? 4 : 16;       // accumulator registers per tile
+  constexpr bool kF16 = EPI == kEpiF16;
   constexpr int RBA = BK;                     // activation bytes per row per stage
   constexpr int RBW = kI4 ? BK / 2 : BK;      // weight bytes per row per stage
   constexpr int kStageBytes = BM * RBA + BN * RBW;
-  constexpr int LPS = (BM * RBA + BN * RBW) / 1024 / NW;   // DMA instructions per wave per stage
+  constexpr int LPS = dma_per_wave<BM, RBA, NW>() + dma_per_wave<BN, RBW, NW>();   // per wave per stage
   static_assert(!kI4 || BK == 128, "int4 weights use 128-code stages (64-byte packed rows)");
   static_assert(BK == 64 || BK == 128, "stage depth");
-  static_assert(TM * MF == WTM && TN * MF == WTN, "wave tile must be a multiple of the MFMA tile");
+  static_assert(TM * 16 == WTM && TN * 16 == WTN, "wave tile must be a multiple of the MFMA tile");
 
-  __shared__ __attribute__((aligned(1024))) int8_t smem[NS * kStageBytes];
+  // NS operand stages, the 1 KiB zero-fill pad when the DMA blocks do not
+  // split evenly over the waves, then (fp16 store stage only) the tile's
+  // scales: s_a of its BM rows followed by s_w of its BN columns, zero past M / N.
+  constexpr bool kPad = (BM * RBA / 1024) % NW != 0 || (BN * RBW / 1024) % NW != 0;
+  constexpr int kPadBytes = kPad ? 1024 : 0;
+  constexpr int kScaleBytes = kF16 ? (BM + BN) * 4 : 0;
+  __shared__ __attribute__((aligned(1024))) int8_t smem[NS * kStageBytes + kPadBytes + kScaleBytes];
+  int8_t* const pad = smem + NS * kStageBytes;
+  float* const lsc = reinterpret_cast<float*>(smem + NS * kStageBytes + kPadBytes);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = (wave % WGM) * WTM, wn = (wave / WGM) * WTN;
   const int l16 = lane & 15, l4 = lane >> 4;
-  const int l32 = lane & 31, l2 = lane >> 5;
 
   // tile index: XCD-contiguous ranges, then groups of 8 tile-rows of M
   const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
@@ -191,23 +237,49 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
   const __amdgpu_buffer_rsrc_t rw =
       make_rsrc(static_cast<const int8_t*>(Wv) + (int64_t)n0 * ldw, (uint32_t)rows_w * ldw);
 
-  acc_t acc[TN][TM];
+  // Scale loads go out first: their latency overlaps the first stages' DMA,
+  // and the store stage later reads them from LDS instead of global memory.
+  constexpr int kScalesPerThread = (BM + BN + NW * 64 - 1) / (NW * 64);
+  float scl[kScalesPerThread];
+  if constexpr (kF16) {
+#pragma unroll
+    for (int i = 0; i < kScalesPerThread; ++i) {
+      const int t = threadIdx.x + i * NW * 64;
+      float v = 0.0f;
+      if (t < BM) {
+        if (t < rows_a) v = SA[m0 + t];
+      } else if (t < BM + BN) {
+        if (t - BM < rows_w) v = SW[n0 + t - BM];
+      }
+      scl[i] = v;
+    }
+  }
+
+  v4i acc[TN][TM];
 #pragma unroll
   for (int a = 0; a < TN; ++a)
 #pragma unroll
-    for (int b = 0; b < TM; ++b)
-#pragma unroll
-      for (int r = 0; r < NR; ++r) acc[a][b][r] = 0;
+    for (int b = 0; b < TM; ++b) acc[a][b] = zero4();
 
   const int KT = (K + BK - 1) / BK;
   auto issue = [&](int kt) {
     int8_t* st = smem + (kt % NS) * kStageBytes;
-    dma_stage<BM, RBA, NW>(ra, st, wave, lane, lda, kt * RBA, (int)lda);
-    dma_stage<BN, RBW, NW>(rw, st + BM * RBA, wave, lane, ldw, kt * RBW, (int)ldw);
+    dma_stage<BM, RBA, NW>(ra, st, pad, wave, lane, lda, kt * RBA, (int)lda);
+    dma_stage<BN, RBW, NW>(rw, st + BM * RBA, pad, wave, lane, ldw, kt * RBW, (int)ldw);
   };
 
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) issue(s);
+
+  if constexpr (kF16) {
+#pragma unroll
+    for (int i = 0; i < kScalesPerThread; ++i) {
+      const int t = threadIdx.x + i * NW * 64;
+      if (t < BM + BN) lsc[t] = scl[i];
+    }
+    // lgkmcnt(0): the scale writes land before the first stage barrier publishes them
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+  }
 
   for (int kt = 0; kt < KT; ++kt) {
     wait_vmcnt<(NS - 2) * LPS>();
@@ -259,52 +331,42 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
   }
   wait_vmcnt<0>();
 
-  // ---- epilogue: y = fp16(((float)acc * s_a[m]) * s_w[n]), or the raw int32.
-  // Lane l holds column m = l % MF of each tile and, per group q of 4 registers,
-  // the 4 consecutive rows n = 8q + 4(l/32) .. +3 (32x32) or 4(l/16) .. +3 (16x16).
+  // ---- store stage: y = fp16((fp32(acc) * s_a[m]) * s_w[n]), or the raw int32.
+  // Lane l holds column m = l % 16 of each 16x16 tile and the 4 consecutive
+  // rows n = 4(l/16) .. +3, i.e. 4 consecutive outputs of one row of y.
   const bool vec_ok = (N & 3) == 0;
+  const float* const lsa = lsc;
+  const float* const lsw = lsc + BM;
 #pragma unroll
   for (int b = 0; b < TM; ++b) {
-    const int m = m0 + wm + MF * b + (MF == 16 ? l16 : l32);
+    const int ml = wm + 16 * b + l16;
+    const int m = m0 + ml;
     if (m >= M) continue;
     float sam = 0.0f;
-    if constexpr (EPI == kEpiF16) sam = SA[m];
+    if constexpr (kF16) sam = lsa[ml];
 #pragma unroll
     for (int a = 0; a < TN; ++a) {
-#pragma unroll
-      for (int q = 0; q < NR / 4; ++q) {
-        const int n = n0 + wn + MF * a + (MF == 16 ? 4 * l4 : 8 * q + 4 * l2);
-        if (n >= N) continue;
-        if constexpr (EPI == kEpiAccI32) {
-          int32_t* dst = ACC + (int64_t)m * N + n;
-          if (vec_ok && n + 3 < N) {
-            *reinterpret_cast<v4i*>(dst) =
-                v4i{acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]};
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (n + r < N) dst[r] = acc[a][b][4 * q + r];
-          }
+      const int nl = wn + 16 * a + 4 * l4;
+      const int n = n0 + nl;
+      if (n >= N) continue;
+      if constexpr (!kF16) {
+        int32_t* dst = ACC + (int64_t)m * N + n;
+        if (vec_ok && n + 3 < N) {
+          *reinterpret_cast<v4i*>(dst) = acc[a][b];
         } else {
-          float sw[4];
-          if (vec_ok && n + 3 < N) {
-            const float4 s4 = *reinterpret_cast<const float4*>(SW + n);
-            sw[0] = s4.x; sw[1] = s4.y; sw[2] = s4.z; sw[3] = s4.w;
-          } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sw[r] = SW[min(n + r, N - 1)];
-          }
-          h4 o;
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) dst[r] = acc[a][b][r];
+        }
+      } else {
+        const h4 o = dequant4(acc[a][b], sam, *reinterpret_cast<const float4*>(lsw + nl));   // s_w zero past N
+        _Float16* dst = Y + (int64_t)m * N + n;
+        if (vec_ok && n + 3 < N) {
+          *reinterpret_cast<h4*>(dst) = o;
+        } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = (_Float16)(((float)acc[a][b][4 * q + r] * sam) * sw[r]);
-          _Float16* dst = Y + (int64_t)m * N + n;
-          if (vec_ok && n + 3 < N) {
-            *reinterpret_cast<h4*>(dst) = o;
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (n + r < N) dst[r] = o[r];
-          }
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) dst[r] = o[r];
         }
       }
     }
@@ -427,7 +489,7 @@ gemm_skinny_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, c
       const float sam = SA[m];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (n + r < N) Y[(int64_t)m * N + n + r] = (_Float16)(((float)t[r] * sam) * SW[n + r]);
+        if (n + r < N) Y[(int64_t)m * N + n + r] = dequant1(t[r], sam, SW[n + r]);
     }
   } else if constexpr (EPI == kEpiF16) {
 #pragma unroll
@@ -542,7 +604,7 @@ gemm_gemv_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, con
   if (m >= M || n >= N) return;
   const int t = red[0][r][m] + red[1][r][m] + red[2][r][m] + red[3][r][m];
   if constexpr (EPI == kEpiAccI32) ACC[(int64_t)m * N + n] = t;
-  else Y[(int64_t)m * N + n] = (_Float16)(((float)t * SA[m]) * SW[n]);
+  else Y[(int64_t)m * N + n] = dequant1(t, SA[m], SW[n]);
 }
 
 template <int MT, int WK, int EPI>
@@ -614,12 +676,14 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
   constexpr int kScaleBytes = GPS * (BM + BN) * 4 + 256;  // + a landing pad for the spares
   constexpr int kStageBytes = kCodeBytes + kScaleBytes;
   static_assert((BM + BN) % 64 == 0, "scale DMA covers 64 rows per instruction");
-  constexpr int LPS = kCodeBytes / 1024 / NW + kScalePer;
+  static_assert((BM * RB / 1024) % NW == 0 && (BN * RB / 1024) % NW == 0,
+                "code DMA blocks split evenly over the waves (no zero-fill pad here)");
+  constexpr int LPS = dma_per_wave<BM, RB, NW>() + dma_per_wave<BN, RB, NW>() + kScalePer;
   static_assert(TM * 16 == WTM && TN * 16 == WTN, "wave tile must be a multiple of 16");
 
   __shared__ __attribute__((aligned(1024))) int8_t smem[NS * kStageBytes];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = (wave % WGM) * WTM, wn = (wave / WGM) * WTN;
   const int l16 = lane & 15, l4 = lane >> 4;
 
@@ -664,8 +728,8 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
   const int KT = (K + BK - 1) / BK;
   auto issue = [&](int kt) {
     int8_t* st = smem + (kt % NS) * kStageBytes;
-    dma_stage<BM, RB, NW>(ra, st, wave, lane, ld, kt * RB, (int)ld);
-    dma_stage<BN, RB, NW>(rw, st + BM * RB, wave, lane, ld, kt * RB, (int)ld);
+    dma_stage<BM, RB, NW>(ra, st, nullptr, wave, lane, ld, kt * RB, (int)ld);
+    dma_stage<BN, RB, NW>(rw, st + BM * RB, nullptr, wave, lane, ld, kt * RB, (int)ld);
 #pragma unroll
     for (int i = 0; i < kScalePer; ++i) {
       const int j = wave + i * NW;
@@ -787,42 +851,72 @@ hipError_t launch_dma_pg(const GemmArgs& g, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WGM, int WGN, int BK, int NS, int WK, int EPI, int MF = 16>
+template <int BM, int BN, int WGM, int WGN, int BK, int NS, int WK, int EPI>
 hipError_t launch_dma(const GemmArgs& g, hipStream_t st) {
   const int64_t nbm = (g.M + BM - 1) / BM, nbn = (g.N + BN - 1) / BN;
   const dim3 grid((unsigned)(nbm * nbn)), block(WGM * WGN * 64);
-  gemm_dma_kernel<BM, BN, WGM, WGN, BK, NS, WK, EPI, MF><<<grid, block, 0, st>>>(
+  gemm_dma_kernel<BM, BN, WGM, WGN, BK, NS, WK, EPI><<<grid, block, 0, st>>>(
       g.a, g.sa, g.w, g.sw, (int)g.M, (int)g.N, (int)g.K, static_cast<_Float16*>(g.y), g.acc);
   return hipGetLastError();
 }
 
-// Per-channel and W4A8 tiles. The largest tile that still gives every CU a
-// block is used: 256 x 256 (eight waves of 128 (m) x 64 (n), two 64 KiB
-// stages of 128 codes) when there are enough output tiles, then 128 x 256,
-// 128 x 128 and 64 x 128 (four waves). Measured on MI355X with random int8
-// data, 256 x 256 ran fastest among the tested 128/256 shapes, 64/128-code
-// stages and 2-4 stage depths: the int8 MFMA path is power-limited (the
-// shader clock falls to ~1.5 GHz), so fewer LDS and L2 bytes per MFMA matter
-// more than occupancy. Wave tiles stay <= 128 x 64 (128 accumulator
-// registers): 128 x 128 wave tiles made the register allocator shuffle
-// accumulators between MFMAs.
 inline int64_t tiles_of(const GemmArgs& g, int bm, int bn) {
   return ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn);
 }
 
+// Per-channel and W4A8 tile choice. A launch of T tiles runs in about
+// ceil(T / 256) rounds of one block per CU, and a round of BM x BN tiles
+// costs about BM * BN * cost, where `cost` (time per output element per
+// round, relative) was measured on MI355X at K = 2560 with quantized
+// Gaussian codes: large tiles reuse each staged byte over more MFMAs, small
+// tiles fill the 256 CUs when M or N is small. The candidate with the lowest
+// ceil(T / 256) * BM * BN * cost is launched (ties: the earlier one). With
+// these costs e.g. M=4096 N=10240 takes 256 x 320 (512 tiles: two full
+// rounds) and M=1024 N=10240 or M=4096 N=2560 take 128 x 320 (256 tiles).
+struct TileCost {
+  int bm, bn, cost;
+};
+
+template <int NC>
+int cheapest_tile(const GemmArgs& g, const TileCost (&c)[NC]) {
+  int best = 0;
+  int64_t best_est = 0;
+  for (int i = 0; i < NC; ++i) {
+    const int64_t est = (tiles_of(g, c[i].bm, c[i].bn) + 255) / 256 * c[i].bm * c[i].bn * c[i].cost;
+    if (i == 0 || est < best_est) {
+      best = i;
+      best_est = est;
+    }
+  }
+  return best;
+}
+
+// Wave tiles stay <= 128 x 80 (160 accumulator registers) with two waves per
+// SIMD: larger wave tiles (128 x 128) made the register allocator shuffle
+// accumulators between MFMAs.
 template <int WK, int EPI>
 hipError_t launch_pc(const GemmArgs& g, hipStream_t st) {
-  constexpr int kFill = 224;   // blocks needed to keep most of the 256 CUs busy
   if constexpr (WK == kWeightI4) {
-    if (tiles_of(g, 128, 256) >= kFill) return launch_dma<128, 256, 2, 4, 128, 2, WK, EPI>(g, st);
-    if (tiles_of(g, 128, 128) >= kFill) return launch_dma<128, 128, 2, 2, 128, 2, WK, EPI>(g, st);
-    return launch_dma<64, 64, 1, 4, 128, 2, WK, EPI>(g, st);
+    static constexpr TileCost kTiles[] = {
+        {256, 320, 62}, {128, 320, 92}, {128, 256, 102}, {128, 128, 105}, {64, 64, 194}};
+    switch (cheapest_tile(g, kTiles)) {
+      case 0: return launch_dma<256, 320, 2, 4, 128, 2, WK, EPI>(g, st);
+      case 1: return launch_dma<128, 320, 2, 4, 128, 2, WK, EPI>(g, st);
+      case 2: return launch_dma<128, 256, 2, 4, 128, 2, WK, EPI>(g, st);
+      case 3: return launch_dma<128, 128, 2, 2, 128, 2, WK, EPI>(g, st);
+      default: return launch_dma<64, 64, 1, 4, 128, 2, WK, EPI>(g, st);
+    }
   } else {
-    if (tiles_of(g, 256, 256) >= kFill) return launch_dma<256, 256, 2, 4, 128, 2, WK, EPI>(g, st);
-    if (tiles_of(g, 128, 256) >= kFill) return launch_dma<128, 256, 2, 4, 128, 2, WK, EPI>(g, st);
-    if (tiles_of(g, 128, 128) >= kFill) return launch_dma<128, 128, 2, 2, 64, 3, WK, EPI>(g, st);
-    if (tiles_of(g, 64, 128) >= kFill) return launch_dma<64, 128, 1, 4, 64, 3, WK, EPI>(g, st);
-    return launch_dma<64, 64, 1, 4, 64, 3, WK, EPI>(g, st);
+    static constexpr TileCost kTiles[] = {{256, 320, 62}, {128, 320, 92}, {128, 256, 102},
+                                          {128, 128, 105}, {64, 160, 167}, {64, 64, 194}};
+    switch (cheapest_tile(g, kTiles)) {
+      case 0: return launch_dma<256, 320, 2, 4, 128, 2, WK, EPI>(g, st);
+      case 1: return launch_dma<128, 320, 2, 4, 128, 2, WK, EPI>(g, st);
+      case 2: return launch_dma<128, 256, 2, 4, 128, 2, WK, EPI>(g, st);
+      case 3: return launch_dma<128, 128, 2, 2, 64, 3, WK, EPI>(g, st);
+      case 4: return launch_dma<64, 160, 2, 2, 128, 2, WK, EPI>(g, st);
+      default: return launch_dma<64, 64, 1, 4, 64, 3, WK, EPI>(g, st);
+    }
   }
 }
 
