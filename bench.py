@@ -101,8 +101,9 @@ def algorithmic(mode, M, N, K, gs):
 def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_bytes=512 * 2 ** 20):
     """Times `steps` passes of quant_act + GEMM for one workload, rotating over
     enough buffer sets to keep the working set out of the 256 MB last-level
-    cache. Returns per-kernel average times from HIP events on the launch stream."""
-    import numpy as np
+    cache. Returns the time per step and each kernel's average launch duration,
+    all from HIP events on the launch stream (events only around each timed
+    loop, so no event sits between two timed launches)."""
     dev = torch.device("cuda:0")
     x_h = torch.from_numpy(inputs.activations(M, K, seed=0))
     w_h = torch.from_numpy(inputs.weights(N, K, seed=0))
@@ -128,29 +129,31 @@ def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_byte
         else:
             cider.cider_w8a8_gemm(xq, sa, wq, sw, gs, y, stream=stream)
 
+    def timed(body):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for i in range(steps):
+            body(*sets[i % R])
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps
+
+    def step(x, xq, sa, wq, sw, y):
+        cider.cider_quant_act(x, gs, xq, sa, stream=stream)
+        gemm(xq, sa, wq, sw, y)
+
     for i in range(warmup):
-        x, xq, sa, wq, sw, y = sets[i % R]
-        cider.cider_quant_act(x, gs, xq, sa, stream=stream)
-        gemm(xq, sa, wq, sw, y)
+        step(*sets[i % R])
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(steps):
-        x, xq, sa, wq, sw, y = sets[i % R]
-        ev[i][0].record(stream)
-        cider.cider_quant_act(x, gs, xq, sa, stream=stream)
-        ev[i][1].record(stream)
-        gemm(xq, sa, wq, sw, y)
-        ev[i][2].record(stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    g_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    # the timed steps: quant + GEMM back to back, events only around the region
+    step_ms = timed(step)
+    # each kernel's average launch duration: the same launches, one kernel kind
+    # at a time, back to back between two events on the launch stream
+    q_ms = timed(lambda x, xq, sa, wq, sw, y: cider.cider_quant_act(x, gs, xq, sa, stream=stream))
+    g_ms = timed(lambda x, xq, sa, wq, sw, y: gemm(xq, sa, wq, sw, y))
     del sets
     torch.cuda.empty_cache()
-    return {"ms_per_step": total_ms / steps, "quant_ms": q_ms, "gemm_ms": g_ms, "ops": ops,
+    return {"ms_per_step": step_ms, "quant_ms": q_ms, "gemm_ms": g_ms, "ops": ops,
             "gemm_bytes": gemm_bytes, "quant_bytes": quant_bytes, "sets": R}
 
 
