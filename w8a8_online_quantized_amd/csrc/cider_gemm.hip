@@ -182,11 +182,11 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WGM, int WGN, int BK, int NS, int WK, int EPI>
+template <int BM, int BN, int WGM, int WGN, int BK, int NS, int WK, int EPI, bool SPLIT = false>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, const void* __restrict__ Wv,
                 const float* __restrict__ SW, int M, int N, int K, _Float16* __restrict__ Y,
-                int32_t* __restrict__ ACC) {
+                int32_t* __restrict__ ACC, int splits, int32_t* __restrict__ WS) {
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int TM = WTM / 16, TN = WTN / 16;
@@ -214,14 +214,21 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
   const int wm = (wave % WGM) * WTM, wn = (wave / WGM) * WTN;
   const int l16 = lane & 15, l4 = lane >> 4;
 
-  // tile index: XCD-contiguous ranges, then groups of 8 tile-rows of M
+  // Work unit = (tile, K split); units are numbered tile-major and each of the
+  // 8 XCDs (block b runs on XCD b % 8) takes a contiguous range of them, so
+  // the splits of one tile share an L2. Tiles are then ordered in groups of 8
+  // tile-rows of M (L2 reuse of the weight tiles).
   const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
   const int total = nbm * nbn;
-  int tile;
+  const int nsplit = SPLIT ? splits : 1;
+  int tile, split;
   {
+    const int units = total * nsplit;
     const int b = blockIdx.x, xcd = b & 7, idx = b >> 3;
-    const int per = total >> 3, rem = total & 7;
-    tile = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    const int per = units >> 3, rem = units & 7;
+    const int unit = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    tile = unit / nsplit;
+    split = unit - tile * nsplit;
   }
   constexpr int kGroupM = 8;
   const int group = tile / (kGroupM * nbn);
@@ -230,6 +237,9 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
   const int tm = first_m + (tile % (kGroupM * nbn)) % gsz;
   const int tn = (tile % (kGroupM * nbn)) / gsz;
   const int m0 = tm * BM, n0 = tn * BN;
+  // this unit's codes [k0, k1): whole stages, the last split takes the rest
+  const int kc = ((K + nsplit - 1) / nsplit + BK - 1) / BK * BK;
+  const int k0 = split * kc, k1 = min(K, k0 + kc);
 
   const uint32_t lda = (uint32_t)K, ldw = kI4 ? (uint32_t)K / 2 : (uint32_t)K;
   const int rows_a = min(BM, M - m0), rows_w = min(BN, N - n0);
@@ -261,11 +271,13 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
 #pragma unroll
     for (int b = 0; b < TM; ++b) acc[a][b] = zero4();
 
-  const int KT = (K + BK - 1) / BK;
+  const int KT = (k1 - k0 + BK - 1) / BK;
+  const int kb1a = k1, kb1w = kI4 ? k1 / 2 : k1;
   auto issue = [&](int kt) {
     int8_t* st = smem + (kt % NS) * kStageBytes;
-    dma_stage<BM, RBA, NW>(ra, st, pad, wave, lane, lda, kt * RBA, (int)lda);
-    dma_stage<BN, RBW, NW>(rw, st + BM * RBA, pad, wave, lane, ldw, kt * RBW, (int)ldw);
+    const int kb = k0 + kt * BK;   // first code of stage kt
+    dma_stage<BM, RBA, NW>(ra, st, pad, wave, lane, lda, kb, kb1a);
+    dma_stage<BN, RBW, NW>(rw, st + BM * RBA, pad, wave, lane, ldw, kI4 ? kb / 2 : kb, kb1w);
   };
 
 #pragma unroll
@@ -330,6 +342,46 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
     }
   }
   wait_vmcnt<0>();
+
+  if constexpr (SPLIT) {
+    // Split-K: every unit writes its int32 partial tile to the workspace (in
+    // register order: one contiguous KiB per wave instruction), then bumps
+    // the tile's arrival counter. The last of the tile's `splits` units adds
+    // the others' partials (integer sums: exact in any order), resets the
+    // counter to zero for the next call and runs the store stage.
+    // Workspace: [total] int32 counters (256-byte padded), then
+    // [total][splits][BM * BN] int32 partials.
+    int32_t* const ctr = WS;
+    int32_t* const parts = WS + ((total + 63) & ~63);
+    constexpr int kTileInts = BM * BN;
+    int32_t* const mine = parts + ((int64_t)tile * splits + split) * kTileInts;
+#pragma unroll
+    for (int a = 0; a < TN; ++a)
+#pragma unroll
+      for (int b = 0; b < TM; ++b)
+        *reinterpret_cast<v4i*>(mine + ((a * TM + b) * NW * 64 + threadIdx.x) * 4) = acc[a][b];
+    __threadfence();   // publish this thread's partial at device scope
+    __shared__ int last_flag;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int seen = __hip_atomic_fetch_add(ctr + tile, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = seen == splits - 1;
+      if (last) __hip_atomic_store(ctr + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last_flag = last;
+    }
+    __syncthreads();
+    if (!last_flag) return;
+    __threadfence();   // acquire: the other units' partials are visible
+    for (int s = 0; s < splits; ++s) {
+      if (s == split) continue;
+      const int32_t* other = parts + ((int64_t)tile * splits + s) * kTileInts;
+#pragma unroll
+      for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int b = 0; b < TM; ++b)
+          acc[a][b] += *reinterpret_cast<const v4i*>(other + ((a * TM + b) * NW * 64 + threadIdx.x) * 4);
+    }
+  }
 
   // ---- store stage: y = fp16((fp32(acc) * s_a[m]) * s_w[n]), or the raw int32.
   // Lane l holds column m = l % 16 of each 16x16 tile and the 4 consecutive
@@ -651,11 +703,17 @@ hipError_t launch_skinny(const GemmArgs& g, hipStream_t st) {
 
 // ---------------------------------------------------------------------------
 // Per-group variant of the direct-to-LDS pipeline (gs = 64 or 128 along K, for
-// both operands). Each 128-code stage also gathers the stage's group scales
-// into LDS with 4-byte DMA loads (lane L fetches the scale of tile row 64p+L),
-// so the scales arrive with the codes and are covered by the same vmcnt wait.
-// After the MFMAs of a group, every accumulator element is folded into an fp32
-// sum as ((float)acc * s_a[m,g]) * s_w[n,g] and the int32 accumulator restarts.
+// both operands). Each 128-code stage also gathers its group scales into LDS
+// with 4-byte DMA loads (lane L fetches the scale of tile row 64p+L), so the
+// scales arrive with the codes under the same vmcnt wait; they go to a ring of
+// NS+1 scale slots, one deeper than the code stages, so a stage's scales stay
+// valid while the next stage runs.
+// Group g's first MFMA step visits each 16x16 tile once: it folds the tile's
+// int32 sum of group g-1 into the fp32 sum, fp32(acc) * s_a[m,g-1] *
+// s_w[n,g-1], and then starts the tile's group-g sum with a zero-accumulator
+// MFMA. The fold's VALU work thus sits between independent MFMAs, which the
+// SIMD overlaps with the matrix cores, instead of waiting for a group's MFMAs
+// to drain. (Group -1 is a zero accumulator with zero scales.)
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int WGM, int WGN, int NS, int GS, int EPI>
 __global__ void __launch_bounds__(WGM * WGN * 64)
@@ -667,21 +725,28 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int TM = WTM / 16, TN = WTN / 16;
   constexpr int GPS = BK / GS;                           // groups per stage
+  constexpr int KPG = GS / 64;                           // 64-code MFMA steps per group
   constexpr int kCodeBytes = (BM + BN) * RB;
+  constexpr bool kF16 = EPI == kEpiF16;
   // 4-byte DMA instructions per stage and per wave (spares load nothing). The
   // int32-accumulator variant has no scales (its scale pointers are null), so
   // it issues none.
-  constexpr int kScaleInstr = EPI == kEpiAccI32 ? 0 : GPS * (BM + BN) / 64;
+  // A group's scales sit in LDS as [BMp] s_a then [BNp] s_w (tile rows padded
+  // to 64: one 4-byte DMA instruction per 64 rows; rows past the tile load 0)
+  constexpr int BMp = (BM + 63) / 64 * 64, BNp = (BN + 63) / 64 * 64, kSeg = BMp + BNp;
+  constexpr int kScaleInstr = kF16 ? GPS * kSeg / 64 : 0;
   constexpr int kScalePer = (kScaleInstr + NW - 1) / NW;
-  constexpr int kScaleBytes = GPS * (BM + BN) * 4 + 256;  // + a landing pad for the spares
-  constexpr int kStageBytes = kCodeBytes + kScaleBytes;
-  static_assert((BM + BN) % 64 == 0, "scale DMA covers 64 rows per instruction");
-  static_assert((BM * RB / 1024) % NW == 0 && (BN * RB / 1024) % NW == 0,
-                "code DMA blocks split evenly over the waves (no zero-fill pad here)");
+  constexpr int kSlotFloats = GPS * kSeg;                // one stage's scales: [GPS][kSeg]
+  constexpr int NSR = NS + 1;                            // scale ring slots
   constexpr int LPS = dma_per_wave<BM, RB, NW>() + dma_per_wave<BN, RB, NW>() + kScalePer;
   static_assert(TM * 16 == WTM && TN * 16 == WTN, "wave tile must be a multiple of 16");
 
-  __shared__ __attribute__((aligned(1024))) int8_t smem[NS * kStageBytes];
+  // NS code stages, the scale ring, a 1 KiB landing pad for spare DMAs
+  constexpr int kRingOff = NS * kCodeBytes;
+  constexpr int kPadOff = kRingOff + NSR * kSlotFloats * 4;
+  __shared__ __attribute__((aligned(1024))) int8_t smem[kPadOff + 1024];
+  float* const ring = reinterpret_cast<float*>(smem + kRingOff);
+  int8_t* const pad = smem + kPadOff;
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = (wave % WGM) * WTM, wn = (wave / WGM) * WTN;
@@ -710,9 +775,9 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (int64_t)n0 * K, (uint32_t)rows_w * ld);
   // scale descriptors (never dereferenced by the int32-accumulator variant)
   const __amdgpu_buffer_rsrc_t rsa =
-      make_rsrc(SA + (EPI == kEpiF16 ? (int64_t)m0 * G : 0), EPI == kEpiF16 ? (uint32_t)rows_a * G * 4 : 0u);
+      make_rsrc(SA + (kF16 ? (int64_t)m0 * G : 0), kF16 ? (uint32_t)rows_a * G * 4 : 0u);
   const __amdgpu_buffer_rsrc_t rsw =
-      make_rsrc(SW + (EPI == kEpiF16 ? (int64_t)n0 * G : 0), EPI == kEpiF16 ? (uint32_t)rows_w * G * 4 : 0u);
+      make_rsrc(SW + (kF16 ? (int64_t)n0 * G : 0), kF16 ? (uint32_t)rows_w * G * 4 : 0u);
 
   v4i acc[TN][TM];
   float facc[TN][TM][4];
@@ -727,29 +792,57 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
 
   const int KT = (K + BK - 1) / BK;
   auto issue = [&](int kt) {
-    int8_t* st = smem + (kt % NS) * kStageBytes;
-    dma_stage<BM, RB, NW>(ra, st, nullptr, wave, lane, ld, kt * RB, (int)ld);
-    dma_stage<BN, RB, NW>(rw, st + BM * RB, nullptr, wave, lane, ld, kt * RB, (int)ld);
+    int8_t* st = smem + (kt % NS) * kCodeBytes;
+    dma_stage<BM, RB, NW>(ra, st, pad, wave, lane, ld, kt * RB, (int)ld);
+    dma_stage<BN, RB, NW>(rw, st + BM * RB, pad, wave, lane, ld, kt * RB, (int)ld);
+    float* slot = ring + (kt % NSR) * kSlotFloats;
 #pragma unroll
     for (int i = 0; i < kScalePer; ++i) {
       const int j = wave + i * NW;
       if (j >= kScaleInstr) {   // keeps every wave's vmcnt count equal
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(st + kCodeBytes + GPS * (BM + BN) * 4), 4,
-                                                 0x80000000u, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)pad, 4, 0x80000000u, 0, 0, 0);
         continue;
       }
-      const int gi = j / ((BM + BN) / 64), p = j % ((BM + BN) / 64);
+      const int gi = j / (kSeg / 64), p = j % (kSeg / 64);
       const int g = kt * GPS + gi;
-      int8_t* dst = st + kCodeBytes + (gi * (BM + BN) + 64 * p) * 4;
-      if (p < BM / 64) {
+      float* dst = slot + gi * kSeg + 64 * p;
+      // rows past the tile's valid rows are past the descriptor's range: zero
+      if (p < BMp / 64) {
         const uint32_t off = g < G ? ((uint32_t)(64 * p + lane) * G + g) * 4 : 0x80000000u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)dst, 4, off, 0, 0, 0);
       } else {
-        const uint32_t off = g < G ? ((uint32_t)(64 * (p - BM / 64) + lane) * G + g) * 4 : 0x80000000u;
+        const uint32_t off = g < G ? ((uint32_t)(64 * (p - BMp / 64) + lane) * G + g) * 4 : 0x80000000u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_void*)dst, 4, off, 0, 0, 0);
       }
     }
   };
+
+  // fold tile (a, b)'s finished group-g sum (scales at gsc, its [kSeg] slice)
+  auto fold_tile = [&](int a, int b, const float* gsc, int g) {
+    if constexpr (kF16) {
+      const float sam = gsc[wm + 16 * b + l16];
+      const float4 s4 = *reinterpret_cast<const float4*>(gsc + BMp + wn + 16 * a + 4 * l4);
+      facc[a][b][0] += ((float)acc[a][b][0] * sam) * s4.x;
+      facc[a][b][1] += ((float)acc[a][b][1] * sam) * s4.y;
+      facc[a][b][2] += ((float)acc[a][b][2] * sam) * s4.z;
+      facc[a][b][3] += ((float)acc[a][b][3] * sam) * s4.w;
+    } else {
+      if (g < 0 || g >= G) return;
+      const int m = m0 + wm + 16 * b + l16, n = n0 + wn + 16 * a + 4 * l4;
+      if (m < M) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < N) ACC[((int64_t)g * M + m) * N + n + r] = acc[a][b][r];
+      }
+    }
+  };
+
+  // group -1's scales: a zero slot (the ring slot that stage -1 would use)
+  if constexpr (kF16) {
+    float* z = ring + (NSR - 1) * kSlotFloats;
+    for (int i = threadIdx.x; i < kSlotFloats; i += NW * 64) z[i] = 0.0f;
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): visible after the first stage barrier
+  }
 
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) issue(s);
@@ -757,65 +850,52 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
   for (int kt = 0; kt < KT; ++kt) {
     wait_vmcnt<(NS - 2) * LPS>();
     stage_barrier();
-    issue(kt + NS - 1);
-    const int8_t* sa_ = smem + (kt % NS) * kStageBytes;
+    issue(kt + NS - 1);   // past the end: out-of-range offsets, zero fill, never read
+    const int8_t* sa_ = smem + (kt % NS) * kCodeBytes;
     const int8_t* sw_ = sa_ + BM * RB;
-    const float* sc = reinterpret_cast<const float*>(sa_ + kCodeBytes);
+    const float* cur = ring + (kt % NSR) * kSlotFloats;
+    const float* prev = ring + ((kt + NSR - 1) % NSR) * kSlotFloats;
 #pragma unroll
-    for (int ks = 0; ks < BK / 64; ++ks) {
-      v4i wf[TN], af[TM];
+    for (int gi = 0; gi < GPS; ++gi) {
+      // keep each group's fragment loads with its own MFMAs (bounds register use)
+      if (gi > 0) __builtin_amdgcn_sched_barrier(0);
+      const int g = kt * GPS + gi;
+      const float* psc = gi == 0 ? prev + (GPS - 1) * kSeg : cur + (gi - 1) * kSeg;
 #pragma unroll
-      for (int a = 0; a < TN; ++a)
-        wf[a] = *reinterpret_cast<const v4i*>(sw_ + tile_off<RB>(wn + 16 * a + l16, 4 * ks + l4));
+      for (int s = 0; s < KPG; ++s) {
+        const int ks = gi * KPG + s;
+        v4i wf[TN], af[TM];
 #pragma unroll
-      for (int b = 0; b < TM; ++b)
-        af[b] = *reinterpret_cast<const v4i*>(sa_ + tile_off<RB>(wm + 16 * b + l16, 4 * ks + l4));
-#pragma unroll
-      for (int a = 0; a < TN; ++a)
+        for (int a = 0; a < TN; ++a)
+          wf[a] = *reinterpret_cast<const v4i*>(sw_ + tile_off<RB>(wn + 16 * a + l16, 4 * ks + l4));
 #pragma unroll
         for (int b = 0; b < TM; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[a], af[b], acc[a][b], 0, 0, 0);
-      if ((ks + 1) * 64 % GS == 0) {   // a group ends here
-        const int gi = (ks * 64) / GS;
-        const int g = kt * GPS + gi;
-        if (g < G) {
-          if constexpr (EPI == kEpiAccI32) {
-#pragma unroll
-            for (int a = 0; a < TN; ++a)
-#pragma unroll
-              for (int b = 0; b < TM; ++b) {
-                const int m = m0 + wm + 16 * b + l16, n = n0 + wn + 16 * a + 4 * l4;
-                if (m < M) {
-#pragma unroll
-                  for (int r = 0; r < 4; ++r)
-                    if (n + r < N) ACC[((int64_t)g * M + m) * N + n + r] = acc[a][b][r];
-                }
-              }
-          } else {
-            const float* gsc = sc + gi * (BM + BN);
-            float sam[TM];
-#pragma unroll
-            for (int b = 0; b < TM; ++b) sam[b] = gsc[wm + 16 * b + l16];
-#pragma unroll
-            for (int a = 0; a < TN; ++a) {
-              const float4 s4 = *reinterpret_cast<const float4*>(gsc + BM + wn + 16 * a + 4 * l4);
-              const float swn[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-              for (int b = 0; b < TM; ++b)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) facc[a][b][r] += ((float)acc[a][b][r] * sam[b]) * swn[r];
-            }
-          }
-        }
+          af[b] = *reinterpret_cast<const v4i*>(sa_ + tile_off<RB>(wm + 16 * b + l16, 4 * ks + l4));
 #pragma unroll
         for (int a = 0; a < TN; ++a)
 #pragma unroll
-          for (int b = 0; b < TM; ++b) acc[a][b] = zero4();
+          for (int b = 0; b < TM; ++b) {
+            if (s == 0) {
+              fold_tile(a, b, psc, g - 1);
+              acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[a], af[b], zero4(), 0, 0, 0);
+            } else {
+              acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[a], af[b], acc[a][b], 0, 0, 0);
+            }
+          }
       }
     }
   }
+  // the last group (its slot was not overwritten: later zero-fill stages used other slots)
+  {
+    const int g = KT * GPS - 1;
+    const float* lsc = ring + ((KT - 1) % NSR) * kSlotFloats + (GPS - 1) * kSeg;
+#pragma unroll
+    for (int a = 0; a < TN; ++a)
+#pragma unroll
+      for (int b = 0; b < TM; ++b) fold_tile(a, b, lsc, g);
+  }
   wait_vmcnt<0>();
-  if constexpr (EPI == kEpiF16) {
+  if constexpr (kF16) {
     const bool vec_ok = (N & 3) == 0;
 #pragma unroll
     for (int b = 0; b < TM; ++b) {
@@ -856,7 +936,26 @@ hipError_t launch_dma(const GemmArgs& g, hipStream_t st) {
   const int64_t nbm = (g.M + BM - 1) / BM, nbn = (g.N + BN - 1) / BN;
   const dim3 grid((unsigned)(nbm * nbn)), block(WGM * WGN * 64);
   gemm_dma_kernel<BM, BN, WGM, WGN, BK, NS, WK, EPI><<<grid, block, 0, st>>>(
-      g.a, g.sa, g.w, g.sw, (int)g.M, (int)g.N, (int)g.K, static_cast<_Float16*>(g.y), g.acc);
+      g.a, g.sa, g.w, g.sw, (int)g.M, (int)g.N, (int)g.K, static_cast<_Float16*>(g.y), g.acc, 1, nullptr);
+  return hipGetLastError();
+}
+
+// Workspace bytes a split-K launch of BM x BN tiles needs: arrival counters
+// (256-byte padded) and one int32 partial tile per (tile, split).
+inline int64_t split_ws_bytes(int64_t M, int64_t N, int bm, int bn, int splits) {
+  const int64_t total = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+  return ((total + 63) & ~int64_t(63)) * 4 + total * splits * (int64_t)bm * bn * 4;
+}
+
+// Split-K launch; g.ws must hold split_ws_bytes(...) bytes whose counter part
+// is zero (each launch leaves it zero again).
+template <int BM, int BN, int WGM, int WGN, int BK, int NS, int WK, int EPI>
+hipError_t launch_dma_split(const GemmArgs& g, int splits, hipStream_t st) {
+  const int64_t nbm = (g.M + BM - 1) / BM, nbn = (g.N + BN - 1) / BN;
+  const dim3 grid((unsigned)(nbm * nbn * splits)), block(WGM * WGN * 64);
+  gemm_dma_kernel<BM, BN, WGM, WGN, BK, NS, WK, EPI, true><<<grid, block, 0, st>>>(
+      g.a, g.sa, g.w, g.sw, (int)g.M, (int)g.N, (int)g.K, static_cast<_Float16*>(g.y), g.acc, splits,
+      static_cast<int32_t*>(g.ws));
   return hipGetLastError();
 }
 
@@ -920,14 +1019,30 @@ hipError_t launch_pc(const GemmArgs& g, hipStream_t st) {
   }
 }
 
-// Per-group tiles: the fp32 running sums double the accumulator registers,
-// so wave tiles stay at 64 x 64 (64 int32 + 64 fp32 registers per lane).
+// Per-group tiles, chosen by the same round-count estimate with costs measured
+// on MI355X at K = 10240 (the fp32 fold after every group makes per-group
+// VALU-heavy, so its costs differ from the per-channel ones). Wave tiles stay
+// at 64 x 64 / 64 x 80: the fp32 sums double the accumulator registers.
+// 256 x 160 is used for gs 128 only: with gs 64 (a fold at every MFMA step)
+// its registers spill.
 template <int GS, int EPI>
 hipError_t launch_pg(const GemmArgs& g, hipStream_t st) {
-  constexpr int kFill = 224;
-  if (tiles_of(g, 256, 128) >= kFill) return launch_dma_pg<256, 128, 4, 2, 2, GS, EPI>(g, st);
-  if (tiles_of(g, 128, 128) >= kFill) return launch_dma_pg<128, 128, 2, 2, 2, GS, EPI>(g, st);
-  return launch_dma_pg<64, 64, 1, 4, 2, GS, EPI>(g, st);
+  if constexpr (GS == 128) {
+    static constexpr TileCost kTiles[] = {{256, 160, 521}, {256, 128, 540}, {128, 128, 770}, {64, 64, 778}};
+    switch (cheapest_tile(g, kTiles)) {
+      case 0: return launch_dma_pg<256, 160, 4, 2, 2, GS, EPI>(g, st);
+      case 1: return launch_dma_pg<256, 128, 4, 2, 2, GS, EPI>(g, st);
+      case 2: return launch_dma_pg<128, 128, 2, 2, 2, GS, EPI>(g, st);
+      default: return launch_dma_pg<64, 64, 1, 4, 2, GS, EPI>(g, st);
+    }
+  } else {
+    static constexpr TileCost kTiles[] = {{256, 128, 665}, {128, 128, 1125}, {64, 64, 877}};
+    switch (cheapest_tile(g, kTiles)) {
+      case 0: return launch_dma_pg<256, 128, 4, 2, 2, GS, EPI>(g, st);
+      case 1: return launch_dma_pg<128, 128, 2, 2, 2, GS, EPI>(g, st);
+      default: return launch_dma_pg<64, 64, 1, 4, 2, GS, EPI>(g, st);
+    }
+  }
 }
 
 template <int EPI>

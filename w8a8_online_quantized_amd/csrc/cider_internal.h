@@ -28,6 +28,8 @@ struct GemmArgs {
   int group_size;    // 0, 64, 128
   void* y;           // fp16 [M, N]
   int32_t* acc;      // int32 [M, N] or [G, M, N] (accumulator test hook)
+  void* ws = nullptr;     // split-K workspace (counters zero on entry), or null
+  int64_t ws_bytes = 0;
 };
 
 hipError_t launch_gemm(const GemmArgs& args, WeightKind wk, Epilogue epi, hipStream_t stream);
