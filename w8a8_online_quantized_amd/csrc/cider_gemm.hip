@@ -273,9 +273,51 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
 
   const int KT = (k1 - k0 + BK - 1) / BK;
   const int kb1a = k1, kb1w = kI4 ? k1 / 2 : k1;
+  // Each lane's DMA byte offsets at code 0, computed once per tile: a stage
+  // that lies wholly inside [k0, k1) then needs one add per load and no range
+  // checks (a uniform branch picks that path; the last stage of a ragged K
+  // goes through dma_stage's per-lane checks).
+  constexpr int kIA = dma_per_wave<BM, RBA, NW>(), kIW = dma_per_wave<BN, RBW, NW>();
+  constexpr int kBA = BM * RBA / 1024, kBW = BN * RBW / 1024;
+  uint32_t offa[kIA], offw[kIW];
+#pragma unroll
+  for (int i = 0; i < kIA; ++i) {
+    const int r = (wave + i * NW) * (1024 / RBA) + lane / (RBA / 16);
+    offa[i] = (uint32_t)r * lda + (uint32_t)(slot_of<RBA>(r, lane % (RBA / 16)) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < kIW; ++i) {
+    const int r = (wave + i * NW) * (1024 / RBW) + lane / (RBW / 16);
+    offw[i] = (uint32_t)r * ldw + (uint32_t)(slot_of<RBW>(r, lane % (RBW / 16)) * 16);
+  }
   auto issue = [&](int kt) {
     int8_t* st = smem + (kt % NS) * kStageBytes;
     const int kb = k0 + kt * BK;   // first code of stage kt
+    if (kb + BK <= k1) {
+#pragma unroll
+      for (int i = 0; i < kIA; ++i) {
+        const int j = wave + i * NW;
+        int8_t* dst = st + j * 1024;
+        uint32_t off = offa[i] + (uint32_t)kb;
+        if (kBA % NW != 0 && j >= kBA) {
+          dst = pad;
+          off = 0x80000000u;
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)dst, 16, off, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < kIW; ++i) {
+        const int j = wave + i * NW;
+        int8_t* dst = st + BM * RBA + j * 1024;
+        uint32_t off = offw[i] + (uint32_t)(kI4 ? kb / 2 : kb);
+        if (kBW % NW != 0 && j >= kBW) {
+          dst = pad;
+          off = 0x80000000u;
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)dst, 16, off, 0, 0, 0);
+      }
+      return;
+    }
     dma_stage<BM, RBA, NW>(ra, st, pad, wave, lane, lda, kb, kb1a);
     dma_stage<BN, RBW, NW>(rw, st + BM * RBA, pad, wave, lane, ldw, kI4 ? kb / 2 : kb, kb1w);
   };
@@ -571,16 +613,6 @@ gemm_gemv_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, con
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int Kpad = (K + kCodes - 1) / kCodes * kCodes;
 
-  // stage x (rows >= M and codes >= K as zero)
-  for (int i = threadIdx.x; i < MT * Kpad / 16; i += 256) {
-    const int m = i / (Kpad / 16), c = i % (Kpad / 16);
-    v4i v = zero4();
-    if (m < M && c * 16 < K) v = *reinterpret_cast<const v4i*>(X + (int64_t)m * K + c * 16);
-    if constexpr (kI4) v = even_odd_bytes(v);
-    *reinterpret_cast<v4i*>(xs + m * Kpad + c * 16) = v;
-  }
-  __syncthreads();
-
   const int n0 = blockIdx.x * 8;
   const int row = lane >> 3, sub = lane & 7;
   const int rows_w = min(8, N - n0);
@@ -592,8 +624,8 @@ gemm_gemv_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, con
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = 0;
 
-  for (int base = wave; base < steps; base += 4 * kBatch) {
-    v4i wv[kBatch];
+  // a batch = this wave's next kBatch 128-byte steps (steps base, base+4, ...)
+  auto load_batch = [&](v4i (&wv)[kBatch], int base) {
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int st = base + 4 * i;
@@ -601,6 +633,8 @@ gemm_gemv_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, con
       const bool in = st < steps && kb < ldw;
       wv[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, in ? (uint32_t)row * ldw + kb : 0x80000000u, 0, 0);
     }
+  };
+  auto process = [&](const v4i (&wv)[kBatch], int base) {
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int st = base + 4 * i;
@@ -638,6 +672,30 @@ gemm_gemv_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, con
         }
       }
     }
+  };
+
+  // the first weight batch goes out before x is staged, so the weight stream
+  // and the x loads overlap; later batches load one batch ahead
+  v4i wa[kBatch], wb[kBatch];
+  load_batch(wa, wave);
+
+  // stage x (rows >= M and codes >= K as zero)
+  for (int i = threadIdx.x; i < MT * Kpad / 16; i += 256) {
+    const int m = i / (Kpad / 16), c = i % (Kpad / 16);
+    v4i v = zero4();
+    if (m < M && c * 16 < K) v = *reinterpret_cast<const v4i*>(X + (int64_t)m * K + c * 16);
+    if constexpr (kI4) v = even_odd_bytes(v);
+    *reinterpret_cast<v4i*>(xs + m * Kpad + c * 16) = v;
+  }
+  __syncthreads();
+
+  constexpr int kStride = 4 * kBatch;          // steps between a wave's batches
+  for (int base = wave; base < steps; base += 2 * kStride) {
+    if (base + kStride < steps) load_batch(wb, base + kStride);
+    process(wa, base);
+    if (base + kStride >= steps) break;
+    if (base + 2 * kStride < steps) load_batch(wa, base + 2 * kStride);
+    process(wb, base + kStride);
   }
   // sum the 8 lanes of each row (integer: order does not matter)
 #pragma unroll
