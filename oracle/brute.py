@@ -19,7 +19,7 @@ from __future__ import annotations
 from fractions import Fraction
 
 __all__ = ["round_binary", "f32", "f16", "rint_half_even", "quantize_row",
-           "dot", "dequant", "dequant_groups", "linear"]
+           "dot", "dequant", "dequant_groups", "linear", "mv"]
 
 _INF = float("inf")
 
@@ -123,3 +123,20 @@ def linear(x_rows, w_codes, w_scales, group_size: int):
             out.append(dequant_groups(accs, sa[m], w_scales[n]))
         y.append(out)
     return y, qa, sa
+
+
+def mv(x_rows, w_codes, w_scales, group_size: int):
+    """Decode MV (README kernel pipeline, Decode: int8_mv; no activation
+    quantization): y[m][n] = f16( sum_k x[m][k] * code[n][k] * scale[n][g(k)] ),
+    the sum exact. x_rows: fp16-valued numbers; w_codes: int rows; w_scales:
+    per row a list of G scale Fractions."""
+    K = len(x_rows[0]) if x_rows else 0
+    gs = K if group_size == 0 else group_size
+    y = []
+    for row in x_rows:
+        out = []
+        for codes, scales in zip(w_codes, w_scales):
+            t = sum(Fraction(row[k]) * int(codes[k]) * scales[k // gs] for k in range(K))
+            out.append(f16(t))
+        y.append(out)
+    return y

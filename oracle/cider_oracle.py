@@ -23,6 +23,10 @@ top-level Cider README, a community translation of the upstream README):
   the int32 accumulator times the activation scale times the weight scale,
   per element, in fp16.
 * Section "说明" (Notes): scales come from the min-max rule by default.
+* Section "架构 / Metal Kernel 流水线", Decode (M = 1): int8_mv multiplies
+  fp16 activations by int8 weights dequantized on the fly, without
+  quantizing the activations (per-channel and per-group MV kernels in the
+  file list).
 
 Readings taken where the pages are silent (each is also listed in the design
 notes of the repository):
@@ -44,6 +48,10 @@ notes of the repository):
   exact (at most 52 significant bits) and only the last product and the
   group sum round.
 
+* decode MV: y = sum_k x[m,k] * (w_q[n,k] * s_w[n,g(k)]), the exact value
+  rounded once to fp16 (evaluated in fp64: each product is exact, the sum's
+  relative error is about K * 2^-53).
+
 Integer accumulation is done as an fp64 matmul of int8-valued arrays. Every
 product and partial sum is an integer of magnitude at most 127*127*K, which
 is below 2**53 for every K this module accepts, so each fp64 operation
@@ -56,7 +64,7 @@ import numpy as np
 __all__ = [
     "QMAX_INT8", "QMAX_INT4", "quantize_rows", "quantize_act", "quantize_weight",
     "pack_int4", "unpack_int4", "int_dot", "int_dot_groups", "dequant_per_channel",
-    "dequant_per_group", "w8a8_linear", "w4a8_linear", "num_groups",
+    "dequant_per_group", "w8a8_linear", "w4a8_linear", "num_groups", "int8_mv",
 ]
 
 QMAX_INT8 = 127
@@ -200,3 +208,27 @@ def w4a8_linear(x: np.ndarray, w_packed: np.ndarray, s_w: np.ndarray):
     q_a, s_a = quantize_act(x, 0)
     y = dequant_per_channel(int_dot(q_a, unpack_int4(w_packed)), s_a, s_w)
     return y, q_a, s_a
+
+
+def int8_mv(x: np.ndarray, w_q: np.ndarray, s_w: np.ndarray, group_size: int = 0) -> np.ndarray:
+    """Decode matrix-vector product (README section "架构 / Metal Kernel 流水线",
+    Decode (M = 1): int8_mv multiplies fp16 activations by int8 weights that are
+    dequantized on the fly, with no activation quantization; the README's file
+    list names a per-channel and a per-group MV kernel).
+
+    y[m, n] = fp16( sum_k x[m, k] * (w_q[n, k] * s_w[n, g(k)]) ), g(k) = k // group_size
+    (g = 0 for per-channel, group_size 0). x is fp16 [M, K], w_q int8 [N, K],
+    s_w fp32 [N] or [N, K / group_size].
+
+    The dequantized weight w_q * s_w is exact in fp64 (8 + 24 significant bits)
+    and so is its product with an fp16 activation; the sum over k is an fp64
+    matmul (relative error about K * 2^-53, far below the one fp16 rounding that
+    follows). This is the plain definition, rounded once."""
+    M, K = x.shape
+    N = w_q.shape[0]
+    G = num_groups(K, group_size)
+    gs = K if group_size == 0 else group_size
+    s = np.asarray(s_w, np.float32).reshape(N, G).astype(np.float64)
+    w_deq = w_q.astype(np.float64) * np.repeat(s, gs, axis=1)
+    with np.errstate(over="ignore"):
+        return (x.astype(np.float64) @ w_deq.T).astype(np.float16)

@@ -2,7 +2,7 @@
 
 Each check takes an implementation namespace with the oracle's primitive
 functions (quantize_rows, pack_int4, unpack_int4, int_dot, int_dot_groups,
-dequant_per_channel, dequant_per_group) and raises AssertionError when the
+dequant_per_channel, dequant_per_group, int8_mv) and raises AssertionError when the
 implementation disagrees with:
 
 * hand-derived worked examples stored under tests/golden/ (closed forms);
@@ -295,10 +295,108 @@ def check_int4_bound_and_cosine(impl, M=48, N=96, seed=0):
     assert cosine(y, ref) >= 0.98
 
 
+
+# ------------------------------------------------------------------ decode MV
+def check_golden_mv(impl):
+    for c in _load("int8_mv.json")["cases"]:
+        x = np.array(c["x"], np.float16)
+        y = impl.int8_mv(x, np.array(c["w_q"], np.int8), np.array(c["s_w"], np.float32), c["group_size"])
+        assert y.tolist() == c["y"], (c["name"], y.tolist(), c["y"])
+
+
+def check_brute_mv(impl, trials=30, seed=11):
+    rng = np.random.default_rng(seed)
+    for t in range(trials):
+        M, N = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        gs = [0, 2, 4, 8][t % 4]
+        K = 8 * int(rng.integers(1, 3)) if gs else int(rng.integers(1, 12))
+        x = _rand_fp16(rng, (M, K), ["normal", "wide", "ties"][t % 3])
+        G = 1 if gs == 0 else K // gs
+        q = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+        sw = (np.abs(rng.standard_normal((N, G))) * 2.0 ** rng.integers(-12, 2, size=(N, G))).astype(np.float32)
+        with np.errstate(over="ignore"):
+            y = impl.int8_mv(x, q, sw, gs)
+        by = brute.mv([[float(v) for v in row] for row in x], q.astype(int).tolist(),
+                      [[Fraction(float(v)) for v in row] for row in sw], gs)
+        for m in range(M):
+            for n in range(N):
+                assert float(y[m, n]) == float(by[m][n]), (t, m, n, y[m, n], float(by[m][n]))
+
+
+def check_mv_gs_equals_k(impl, seed=12):
+    rng = np.random.default_rng(seed)
+    K = 128
+    x = (rng.standard_normal((3, K)) * 2).astype(np.float16)
+    q = rng.integers(-127, 128, size=(7, K)).astype(np.int8)
+    sw = (np.abs(rng.standard_normal((7, 1))) * 1e-2).astype(np.float32)
+    y0 = impl.int8_mv(x, q, sw, 0)
+    y1 = impl.int8_mv(x, q, sw, K)
+    assert np.array_equal(y0.view(np.uint16), y1.view(np.uint16))
+
+
+def check_mv_pow2_scaling(impl, seed=13):
+    """Scaling x by 2^k scales y by 2^k exactly (no overflow / underflow here)."""
+    rng = np.random.default_rng(seed)
+    K = 64
+    x = (rng.standard_normal((4, K))).astype(np.float16)
+    q = rng.integers(-127, 128, size=(9, K)).astype(np.int8)
+    for gs in (0, 32):
+        G = 1 if gs == 0 else K // gs
+        sw = (np.abs(rng.standard_normal((9, G))) * 1e-2 + 1e-3).astype(np.float32)
+        y = impl.int8_mv(x, q, sw, gs).astype(np.float64)
+        for k in (-2, 1, 3):
+            y2 = impl.int8_mv((x.astype(np.float32) * 2.0 ** k).astype(np.float16), q, sw, gs).astype(np.float64)
+            ok = np.abs(y) >= 2.0 ** -12
+            assert np.array_equal(y2[ok], y[ok] * 2.0 ** k), (gs, k)
+
+
+def check_mv_matches_lossless_w8a8(impl, seed=14):
+    """On activations that per-token quantization reproduces exactly (each row
+    is codes * 2^-3 with some |code| = 127, so s_a = 2^-3 and the codes come
+    back unchanged), the decode MV and the W8A8 linear compute the same exact
+    value acc * s_a * s_w, so their fp16 outputs agree bit for bit."""
+    rng = np.random.default_rng(seed)
+    K, N = 256, 40
+    codes = rng.integers(-127, 128, size=(5, K))
+    codes[:, 7] = 127
+    x = (codes * 0.125).astype(np.float16)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    qw, sw = impl.quantize_rows(w, 0, 127)
+    qa, sa = impl.quantize_rows(x, 0, 127)
+    assert np.array_equal(qa, codes.astype(np.int8)) and np.all(sa == 0.125)
+    y8 = _linear(impl, x, qw, sw, 0)
+    ymv = impl.int8_mv(x, qw, sw, 0)
+    assert np.array_equal(y8.view(np.uint16), ymv.view(np.uint16))
+
+
+def check_mv_exact_sum(impl, trials=12, seed=15):
+    """Large cancelling products next to tiny ones. Every product x*q is a
+    multiple of 2^-24 below 2^22, so with K = 64 every partial sum fits the
+    53-bit fp64 significand exactly, in any order: the oracle must return the
+    exact sum rounded once (the brute force), which an fp32 running sum loses."""
+    rng = np.random.default_rng(seed)
+    K = 64
+    for t in range(trials):
+        x = (rng.uniform(0.5, 1.0, (2, K)) * 2.0 ** rng.integers(-14, -6, size=(2, K))).astype(np.float64)
+        q = rng.integers(-127, 128, size=(3, K)).astype(np.int8)
+        for i, j in ((0, K - 1), (2 + t % 7, 40 + t % 11), (20, 21)):
+            big = float(2 ** 14 + 2 ** rng.integers(0, 10))
+            x[:, i], x[:, j] = big, -big
+            q[:, j] = q[:, i]
+        x = x.astype(np.float16)
+        sw = np.full((3, 1), 2.0 ** -8, np.float32)
+        y = impl.int8_mv(x, q, sw, 0)
+        by = brute.mv([[float(v) for v in row] for row in x], q.astype(int).tolist(),
+                      [[Fraction(float(v)) for v in row] for row in sw], 0)
+        for m in range(2):
+            for n in range(3):
+                assert float(y[m, n]) == float(by[m][n]), (t, m, n, float(y[m, n]), float(by[m][n]))
+
 ALL_CHECKS = [
     check_golden_quant, check_golden_division, check_golden_int4, check_golden_integer_gemm,
     check_closed_form_k10240, check_brute_quant, check_brute_linear,
     check_brute_int4, check_pow2_invariance, check_sign_and_range,
     check_k_permutation, check_gs_equals_k, check_error_bound_and_cosine,
-    check_int4_bound_and_cosine,
+    check_int4_bound_and_cosine, check_golden_mv, check_brute_mv, check_mv_gs_equals_k,
+    check_mv_pow2_scaling, check_mv_matches_lossless_w8a8, check_mv_exact_sum,
 ]

@@ -12,7 +12,7 @@ from tests import oracle_pins as pins
 def _impl(**over):
     base = {name: getattr(O, name) for name in (
         "quantize_rows", "pack_int4", "unpack_int4", "int_dot", "int_dot_groups",
-        "dequant_per_channel", "dequant_per_group")}
+        "dequant_per_channel", "dequant_per_group", "int8_mv")}
     base.update(over)
     ns = types.SimpleNamespace(**base)
     return ns
@@ -95,6 +95,32 @@ def _groups_off_by_one(qa, qw, group_size):
     return out
 
 
+def _mv_variant(kind):
+    def mv(x, w_q, s_w, group_size=0):
+        M, K = x.shape
+        N = w_q.shape[0]
+        G = O.num_groups(K, group_size)
+        gs = K if group_size == 0 else group_size
+        s = np.asarray(s_w, np.float32).reshape(N, G).astype(np.float64)
+        if kind == "group_mod":            # scale index k % G instead of k // gs
+            sk = s[:, np.arange(K) % G]
+        else:
+            sk = np.repeat(s, gs, axis=1)
+        w = w_q.astype(np.float64) * sk
+        xx = x.astype(np.float64)
+        if kind == "no_scale":
+            w = w_q.astype(np.float64)
+        elif kind == "fp16_weights":       # dequantized weight rounded to fp16 first
+            w = w.astype(np.float16).astype(np.float64)
+        elif kind == "quantized_x":        # W8A8 semantics instead of fp16 activations
+            qa, sa = O.quantize_rows(x, 0, 127)
+            xx = qa.astype(np.float64) * sa.astype(np.float64)
+        elif kind == "fp32_sum":
+            return (x.astype(np.float32) @ w.astype(np.float32).T).astype(np.float16)
+        return (xx @ w.T).astype(np.float16)
+    return mv
+
+
 MUTANTS = {
     "round_half_up": _impl(quantize_rows=_quant_variant(rounding="up")),
     "scale_over_128": _impl(quantize_rows=_quant_variant(divisor_bias=1)),
@@ -110,6 +136,11 @@ MUTANTS = {
     "per_group_drops_a_group": _impl(dequant_per_group=_pg_drop_last_group),
     "per_group_row_scale": _impl(dequant_per_group=_pg_row_scale),
     "per_group_misaligned": _impl(int_dot_groups=_groups_off_by_one),
+    "mv_without_weight_scale": _impl(int8_mv=_mv_variant("no_scale")),
+    "mv_group_index_modulo": _impl(int8_mv=_mv_variant("group_mod")),
+    "mv_fp16_dequantized_weight": _impl(int8_mv=_mv_variant("fp16_weights")),
+    "mv_quantizes_activations": _impl(int8_mv=_mv_variant("quantized_x")),
+    "mv_fp32_sum": _impl(int8_mv=_mv_variant("fp32_sum")),
 }
 
 
