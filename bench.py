@@ -92,6 +92,8 @@ def algorithmic(mode, M, N, K, gs):
     """Integer ops and HBM bytes one GEMM launch must move, and the bytes of the
     activation quantization (fp16 in, int8 + fp32 scales out)."""
     G = 1 if gs == 0 else K // gs
+    if mode == "int8_mv":   # decode MV: fp16 x and int8 weights in, fp16 y out, no quantization
+        return 2.0 * M * N * K, 2 * M * K + N * K + 4 * N * G + 2 * M * N, 0
     wbytes = N * K // 2 if mode == "w4a8" else N * K
     gemm_bytes = M * K + wbytes + 4 * M * G + 4 * N * G + 2 * M * N
     quant_bytes = 2 * M * K + M * K + 4 * M * G
@@ -109,6 +111,8 @@ def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_byte
     w_h = torch.from_numpy(inputs.weights(N, K, seed=0))
     ops, gemm_bytes, quant_bytes = algorithmic(mode, M, N, K, gs)
     R = max(2, -(-min_set_bytes // (gemm_bytes + quant_bytes)))
+    if mode == "int8_mv":
+        return measure_mv(cider, torch, x_h, w_h, M, N, K, gs, steps, warmup, R, ops, gemm_bytes)
     bits = 4 if mode == "w4a8" else 8
     w_dev = w_h.to(dev)
     wq0, sw0 = cider.cider_quant_weight(w_dev, bits, gs)
@@ -155,6 +159,34 @@ def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_byte
     torch.cuda.empty_cache()
     return {"ms_per_step": step_ms, "quant_ms": q_ms, "gemm_ms": g_ms, "ops": ops,
             "gemm_bytes": gemm_bytes, "quant_bytes": quant_bytes, "sets": R}
+
+
+def measure_mv(cider, torch, x_h, w_h, M, N, K, gs, steps, warmup, R, ops, nbytes):
+    """The decode MV alone (it has no quantization step), rotating buffer sets."""
+    dev = torch.device("cuda:0")
+    w_dev = w_h.to(dev)
+    wq0, sw0 = cider.cider_quant_weight(w_dev, 8, gs)
+    del w_dev
+    sets = [(x_h.to(dev), wq0.clone(), sw0.clone(), torch.empty((M, N), dtype=torch.float16, device=dev))
+            for _ in range(R)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        x, wq, sw, y = sets[i % R]
+        cider.cider_int8_mv(x, wq, sw, gs, y, stream=stream)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        x, wq, sw, y = sets[i % R]
+        cider.cider_int8_mv(x, wq, sw, gs, y, stream=stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    del sets
+    torch.cuda.empty_cache()
+    return {"ms_per_step": ms, "quant_ms": 0.0, "gemm_ms": ms, "ops": ops, "gemm_bytes": nbytes,
+            "quant_bytes": 0, "sets": R}
 
 
 def roofline_of(ops, nbytes, ms):
@@ -211,7 +243,9 @@ def measure_stack(cider, torch, inputs, steps, warmup, layers=28, M=1024, dims=(
 SWEEP = ([("w8a8_pc", M, 10240, 2560, 0) for M in (1, 128, 1024, 4096, 8192)] +
          [("w8a8_pc", M, 2560, 10240, 0) for M in (1, 128, 1024, 4096, 8192)] +
          [("w8a8_pg", M, 2560, 10240, gs) for gs in (128, 64) for M in (128, 1024, 4096)] +
-         [("w4a8", M, 10240, 2560, 0) for M in (1, 1024, 8192)])
+         [("w4a8", M, 10240, 2560, 0) for M in (1, 1024, 8192)] +
+         [("int8_mv", 1, 10240, 2560, 0), ("int8_mv", 1, 2560, 10240, 0), ("int8_mv", 1, 10240, 2560, 128),
+          ("int8_mv", 1, 2560, 10240, 128), ("int8_mv", 1, 2560, 10240, 64)])
 
 
 def main():
@@ -293,7 +327,7 @@ def main():
             rows.append({"mode": mode, "M": m, "N": n, "K": k, "group_size": gs,
                          "gemm_us": round(rr["gemm_ms"] * 1e3, 2), "quant_us": round(rr["quant_ms"] * 1e3, 2),
                          "gemm_roofline": roofline_of(rr["ops"], rr["gemm_bytes"], rr["gemm_ms"]),
-                         "quant_GBs": round(rr["quant_bytes"] / (rr["quant_ms"] * 1e-3) / 1e9, 1),
+                         "quant_GBs": round(rr["quant_bytes"] / (rr["quant_ms"] * 1e-3) / 1e9, 1) if rr["quant_ms"] else None,
                          "linear_TOPs": round(rr["ops"] / (rr["ms_per_step"] * 1e-3) / 1e12, 2)})
             print(json.dumps({"sweep_row": rows[-1]}), file=sys.stderr, flush=True)
         out["sweep"] = rows

@@ -115,6 +115,26 @@ cider_status_t cider_w4a8_gemm(const int8_t* x_q, const float* x_scale, const ui
                                const float* w_scale, int64_t M, int64_t N, int64_t K,
                                void* y_f16, void* stream);
 
+/* Decode matrix-vector product, the README's int8_mv (section "架构 / Metal
+ * Kernel 流水线", Decode (M = 1): the activations are not quantized; the int8
+ * weights are dequantized on the fly; the file list names a per-channel and a
+ * per-group MV kernel):
+ *   y[m,n] = fp16( sum_k x[m,k] * w_q[n,k] * w_scale[n, g(k)] ),
+ *   g(k) = k / group_size (group_size 0: one scale per row, w_scale[n]).
+ *   x_f16   : fp16 [M, K] activations, 0 <= M <= CIDER_MV_MAX_M.
+ *   w_q     : int8 [N, K] weight codes (as cider_quant_weight makes them).
+ *   w_scale : fp32 [N] (group_size 0) or [N, K/group_size].
+ *   y_f16   : fp16 [M, N] (output).
+ * The sum is accumulated in fp32 (each fp16 x int8 product is exact in fp32);
+ * its order is fixed, so results are deterministic, and its error is within
+ * the fp32 summation bound (K/32 + 24) * 2^-24 * sum_k |x*w_q*w_scale|. The
+ * per-channel scale multiplies the fp32 sum (fp32 product, then fp16).
+ * K, group_size, alignment and errors as for cider_w8a8_gemm.
+ */
+#define CIDER_MV_MAX_M 4
+cider_status_t cider_int8_mv(const void* x_f16, const int8_t* w_q, const float* w_scale, int64_t M,
+                             int64_t N, int64_t K, int32_t group_size, void* y_f16, void* stream);
+
 /* Test hook: the same matmul main loops with an int32 store instead of the
  * dequant, so the accumulators can be compared bit-exactly.
  *   mode 0: w = int8 [N, K] codes; mode 1: w = packed int4 [N, K/2] (group_size 0).

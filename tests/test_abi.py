@@ -57,6 +57,8 @@ def test_empty_work_is_success_without_pointers():
     assert L.cider_w8a8_gemm(NULL, NULL, NULL, NULL, 16, 0, 64, 0, NULL, NULL) == 0
     assert L.cider_w4a8_gemm(NULL, NULL, NULL, NULL, 0, 16, 64, NULL, NULL) == 0
     assert L.cider_gemm_acc_i32(0, NULL, NULL, 0, 4, 64, 0, NULL, NULL) == 0
+    assert L.cider_int8_mv(NULL, NULL, NULL, 0, 16, 64, 0, NULL, NULL) == 0
+    assert L.cider_int8_mv(NULL, NULL, NULL, 2, 0, 64, 0, NULL, NULL) == 0
 
 
 def test_quant_weight_rejects():
@@ -85,6 +87,19 @@ def test_gemm_rejects():
     assert a(2, P, P, 4, 4, 64, 0, P, NULL) == INV
     assert a(1, P, P, 4, 4, 64, 64, P, NULL) == INV
     assert a(0, P, P, 4, 4, 64, 0, NULL, NULL) == INV
+
+
+def test_int8_mv_rejects():
+    mv = L.cider_int8_mv
+    assert mv(P, P, P, 5, 4, 64, 0, P, NULL) == INV                      # M above CIDER_MV_MAX_M
+    assert mv(P, P, P, -1, 4, 64, 0, P, NULL) == INV
+    assert mv(P, P, P, 1, 4, 40, 0, P, NULL) == INV                      # K % 16
+    assert mv(P, P, P, 1, 4, 192, 128, P, NULL) == INV                   # K % gs
+    assert mv(P, P, P, 1, 4, 128, 32, P, NULL) == INV                    # gs
+    assert mv(NULL, P, P, 1, 4, 64, 0, P, NULL) == INV
+    assert mv(P, P, NULL, 1, 4, 64, 0, P, NULL) == INV
+    assert mv(MIS, P, P, 1, 4, 64, 0, P, NULL) == INV
+    assert mv(P, P, P, 1, 4, 64, 0, MIS, NULL) == INV
 
 
 def test_not_available_without_gpu():

@@ -33,6 +33,7 @@ SIGNATURES = {
     "cider_w8a8_gemm": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p]),
     "cider_w4a8_gemm": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p]),
     "cider_gemm_acc_i32": (ctypes.c_int, [_c_i32, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p]),
+    "cider_int8_mv": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p]),
     "cider_stack_workspace_layout": (ctypes.c_int64, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                                       ctypes.POINTER(ctypes.c_int64)]),
     "cider_stack_forward": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p,
@@ -172,6 +173,25 @@ def cider_w8a8_gemm(x_q, x_scale, w_q, w_scale, group_size: int = 0, y=None, str
     _need(y, torch.float16, (M, N), "y")
     _check("cider_w8a8_gemm", lib().cider_w8a8_gemm(_ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale),
                                                     M, N, K, group_size, _ptr(y), _stream(stream)))
+    return y
+
+
+def cider_int8_mv(x, w_q, w_scale, group_size: int = 0, y=None, stream=None):
+    """Decode MV: fp16 x [M, K] (M <= 4) times int8 weights dequantized on the
+    fly -> fp16 y [M, N]; no activation quantization."""
+    import torch
+    M, K = x.shape
+    N = w_q.shape[0]
+    _need(x, torch.float16, (M, K), "x")
+    _need(w_q, torch.int8, (N, K), "w_q")
+    if group_size and K % group_size:
+        raise ValueError("K must be a multiple of group_size")
+    _need(w_scale, torch.float32, _scale_shape(N, K, group_size), "w_scale")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    _need(y, torch.float16, (M, N), "y")
+    _check("cider_int8_mv", lib().cider_int8_mv(_ptr(x), _ptr(w_q), _ptr(w_scale), M, N, K, group_size,
+                                                _ptr(y), _stream(stream)))
     return y
 
 

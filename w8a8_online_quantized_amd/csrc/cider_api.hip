@@ -142,6 +142,19 @@ cider_status_t cider_w4a8_gemm(const int8_t* x_q, const float* x_scale, const ui
   return gemm_common(g, cider::kWeightI4, cider::kEpiF16, stream);
 }
 
+cider_status_t cider_int8_mv(const void* x_f16, const int8_t* w_q, const float* w_scale, int64_t M, int64_t N,
+                             int64_t K, int32_t group_size, void* y_f16, void* stream) {
+  if (M < 0 || M > CIDER_MV_MAX_M || !gemm_sizes_ok(M, N) || !valid_gs(group_size) || !valid_k(K, 16, group_size))
+    return CIDER_ERROR_INVALID_VALUE;
+  if (M == 0 || N == 0) return CIDER_SUCCESS;
+  if (!x_f16 || !w_q || !w_scale || !y_f16) return CIDER_ERROR_INVALID_VALUE;
+  if (!aligned16(x_f16) || !aligned16(w_q) || !aligned16(w_scale) || !aligned16(y_f16))
+    return CIDER_ERROR_INVALID_VALUE;
+  if (!device_is_gfx950()) return CIDER_ERROR_NOT_SUPPORTED;
+  cider::MvArgs a{x_f16, w_q, w_scale, M, N, K, group_size, y_f16};
+  return from_hip(cider::launch_mv(a, static_cast<hipStream_t>(stream)));
+}
+
 cider_status_t cider_gemm_acc_i32(int32_t mode, const int8_t* x_q, const void* w, int64_t M, int64_t N,
                                   int64_t K, int32_t group_size, int32_t* acc, void* stream) {
   if (mode != 0 && mode != 1) return CIDER_ERROR_INVALID_VALUE;

@@ -34,4 +34,16 @@ struct GemmArgs {
 
 hipError_t launch_gemm(const GemmArgs& args, WeightKind wk, Epilogue epi, hipStream_t stream);
 
+struct MvArgs {
+  const void* x;     // fp16 activations [M, K], 1 <= M <= 4
+  const int8_t* w;   // int8 weight codes [N, K]
+  const float* sw;   // weight scales [N] or [N, K / group_size]
+  int64_t M, N, K;
+  int group_size;    // 0, 64, 128
+  void* y;           // fp16 [M, N]
+};
+
+// Decode matrix-vector product (no activation quantization).
+hipError_t launch_mv(const MvArgs& args, hipStream_t stream);
+
 }  // namespace cider
