@@ -19,7 +19,7 @@ from __future__ import annotations
 from fractions import Fraction
 
 __all__ = ["round_binary", "f32", "f16", "rint_half_even", "quantize_row",
-           "dot", "dequant", "dequant_groups", "linear", "mv"]
+           "dot", "dequant", "dequant_groups", "linear", "mv", "linear_token_group"]
 
 _INF = float("inf")
 
@@ -137,6 +137,23 @@ def mv(x_rows, w_codes, w_scales, group_size: int):
         out = []
         for codes, scales in zip(w_codes, w_scales):
             t = sum(Fraction(row[k]) * int(codes[k]) * scales[k // gs] for k in range(K))
+            out.append(f16(t))
+        y.append(out)
+    return y
+
+
+def linear_token_group(x_rows, w_codes, w_scales, group_size: int):
+    """Per-token activation codes (one scale per row) against per-group weight
+    codes: y[m][n] = f16( sum_g acc_g * s_a[m] * s_w[n][g] ), exact."""
+    K = len(x_rows[0]) if x_rows else 0
+    y = []
+    for row in x_rows:
+        c, s = quantize_row(row, 0, 127)
+        out = []
+        for n in range(len(w_codes)):
+            t = sum(Fraction(dot(c[g * group_size:(g + 1) * group_size],
+                                 w_codes[n][g * group_size:(g + 1) * group_size])) * s[0] * w_scales[n][g]
+                    for g in range(K // group_size))
             out.append(f16(t))
         y.append(out)
     return y

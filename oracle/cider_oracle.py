@@ -48,6 +48,9 @@ notes of the repository):
   exact (at most 52 significant bits) and only the last product and the
   group sum round.
 
+* per-token activations x per-group weights (the quantization table's
+  per-token activations with per-group weights): y = sum_g acc_g * s_a[m] *
+  s_w[n,g], in fp64, rounded once to fp16.
 * decode MV: y = sum_k x[m,k] * (w_q[n,k] * s_w[n,g(k)]), the exact value
   rounded once to fp16 (evaluated in fp64: each product is exact, the sum's
   relative error is about K * 2^-53).
@@ -65,6 +68,7 @@ __all__ = [
     "QMAX_INT8", "QMAX_INT4", "quantize_rows", "quantize_act", "quantize_weight",
     "pack_int4", "unpack_int4", "int_dot", "int_dot_groups", "dequant_per_channel",
     "dequant_per_group", "w8a8_linear", "w4a8_linear", "num_groups", "int8_mv",
+    "dequant_token_group", "w8a8_linear_token_group",
 ]
 
 QMAX_INT8 = 127
@@ -232,3 +236,25 @@ def int8_mv(x: np.ndarray, w_q: np.ndarray, s_w: np.ndarray, group_size: int = 0
     w_deq = w_q.astype(np.float64) * np.repeat(s, gs, axis=1)
     with np.errstate(over="ignore"):
         return (x.astype(np.float64) @ w_deq.T).astype(np.float16)
+
+
+def dequant_token_group(acc_g: np.ndarray, s_a: np.ndarray, s_w: np.ndarray) -> np.ndarray:
+    """Per-token activation scale times per-group weight scales (the README's
+    quantization table: activations symmetric INT8 per token in every mode,
+    weights per-channel or per-group): y[m, n] = fp16( sum_g acc_g[g, m, n] *
+    s_a[m] * s_w[n, g] ), evaluated in fp64 (acc * s_a exact), rounded once."""
+    G = acc_g.shape[0]
+    sa = s_a.reshape(-1).astype(np.float64)[:, None]
+    y = np.zeros(acc_g.shape[1:], np.float64)
+    for g in range(G):
+        y += (acc_g[g].astype(np.float64) * sa) * s_w[:, g].astype(np.float64)[None, :]
+    with np.errstate(over="ignore"):
+        return y.astype(np.float16)
+
+
+def w8a8_linear_token_group(x: np.ndarray, w_q: np.ndarray, s_w: np.ndarray, group_size: int):
+    """Per-token activation codes (one scale per row of x) against per-group
+    weight codes (group_size 64 or 128 along K). Returns (y, q_a, s_a)."""
+    q_a, s_a = quantize_act(x, 0)
+    y = dequant_token_group(int_dot_groups(q_a, w_q, group_size), s_a, s_w)
+    return y, q_a, s_a

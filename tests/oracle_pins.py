@@ -2,7 +2,7 @@
 
 Each check takes an implementation namespace with the oracle's primitive
 functions (quantize_rows, pack_int4, unpack_int4, int_dot, int_dot_groups,
-dequant_per_channel, dequant_per_group, int8_mv) and raises AssertionError when the
+dequant_per_channel, dequant_per_group, int8_mv, dequant_token_group) and raises AssertionError when the
 implementation disagrees with:
 
 * hand-derived worked examples stored under tests/golden/ (closed forms);
@@ -392,6 +392,61 @@ def check_mv_exact_sum(impl, trials=12, seed=15):
             for n in range(3):
                 assert float(y[m, n]) == float(by[m][n]), (t, m, n, float(y[m, n]), float(by[m][n]))
 
+
+# ------------------------------------------------- per-token x per-group weight
+def check_golden_token_group(impl):
+    for c in _load("token_group.json")["cases"]:
+        x = np.array(c["x"], np.float16)
+        qa, sa = impl.quantize_rows(x, 0, 127)
+        assert qa.tolist() == c["q_a"] and sa[:, 0].tolist() == c["s_a"]
+        wq = np.array(c["w_q"], np.int8)
+        y = impl.dequant_token_group(impl.int_dot_groups(qa, wq, c["group_size"]), sa[:, 0],
+                                     np.array(c["s_w"], np.float32))
+        assert y.tolist() == c["y"], (y.tolist(), c["y"])
+
+
+def check_brute_token_group(impl, trials=20, seed=16):
+    rng = np.random.default_rng(seed)
+    for t in range(trials):
+        M, N = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        gs = [2, 4, 8][t % 3]
+        K = gs * int(rng.integers(1, 4))
+        x = _rand_fp16(rng, (M, K), ["normal", "wide", "ties"][t % 3])
+        w = _rand_fp16(rng, (N, K), ["normal", "wide", "small"][t % 3])
+        qw, sw = impl.quantize_rows(w, gs, 127)
+        qa, sa = impl.quantize_rows(x, 0, 127)
+        with np.errstate(over="ignore"):
+            y = impl.dequant_token_group(impl.int_dot_groups(qa, qw, gs), sa[:, 0], sw)
+        by = brute.linear_token_group([[float(v) for v in row] for row in x], qw.astype(int).tolist(),
+                                      [[Fraction(float(v)) for v in row] for row in sw], gs)
+        for m in range(M):
+            for n in range(N):
+                assert float(y[m, n]) == float(by[m][n]), (t, m, n, y[m, n], float(by[m][n]))
+
+
+def check_token_group_reductions(impl, seed=17):
+    """One group spanning K is per-channel; activations whose groups all have
+    the same max|x| make per-group activation codes equal the per-token ones,
+    and then per-group and per-token x per-group coincide bit for bit."""
+    rng = np.random.default_rng(seed)
+    K, gs = 256, 64
+    x = (rng.standard_normal((6, K)) * 2).astype(np.float16)
+    w = (rng.standard_normal((9, K)) * 0.02).astype(np.float16)
+    qa, sa = impl.quantize_rows(x, 0, 127)
+    qw0, sw0 = impl.quantize_rows(w, 0, 127)
+    y0 = impl.dequant_per_channel(impl.int_dot(qa, qw0), sa[:, 0], sw0[:, 0])
+    y1 = impl.dequant_token_group(impl.int_dot_groups(qa, qw0, K), sa[:, 0], sw0)
+    assert np.array_equal(y0.view(np.uint16), y1.view(np.uint16))
+    x[:, ::gs] = np.float16(8.0)          # every group of every row: max|x| = 8
+    qa, sa = impl.quantize_rows(x, 0, 127)
+    qag, sag = impl.quantize_rows(x, gs, 127)
+    assert np.array_equal(qa, qag) and np.all(sag == sa)
+    qw, sw = impl.quantize_rows(w, gs, 127)
+    acc = impl.int_dot_groups(qa, qw, gs)
+    y2 = impl.dequant_per_group(acc, sag, sw)
+    y3 = impl.dequant_token_group(acc, sa[:, 0], sw)
+    assert np.array_equal(y2.view(np.uint16), y3.view(np.uint16))
+
 ALL_CHECKS = [
     check_golden_quant, check_golden_division, check_golden_int4, check_golden_integer_gemm,
     check_closed_form_k10240, check_brute_quant, check_brute_linear,
@@ -399,4 +454,5 @@ ALL_CHECKS = [
     check_k_permutation, check_gs_equals_k, check_error_bound_and_cosine,
     check_int4_bound_and_cosine, check_golden_mv, check_brute_mv, check_mv_gs_equals_k,
     check_mv_pow2_scaling, check_mv_matches_lossless_w8a8, check_mv_exact_sum,
+    check_golden_token_group, check_brute_token_group, check_token_group_reductions,
 ]

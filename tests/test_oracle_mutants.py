@@ -12,7 +12,7 @@ from tests import oracle_pins as pins
 def _impl(**over):
     base = {name: getattr(O, name) for name in (
         "quantize_rows", "pack_int4", "unpack_int4", "int_dot", "int_dot_groups",
-        "dequant_per_channel", "dequant_per_group", "int8_mv")}
+        "dequant_per_channel", "dequant_per_group", "int8_mv", "dequant_token_group")}
     base.update(over)
     ns = types.SimpleNamespace(**base)
     return ns
@@ -121,6 +121,18 @@ def _mv_variant(kind):
     return mv
 
 
+def _tg_variant(kind):
+    def f(acc_g, s_a, s_w):
+        if kind == "no_act_scale":
+            s_a = np.ones_like(s_a)
+        elif kind == "first_group_scale":
+            s_w = np.repeat(s_w[:, :1], s_w.shape[1], axis=1)
+        elif kind == "reversed_groups":
+            s_w = s_w[:, ::-1]
+        return O.dequant_token_group(acc_g, s_a, s_w)
+    return f
+
+
 MUTANTS = {
     "round_half_up": _impl(quantize_rows=_quant_variant(rounding="up")),
     "scale_over_128": _impl(quantize_rows=_quant_variant(divisor_bias=1)),
@@ -141,6 +153,9 @@ MUTANTS = {
     "mv_fp16_dequantized_weight": _impl(int8_mv=_mv_variant("fp16_weights")),
     "mv_quantizes_activations": _impl(int8_mv=_mv_variant("quantized_x")),
     "mv_fp32_sum": _impl(int8_mv=_mv_variant("fp32_sum")),
+    "token_group_without_act_scale": _impl(dequant_token_group=_tg_variant("no_act_scale")),
+    "token_group_first_weight_scale": _impl(dequant_token_group=_tg_variant("first_group_scale")),
+    "token_group_reversed_scales": _impl(dequant_token_group=_tg_variant("reversed_groups")),
 }
 
 
