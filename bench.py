@@ -95,8 +95,9 @@ def algorithmic(mode, M, N, K, gs):
     if mode == "int8_mv":   # decode MV: fp16 x and int8 weights in, fp16 y out, no quantization
         return 2.0 * M * N * K, 2 * M * K + N * K + 4 * N * G + 2 * M * N, 0
     wbytes = N * K // 2 if mode == "w4a8" else N * K
-    gemm_bytes = M * K + wbytes + 4 * M * G + 4 * N * G + 2 * M * N
-    quant_bytes = 2 * M * K + M * K + 4 * M * G
+    Ga = 1 if mode == "w8a8_tokpg" else G   # per-token activations x per-group weights
+    gemm_bytes = M * K + wbytes + 4 * M * Ga + 4 * N * G + 2 * M * N
+    quant_bytes = 2 * M * K + M * K + 4 * M * Ga
     return 2.0 * M * N * K, gemm_bytes, quant_bytes
 
 
@@ -114,6 +115,7 @@ def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_byte
     if mode == "int8_mv":
         return measure_mv(cider, torch, x_h, w_h, M, N, K, gs, steps, warmup, R, ops, gemm_bytes)
     bits = 4 if mode == "w4a8" else 8
+    ags = 0 if mode == "w8a8_tokpg" else gs   # activation group size
     w_dev = w_h.to(dev)
     wq0, sw0 = cider.cider_quant_weight(w_dev, bits, gs)
     del w_dev
@@ -121,7 +123,7 @@ def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_byte
     for _ in range(R):
         x = x_h.to(dev)
         xq = torch.empty((M, K), dtype=torch.int8, device=dev)
-        sa = torch.empty((M,) if gs == 0 else (M, K // gs), dtype=torch.float32, device=dev)
+        sa = torch.empty((M,) if ags == 0 else (M, K // ags), dtype=torch.float32, device=dev)
         y = torch.empty((M, N), dtype=torch.float16, device=dev)
         sets.append((x, xq, sa, wq0.clone(), sw0.clone(), y))
     torch.cuda.synchronize()
@@ -130,6 +132,8 @@ def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_byte
     def gemm(xq, sa, wq, sw, y):
         if mode == "w4a8":
             cider.cider_w4a8_gemm(xq, sa, wq, sw, y, stream=stream)
+        elif mode == "w8a8_tokpg":
+            cider.cider_w8a8_gemm_token_group(xq, sa, wq, sw, gs, y, stream=stream)
         else:
             cider.cider_w8a8_gemm(xq, sa, wq, sw, gs, y, stream=stream)
 
@@ -143,7 +147,7 @@ def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_byte
         return start.elapsed_time(end) / steps
 
     def step(x, xq, sa, wq, sw, y):
-        cider.cider_quant_act(x, gs, xq, sa, stream=stream)
+        cider.cider_quant_act(x, ags, xq, sa, stream=stream)
         gemm(xq, sa, wq, sw, y)
 
     for i in range(warmup):
@@ -153,7 +157,7 @@ def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_byte
     step_ms = timed(step)
     # each kernel's average launch duration: the same launches, one kernel kind
     # at a time, back to back between two events on the launch stream
-    q_ms = timed(lambda x, xq, sa, wq, sw, y: cider.cider_quant_act(x, gs, xq, sa, stream=stream))
+    q_ms = timed(lambda x, xq, sa, wq, sw, y: cider.cider_quant_act(x, ags, xq, sa, stream=stream))
     g_ms = timed(lambda x, xq, sa, wq, sw, y: gemm(xq, sa, wq, sw, y))
     del sets
     torch.cuda.empty_cache()
@@ -243,6 +247,7 @@ def measure_stack(cider, torch, inputs, steps, warmup, layers=28, M=1024, dims=(
 SWEEP = ([("w8a8_pc", M, 10240, 2560, 0) for M in (1, 128, 1024, 4096, 8192)] +
          [("w8a8_pc", M, 2560, 10240, 0) for M in (1, 128, 1024, 4096, 8192)] +
          [("w8a8_pg", M, 2560, 10240, gs) for gs in (128, 64) for M in (128, 1024, 4096)] +
+         [("w8a8_tokpg", M, 2560, 10240, gs) for gs in (128, 64) for M in (16, 128, 1024, 4096)] +
          [("w4a8", M, 10240, 2560, 0) for M in (1, 1024, 8192)] +
          [("int8_mv", 1, 10240, 2560, 0), ("int8_mv", 1, 2560, 10240, 0), ("int8_mv", 1, 10240, 2560, 128),
           ("int8_mv", 1, 2560, 10240, 128), ("int8_mv", 1, 2560, 10240, 64)])

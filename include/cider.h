@@ -115,6 +115,23 @@ cider_status_t cider_w4a8_gemm(const int8_t* x_q, const float* x_scale, const ui
                                const float* w_scale, int64_t M, int64_t N, int64_t K,
                                void* y_f16, void* stream);
 
+/* W8A8 GEMM with per-token activation scales and per-group weight scales
+ * (the README's "量化" table quantizes activations per token in every mode,
+ * while its "W8A8 量化粒度" table offers per-group weights):
+ *   y[m,n] = fp16( x_scale[m] * sum_g (float)acc_g[m,n] * w_scale[n,g] ),
+ *   acc_g as above. The group sum is accumulated in fp32 (one fma per group,
+ *   in group order; for M <= 16 per-wave partial sums are then added in wave
+ *   order), multiplied by x_scale[m] in fp32 and rounded to fp16. Its error
+ *   is within (K/group_size + 17) * 2^-24 * x_scale[m] * sum_g |acc_g *
+ *   w_scale[n,g]| plus the fp16 rounding; results are deterministic.
+ *   x_q [M, K] int8 with x_scale fp32 [M] (cider_quant_act with group_size 0);
+ *   w_q [N, K] int8 with w_scale fp32 [N, K/group_size]; group_size 64 or 128.
+ * K, alignment and errors as for cider_w8a8_gemm.
+ */
+cider_status_t cider_w8a8_gemm_token_group(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
+                                           const float* w_scale, int64_t M, int64_t N, int64_t K,
+                                           int32_t group_size, void* y_f16, void* stream);
+
 /* Decode matrix-vector product, the README's int8_mv (section "架构 / Metal
  * Kernel 流水线", Decode (M = 1): the activations are not quantized; the int8
  * weights are dequantized on the fly; the file list names a per-channel and a

@@ -59,6 +59,8 @@ def test_empty_work_is_success_without_pointers():
     assert L.cider_gemm_acc_i32(0, NULL, NULL, 0, 4, 64, 0, NULL, NULL) == 0
     assert L.cider_int8_mv(NULL, NULL, NULL, 0, 16, 64, 0, NULL, NULL) == 0
     assert L.cider_int8_mv(NULL, NULL, NULL, 2, 0, 64, 0, NULL, NULL) == 0
+    assert L.cider_w8a8_gemm_token_group(NULL, NULL, NULL, NULL, 0, 16, 128, 64, NULL, NULL) == 0
+    assert L.cider_w8a8_gemm_token_group(NULL, NULL, NULL, NULL, 16, 0, 128, 128, NULL, NULL) == 0
 
 
 def test_quant_weight_rejects():
@@ -100,6 +102,19 @@ def test_int8_mv_rejects():
     assert mv(P, P, NULL, 1, 4, 64, 0, P, NULL) == INV
     assert mv(MIS, P, P, 1, 4, 64, 0, P, NULL) == INV
     assert mv(P, P, P, 1, 4, 64, 0, MIS, NULL) == INV
+
+
+def test_token_group_rejects():
+    t = L.cider_w8a8_gemm_token_group
+    assert t(P, P, P, P, 4, 4, 128, 0, P, NULL) == INV                    # needs per-group weights
+    assert t(P, P, P, P, 4, 4, 128, 32, P, NULL) == INV
+    assert t(P, P, P, P, 4, 4, 192, 128, P, NULL) == INV                  # K % gs
+    assert t(P, P, P, P, -1, 4, 128, 64, P, NULL) == INV
+    assert t(P, P, P, P, 4, 4, 133120 + 128, 64, P, NULL) == INV          # int32 range guard
+    assert t(NULL, P, P, P, 4, 4, 128, 64, P, NULL) == INV
+    assert t(P, NULL, P, P, 4, 4, 128, 64, P, NULL) == INV
+    assert t(P, P, P, P, 4, 4, 128, 64, NULL, NULL) == INV
+    assert t(P, MIS, P, P, 4, 4, 128, 64, P, NULL) == INV
 
 
 def test_not_available_without_gpu():

@@ -33,6 +33,8 @@ SIGNATURES = {
     "cider_w8a8_gemm": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p]),
     "cider_w4a8_gemm": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p]),
     "cider_gemm_acc_i32": (ctypes.c_int, [_c_i32, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p]),
+    "cider_w8a8_gemm_token_group": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p,
+                                                   _c_p]),
     "cider_int8_mv": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p]),
     "cider_stack_workspace_layout": (ctypes.c_int64, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                                       ctypes.POINTER(ctypes.c_int64)]),
@@ -176,6 +178,27 @@ def cider_w8a8_gemm(x_q, x_scale, w_q, w_scale, group_size: int = 0, y=None, str
     return y
 
 
+def cider_w8a8_gemm_token_group(x_q, x_scale, w_q, w_scale, group_size: int, y=None, stream=None):
+    """Per-token activation codes (x_scale [M]) times per-group weight codes
+    (w_scale [N, K/group_size], group_size 64 or 128) -> fp16 y [M, N]."""
+    import torch
+    M, K = x_q.shape
+    N = w_q.shape[0]
+    _need(x_q, torch.int8, (M, K), "x_q")
+    _need(w_q, torch.int8, (N, K), "w_q")
+    if group_size not in (64, 128) or K % group_size:
+        raise ValueError("group_size must be 64 or 128 and divide K")
+    _need(x_scale, torch.float32, (M,), "x_scale")
+    _need(w_scale, torch.float32, _scale_shape(N, K, group_size), "w_scale")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x_q.device)
+    _need(y, torch.float16, (M, N), "y")
+    _check("cider_w8a8_gemm_token_group",
+           lib().cider_w8a8_gemm_token_group(_ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale), M, N, K,
+                                             group_size, _ptr(y), _stream(stream)))
+    return y
+
+
 def cider_int8_mv(x, w_q, w_scale, group_size: int = 0, y=None, stream=None):
     """Decode MV: fp16 x [M, K] (M <= 4) times int8 weights dequantized on the
     fly -> fp16 y [M, N]; no activation quantization."""
@@ -235,6 +258,12 @@ def w8a8_linear(x, w_q, w_scale, group_size: int = 0, stream=None):
     """The README's per-channel / per-group linear: quantize x, then the fused GEMM."""
     x_q, x_scale = cider_quant_act(x, group_size, stream=stream)
     return cider_w8a8_gemm(x_q, x_scale, w_q, w_scale, group_size, stream=stream)
+
+
+def w8a8_linear_token_group(x, w_q, w_scale, group_size: int, stream=None):
+    """Per-token activation quantization, then the per-group-weight GEMM."""
+    x_q, x_scale = cider_quant_act(x, 0, stream=stream)
+    return cider_w8a8_gemm_token_group(x_q, x_scale, w_q, w_scale, group_size, stream=stream)
 
 
 def w4a8_linear(x, w_packed, w_scale, stream=None):

@@ -58,6 +58,13 @@ __device__ __forceinline__ _Float16 dequant1(int32_t acc, float sa, float sw) {
   return (_Float16)t;
 }
 
+// fp16(fp32(t * s)): a finished fp32 sum times one scale (two roundings, as above).
+__device__ __forceinline__ _Float16 scale1(float t, float s) {
+  t = t * s;
+  asm("" : "+v"(t));
+  return (_Float16)t;
+}
+
 // Four consecutive outputs of one row (the same rounding as dequant1).
 __device__ __forceinline__ h4 dequant4(v4i acc, float sa, float4 sw) {
   float4 t;
@@ -541,6 +548,13 @@ gemm_skinny_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, c
             for (int r = 0; r < 4; ++r)
               if (n + r < N) ACC[((int64_t)u * M + m) * N + n + r] = acc[r];
           }
+        } else if constexpr (EPI == kEpiF16Tok) {
+          // per-token activations: s_a[m] is applied once, in the store stage
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float sw = SW[(int64_t)min(n0 + 4 * l4 + r, N - 1) * G + u];
+            facc[r] = __builtin_fmaf((float)acc[r], sw, facc[r]);
+          }
         } else {
           const float sa = SA[(int64_t)min(l16, M - 1) * G + u];
 #pragma unroll
@@ -589,6 +603,11 @@ gemm_skinny_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, c
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       if (n + r < N) Y[(int64_t)m * N + n + r] = (_Float16)t[r];
+  } else if constexpr (EPI == kEpiF16Tok) {
+    const float sam = SA[m];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (n + r < N) Y[(int64_t)m * N + n + r] = scale1(t[r], sam);
   }
 }
 
@@ -772,6 +791,9 @@ hipError_t launch_skinny(const GemmArgs& g, hipStream_t st) {
 // MFMA. The fold's VALU work thus sits between independent MFMAs, which the
 // SIMD overlaps with the matrix cores, instead of waiting for a group's MFMAs
 // to drain. (Group -1 is a zero accumulator with zero scales.)
+// With per-token activation scales (kEpiF16Tok) only the s_w segments are
+// gathered, the fold is fp32(acc) * s_w[n,g-1] added with one fma, and s_a[m]
+// multiplies the finished fp32 sum in the store stage.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int WGM, int WGN, int NS, int GS, int EPI>
 __global__ void __launch_bounds__(WGM * WGN * 64)
@@ -785,13 +807,15 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
   constexpr int GPS = BK / GS;                           // groups per stage
   constexpr int KPG = GS / 64;                           // 64-code MFMA steps per group
   constexpr int kCodeBytes = (BM + BN) * RB;
-  constexpr bool kF16 = EPI == kEpiF16;
+  constexpr bool kF16 = EPI != kEpiAccI32;
+  constexpr bool kTok = EPI == kEpiF16Tok;
   // 4-byte DMA instructions per stage and per wave (spares load nothing). The
   // int32-accumulator variant has no scales (its scale pointers are null), so
   // it issues none.
   // A group's scales sit in LDS as [BMp] s_a then [BNp] s_w (tile rows padded
-  // to 64: one 4-byte DMA instruction per 64 rows; rows past the tile load 0)
-  constexpr int BMp = (BM + 63) / 64 * 64, BNp = (BN + 63) / 64 * 64, kSeg = BMp + BNp;
+  // to 64: one 4-byte DMA instruction per 64 rows; rows past the tile load 0);
+  // per-token activation scales have no s_a segment.
+  constexpr int BMp = kTok ? 0 : (BM + 63) / 64 * 64, BNp = (BN + 63) / 64 * 64, kSeg = BMp + BNp;
   constexpr int kScaleInstr = kF16 ? GPS * kSeg / 64 : 0;
   constexpr int kScalePer = (kScaleInstr + NW - 1) / NW;
   constexpr int kSlotFloats = GPS * kSeg;                // one stage's scales: [GPS][kSeg]
@@ -833,7 +857,7 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (int64_t)n0 * K, (uint32_t)rows_w * ld);
   // scale descriptors (never dereferenced by the int32-accumulator variant)
   const __amdgpu_buffer_rsrc_t rsa =
-      make_rsrc(SA + (kF16 ? (int64_t)m0 * G : 0), kF16 ? (uint32_t)rows_a * G * 4 : 0u);
+      make_rsrc(SA + (kF16 && !kTok ? (int64_t)m0 * G : 0), kF16 && !kTok ? (uint32_t)rows_a * G * 4 : 0u);
   const __amdgpu_buffer_rsrc_t rsw =
       make_rsrc(SW + (kF16 ? (int64_t)n0 * G : 0), kF16 ? (uint32_t)rows_w * G * 4 : 0u);
 
@@ -858,7 +882,7 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
     for (int i = 0; i < kScalePer; ++i) {
       const int j = wave + i * NW;
       if (j >= kScaleInstr) {   // keeps every wave's vmcnt count equal
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)pad, 4, 0x80000000u, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_void*)pad, 4, 0x80000000u, 0, 0, 0);
         continue;
       }
       const int gi = j / (kSeg / 64), p = j % (kSeg / 64);
@@ -877,7 +901,13 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
 
   // fold tile (a, b)'s finished group-g sum (scales at gsc, its [kSeg] slice)
   auto fold_tile = [&](int a, int b, const float* gsc, int g) {
-    if constexpr (kF16) {
+    if constexpr (kTok) {
+      const float4 s4 = *reinterpret_cast<const float4*>(gsc + wn + 16 * a + 4 * l4);
+      facc[a][b][0] = __builtin_fmaf((float)acc[a][b][0], s4.x, facc[a][b][0]);
+      facc[a][b][1] = __builtin_fmaf((float)acc[a][b][1], s4.y, facc[a][b][1]);
+      facc[a][b][2] = __builtin_fmaf((float)acc[a][b][2], s4.z, facc[a][b][2]);
+      facc[a][b][3] = __builtin_fmaf((float)acc[a][b][3], s4.w, facc[a][b][3]);
+    } else if constexpr (kF16) {
       const float sam = gsc[wm + 16 * b + l16];
       const float4 s4 = *reinterpret_cast<const float4*>(gsc + BMp + wn + 16 * a + 4 * l4);
       facc[a][b][0] += ((float)acc[a][b][0] * sam) * s4.x;
@@ -959,13 +989,14 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
     for (int b = 0; b < TM; ++b) {
       const int m = m0 + wm + 16 * b + l16;
       if (m >= M) continue;
+      const float sam = kTok ? SA[m] : 1.0f;
 #pragma unroll
       for (int a = 0; a < TN; ++a) {
         const int n = n0 + wn + 16 * a + 4 * l4;
         if (n >= N) continue;
         h4 o;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = (_Float16)facc[a][b][r];
+        for (int r = 0; r < 4; ++r) o[r] = kTok ? scale1(facc[a][b][r], sam) : (_Float16)facc[a][b][r];
         _Float16* dst = Y + (int64_t)m * N + n;
         if (vec_ok && n + 3 < N) {
           *reinterpret_cast<h4*>(dst) = o;
@@ -1123,10 +1154,20 @@ hipError_t launch_epi(const GemmArgs& g, WeightKind wk, hipStream_t st) {
   }
 }
 
+// Per-token activations x per-group int8 weights: the skinny kernel for
+// M <= 16, else the per-group pipeline (tile costs as for per-group scales).
+hipError_t launch_tok(const GemmArgs& g, hipStream_t st) {
+  if (g.M <= 16)
+    return g.group_size == 64 ? launch_skinny<kWeightI8, 64, kEpiF16Tok>(g, st)
+                              : launch_skinny<kWeightI8, 128, kEpiF16Tok>(g, st);
+  return g.group_size == 64 ? launch_pg<64, kEpiF16Tok>(g, st) : launch_pg<128, kEpiF16Tok>(g, st);
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs& g, WeightKind wk, Epilogue epi, hipStream_t st) {
   // Tile table by M (the README's tile section also switches configs by M).
+  if (epi == kEpiF16Tok) return launch_tok(g, st);
   return epi == kEpiF16 ? launch_epi<kEpiF16>(g, wk, st) : launch_epi<kEpiAccI32>(g, wk, st);
 }
 

@@ -13,15 +13,16 @@ namespace cider {
 hipError_t launch_quant_rows(const void* x, int64_t R, int64_t K, int group_size, int qmax,
                              void* q, float* s, hipStream_t stream);
 
-// Epilogue kinds of the GEMM kernels.
-enum Epilogue { kEpiF16 = 0, kEpiAccI32 = 1 };
+// Epilogue kinds of the GEMM kernels. kEpiF16Tok: per-group weight scales
+// [N, G] with per-token activation scales [M] (int8 weights, gs 64 / 128).
+enum Epilogue { kEpiF16 = 0, kEpiAccI32 = 1, kEpiF16Tok = 2 };
 
 // Weight encodings of the GEMM kernels.
 enum WeightKind { kWeightI8 = 0, kWeightI4 = 1 };
 
 struct GemmArgs {
   const int8_t* a;   // activation codes [M, K]
-  const float* sa;   // activation scales [M] or [M, G]
+  const float* sa;   // activation scales [M] or [M, G] ([M] for kEpiF16Tok)
   const void* w;     // weight codes [N, K] int8 or packed [N, K/2]
   const float* sw;   // weight scales [N] or [N, G]
   int64_t M, N, K;
