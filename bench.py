@@ -223,25 +223,34 @@ def measure_stack(cider, torch, inputs, steps, warmup, layers=28, M=1024, dims=(
             del w
         Ls.append(L)
     x = torch.from_numpy(inputs.activations(M, hidden, seed=0)).to(dev)
-    y, ws = cider.cider_stack_forward(x, Ls, dims)
-    for _ in range(warmup):
-        cider.cider_stack_forward(x, Ls, dims, workspace=ws, y=y)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     stream = torch.cuda.current_stream()
-    e0.record(stream)
-    for _ in range(steps):
-        cider.cider_stack_forward(x, Ls, dims, workspace=ws, y=y, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+
+    def timed(layers_):
+        y, ws = cider.cider_stack_forward(x, layers_, dims)
+        for _ in range(warmup):
+            cider.cider_stack_forward(x, layers_, dims, workspace=ws, y=y)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            cider.cider_stack_forward(x, layers_, dims, workspace=ws, y=y, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms_sep = timed(Ls)
+    # the same weights with q/k/v and gate/up adjacent: one GEMM per group
+    Ls = [cider.fuse_stack_layer(L) for L in Ls]
+    torch.cuda.empty_cache()
+    ms = timed(Ls)
     ops = 2.0 * M * layers * sum(n * k for n, k in shapes.values())
-    del Ls, ws
+    del Ls
     torch.cuda.empty_cache()
     return {"workload": f"{layers}-layer linear stack, seq {M}, hidden {hidden}, q {q_dim}, kv {kv_dim}, "
-                        f"mlp {mlp_dim}: {4 * layers} quantizations + {7 * layers} GEMMs per pass",
+                        f"mlp {mlp_dim}: {4 * layers} quantizations + {4 * layers} GEMMs per pass "
+                        f"(q/k/v and gate/up fused)",
             "ms_per_pass": round(ms, 4), "TOP/s": round(ops / (ms * 1e-3) / 1e12, 2), "ops_per_pass": ops,
-            "steps": steps}
+            "ms_per_pass_unfused": round(ms_sep, 4), "steps": steps}
 
 
 SWEEP = ([("w8a8_pc", M, 10240, 2560, 0) for M in (1, 128, 1024, 4096, 8192)] +

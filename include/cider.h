@@ -132,6 +132,25 @@ cider_status_t cider_w8a8_gemm_token_group(const int8_t* x_q, const float* x_sca
                                            const float* w_scale, int64_t M, int64_t N, int64_t K,
                                            int32_t group_size, void* y_f16, void* stream);
 
+/* Same-input projections as one GEMM (the README's experimental SplitLinear
+ * page prepares the input of the Q/K/V and gate/up projections once): the
+ * per-channel W8A8 GEMM of x_q against the row-concatenation of n_parts
+ * weight matrices, each part's output columns written to its own matrix.
+ *   w_q     : int8 [N, K] with N = sum(part_n), part i = rows
+ *             [sum(part_n[<i]), sum(part_n[<=i])); w_scale fp32 [N].
+ *   part_n  : HOST array of n_parts widths, each > 0 and a multiple of 16,
+ *             1 <= n_parts <= CIDER_SPLIT_MAX_PARTS.
+ *   y_parts : HOST array of n_parts DEVICE pointers, y_parts[i] fp16
+ *             [M, part_n[i]] (output).
+ * Every output equals the one cider_w8a8_gemm computes for that part alone,
+ * bit for bit (per-channel dequant as above). x_q, x_scale, K and errors as
+ * for cider_w8a8_gemm (group_size 0).
+ */
+#define CIDER_SPLIT_MAX_PARTS 4
+cider_status_t cider_w8a8_gemm_split(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
+                                     const float* w_scale, int64_t M, int64_t K, int32_t n_parts,
+                                     const int64_t* part_n, void* const* y_parts, void* stream);
+
 /* Decode matrix-vector product, the README's int8_mv (section "架构 / Metal
  * Kernel 流水线", Decode (M = 1): the activations are not quantized; the int8
  * weights are dequantized on the fly; the file list names a per-channel and a
@@ -171,7 +190,11 @@ cider_status_t cider_gemm_acc_i32(int32_t mode, const int8_t* x_q, const void* w
  *   quant(Q)    -> O = Q Wo^T
  *   quant(O)    -> G = O Wg^T, U = O Wu^T               (one shared quant)
  *   quant(U)    -> h' = U Wd^T                          (the next layer's input)
- * i.e. 4 activation quantizations and 7 GEMMs per layer. K, V and G are
+ * i.e. 4 activation quantizations and 7 GEMMs per layer. When a layer's q, k
+ * and v codes are adjacent in memory in that order (w[1] == w[0] +
+ * q_dim*hidden, w[2] == w[1] + kv_dim*hidden) and so are their scales, the
+ * three run as one GEMM over the concatenated rows (cider_w8a8_gemm_split);
+ * likewise gate and up. The results are bit-identical either way. K, V and G are
  * computed and kept in the workspace but not consumed (there is no attention
  * or activation function: this is the linear-layer work of the stack only).
  * Shapes: Wq [q_dim, hidden], Wk/Wv [kv_dim, hidden], Wo [hidden, q_dim],

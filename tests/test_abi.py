@@ -117,6 +117,27 @@ def test_token_group_rejects():
     assert t(P, MIS, P, P, 4, 4, 128, 64, P, NULL) == INV
 
 
+def test_split_rejects():
+    sp = L.cider_w8a8_gemm_split
+    n3 = (ctypes.c_int64 * 3)(32, 16, 48)
+    y3 = (ctypes.c_void_p * 3)(1 << 20, 1 << 21, 1 << 22)
+    cast = lambda a: ctypes.cast(a, ctypes.c_void_p)
+    assert sp(P, P, P, P, 4, 64, 0, cast(n3), cast(y3), NULL) == INV        # no parts
+    assert sp(P, P, P, P, 4, 64, 5, cast(n3), cast(y3), NULL) == INV        # above CIDER_SPLIT_MAX_PARTS
+    bad = (ctypes.c_int64 * 3)(32, 8, 48)
+    assert sp(P, P, P, P, 4, 64, 3, cast(bad), cast(y3), NULL) == INV       # width % 16
+    zero = (ctypes.c_int64 * 3)(32, 0, 48)
+    assert sp(P, P, P, P, 4, 64, 3, cast(zero), cast(y3), NULL) == INV
+    assert sp(P, P, P, P, 4, 40, 3, cast(n3), cast(y3), NULL) == INV        # K % 16
+    assert sp(P, P, P, P, 4, 64, 3, NULL, cast(y3), NULL) == INV
+    ynull = (ctypes.c_void_p * 3)(1 << 20, None, 1 << 22)
+    assert sp(P, P, P, P, 4, 64, 3, cast(n3), cast(ynull), NULL) == INV
+    ymis = (ctypes.c_void_p * 3)(1 << 20, (1 << 21) + 8, 1 << 22)
+    assert sp(P, P, P, P, 4, 64, 3, cast(n3), cast(ymis), NULL) == INV
+    assert sp(NULL, P, P, P, 4, 64, 3, cast(n3), cast(y3), NULL) == INV
+    assert sp(NULL, NULL, NULL, NULL, 0, 64, 3, cast(n3), cast(y3), NULL) == 0   # empty work
+
+
 def test_not_available_without_gpu():
     import torch
     if torch.cuda.is_available():

@@ -72,3 +72,24 @@ def test_stack_chain(M, dims, n_layers):
         assert np.array_equal(h.view(np.uint16), host(y_prev).view(np.uint16))
         inp = h[rows]
     check_last_layer(c, x, ws, offs, y, M, dims, H[-1], rows, inp)
+
+
+@pytest.mark.parametrize("M,dims", [(70, (256, 256, 128, 512)), (9, (256, 256, 128, 512)),
+                                    (1024, (2048, 2048, 1024, 6144))])
+def test_stack_fused_projections_are_bit_identical(M, dims):
+    """Adjacent q/k/v and gate/up weights run as one GEMM each; every output
+    and intermediate equals the unfused run bit for bit."""
+    c = cider()
+    x = inputs.activations(M, dims[0], seed=10)
+    layers, _ = make_layers(c, 2, dims, seed0=5)
+    fused = [c.fuse_stack_layer(L) for L in layers]
+    y0, ws0 = c.cider_stack_forward(dev(x), layers, dims)
+    y1, ws1 = c.cider_stack_forward(dev(x), fused, dims)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(y0).view(np.uint16), host(y1).view(np.uint16))
+    _, offs = c.cider_stack_workspace_layout(M, *dims)
+    for n in ("q", "k", "v", "o", "gate", "up"):
+        a = host(c.stack_region(ws0, offs, n, M, *dims))
+        b = host(c.stack_region(ws1, offs, n, M, *dims))
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), n
+

@@ -35,6 +35,7 @@ SIGNATURES = {
     "cider_gemm_acc_i32": (ctypes.c_int, [_c_i32, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p]),
     "cider_w8a8_gemm_token_group": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p,
                                                    _c_p]),
+    "cider_w8a8_gemm_split": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_p, _c_p, _c_p]),
     "cider_int8_mv": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p]),
     "cider_stack_workspace_layout": (ctypes.c_int64, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                                       ctypes.POINTER(ctypes.c_int64)]),
@@ -199,6 +200,32 @@ def cider_w8a8_gemm_token_group(x_q, x_scale, w_q, w_scale, group_size: int, y=N
     return y
 
 
+def cider_w8a8_gemm_split(x_q, x_scale, w_q, w_scale, part_n, ys=None, stream=None):
+    """Per-channel GEMM of x_q against row-concatenated weights w_q [sum(part_n), K];
+    returns one fp16 [M, part_n[i]] output per part."""
+    import torch
+    M, K = x_q.shape
+    N = w_q.shape[0]
+    part_n = [int(n) for n in part_n]
+    if sum(part_n) != N:
+        raise ValueError("part widths must add up to the weight rows")
+    _need(x_q, torch.int8, (M, K), "x_q")
+    _need(w_q, torch.int8, (N, K), "w_q")
+    _need(x_scale, torch.float32, (M,), "x_scale")
+    _need(w_scale, torch.float32, (N,), "w_scale")
+    if ys is None:
+        ys = [torch.empty((M, n), dtype=torch.float16, device=x_q.device) for n in part_n]
+    for i, (y, n) in enumerate(zip(ys, part_n)):
+        _need(y, torch.float16, (M, n), f"ys[{i}]")
+    arr_n = (ctypes.c_int64 * len(part_n))(*part_n)
+    arr_y = (ctypes.c_void_p * len(ys))(*[y.data_ptr() for y in ys])
+    _check("cider_w8a8_gemm_split",
+           lib().cider_w8a8_gemm_split(_ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale), M, K, len(part_n),
+                                       ctypes.cast(arr_n, ctypes.c_void_p), ctypes.cast(arr_y, ctypes.c_void_p),
+                                       _stream(stream)))
+    return ys
+
+
 def cider_int8_mv(x, w_q, w_scale, group_size: int = 0, y=None, stream=None):
     """Decode MV: fp16 x [M, K] (M <= 4) times int8 weights dequantized on the
     fly -> fp16 y [M, N]; no activation quantization."""
@@ -286,6 +313,23 @@ def stack_region(workspace, offsets, name, M, hidden, q_dim, kv_dim, mlp_dim):
     n = dims[name]
     start = offsets[name]
     return workspace[start:start + 2 * M * n].view(torch.float16).view(M, n)
+
+
+def fuse_stack_layer(layer):
+    """A copy of one stack layer ({name: (codes, scales)}) whose q/k/v and
+    gate/up codes and scales live back to back in one allocation each, so
+    that cider_stack_forward runs each group as one GEMM."""
+    import torch
+    out = dict(layer)
+    for group in (("q", "k", "v"), ("gate", "up")):
+        wcat = torch.cat([layer[n][0] for n in group])
+        scat = torch.cat([layer[n][1] for n in group])
+        r = 0
+        for n in group:
+            rows = layer[n][0].shape[0]
+            out[n] = (wcat[r:r + rows], scat[r:r + rows])
+            r += rows
+    return out
 
 
 def cider_stack_forward(x, layers, dims, workspace=None, y=None, stream=None):

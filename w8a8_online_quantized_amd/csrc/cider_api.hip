@@ -155,6 +155,34 @@ cider_status_t cider_w8a8_gemm_token_group(const int8_t* x_q, const float* x_sca
   return gemm_common(g, cider::kWeightI8, cider::kEpiF16Tok, stream);
 }
 
+cider_status_t cider_w8a8_gemm_split(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
+                                     const float* w_scale, int64_t M, int64_t K, int32_t n_parts,
+                                     const int64_t* part_n, void* const* y_parts, void* stream) {
+  if (M < 0 || M >= (int64_t(1) << 31) || !valid_k(K, 16, 0)) return CIDER_ERROR_INVALID_VALUE;
+  if (n_parts < 1 || n_parts > CIDER_SPLIT_MAX_PARTS || !part_n || !y_parts) return CIDER_ERROR_INVALID_VALUE;
+  cider::OutSplit sp{};
+  int64_t N = 0;
+  for (int32_t i = 0; i < n_parts; ++i) {
+    if (part_n[i] <= 0 || part_n[i] % 16 != 0) return CIDER_ERROR_INVALID_VALUE;
+    N += part_n[i];
+    if (N >= (int64_t(1) << 31)) return CIDER_ERROR_INVALID_VALUE;
+    sp.y[i] = static_cast<_Float16*>(y_parts[i]);
+    sp.end[i] = (int)N;
+  }
+  for (int32_t i = n_parts; i < CIDER_SPLIT_MAX_PARTS; ++i) {
+    sp.y[i] = sp.y[n_parts - 1];
+    sp.end[i] = (int)N;
+  }
+  if (M == 0) return CIDER_SUCCESS;
+  if (!x_q || !x_scale || !w_q || !w_scale) return CIDER_ERROR_INVALID_VALUE;
+  if (!aligned16(x_q) || !aligned16(x_scale) || !aligned16(w_q) || !aligned16(w_scale)) return CIDER_ERROR_INVALID_VALUE;
+  for (int32_t i = 0; i < n_parts; ++i)
+    if (!y_parts[i] || !aligned16(y_parts[i])) return CIDER_ERROR_INVALID_VALUE;
+  cider::GemmArgs g{x_q, x_scale, w_q, w_scale, M, N, K, 0, sp.y[0], nullptr};
+  g.split = sp;
+  return gemm_common(g, cider::kWeightI8, cider::kEpiF16Split, stream);
+}
+
 cider_status_t cider_int8_mv(const void* x_f16, const int8_t* w_q, const float* w_scale, int64_t M, int64_t N,
                              int64_t K, int32_t group_size, void* y_f16, void* stream) {
   if (M < 0 || M > CIDER_MV_MAX_M || !gemm_sizes_ok(M, N) || !valid_gs(group_size) || !valid_k(K, 16, group_size))
@@ -228,19 +256,50 @@ cider_status_t cider_stack_forward(const void* x_f16, int64_t M, int64_t hidden,
     cider::GemmArgs a{xq, sa, L.w[j], L.s[j], M, N, K, 0, out, nullptr};
     return cider::launch_gemm(a, cider::kWeightI8, cider::kEpiF16, st);
   };
+  // Projections j, j+1[, j+2] of one input as one GEMM when their codes and
+  // scales are adjacent in memory, in that order (columns split to `outs`).
+  auto adjacent = [&](const cider_stack_layer_t& L, int j, int parts, const int64_t* n) {
+    for (int i = 1; i < parts; ++i) {
+      if (L.w[j + i] != L.w[j + i - 1] + n[i - 1] * hidden) return false;
+      if (L.s[j + i] != L.s[j + i - 1] + n[i - 1]) return false;
+    }
+    return true;
+  };
+  auto gemm_fused = [&](const cider_stack_layer_t& L, int j, int parts, const int64_t* n, void* const* outs) {
+    cider::GemmArgs a{xq, sa, L.w[j], L.s[j], M, 0, hidden, 0, outs[0], nullptr};
+    int64_t end = 0;
+    for (int i = 0; i < cider::kMaxSplitParts; ++i) {
+      if (i < parts) end += n[i];
+      a.split.y[i] = static_cast<_Float16*>(outs[i < parts ? i : parts - 1]);
+      a.split.end[i] = (int)end;
+    }
+    a.N = end;
+    return cider::launch_gemm(a, cider::kWeightI8, cider::kEpiF16Split, st);
+  };
+  const int64_t n_qkv[3] = {q_dim, kv_dim, kv_dim}, n_gu[2] = {mlp_dim, mlp_dim};
   const void* in = x_f16;
   for (int32_t l = 0; l < n_layers; ++l) {
     const cider_stack_layer_t& L = layers[l];
     void* out = l + 1 == n_layers ? y_f16 : h;
+    void* const qkv_out[3] = {q, k, v};
+    void* const gu_out[2] = {g, u};
     hipError_t e = quant(in, hidden);
-    if (e == hipSuccess) e = gemm(L, 0, q_dim, hidden, q);
-    if (e == hipSuccess) e = gemm(L, 1, kv_dim, hidden, k);
-    if (e == hipSuccess) e = gemm(L, 2, kv_dim, hidden, v);
+    if (adjacent(L, 0, 3, n_qkv)) {
+      if (e == hipSuccess) e = gemm_fused(L, 0, 3, n_qkv, qkv_out);
+    } else {
+      if (e == hipSuccess) e = gemm(L, 0, q_dim, hidden, q);
+      if (e == hipSuccess) e = gemm(L, 1, kv_dim, hidden, k);
+      if (e == hipSuccess) e = gemm(L, 2, kv_dim, hidden, v);
+    }
     if (e == hipSuccess) e = quant(q, q_dim);
     if (e == hipSuccess) e = gemm(L, 3, hidden, q_dim, o);
     if (e == hipSuccess) e = quant(o, hidden);
-    if (e == hipSuccess) e = gemm(L, 4, mlp_dim, hidden, g);
-    if (e == hipSuccess) e = gemm(L, 5, mlp_dim, hidden, u);
+    if (adjacent(L, 4, 2, n_gu)) {
+      if (e == hipSuccess) e = gemm_fused(L, 4, 2, n_gu, gu_out);
+    } else {
+      if (e == hipSuccess) e = gemm(L, 4, mlp_dim, hidden, g);
+      if (e == hipSuccess) e = gemm(L, 5, mlp_dim, hidden, u);
+    }
     if (e == hipSuccess) e = quant(u, mlp_dim);
     if (e == hipSuccess) e = gemm(L, 6, hidden, mlp_dim, out);
     if (e != hipSuccess) return CIDER_ERROR_LAUNCH;

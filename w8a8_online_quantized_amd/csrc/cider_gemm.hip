@@ -193,12 +193,12 @@ template <int BM, int BN, int WGM, int WGN, int BK, int NS, int WK, int EPI, boo
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, const void* __restrict__ Wv,
                 const float* __restrict__ SW, int M, int N, int K, _Float16* __restrict__ Y,
-                int32_t* __restrict__ ACC, int splits, int32_t* __restrict__ WS) {
+                int32_t* __restrict__ ACC, int splits, int32_t* __restrict__ WS, OutSplit osp) {
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int TM = WTM / 16, TN = WTN / 16;
   constexpr bool kI4 = WK == kWeightI4;
-  constexpr bool kF16 = EPI == kEpiF16;
+  constexpr bool kF16 = EPI == kEpiF16 || EPI == kEpiF16Split;
   constexpr int RBA = BK;                     // activation bytes per row per stage
   constexpr int RBW = kI4 ? BK / 2 : BK;      // weight bytes per row per stage
   constexpr int kStageBytes = BM * RBA + BN * RBW;
@@ -462,6 +462,14 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
       } else {
         const h4 o = dequant4(acc[a][b], sam, *reinterpret_cast<const float4*>(lsw + nl));   // s_w zero past N
         _Float16* dst = Y + (int64_t)m * N + n;
+        if constexpr (EPI == kEpiF16Split) {
+          // the part holding columns n .. n+3 (part widths are multiples of 4)
+          const bool p1 = n >= osp.end[0], p2 = n >= osp.end[1], p3 = n >= osp.end[2];
+          const int start = p3 ? osp.end[2] : p2 ? osp.end[1] : p1 ? osp.end[0] : 0;
+          const int stop = p3 ? osp.end[3] : p2 ? osp.end[2] : p1 ? osp.end[1] : osp.end[0];
+          _Float16* base = p3 ? osp.y[3] : p2 ? osp.y[2] : p1 ? osp.y[1] : osp.y[0];
+          dst = base + (int64_t)m * (stop - start) + (n - start);
+        }
         if (vec_ok && n + 3 < N) {
           *reinterpret_cast<h4*>(dst) = o;
         } else {
@@ -1025,7 +1033,7 @@ hipError_t launch_dma(const GemmArgs& g, hipStream_t st) {
   const int64_t nbm = (g.M + BM - 1) / BM, nbn = (g.N + BN - 1) / BN;
   const dim3 grid((unsigned)(nbm * nbn)), block(WGM * WGN * 64);
   gemm_dma_kernel<BM, BN, WGM, WGN, BK, NS, WK, EPI><<<grid, block, 0, st>>>(
-      g.a, g.sa, g.w, g.sw, (int)g.M, (int)g.N, (int)g.K, static_cast<_Float16*>(g.y), g.acc, 1, nullptr);
+      g.a, g.sa, g.w, g.sw, (int)g.M, (int)g.N, (int)g.K, static_cast<_Float16*>(g.y), g.acc, 1, nullptr, g.split);
   return hipGetLastError();
 }
 
@@ -1044,7 +1052,7 @@ hipError_t launch_dma_split(const GemmArgs& g, int splits, hipStream_t st) {
   const dim3 grid((unsigned)(nbm * nbn * splits)), block(WGM * WGN * 64);
   gemm_dma_kernel<BM, BN, WGM, WGN, BK, NS, WK, EPI, true><<<grid, block, 0, st>>>(
       g.a, g.sa, g.w, g.sw, (int)g.M, (int)g.N, (int)g.K, static_cast<_Float16*>(g.y), g.acc, splits,
-      static_cast<int32_t*>(g.ws));
+      static_cast<int32_t*>(g.ws), g.split);
   return hipGetLastError();
 }
 
@@ -1168,6 +1176,23 @@ hipError_t launch_tok(const GemmArgs& g, hipStream_t st) {
 hipError_t launch_gemm(const GemmArgs& g, WeightKind wk, Epilogue epi, hipStream_t st) {
   // Tile table by M (the README's tile section also switches configs by M).
   if (epi == kEpiF16Tok) return launch_tok(g, st);
+  if (epi == kEpiF16Split) {
+    if (g.M > 16) return launch_pc<kWeightI8, kEpiF16Split>(g, st);
+    // small M: one launch per part over its rows of the weights (the same
+    // per-channel arithmetic, so the same bits as the fused launch)
+    int start = 0;
+    for (int i = 0; i < kMaxSplitParts && start < g.N; ++i) {
+      GemmArgs p = g;
+      p.w = static_cast<const int8_t*>(g.w) + (int64_t)start * g.K;
+      p.sw = g.sw + start;
+      p.N = g.split.end[i] - start;
+      p.y = g.split.y[i];
+      const hipError_t e = launch_epi<kEpiF16>(p, kWeightI8, st);
+      if (e != hipSuccess) return e;
+      start = g.split.end[i];
+    }
+    return hipSuccess;
+  }
   return epi == kEpiF16 ? launch_epi<kEpiF16>(g, wk, st) : launch_epi<kEpiAccI32>(g, wk, st);
 }
 

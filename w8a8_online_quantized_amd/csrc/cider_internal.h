@@ -15,7 +15,18 @@ hipError_t launch_quant_rows(const void* x, int64_t R, int64_t K, int group_size
 
 // Epilogue kinds of the GEMM kernels. kEpiF16Tok: per-group weight scales
 // [N, G] with per-token activation scales [M] (int8 weights, gs 64 / 128).
-enum Epilogue { kEpiF16 = 0, kEpiAccI32 = 1, kEpiF16Tok = 2 };
+// kEpiF16Split: per-channel fp16 output whose columns go to up to 4 separate
+// matrices (GemmArgs::split).
+enum Epilogue { kEpiF16 = 0, kEpiAccI32 = 1, kEpiF16Tok = 2, kEpiF16Split = 3 };
+
+// Column split of a GEMM's output: columns [end[i-1], end[i]) (end[-1] = 0)
+// go to y[i], a row-major fp16 matrix of end[i] - end[i-1] columns. Unused
+// trailing parts repeat the last end and are never selected.
+constexpr int kMaxSplitParts = 4;
+struct OutSplit {
+  _Float16* y[kMaxSplitParts];
+  int end[kMaxSplitParts];
+};
 
 // Weight encodings of the GEMM kernels.
 enum WeightKind { kWeightI8 = 0, kWeightI4 = 1 };
@@ -31,6 +42,7 @@ struct GemmArgs {
   int32_t* acc;      // int32 [M, N] or [G, M, N] (accumulator test hook)
   void* ws = nullptr;     // split-K workspace (counters zero on entry), or null
   int64_t ws_bytes = 0;
+  OutSplit split{};       // kEpiF16Split only
 };
 
 hipError_t launch_gemm(const GemmArgs& args, WeightKind wk, Epilogue epi, hipStream_t stream);
