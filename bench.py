@@ -92,7 +92,7 @@ def algorithmic(mode, M, N, K, gs):
     """Integer ops and HBM bytes one GEMM launch must move, and the bytes of the
     activation quantization (fp16 in, int8 + fp32 scales out)."""
     G = 1 if gs == 0 else K // gs
-    if mode == "int8_mv":   # decode MV: fp16 x and int8 weights in, fp16 y out, no quantization
+    if mode in ("int8_mv", "w8a8_linear"):   # fp16 x and int8 weights in, fp16 y out, one launch
         return 2.0 * M * N * K, 2 * M * K + N * K + 4 * N * G + 2 * M * N, 0
     wbytes = N * K // 2 if mode == "w4a8" else N * K
     Ga = 1 if mode == "w8a8_tokpg" else G   # per-token activations x per-group weights
@@ -112,8 +112,8 @@ def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_byte
     w_h = torch.from_numpy(inputs.weights(N, K, seed=0))
     ops, gemm_bytes, quant_bytes = algorithmic(mode, M, N, K, gs)
     R = max(2, -(-min_set_bytes // (gemm_bytes + quant_bytes)))
-    if mode == "int8_mv":
-        return measure_mv(cider, torch, x_h, w_h, M, N, K, gs, steps, warmup, R, ops, gemm_bytes)
+    if mode in ("int8_mv", "w8a8_linear"):
+        return measure_mv(cider, torch, x_h, w_h, M, N, K, gs, steps, warmup, R, ops, gemm_bytes, mode)
     bits = 4 if mode == "w4a8" else 8
     ags = 0 if mode == "w8a8_tokpg" else gs   # activation group size
     w_dev = w_h.to(dev)
@@ -165,8 +165,10 @@ def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_byte
             "gemm_bytes": gemm_bytes, "quant_bytes": quant_bytes, "sets": R}
 
 
-def measure_mv(cider, torch, x_h, w_h, M, N, K, gs, steps, warmup, R, ops, nbytes):
-    """The decode MV alone (it has no quantization step), rotating buffer sets."""
+def measure_mv(cider, torch, x_h, w_h, M, N, K, gs, steps, warmup, R, ops, nbytes, mode="int8_mv"):
+    """One-launch fp16-in calls, rotating buffer sets: the decode MV (no
+    activation quantization) or the one-call linear (quantization inside the
+    GEMV kernel)."""
     dev = torch.device("cuda:0")
     w_dev = w_h.to(dev)
     wq0, sw0 = cider.cider_quant_weight(w_dev, 8, gs)
@@ -175,15 +177,20 @@ def measure_mv(cider, torch, x_h, w_h, M, N, K, gs, steps, warmup, R, ops, nbyte
             for _ in range(R)]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+
+    def call(x, wq, sw, y):
+        if mode == "int8_mv":
+            cider.cider_int8_mv(x, wq, sw, gs, y, stream=stream)
+        else:
+            cider.cider_linear(x, wq, sw, 8, gs, None, y, stream=stream)
+
     for i in range(warmup):
-        x, wq, sw, y = sets[i % R]
-        cider.cider_int8_mv(x, wq, sw, gs, y, stream=stream)
+        call(*sets[i % R])
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(steps):
-        x, wq, sw, y = sets[i % R]
-        cider.cider_int8_mv(x, wq, sw, gs, y, stream=stream)
+        call(*sets[i % R])
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
@@ -259,7 +266,8 @@ SWEEP = ([("w8a8_pc", M, 10240, 2560, 0) for M in (1, 128, 1024, 4096, 8192)] +
          [("w8a8_tokpg", M, 2560, 10240, gs) for gs in (128, 64) for M in (16, 128, 1024, 4096)] +
          [("w4a8", M, 10240, 2560, 0) for M in (1, 1024, 8192)] +
          [("int8_mv", 1, 10240, 2560, 0), ("int8_mv", 1, 2560, 10240, 0), ("int8_mv", 1, 10240, 2560, 128),
-          ("int8_mv", 1, 2560, 10240, 128), ("int8_mv", 1, 2560, 10240, 64)])
+          ("int8_mv", 1, 2560, 10240, 128), ("int8_mv", 1, 2560, 10240, 64)] +
+         [("w8a8_linear", 1, 10240, 2560, 0), ("w8a8_linear", 1, 2560, 10240, 0), ("w8a8_linear", 4, 10240, 2560, 0)])
 
 
 def main():

@@ -41,7 +41,8 @@
  *     CIDER_ERROR_LAUNCH. A kernel fault surfaces at the caller's next
  *     synchronization, as usual in HIP.
  *   - Zero-sized work (M == 0 or N == 0) returns CIDER_SUCCESS and launches
- *     nothing; the pointers may then be NULL.
+ *     nothing; the pointers may then be NULL. Size queries (int64_t results)
+ *     return -1 for invalid arguments.
  *   - K must be a positive multiple of 16 (of 32 for int4 weights) and at most
  *     CIDER_MAX_K, which keeps |acc| = |sum of K products of codes| <= 127*127*K
  *     below 2^31. Per-group calls need K % group_size == 0.
@@ -114,6 +115,28 @@ cider_status_t cider_w8a8_gemm(const int8_t* x_q, const float* x_scale, const in
 cider_status_t cider_w4a8_gemm(const int8_t* x_q, const float* x_scale, const uint8_t* w_packed,
                                const float* w_scale, int64_t M, int64_t N, int64_t K,
                                void* y_f16, void* stream);
+
+/* The whole linear layer in one call, fp16 x in and fp16 y out (the README's
+ * perchannel_linear / w4a8_linear take fp16 activations): the activation
+ * quantization of cider_quant_act followed by cider_w8a8_gemm (bits 8) or
+ * cider_w4a8_gemm (bits 4), with identical results.
+ *   w : bits 8: int8 [N, K] codes, w_scale fp32 [N] or [N, K/group_size];
+ *       bits 4: packed uint8 [N, K/2], w_scale fp32 [N] (group_size 0).
+ *   For group_size 0 and M <= 4 (when the M activation rows' codes fit the
+ *   GEMV kernel's 64 KiB staging area: M' * ceil(K/256)*256 <= 65536 with
+ *   M' = 1, 2, 4 for M = 1, 2, 3..4) it is ONE kernel launch that quantizes
+ *   the activations itself and needs no workspace. Otherwise the codes and
+ *   scales go through `workspace` (device, 16-byte aligned, at least
+ *   cider_linear_workspace_size(M, K, bits, group_size) bytes; its contents
+ *   after the call are the activation codes [M, K] at offset 0 and the scales
+ *   at the next 256-byte boundary).
+ * Sizes, alignment and errors as for cider_quant_act / cider_w8a8_gemm;
+ * `workspace` may be NULL when the size query returns 0.
+ */
+int64_t cider_linear_workspace_size(int64_t M, int64_t K, int32_t bits, int32_t group_size);
+cider_status_t cider_linear(const void* x_f16, const void* w, const float* w_scale, int64_t M, int64_t N,
+                            int64_t K, int32_t bits, int32_t group_size, void* workspace,
+                            int64_t workspace_bytes, void* y_f16, void* stream);
 
 /* W8A8 GEMM with per-token activation scales and per-group weight scales
  * (the README's "量化" table quantizes activations per token in every mode,

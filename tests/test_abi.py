@@ -138,6 +138,26 @@ def test_split_rejects():
     assert sp(NULL, NULL, NULL, NULL, 0, 64, 3, cast(n3), cast(y3), NULL) == 0   # empty work
 
 
+def test_linear_workspace_query_and_rejects():
+    q = L.cider_linear_workspace_size
+    assert q(1, 2560, 8, 0) == 0 and q(4, 16384, 8, 0) == 0 and q(4, 2560, 4, 0) == 0   # one launch
+    assert q(4, 16384 + 256, 8, 0) == 4 * 16640 + 256                     # codes past the 64 KiB staging
+    assert q(5, 1024, 8, 0) == 5 * 1024 + 256
+    assert q(5, 1024, 8, 128) == 5 * 1024 + 256                           # 40 scale bytes
+    assert q(300, 1024, 8, 64) == 300 * 1024 + (4 * 300 * 16 + 255) // 256 * 256
+    assert q(0, 1024, 8, 0) == 0
+    assert q(4, 1024, 6, 0) == -1 and q(4, 1024, 4, 64) == -1 and q(4, 48, 4, 0) == -1 and q(-1, 64, 8, 0) == -1
+    lin = L.cider_linear
+    assert lin(P, P, P, 4, 8, 1024, 6, 0, NULL, 0, P, NULL) == INV        # bits
+    assert lin(P, P, P, 4, 8, 40, 8, 0, NULL, 0, P, NULL) == INV          # K % 16
+    assert lin(P, P, P, 5, 8, 1024, 8, 0, NULL, 0, P, NULL) == INV        # workspace needed
+    assert lin(P, P, P, 5, 8, 1024, 8, 0, P, 100, P, NULL) == INV         # workspace too small
+    assert lin(P, P, P, 5, 8, 1024, 8, 0, MIS, 1 << 20, P, NULL) == INV
+    assert lin(NULL, P, P, 1, 8, 1024, 8, 0, NULL, 0, P, NULL) == INV
+    assert lin(P, P, P, 1, 8, 1024, 8, 0, NULL, 0, MIS, NULL) == INV
+    assert lin(NULL, NULL, NULL, 0, 8, 1024, 8, 0, NULL, 0, NULL, NULL) == 0  # empty work
+
+
 def test_not_available_without_gpu():
     import torch
     if torch.cuda.is_available():

@@ -1,0 +1,90 @@
+"""The one-call linear (cider_linear): fp16 x -> quantization -> GEMM -> fp16 y.
+
+Its outputs must equal, bit for bit, the two calls it stands for
+(cider_quant_act then cider_w8a8_gemm / cider_w4a8_gemm), and meet the
+oracle's per-channel bar (|y - o| <= 1e-3*|o| + 2^-14, at most one fp16 ulp;
+per-group: 2e-3 plus the fp32 summation bound). The one-launch route
+(per-channel, M <= 4: the GEMV kernel quantizes its activations itself) and
+the workspace route are both covered, for int8 and packed int4 weights.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from w8a8_online_quantized_amd import inputs
+from tests.test_gpu_parity import assert_y_close, cider, dev, host, pg_sum_bound
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+ONE_LAUNCH = [(1, 10240, 2560), (2, 2560, 10240), (3, 300, 1056), (4, 130, 16384), (1, 17, 32), (1, 64, 32768)]
+
+
+def _two_calls(c, xd, wq, sw, bits, gs):
+    xq, sa = c.cider_quant_act(xd, gs)
+    if bits == 8:
+        return host(c.cider_w8a8_gemm(xq, sa, wq, sw, gs))
+    return host(c.cider_w4a8_gemm(xq, sa, wq, sw))
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("M,N,K", ONE_LAUNCH)
+def test_one_launch_linear(M, N, K, bits):
+    c = cider()
+    assert c.cider_linear_workspace_size(M, K, bits, 0) == 0
+    x = inputs.activations(M, K, seed=41)
+    w = inputs.weights(N, K, seed=41)
+    xd = dev(x)
+    wq, sw = c.cider_quant_weight(dev(w), bits, 0)
+    y = host(c.cider_linear(xd, wq, sw, bits, 0))
+    assert np.array_equal(y.view(np.uint16), _two_calls(c, xd, wq, sw, bits, 0).view(np.uint16))
+    wqo, swo = oracle.quantize_weight(w, bits, 0)
+    yo = oracle.w8a8_linear(x, wqo, swo, 0)[0] if bits == 8 else oracle.w4a8_linear(x, wqo, swo)[0]
+    assert_y_close(y, yo, 1e-3, max_ulp=1, what=f"linear{bits} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K,bits,gs", [(5, 200, 1024, 8, 0), (16, 300, 2560, 4, 0), (70, 260, 1152, 8, 64),
+                                           (9, 130, 1024, 8, 128), (300, 650, 2560, 8, 0), (4, 100, 1024, 8, 128),
+                                           (1024, 2560, 10240, 8, 128)])
+def test_workspace_linear(M, N, K, bits, gs):
+    c = cider()
+    need = c.cider_linear_workspace_size(M, K, bits, gs)
+    assert need >= M * K
+    x = inputs.activations(M, K, seed=42)
+    w = inputs.weights(N, K, seed=42)
+    xd = dev(x)
+    wq, sw = c.cider_quant_weight(dev(w), bits, gs)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    y = host(c.cider_linear(xd, wq, sw, bits, gs, workspace=ws))
+    assert np.array_equal(y.view(np.uint16), _two_calls(c, xd, wq, sw, bits, gs).view(np.uint16))
+    rows = np.arange(M) if M <= 300 else np.unique(np.r_[0, M - 1, np.random.default_rng(3).integers(0, M, 24)])
+    wqo, swo = oracle.quantize_weight(w, bits, gs)
+    if bits == 4:
+        yo = oracle.w4a8_linear(x[rows], wqo, swo)[0]
+        assert_y_close(y[rows], yo, 1e-3, max_ulp=1, what=f"linear4 {M}x{N}x{K}")
+    elif gs == 0:
+        yo = oracle.w8a8_linear(x[rows], wqo, swo, 0)[0]
+        assert_y_close(y[rows], yo, 1e-3, max_ulp=1, what=f"linear8 {M}x{N}x{K}")
+    else:
+        yo, qo, sao = oracle.w8a8_linear(x[rows], wqo, swo, gs)
+        e = pg_sum_bound(qo, sao, wqo, swo, gs, np.arange(len(rows)))
+        assert_y_close(y[rows], yo, 2e-3, extra_atol=e, what=f"linear pg{gs} {M}x{N}x{K}")
+
+
+def test_one_launch_special_rows():
+    """A zero row gives zeros; rows of extreme magnitude quantize as the
+    standalone quantizer does (same codes, same outputs)."""
+    c = cider()
+    K, N = 2560, 256
+    rng = np.random.default_rng(43)
+    x = (rng.standard_normal((4, K)) * 0.3).astype(np.float16)
+    x[1] = 0
+    x[2, :] = np.float16(6.0e-8)                     # subnormal fp16 row
+    x[3, ::7] = np.float16(60000.0)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    xd = dev(x)
+    wq, sw = c.cider_quant_weight(dev(w), 8, 0)
+    y = host(c.cider_linear(xd, wq, sw, 8, 0))
+    assert not y[1].any()
+    assert np.array_equal(y.view(np.uint16), _two_calls(c, xd, wq, sw, 8, 0).view(np.uint16))

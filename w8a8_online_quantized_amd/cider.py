@@ -36,6 +36,9 @@ SIGNATURES = {
     "cider_w8a8_gemm_token_group": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p,
                                                    _c_p]),
     "cider_w8a8_gemm_split": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_p, _c_p, _c_p]),
+    "cider_linear_workspace_size": (ctypes.c_int64, [_c_i64, _c_i64, _c_i32, _c_i32]),
+    "cider_linear": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_p, _c_i64, _c_p,
+                                    _c_p]),
     "cider_int8_mv": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p]),
     "cider_stack_workspace_layout": (ctypes.c_int64, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                                       ctypes.POINTER(ctypes.c_int64)]),
@@ -224,6 +227,39 @@ def cider_w8a8_gemm_split(x_q, x_scale, w_q, w_scale, part_n, ys=None, stream=No
                                        ctypes.cast(arr_n, ctypes.c_void_p), ctypes.cast(arr_y, ctypes.c_void_p),
                                        _stream(stream)))
     return ys
+
+
+def cider_linear_workspace_size(M: int, K: int, bits: int = 8, group_size: int = 0) -> int:
+    """Workspace bytes cider_linear needs (0: one launch, no workspace)."""
+    n = int(lib().cider_linear_workspace_size(M, K, bits, group_size))
+    if n < 0:
+        raise ValueError("invalid linear sizes")
+    return n
+
+
+def cider_linear(x, w, w_scale, bits: int = 8, group_size: int = 0, workspace=None, y=None, stream=None):
+    """fp16 x [M, K] -> fp16 y [M, N] through the quantized linear (w: int8
+    codes [N, K] for bits 8, packed uint8 [N, K/2] for bits 4)."""
+    import torch
+    M, K = x.shape
+    N = w.shape[0]
+    _need(x, torch.float16, (M, K), "x")
+    if bits == 8:
+        _need(w, torch.int8, (N, K), "w")
+    else:
+        _need(w, torch.uint8, (N, K // 2), "w")
+    _need(w_scale, torch.float32, _scale_shape(N, K, group_size), "w_scale")
+    need = cider_linear_workspace_size(M, K, bits, group_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    _need(y, torch.float16, (M, N), "y")
+    wsp = _ptr(workspace) if workspace is not None else None
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("cider_linear", lib().cider_linear(_ptr(x), _ptr(w), _ptr(w_scale), M, N, K, bits, group_size, wsp, wsb,
+                                              _ptr(y), _stream(stream)))
+    return y
 
 
 def cider_int8_mv(x, w_q, w_scale, group_size: int = 0, y=None, stream=None):

@@ -183,6 +183,39 @@ cider_status_t cider_w8a8_gemm_split(const int8_t* x_q, const float* x_scale, co
   return gemm_common(g, cider::kWeightI8, cider::kEpiF16Split, stream);
 }
 
+int64_t cider_linear_workspace_size(int64_t M, int64_t K, int32_t bits, int32_t group_size) {
+  if (M < 0 || !valid_gs(group_size) || (bits != 8 && bits != 4)) return -1;
+  if (bits == 4 && group_size != 0) return -1;
+  if (!valid_k(K, bits == 4 ? 32 : 16, group_size)) return -1;
+  if (M == 0 || cider::linear_is_one_launch(M, K, group_size)) return 0;
+  const int64_t G = group_size ? K / group_size : 1;
+  return (M * K + 255) / 256 * 256 + (4 * M * G + 255) / 256 * 256;
+}
+
+cider_status_t cider_linear(const void* x_f16, const void* w, const float* w_scale, int64_t M, int64_t N,
+                            int64_t K, int32_t bits, int32_t group_size, void* workspace,
+                            int64_t workspace_bytes, void* y_f16, void* stream) {
+  const int64_t need = cider_linear_workspace_size(M, K, bits, group_size);
+  if (need < 0 || !gemm_sizes_ok(M, N)) return CIDER_ERROR_INVALID_VALUE;
+  if (M == 0 || N == 0) return CIDER_SUCCESS;
+  if (!x_f16 || !w || !w_scale || !y_f16) return CIDER_ERROR_INVALID_VALUE;
+  if (!aligned16(x_f16) || !aligned16(w) || !aligned16(w_scale) || !aligned16(y_f16)) return CIDER_ERROR_INVALID_VALUE;
+  if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need)) return CIDER_ERROR_INVALID_VALUE;
+  if (!device_is_gfx950()) return CIDER_ERROR_NOT_SUPPORTED;
+  const cider::WeightKind wk = bits == 4 ? cider::kWeightI4 : cider::kWeightI8;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (need == 0) {   // one launch: the GEMV kernel quantizes its activations itself
+    cider::GemmArgs g{static_cast<const int8_t*>(x_f16), nullptr, w, w_scale, M, N, K, 0, y_f16, nullptr};
+    return from_hip(cider::launch_gemm(g, wk, cider::kEpiF16Linear, st));
+  }
+  int8_t* xq = static_cast<int8_t*>(workspace);
+  float* sa = reinterpret_cast<float*>(static_cast<char*>(workspace) + (M * K + 255) / 256 * 256);
+  hipError_t e = cider::launch_quant_rows(x_f16, M, K, group_size, 127, xq, sa, st);
+  if (e != hipSuccess) return from_hip(e);
+  cider::GemmArgs g{xq, sa, w, w_scale, M, N, K, group_size, y_f16, nullptr};
+  return from_hip(cider::launch_gemm(g, wk, cider::kEpiF16, st));
+}
+
 cider_status_t cider_int8_mv(const void* x_f16, const int8_t* w_q, const float* w_scale, int64_t M, int64_t N,
                              int64_t K, int32_t group_size, void* y_f16, void* stream) {
   if (M < 0 || M > CIDER_MV_MAX_M || !gemm_sizes_ok(M, N) || !valid_gs(group_size) || !valid_k(K, 16, group_size))

@@ -35,6 +35,7 @@
 #include <type_traits>
 
 #include "cider_internal.h"
+#include "cider_quant_rule.h"
 
 namespace cider {
 namespace {
@@ -706,11 +707,51 @@ gemm_gemv_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, con
   v4i wa[kBatch], wb[kBatch];
   load_batch(wa, wave);
 
+  // kEpiF16Linear: X holds fp16 rows; each row's scale s = max|x| / 127 is
+  // formed here (block-wide max) and the codes follow the quantizer's rule
+  __shared__ float srow[MT];
+  if constexpr (EPI == kEpiF16Linear) {
+    const uint4* xh = reinterpret_cast<const uint4*>(X);
+    const int C = K / 8;
+    __shared__ uint32_t wmax[4][MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      uint32_t a = 0;
+      if (m < M)
+        for (int c = threadIdx.x; c < C; c += 256) a = max(a, abs_max_bits(xh[(int64_t)m * C + c]));
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) a = max(a, (uint32_t)__shfl_xor((int)a, off));
+      if (lane == 0) wmax[wave][m] = a;
+    }
+    __syncthreads();
+    if (threadIdx.x < MT) {
+      const int m = threadIdx.x;
+      const uint32_t a = max(max(wmax[0][m], wmax[1][m]), max(wmax[2][m], wmax[3][m]));
+      srow[m] = half_bits_to_float(a) / 127.0f;
+    }
+    __syncthreads();
+  }
+
   // stage x (rows >= M and codes >= K as zero)
   for (int i = threadIdx.x; i < MT * Kpad / 16; i += 256) {
     const int m = i / (Kpad / 16), c = i % (Kpad / 16);
     v4i v = zero4();
-    if (m < M && c * 16 < K) v = *reinterpret_cast<const v4i*>(X + (int64_t)m * K + c * 16);
+    if constexpr (EPI == kEpiF16Linear) {
+      const float sc = m < MT ? srow[m] : 0.0f;
+      if (m < M && c * 16 < K && sc != 0.0f) {
+        const uint4* xp = reinterpret_cast<const uint4*>(X) + ((int64_t)m * K + c * 16) / 8;
+        const float inv = 1.0f / sc;
+        int q[16];
+        codes_of_chunk(xp[0], sc, inv, 127.0f, q);
+        codes_of_chunk(xp[1], sc, inv, 127.0f, q + 8);
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          v[d] = (q[4 * d] & 0xFF) | ((q[4 * d + 1] & 0xFF) << 8) | ((q[4 * d + 2] & 0xFF) << 16) |
+                 (int)((uint32_t)(q[4 * d + 3] & 0xFF) << 24);
+      }
+    } else {
+      if (m < M && c * 16 < K) v = *reinterpret_cast<const v4i*>(X + (int64_t)m * K + c * 16);
+    }
     if constexpr (kI4) v = even_odd_bytes(v);
     *reinterpret_cast<v4i*>(xs + m * Kpad + c * 16) = v;
   }
@@ -741,6 +782,7 @@ gemm_gemv_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, con
   if (m >= M || n >= N) return;
   const int t = red[0][r][m] + red[1][r][m] + red[2][r][m] + red[3][r][m];
   if constexpr (EPI == kEpiAccI32) ACC[(int64_t)m * N + n] = t;
+  else if constexpr (EPI == kEpiF16Linear) Y[(int64_t)m * N + n] = dequant1(t, srow[m], SW[n]);
   else Y[(int64_t)m * N + n] = dequant1(t, SA[m], SW[n]);
 }
 
@@ -758,7 +800,7 @@ hipError_t launch_gemv_m(const GemmArgs& g, hipStream_t st) {
 // M <= 4 with the staged activations fitting in LDS (<= 64 KiB).
 inline bool gemv_fits(const GemmArgs& g) {
   const int64_t mt = g.M <= 1 ? 1 : (g.M <= 2 ? 2 : 4);
-  return g.M <= 4 && mt * (g.K + 255) / 256 * 256 <= 65536;
+  return g.M <= 4 && mt * ((g.K + 255) / 256 * 256) <= 65536;
 }
 
 template <int WK, int EPI>
@@ -1173,9 +1215,18 @@ hipError_t launch_tok(const GemmArgs& g, hipStream_t st) {
 
 }  // namespace
 
+bool linear_is_one_launch(int64_t M, int64_t K, int group_size) {
+  GemmArgs g{};
+  g.M = M;
+  g.K = K;
+  return group_size == 0 && M >= 1 && gemv_fits(g);
+}
+
 hipError_t launch_gemm(const GemmArgs& g, WeightKind wk, Epilogue epi, hipStream_t st) {
   // Tile table by M (the README's tile section also switches configs by M).
   if (epi == kEpiF16Tok) return launch_tok(g, st);
+  if (epi == kEpiF16Linear)   // g.a holds fp16 activations; linear_is_one_launch() holds
+    return wk == kWeightI4 ? launch_gemv<kWeightI4, kEpiF16Linear>(g, st) : launch_gemv<kWeightI8, kEpiF16Linear>(g, st);
   if (epi == kEpiF16Split) {
     if (g.M > 16) return launch_pc<kWeightI8, kEpiF16Split>(g, st);
     // small M: one launch per part over its rows of the weights (the same

@@ -17,7 +17,9 @@ hipError_t launch_quant_rows(const void* x, int64_t R, int64_t K, int group_size
 // [N, G] with per-token activation scales [M] (int8 weights, gs 64 / 128).
 // kEpiF16Split: per-channel fp16 output whose columns go to up to 4 separate
 // matrices (GemmArgs::split).
-enum Epilogue { kEpiF16 = 0, kEpiAccI32 = 1, kEpiF16Tok = 2, kEpiF16Split = 3 };
+// kEpiF16Linear: the GEMV kernel takes fp16 activations and quantizes them
+// itself (per token), then dequantizes as kEpiF16.
+enum Epilogue { kEpiF16 = 0, kEpiAccI32 = 1, kEpiF16Tok = 2, kEpiF16Split = 3, kEpiF16Linear = 4 };
 
 // Column split of a GEMM's output: columns [end[i-1], end[i]) (end[-1] = 0)
 // go to y[i], a row-major fp16 matrix of end[i] - end[i-1] columns. Unused
@@ -46,6 +48,10 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(const GemmArgs& args, WeightKind wk, Epilogue epi, hipStream_t stream);
+
+// True when the one-launch linear applies: per-channel, M <= 4 and the
+// activation codes fit the GEMV kernel's LDS staging.
+bool linear_is_one_launch(int64_t M, int64_t K, int group_size);
 
 struct MvArgs {
   const void* x;     // fp16 activations [M, K], 1 <= M <= 4

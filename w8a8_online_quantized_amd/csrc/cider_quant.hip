@@ -6,10 +6,7 @@
 // INT8 or zero-point-8 INT4 weights). Per-group scales (section "W8A8 量化粒度",
 // gs = 64 / 128) use the same rule on each run of gs elements along K.
 //
-// Rule (one group = a row, or gs consecutive elements of a row):
-//   s = max|v| / qmax              (fp32, one correctly rounded division)
-//   q = clamp(rint(v / s), +-qmax) (v / s one correctly rounded fp32 division,
-//                                   rint = ties to even); s == 0 -> q = 0.
+// The element rule (scale, codes) is in cider_quant_rule.h.
 //
 // HBM-bound: 2 bytes read, 1 (or 0.5) byte written per element. One wave owns
 // one row; each lane owns 16-byte chunks (8 fp16) at a 64-chunk stride, so a
@@ -17,53 +14,15 @@
 // registers between the max pass and the code pass.
 //
 // The division v / s costs a ~10-instruction correctly rounded sequence; with
-// 8 elements per chunk it would make the kernel ALU-bound. Instead each code
-// is first formed from r = v * fl(1/s). |r - fl(v/s)| <= 3 * 2^-24 * 128 <
-// 2.3e-5, so when r is at least 2^-13 away from every half-integer both values
-// round to the same integer; only the rare remaining elements take the exact
-// division. The result is bit-identical to always dividing.
+// 8 elements per chunk it would make the kernel ALU-bound, hence the
+// reciprocal-first form of the rule's code_of.
 #include "cider_internal.h"
+#include "cider_quant_rule.h"
 
 namespace cider {
 namespace {
 
 constexpr int kWaves = 4;                 // waves (rows) per workgroup
-constexpr float kNearHalf = 0.4998779296875f;   // 0.5 - 2^-13
-
-__device__ __forceinline__ uint32_t abs_max_bits(uint4 v) {
-  // fp16 magnitudes compare like their 15-bit patterns (finite inputs).
-  uint32_t m = 0;
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t a = w[i] & 0x7FFF7FFFu;
-    m = max(m, max(a & 0xFFFFu, a >> 16));
-  }
-  return m;
-}
-
-__device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
-  return (float)__builtin_bit_cast(_Float16, (unsigned short)bits);
-}
-
-// Code of one element given the group scale s (> 0) and inv = fl(1/s).
-__device__ __forceinline__ int code_of(float v, float s, float inv, float qmax) {
-  const float r = v * inv;
-  float t = __builtin_rintf(r);
-  if (__builtin_fabsf(r - t) > kNearHalf) t = __builtin_rintf(v / s);
-  t = __builtin_fminf(__builtin_fmaxf(t, -qmax), qmax);
-  return (int)t;
-}
-
-// 8 codes of one 16-byte chunk (8 fp16 values).
-__device__ __forceinline__ void codes_of_chunk(uint4 v, float s, float inv, float qmax, int q[8]) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    q[2 * i] = code_of(half_bits_to_float(w[i] & 0xFFFFu), s, inv, qmax);
-    q[2 * i + 1] = code_of(half_bits_to_float(w[i] >> 16), s, inv, qmax);
-  }
-}
 
 __device__ __forceinline__ void store_codes(void* q, int64_t row, int64_t K, int chunk, bool pack4,
                                             const int c[8]) {
