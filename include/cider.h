@@ -122,10 +122,10 @@ cider_status_t cider_w4a8_gemm(const int8_t* x_q, const float* x_scale, const ui
  * cider_w4a8_gemm (bits 4), with identical results.
  *   w : bits 8: int8 [N, K] codes, w_scale fp32 [N] or [N, K/group_size];
  *       bits 4: packed uint8 [N, K/2], w_scale fp32 [N] (group_size 0).
- *   For group_size 0 and M <= 4 (when the M activation rows' codes fit the
- *   GEMV kernel's 64 KiB staging area: M' * ceil(K/256)*256 <= 65536 with
- *   M' = 1, 2, 4 for M = 1, 2, 3..4) it is ONE kernel launch that quantizes
- *   the activations itself and needs no workspace. Otherwise the codes and
+ *   For group_size 0 and M <= 2 (when the M activation rows' codes fit the
+ *   GEMV kernel's 64 KiB staging area: M * ceil(K/256)*256 <= 65536) it is
+ *   ONE kernel launch that quantizes the activations itself and needs no
+ *   workspace. Otherwise the codes and
  *   scales go through `workspace` (device, 16-byte aligned, at least
  *   cider_linear_workspace_size(M, K, bits, group_size) bytes; its contents
  *   after the call are the activation codes [M, K] at offset 0 and the scales

@@ -140,8 +140,9 @@ def test_split_rejects():
 
 def test_linear_workspace_query_and_rejects():
     q = L.cider_linear_workspace_size
-    assert q(1, 2560, 8, 0) == 0 and q(4, 16384, 8, 0) == 0 and q(4, 2560, 4, 0) == 0   # one launch
-    assert q(4, 16384 + 256, 8, 0) == 4 * 16640 + 256                     # codes past the 64 KiB staging
+    assert q(1, 2560, 8, 0) == 0 and q(2, 32768, 8, 0) == 0 and q(2, 2560, 4, 0) == 0   # one launch
+    assert q(2, 32768 + 256, 8, 0) == 2 * 33024 + 256                     # codes past the 64 KiB staging
+    assert q(3, 2560, 8, 0) == 3 * 2560 + 256                             # M = 3: separate quantization
     assert q(5, 1024, 8, 0) == 5 * 1024 + 256
     assert q(5, 1024, 8, 128) == 5 * 1024 + 256                           # 40 scale bytes
     assert q(300, 1024, 8, 64) == 300 * 1024 + (4 * 300 * 16 + 255) // 256 * 256

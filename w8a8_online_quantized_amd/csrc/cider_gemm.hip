@@ -32,6 +32,7 @@
 // bytes into codes (nibble - 8) in the order 0,2,4,6 | 1,3,5,7 | ...; the
 // activation bytes are permuted into the same order, so every MFMA / dot4
 // pairs each activation code with its weight code.
+#include <algorithm>
 #include <type_traits>
 
 #include "cider_internal.h"
@@ -641,11 +642,13 @@ gemm_gemv_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, con
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int Kpad = (K + kCodes - 1) / kCodes * kCodes;
 
-  const int n0 = blockIdx.x * 8;
+  // block b owns row groups b, b + gridDim.x, ... of 8 weight rows (one per
+  // block except in the self-quantizing mode, whose grid is capped)
+  int n0 = blockIdx.x * 8;
   const int row = lane >> 3, sub = lane & 7;
-  const int rows_w = min(8, N - n0);
+  int rows_w = min(8, N - n0);
   const uint32_t ldw = kI4 ? (uint32_t)K / 2 : (uint32_t)K;
-  const __amdgpu_buffer_rsrc_t rw =
+  __amdgpu_buffer_rsrc_t rw =
       make_rsrc(static_cast<const int8_t*>(Wv) + (int64_t)n0 * ldw, (uint32_t)rows_w * ldw);
   const int steps = Kpad / kCodes;
   int acc[MT];
@@ -758,40 +761,59 @@ gemm_gemv_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, con
   __syncthreads();
 
   constexpr int kStride = 4 * kBatch;          // steps between a wave's batches
-  for (int base = wave; base < steps; base += 2 * kStride) {
-    if (base + kStride < steps) load_batch(wb, base + kStride);
-    process(wa, base);
-    if (base + kStride >= steps) break;
-    if (base + 2 * kStride < steps) load_batch(wa, base + 2 * kStride);
-    process(wb, base + kStride);
-  }
-  // sum the 8 lanes of each row (integer: order does not matter)
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int off = 1; off < 8; off <<= 1) acc[m] += __shfl_xor(acc[m], off);
   __shared__ int red[4][8][MT];
-  if (sub == 0) {
+  const int nrg = (N + 7) / 8;
+  for (int rg = blockIdx.x; rg < nrg; rg += gridDim.x) {
+    if (rg != (int)blockIdx.x) {
+      n0 = rg * 8;
+      rows_w = min(8, N - n0);
+      rw = make_rsrc(static_cast<const int8_t*>(Wv) + (int64_t)n0 * ldw, (uint32_t)rows_w * ldw);
 #pragma unroll
-    for (int m = 0; m < MT; ++m) red[wave][row][m] = acc[m];
+      for (int m = 0; m < MT; ++m) acc[m] = 0;
+      load_batch(wa, wave);
+    }
+    for (int base = wave; base < steps; base += 2 * kStride) {
+      if (base + kStride < steps) load_batch(wb, base + kStride);
+      process(wa, base);
+      if (base + kStride >= steps) break;
+      if (base + 2 * kStride < steps) load_batch(wa, base + 2 * kStride);
+      process(wb, base + kStride);
+    }
+    // sum the 8 lanes of each row (integer: order does not matter)
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int off = 1; off < 8; off <<= 1) acc[m] += __shfl_xor(acc[m], off);
+    if (sub == 0) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) red[wave][row][m] = acc[m];
+    }
+    __syncthreads();
+    if (threadIdx.x < 8 * MT) {
+      const int r = threadIdx.x / MT, m = threadIdx.x % MT;
+      const int n = n0 + r;
+      if (m < M && n < N) {
+        const int t = red[0][r][m] + red[1][r][m] + red[2][r][m] + red[3][r][m];
+        if constexpr (EPI == kEpiAccI32) ACC[(int64_t)m * N + n] = t;
+        else if constexpr (EPI == kEpiF16Linear) Y[(int64_t)m * N + n] = dequant1(t, srow[m], SW[n]);
+        else Y[(int64_t)m * N + n] = dequant1(t, SA[m], SW[n]);
+      }
+    }
+    __syncthreads();   // red is rewritten by the next row group
   }
-  __syncthreads();
-  if (threadIdx.x >= 8 * MT) return;
-  const int r = threadIdx.x / MT, m = threadIdx.x % MT;
-  const int n = n0 + r;
-  if (m >= M || n >= N) return;
-  const int t = red[0][r][m] + red[1][r][m] + red[2][r][m] + red[3][r][m];
-  if constexpr (EPI == kEpiAccI32) ACC[(int64_t)m * N + n] = t;
-  else if constexpr (EPI == kEpiF16Linear) Y[(int64_t)m * N + n] = dequant1(t, srow[m], SW[n]);
-  else Y[(int64_t)m * N + n] = dequant1(t, SA[m], SW[n]);
 }
+
+constexpr int64_t kLinearBlocks = 512;   // two per CU
 
 template <int MT, int WK, int EPI>
 hipError_t launch_gemv_m(const GemmArgs& g, hipStream_t st) {
   constexpr int kCodes = WK == kWeightI4 ? 256 : 128;
   const int64_t kpad = (g.K + kCodes - 1) / kCodes * kCodes;
   const size_t lds = (size_t)MT * kpad;
-  const dim3 grid((unsigned)((g.N + 7) / 8)), block(256);
+  // the self-quantizing mode repeats the activation quantization in every
+  // block, so its grid is capped (each block then loops over row groups)
+  const int64_t nrg = (g.N + 7) / 8;
+  const dim3 grid((unsigned)(EPI == kEpiF16Linear ? std::min<int64_t>(nrg, kLinearBlocks) : nrg)), block(256);
   gemm_gemv_kernel<MT, WK, EPI><<<grid, block, lds, st>>>(g.a, g.sa, g.w, g.sw, (int)g.M, (int)g.N, (int)g.K,
                                                          static_cast<_Float16*>(g.y), g.acc);
   return hipGetLastError();
@@ -1219,7 +1241,7 @@ bool linear_is_one_launch(int64_t M, int64_t K, int group_size) {
   GemmArgs g{};
   g.M = M;
   g.K = K;
-  return group_size == 0 && M >= 1 && gemv_fits(g);
+  return group_size == 0 && M >= 1 && M <= 2 && gemv_fits(g);
 }
 
 hipError_t launch_gemm(const GemmArgs& g, WeightKind wk, Epilogue epi, hipStream_t st) {

@@ -49,8 +49,10 @@ struct GemmArgs {
 
 hipError_t launch_gemm(const GemmArgs& args, WeightKind wk, Epilogue epi, hipStream_t stream);
 
-// True when the one-launch linear applies: per-channel, M <= 4 and the
-// activation codes fit the GEMV kernel's LDS staging.
+// True when the one-launch linear applies: per-channel, M <= 2 and the
+// activation codes fit the GEMV kernel's LDS staging. (From M = 3 on, the
+// activation quantization that every block repeats costs more than the
+// separate quantization launch it saves.)
 bool linear_is_one_launch(int64_t M, int64_t K, int group_size);
 
 struct MvArgs {
