@@ -18,7 +18,8 @@ from __future__ import annotations
 
 from fractions import Fraction
 
-__all__ = ["round_binary", "f32", "f16", "rint_half_even", "quantize_row",
+__all__ = ["round_binary", "f32", "f16", "f64", "rint_half_even", "quantize_row", "percentile_fp64",
+           "quantize_row_clip",
            "dot", "dequant", "dequant_groups", "linear", "mv", "linear_token_group"]
 
 _INF = float("inf")
@@ -61,6 +62,10 @@ def f16(v) -> Fraction:
     return round_binary(Fraction(v), 11, -14, 15)
 
 
+def f64(v) -> Fraction:
+    return round_binary(Fraction(v), 53, -1022, 1023)
+
+
 def rint_half_even(v: Fraction) -> int:
     fl = v.numerator // v.denominator
     rem = v - fl
@@ -88,6 +93,34 @@ def quantize_row(values, group_size: int, qmax: int):
             else:
                 c = rint_half_even(f32(v / s))
                 codes.append(max(-qmax, min(qmax, c)))
+    return codes, scales
+
+
+def percentile_fp64(mags, percentile: float) -> Fraction:
+    """The clip threshold of one group: position h = (n-1) * (p/100), value
+    a[i] + (h - i) * (a[j] - a[i]) over the ascending magnitudes, each step
+    rounded to fp64 as written, then the result rounded to fp32."""
+    a = sorted(Fraction(m) for m in mags)
+    n = len(a)
+    h = f64(Fraction(n - 1) * f64(Fraction(percentile) / 100))
+    i = h.numerator // h.denominator
+    j = min(i + 1, n - 1)
+    g = h - i
+    return f32(f64(a[i] + f64(g * (a[j] - a[i]))))
+
+
+def quantize_row_clip(values, group_size: int, qmax: int, percentile: float):
+    """quantize_row with s = t / qmax, t = percentile_fp64 of the group."""
+    vals = [Fraction(v) for v in values]
+    K = len(vals)
+    gs = K if group_size == 0 else group_size
+    codes, scales = [], []
+    for g in range(K // gs):
+        grp = vals[g * gs:(g + 1) * gs]
+        s = f32(percentile_fp64([abs(v) for v in grp], percentile) / qmax)
+        scales.append(s)
+        for v in grp:
+            codes.append(0 if s == 0 else max(-qmax, min(qmax, rint_half_even(f32(v / s)))))
     return codes, scales
 
 

@@ -22,7 +22,8 @@ top-level Cider README, a community translation of the upstream README):
   activations symmetric INT8 per token; INT32 accumulation; the output is
   the int32 accumulator times the activation scale times the weight scale,
   per element, in fp16.
-* Section "说明" (Notes): scales come from the min-max rule by default.
+* Section "说明" (Notes): scales come from the min-max rule by default; a
+  percentile rule (clip_percentile=99.9) is offered as well.
 * Section "架构 / Metal Kernel 流水线", Decode (M = 1): int8_mv multiplies
   fp16 activations by int8 weights dequantized on the fly, without
   quantizing the activations (per-channel and per-group MV kernels in the
@@ -51,6 +52,12 @@ notes of the repository):
 * per-token activations x per-group weights (the quantization table's
   per-token activations with per-group weights): y = sum_g acc_g * s_a[m] *
   s_w[n,g], in fp64, rounded once to fp16.
+* percentile-clipped weight scales (the notes name a "99th percentile"
+  method with clip_percentile=99.9; the parameter's value is taken): the
+  group's clip threshold t is the percentile of its magnitudes by linear
+  interpolation between order statistics (numpy's default definition),
+  evaluated as written in fp64 and rounded to fp32; s = t / qmax and the
+  codes follow the min-max rule's code step, so magnitudes above t saturate.
 * decode MV: y = sum_k x[m,k] * (w_q[n,k] * s_w[n,g(k)]), the exact value
   rounded once to fp16 (evaluated in fp64: each product is exact, the sum's
   relative error is about K * 2^-53).
@@ -68,7 +75,8 @@ __all__ = [
     "QMAX_INT8", "QMAX_INT4", "quantize_rows", "quantize_act", "quantize_weight",
     "pack_int4", "unpack_int4", "int_dot", "int_dot_groups", "dequant_per_channel",
     "dequant_per_group", "w8a8_linear", "w4a8_linear", "num_groups", "int8_mv",
-    "dequant_token_group", "w8a8_linear_token_group",
+    "dequant_token_group", "w8a8_linear_token_group", "percentile_threshold", "quantize_rows_clip",
+    "quantize_weight_clip",
 ]
 
 QMAX_INT8 = 127
@@ -130,6 +138,65 @@ def quantize_weight(w: np.ndarray, bits: int = 8, group_size: int = 0):
         if group_size != 0:
             raise ValueError("int4 weights are per output channel only")
         q, s = quantize_rows(w, 0, QMAX_INT4)
+        return pack_int4(q), s[:, 0]
+    raise ValueError("bits must be 8 or 4")
+
+
+def percentile_threshold(mags: np.ndarray, percentile: float) -> np.ndarray:
+    """Clip threshold of each group for percentile-clipped scales (the README's
+    notes section: scales by min-max by default, or by a percentile of the
+    magnitudes, clip_percentile=99.9).
+
+    mags: [..., n] magnitudes (exact fp16 values). The percentile is taken by
+    linear interpolation between order statistics: with a the magnitudes in
+    ascending order, position h = (n - 1) * (percentile / 100), i = floor(h),
+    j = min(i + 1, n - 1): t = a[i] + (h - i) * (a[j] - a[i]). Every step is
+    one rounded fp64 operation in that order (no fused multiply-add); t is
+    then rounded to fp32. Returns fp32 [...].
+    """
+    a = np.sort(np.asarray(mags, np.float64), axis=-1)
+    n = a.shape[-1]
+    h = float(n - 1) * (float(percentile) / 100.0)
+    i = int(np.floor(h))
+    j = min(i + 1, n - 1)
+    g = h - i
+    lo, hi = a[..., i], a[..., j]
+    t = lo + g * (hi - lo)            # numpy rounds the product, then the sum
+    return t.astype(np.float32)
+
+
+def quantize_rows_clip(X: np.ndarray, group_size: int, qmax: int, percentile: float):
+    """As quantize_rows, with each group's scale s = t / qmax (one rounded fp32
+    division) for t = percentile_threshold of the group's magnitudes instead
+    of max|v|. Codes follow the same rule, clamp(rint(v / s), -qmax, qmax),
+    so magnitudes above t saturate at +-qmax; s == 0 gives codes 0."""
+    X = np.asarray(X)
+    if X.dtype != np.float16 or X.ndim != 2:
+        raise TypeError("X must be a 2-D float16 array")
+    if not 0.0 <= percentile <= 100.0:
+        raise ValueError("percentile must lie in [0, 100]")
+    R, K = X.shape
+    G = num_groups(K, group_size)
+    gs = K if group_size == 0 else group_size
+    xg = X.astype(np.float32).reshape(R, G, gs)
+    t = percentile_threshold(np.abs(xg), percentile)
+    s = (t / np.float32(qmax)).astype(np.float32)
+    zero = s == 0
+    r = xg / np.where(zero, np.float32(1), s)[:, :, None]
+    q = np.clip(np.rint(r), -qmax, qmax)
+    q[zero] = 0
+    return q.reshape(R, K).astype(np.int8), s
+
+
+def quantize_weight_clip(w: np.ndarray, bits: int = 8, group_size: int = 0, percentile: float = 99.9):
+    """quantize_weight with percentile-clipped scales (same outputs and layouts)."""
+    if bits == 8:
+        q, s = quantize_rows_clip(w, group_size, QMAX_INT8, percentile)
+        return q, (s[:, 0] if group_size == 0 else s)
+    if bits == 4:
+        if group_size != 0:
+            raise ValueError("int4 weights are per output channel only")
+        q, s = quantize_rows_clip(w, 0, QMAX_INT4, percentile)
         return pack_int4(q), s[:, 0]
     raise ValueError("bits must be 8 or 4")
 

@@ -447,6 +447,87 @@ def check_token_group_reductions(impl, seed=17):
     y3 = impl.dequant_token_group(acc, sa[:, 0], sw)
     assert np.array_equal(y2.view(np.uint16), y3.view(np.uint16))
 
+# ------------------------------------------------- percentile-clipped weight scales
+def check_golden_clip(impl):
+    for c in _load("clip_percentile.json")["cases"]:
+        x = np.array([c["x"]], np.float16)
+        t = impl.percentile_threshold(np.abs(x.astype(np.float32)), c["percentile"])
+        assert float(t[0]) == c["t"], (c["percentile"], float(t[0]), c["t"])
+        q, s = impl.quantize_rows_clip(x, 0, c["qmax"], c["percentile"])
+        assert float(s[0, 0]) == float(np.float32(c["t"]) / np.float32(c["qmax"]))
+        assert q[0].tolist() == c["q"], (c["percentile"], q[0].tolist())
+
+
+def check_brute_clip(impl, trials=48, seed=18):
+    """Exact-rational brute force (its own rounding routines) on tiny groups."""
+    rng = np.random.default_rng(seed)
+    ps = [0.0, 12.5, 50.0, 90.0, 99.0, 99.9, 100.0]
+    for t in range(trials):
+        gs = [0, 2, 4, 8][t % 4]
+        K = (gs or 1) * int(rng.integers(1, 5)) if gs else int(rng.integers(1, 13))
+        x = _rand_fp16(rng, (2, K), ["normal", "wide", "ties", "small"][t % 4])
+        p = ps[t % len(ps)] if t < 2 * len(ps) else float(rng.uniform(0, 100))
+        qmax = 127 if t % 3 else 7
+        q, sc = impl.quantize_rows_clip(x, gs, qmax, p)
+        for r in range(2):
+            bq, bs = brute.quantize_row_clip([float(v) for v in x[r]], gs, qmax, p)
+            assert q[r].tolist() == bq, (t, r, p, q[r].tolist(), bq)
+            assert [float(v) for v in sc[r]] == [float(v) for v in bs], (t, r, p)
+
+
+def check_clip_vs_numpy_percentile(impl, seed=19):
+    """The threshold against numpy.percentile (default method, computed in
+    fp64 by numpy's own code): within one fp32 ulp."""
+    rng = np.random.default_rng(seed)
+    for n in (64, 128, 1000, 2560, 10240):
+        m = np.abs(rng.standard_normal((6, n)).astype(np.float16)).astype(np.float32)
+        m[0, :: 97] *= np.float32(30)
+        for p in (99.9, 99.0, 95.0, 50.0, 1.0, 100.0, 33.3):
+            t = impl.percentile_threshold(m, p)
+            ref = np.percentile(m.astype(np.float64), p, axis=-1).astype(np.float32)
+            ulp = np.spacing(np.abs(ref))
+            assert np.all(np.abs(t.astype(np.float64) - ref) <= ulp), (n, p, t, ref)
+
+
+def check_clip_reductions(impl, seed=20):
+    """Percentile 100 is min-max bit for bit; constant magnitudes make every
+    percentile min-max; a lone outlier is clipped (saturated code, smaller
+    scale, smaller error elsewhere); the threshold grows with the percentile."""
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((8, 256)) * 0.05).astype(np.float16)
+    for gs in (0, 64):
+        for qmax in (127, 7):
+            q1, s1 = impl.quantize_rows_clip(w, gs, qmax, 100.0)
+            q0, s0 = impl.quantize_rows(w, gs, qmax)
+            assert np.array_equal(q1, q0) and np.array_equal(s1, s0)
+    c = np.where(rng.random((4, 128)) < 0.5, np.float16(-0.75), np.float16(0.75)).astype(np.float16)
+    for p in (0.0, 37.5, 99.9):
+        qc, sc = impl.quantize_rows_clip(c, 0, 127, p)
+        q0, s0 = impl.quantize_rows(c, 0, 127)
+        assert np.array_equal(qc, q0) and np.array_equal(sc, s0)
+    K = 2560
+    row = (rng.standard_normal((1, K)) * 0.02).astype(np.float16)
+    big = int(rng.integers(0, K))
+    row[0, big] = np.float16(np.abs(row.astype(np.float32)).max() * 50)
+    qc, sc = impl.quantize_rows_clip(row, 0, 127, 99.9)
+    q0, s0 = impl.quantize_rows(row, 0, 127)
+    assert sc[0, 0] < s0[0, 0] / 10 and abs(int(qc[0, big])) == 127
+    v = row[0].astype(np.float64)
+    keep = np.ones(K, bool)
+    keep[big] = False
+    tval = float(impl.percentile_threshold(np.abs(row.astype(np.float32)), 99.9)[0])
+    inside = keep & (np.abs(v) <= tval)
+    err_c = np.abs(v - float(sc[0, 0]) * qc[0].astype(np.float64))
+    err_0 = np.abs(v - float(s0[0, 0]) * q0[0].astype(np.float64))
+    assert np.all(err_c[inside] <= float(sc[0, 0]) * (0.5 + 1e-6))
+    assert err_c[keep].mean() < err_0[keep].mean() / 5
+    m = np.abs(rng.standard_normal((3, 512)).astype(np.float16)).astype(np.float32)
+    ts = [impl.percentile_threshold(m, p) for p in (10.0, 50.0, 90.0, 99.0, 99.9, 100.0)]
+    for a, b in zip(ts, ts[1:]):
+        assert np.all(a <= b)
+    assert np.array_equal(ts[-1], m.max(axis=-1))
+
+
 ALL_CHECKS = [
     check_golden_quant, check_golden_division, check_golden_int4, check_golden_integer_gemm,
     check_closed_form_k10240, check_brute_quant, check_brute_linear,
@@ -455,4 +536,5 @@ ALL_CHECKS = [
     check_int4_bound_and_cosine, check_golden_mv, check_brute_mv, check_mv_gs_equals_k,
     check_mv_pow2_scaling, check_mv_matches_lossless_w8a8, check_mv_exact_sum,
     check_golden_token_group, check_brute_token_group, check_token_group_reductions,
+    check_golden_clip, check_brute_clip, check_clip_vs_numpy_percentile, check_clip_reductions,
 ]

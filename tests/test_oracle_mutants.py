@@ -12,7 +12,8 @@ from tests import oracle_pins as pins
 def _impl(**over):
     base = {name: getattr(O, name) for name in (
         "quantize_rows", "pack_int4", "unpack_int4", "int_dot", "int_dot_groups",
-        "dequant_per_channel", "dequant_per_group", "int8_mv", "dequant_token_group")}
+        "dequant_per_channel", "dequant_per_group", "int8_mv", "dequant_token_group",
+        "percentile_threshold", "quantize_rows_clip")}
     base.update(over)
     ns = types.SimpleNamespace(**base)
     return ns
@@ -133,6 +134,47 @@ def _tg_variant(kind):
     return f
 
 
+def _clip_variant(kind):
+    """(threshold, quantizer) with one planted mistake in the percentile rule."""
+    def threshold(mags, percentile):
+        a = np.sort(np.asarray(mags, np.float64), axis=-1)
+        if kind == "signed":
+            a = np.sort(np.asarray(mags, np.float64) * np.where(np.arange(a.shape[-1]) % 2, -1, 1), axis=-1)
+        n = a.shape[-1]
+        h = float(n if kind == "n_not_n_minus_1" else n - 1) * (float(percentile) / 100.0)
+        h = min(h, n - 1.0)
+        i = int(np.floor(h))
+        j = min(i + 1, n - 1)
+        g = h - i
+        if kind == "lower":
+            t = a[..., i]
+        elif kind == "higher":
+            t = a[..., j]
+        elif kind == "max":
+            t = a[..., -1]
+        else:
+            t = a[..., i] + g * (a[..., j] - a[..., i])
+        return t.astype(np.float32)
+
+    def quant(X, group_size, qmax, percentile):
+        R, K = X.shape
+        G = O.num_groups(K, group_size)
+        gs = K if group_size == 0 else group_size
+        xg = X.astype(np.float32).reshape(R, G, gs)
+        s = (threshold(np.abs(xg), percentile) / np.float32(qmax)).astype(np.float32)
+        zero = s == 0
+        r = xg / np.where(zero, np.float32(1), s)[:, :, None]
+        q = np.rint(r) if kind == "no_saturation" else np.clip(np.rint(r), -qmax, qmax)
+        q[zero] = 0
+        return q.reshape(R, K).astype(np.int8 if kind != "no_saturation" else np.int64), s
+    return threshold, quant
+
+
+def _clip_impl(kind):
+    t, q = _clip_variant(kind)
+    return _impl(percentile_threshold=t, quantize_rows_clip=q)
+
+
 MUTANTS = {
     "round_half_up": _impl(quantize_rows=_quant_variant(rounding="up")),
     "scale_over_128": _impl(quantize_rows=_quant_variant(divisor_bias=1)),
@@ -156,6 +198,12 @@ MUTANTS = {
     "token_group_without_act_scale": _impl(dequant_token_group=_tg_variant("no_act_scale")),
     "token_group_first_weight_scale": _impl(dequant_token_group=_tg_variant("first_group_scale")),
     "token_group_reversed_scales": _impl(dequant_token_group=_tg_variant("reversed_groups")),
+    "clip_position_n": _clip_impl("n_not_n_minus_1"),
+    "clip_lower_order_statistic": _clip_impl("lower"),
+    "clip_higher_order_statistic": _clip_impl("higher"),
+    "clip_ignores_percentile": _clip_impl("max"),
+    "clip_signed_values": _clip_impl("signed"),
+    "clip_no_saturation": _clip_impl("no_saturation"),
 }
 
 
