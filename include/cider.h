@@ -97,6 +97,24 @@ cider_status_t cider_quant_act(const void* x_f16, int64_t M, int64_t K, int32_t 
 cider_status_t cider_quant_weight(const void* w_f16, int64_t N, int64_t K, int32_t bits,
                                   int32_t group_size, void* w_q, float* w_scale, void* stream);
 
+/* Weight quantization with percentile-clipped scales (the README's notes
+ * section: scales by min-max by default, or by a percentile of the
+ * magnitudes, clip_percentile=99.9). Per group (a row, or group_size
+ * elements of it) the clip threshold t is the `percentile`-th percentile of
+ * the magnitudes |w| by linear interpolation between order statistics:
+ * h = (n-1) * (percentile/100), i = floor(h), j = min(i+1, n-1),
+ * t = a_i + (h-i) * (a_j - a_i) over the ascending magnitudes a, each step
+ * one rounded fp64 operation, then rounded to fp32 (percentile 100 gives
+ * max|w|, i.e. cider_quant_weight). s = t / qmax; codes as for
+ * cider_quant_weight, so magnitudes above t saturate at +-qmax; s == 0
+ * gives codes 0. Outputs and layouts as cider_quant_weight.
+ *   percentile : in [0, 100] (99.9 on the pages).
+ * Sizes and errors as for cider_quant_weight; also N * (K/group_size) < 2^31.
+ */
+cider_status_t cider_quant_weight_clip(const void* w_f16, int64_t N, int64_t K, int32_t bits,
+                                       int32_t group_size, double percentile, void* w_q,
+                                       float* w_scale, void* stream);
+
 /* W8A8 GEMM with fused dequant (pipeline step "matmul_fused_dequant"):
  *   y[m,n] = fp16( sum over groups of ((float)acc_g[m,n] * x_scale[m,g]) * w_scale[n,g] )
  *   acc_g[m,n] = sum_{k in group g} x_q[m,k] * w_q[n,k] (exact int32).

@@ -159,6 +159,20 @@ def test_linear_workspace_query_and_rejects():
     assert lin(NULL, NULL, NULL, 0, 8, 1024, 8, 0, NULL, 0, NULL, NULL) == 0  # empty work
 
 
+def test_quant_weight_clip_rejects():
+    c = L.cider_quant_weight_clip
+    assert c(P, 4, 64, 8, 0, 100.5, P, P, NULL) == INV                  # percentile above 100
+    assert c(P, 4, 64, 8, 0, -0.1, P, P, NULL) == INV
+    assert c(P, 4, 64, 8, 0, float("nan"), P, P, NULL) == INV
+    assert c(P, 4, 64, 6, 0, 99.9, P, P, NULL) == INV                   # bits
+    assert c(P, 4, 64, 4, 64, 99.9, P, P, NULL) == INV                  # int4 is per-channel
+    assert c(P, 4, 48, 4, 0, 99.9, P, P, NULL) == INV                   # int4 needs K % 32
+    assert c(P, 4, 192, 8, 128, 99.9, P, P, NULL) == INV                # K % gs
+    assert c(P, 4, 64, 8, 0, 99.9, P, MIS, NULL) == INV
+    assert c(NULL, 4, 64, 8, 0, 99.9, P, P, NULL) == INV
+    assert c(NULL, 0, 64, 8, 0, 99.9, NULL, NULL, NULL) == 0              # empty work
+
+
 def test_not_available_without_gpu():
     import torch
     if torch.cuda.is_available():

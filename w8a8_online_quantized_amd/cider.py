@@ -39,6 +39,8 @@ SIGNATURES = {
     "cider_linear_workspace_size": (ctypes.c_int64, [_c_i64, _c_i64, _c_i32, _c_i32]),
     "cider_linear": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_p, _c_i64, _c_p,
                                     _c_p]),
+    "cider_quant_weight_clip": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i32, _c_i32, ctypes.c_double, _c_p, _c_p,
+                                               _c_p]),
     "cider_int8_mv": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p]),
     "cider_stack_workspace_layout": (ctypes.c_int64, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                                       ctypes.POINTER(ctypes.c_int64)]),
@@ -160,6 +162,26 @@ def cider_quant_weight(w, bits: int = 8, group_size: int = 0, w_q=None, w_scale=
     _need(w_scale, torch.float32, _scale_shape(N, K, group_size), "w_scale")
     _check("cider_quant_weight", lib().cider_quant_weight(_ptr(w), N, K, bits, group_size, _ptr(w_q),
                                                           _ptr(w_scale), _stream(stream)))
+    return w_q, w_scale
+
+
+def cider_quant_weight_clip(w, bits: int = 8, group_size: int = 0, percentile: float = 99.9, w_q=None,
+                            w_scale=None, stream=None):
+    """cider_quant_weight with percentile-clipped scales (same outputs)."""
+    import torch
+    N, K = w.shape
+    _need(w, torch.float16, (N, K), "w")
+    qshape = (N, K) if bits == 8 else (N, K // 2)
+    qdtype = torch.int8 if bits == 8 else torch.uint8
+    if w_q is None:
+        w_q = torch.empty(qshape, dtype=qdtype, device=w.device)
+    if w_scale is None:
+        w_scale = torch.empty(_scale_shape(N, K, group_size), dtype=torch.float32, device=w.device)
+    _need(w_q, qdtype, qshape, "w_q")
+    _need(w_scale, torch.float32, _scale_shape(N, K, group_size), "w_scale")
+    _check("cider_quant_weight_clip",
+           lib().cider_quant_weight_clip(_ptr(w), N, K, bits, group_size, float(percentile), _ptr(w_q),
+                                         _ptr(w_scale), _stream(stream)))
     return w_q, w_scale
 
 

@@ -106,6 +106,27 @@ cider_status_t cider_quant_weight(const void* w_f16, int64_t N, int64_t K, int32
                                            static_cast<hipStream_t>(stream)));
 }
 
+cider_status_t cider_quant_weight_clip(const void* w_f16, int64_t N, int64_t K, int32_t bits, int32_t group_size,
+                                       double percentile, void* w_q, float* w_scale, void* stream) {
+  if (N < 0 || !valid_gs(group_size)) return CIDER_ERROR_INVALID_VALUE;
+  if (!(percentile >= 0.0 && percentile <= 100.0)) return CIDER_ERROR_INVALID_VALUE;   // NaN fails too
+  if (bits == 8) {
+    if (!valid_k(K, 16, group_size)) return CIDER_ERROR_INVALID_VALUE;
+  } else if (bits == 4) {
+    if (group_size != 0 || !valid_k(K, 32, 0)) return CIDER_ERROR_INVALID_VALUE;
+  } else {
+    return CIDER_ERROR_INVALID_VALUE;
+  }
+  const int64_t G = group_size ? K / group_size : 1;
+  if (N * G >= (int64_t(1) << 31)) return CIDER_ERROR_INVALID_VALUE;
+  if (N == 0) return CIDER_SUCCESS;
+  if (!w_f16 || !w_q || !w_scale || !aligned16(w_f16) || !aligned16(w_q) || !aligned16(w_scale))
+    return CIDER_ERROR_INVALID_VALUE;
+  if (!device_is_gfx950()) return CIDER_ERROR_NOT_SUPPORTED;
+  return from_hip(cider::launch_quant_rows_clip(w_f16, N, K, group_size, bits == 8 ? 127 : 7, percentile, w_q,
+                                                w_scale, static_cast<hipStream_t>(stream)));
+}
+
 static cider_status_t gemm_common(cider::GemmArgs& g, cider::WeightKind wk, cider::Epilogue epi,
                                   void* stream) {
   if (!device_is_gfx950()) return CIDER_ERROR_NOT_SUPPORTED;

@@ -13,6 +13,13 @@ namespace cider {
 hipError_t launch_quant_rows(const void* x, int64_t R, int64_t K, int group_size, int qmax,
                              void* q, float* s, hipStream_t stream);
 
+// The same with percentile-clipped scales: s = t / qmax, t = the percentile
+// (0..100) of the group's magnitudes (linear interpolation between order
+// statistics, fp64, rounded to fp32). R * K / group size groups, one
+// workgroup each.
+hipError_t launch_quant_rows_clip(const void* x, int64_t R, int64_t K, int group_size, int qmax,
+                                  double percentile, void* q, float* s, hipStream_t stream);
+
 // Epilogue kinds of the GEMM kernels. kEpiF16Tok: per-group weight scales
 // [N, G] with per-token activation scales [M] (int8 weights, gs 64 / 128).
 // kEpiF16Split: per-channel fp16 output whose columns go to up to 4 separate

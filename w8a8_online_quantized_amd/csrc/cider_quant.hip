@@ -135,6 +135,99 @@ __global__ __launch_bounds__(256) void quant_rows_two_pass(const uint4* __restri
   }
 }
 
+// Percentile-clipped scales (the README's notes section names a percentile
+// rule, clip_percentile=99.9, beside the default min-max): one workgroup per
+// group (a row, or gs elements of it). The clip threshold is the percentile of
+// the group's magnitudes by linear interpolation between the order statistics
+// i = floor(h) and j = min(i + 1, n - 1), h = (n - 1) * (percentile / 100):
+// t = a_i + (h - i) * (a_j - a_i), each step one rounded fp64 operation, then
+// rounded to fp32; s = t / qmax and the codes follow the element rule, so
+// magnitudes above t saturate. a_i and a_j come from a two-level radix select
+// over the 15-bit magnitude patterns of fp16 (which order like the values):
+// a 256-bin histogram of the high 8 bits finds each rank's bucket, a 128-bin
+// histogram of the low 7 bits inside it the exact pattern. The group is read
+// three times (two histograms, then the codes); weight quantization is offline.
+__global__ __launch_bounds__(256) void quant_rows_clip(const uint4* __restrict__ x, int64_t K, int n, int G,
+                                                       double pfrac, float qmax, bool pack4,
+                                                       void* __restrict__ q, float* __restrict__ s) {
+  __shared__ uint32_t hist_hi[256];
+  __shared__ uint32_t hist_lo[2][128];
+  __shared__ int pick[4];        // bucket and rank within it, for ranks i and j
+  __shared__ float scale;
+  const int64_t row = blockIdx.x / G;
+  const int g = (int)(blockIdx.x % G);
+  const int C = n / 8;                                   // 16-byte chunks in the group
+  const uint4* xg = x + (row * K + (int64_t)g * n) / 8;
+
+  const double h = (double)(n - 1) * pfrac;
+  const int i = (int)__builtin_floor(h);
+  const int j = min(i + 1, n - 1);
+
+  for (int b = threadIdx.x; b < 256; b += 256) hist_hi[b] = 0;
+  if (threadIdx.x < 128) hist_lo[0][threadIdx.x] = hist_lo[1][threadIdx.x] = 0;
+  __syncthreads();
+  for (int c = threadIdx.x; c < C; c += 256) {
+    const uint4 v = xg[c];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) atomicAdd(&hist_hi[((w[e >> 1] >> (16 * (e & 1))) & 0x7FFFu) >> 7], 1u);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t cum = 0;
+    int bi = -1, bj = -1;
+    for (int b = 0; b < 256; ++b) {
+      const uint32_t next = cum + hist_hi[b];
+      if (bi < 0 && (uint32_t)i < next) { bi = b; pick[1] = i - (int)cum; }
+      if (bj < 0 && (uint32_t)j < next) { bj = b; pick[3] = j - (int)cum; }
+      cum = next;
+    }
+    pick[0] = bi;
+    pick[2] = bj;
+  }
+  __syncthreads();
+  const int bi = pick[0], bj = pick[2];
+  for (int c = threadIdx.x; c < C; c += 256) {
+    const uint4 v = xg[c];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t u = (w[e >> 1] >> (16 * (e & 1))) & 0x7FFFu;
+      if ((int)(u >> 7) == bi) atomicAdd(&hist_lo[0][u & 127], 1u);
+      if ((int)(u >> 7) == bj) atomicAdd(&hist_lo[1][u & 127], 1u);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t sel[2];
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t rank = (uint32_t)pick[2 * k + 1];
+      uint32_t cum = 0, lo = 0;
+      for (int b = 0; b < 128; ++b) {
+        const uint32_t next = cum + hist_lo[k][b];
+        if (rank < next) { lo = (uint32_t)b; break; }
+        cum = next;
+      }
+      sel[k] = ((uint32_t)pick[2 * k] << 7) | lo;
+    }
+    const double ai = (double)half_bits_to_float(sel[0]), aj = (double)half_bits_to_float(sel[1]);
+    double prod = (h - (double)i) * (aj - ai);
+    asm("" : "+v"(prod));                 // keep the product and the sum two roundings
+    const float t = (float)(ai + prod);
+    const float sc = t / qmax;
+    s[row * G + g] = sc;
+    scale = sc;
+  }
+  __syncthreads();
+  const float sc = scale;
+  const float inv = 1.0f / sc;
+  for (int c = threadIdx.x; c < C; c += 256) {
+    int cq[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (sc != 0.0f) codes_of_chunk(xg[c], sc, inv, qmax, cq);
+    store_codes(q, row, K, g * C + c, pack4, cq);
+  }
+}
+
 template <int GS>
 hipError_t launch_reg(int cpl, int segs, const uint4* x, int64_t R, int64_t K, float qmax, bool pack4,
                       void* q, float* s, hipStream_t st) {
@@ -151,6 +244,16 @@ hipError_t launch_reg(int cpl, int segs, const uint4* x, int64_t R, int64_t K, f
 }
 
 }  // namespace
+
+hipError_t launch_quant_rows_clip(const void* x, int64_t R, int64_t K, int group_size, int qmax,
+                                  double percentile, void* q, float* s, hipStream_t stream) {
+  const int n = group_size ? group_size : (int)K;
+  const int G = (int)(K / n);
+  quant_rows_clip<<<dim3((unsigned)(R * G)), dim3(256), 0, stream>>>(static_cast<const uint4*>(x), K, n, G,
+                                                                    percentile / 100.0, (float)qmax, qmax == 7,
+                                                                    q, s);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_rows(const void* x, int64_t R, int64_t K, int group_size, int qmax, void* q,
                              float* s, hipStream_t stream) {
