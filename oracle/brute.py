@@ -18,7 +18,7 @@ from __future__ import annotations
 
 from fractions import Fraction
 
-__all__ = ["round_binary", "f32", "f16", "f64", "rint_half_even", "quantize_row", "percentile_fp64",
+__all__ = ["round_binary", "f32", "f16", "f64", "bf16", "linear_bf16", "rint_half_even", "quantize_row", "percentile_fp64",
            "quantize_row_clip",
            "dot", "dequant", "dequant_groups", "linear", "mv", "linear_token_group"]
 
@@ -60,6 +60,11 @@ def f32(v) -> Fraction:
 
 def f16(v) -> Fraction:
     return round_binary(Fraction(v), 11, -14, 15)
+
+
+def bf16(v) -> Fraction:
+    """bfloat16: 8 significand bits, the exponent range of fp32."""
+    return round_binary(Fraction(v), 8, -126, 127)
 
 
 def f64(v) -> Fraction:
@@ -154,6 +159,26 @@ def linear(x_rows, w_codes, w_scales, group_size: int):
             accs = [dot(qa[m][g * gs:(g + 1) * gs], w_codes[n][g * gs:(g + 1) * gs])
                     for g in range(K // gs)]
             out.append(dequant_groups(accs, sa[m], w_scales[n]))
+        y.append(out)
+    return y, qa, sa
+
+
+def linear_bf16(x_rows, w_codes, w_scales, group_size: int):
+    """linear() with the output rounded once to bfloat16 instead of fp16 (the
+    activation rows are bf16 values; the quantization steps are the same)."""
+    K = len(x_rows[0]) if x_rows else 0
+    gs = K if group_size == 0 else group_size
+    qa, sa = [], []
+    for row in x_rows:
+        c, s = quantize_row(row, group_size, 127)
+        qa.append(c)
+        sa.append(s)
+    y = []
+    for m in range(len(x_rows)):
+        out = []
+        for n in range(len(w_codes)):
+            accs = [dot(qa[m][g * gs:(g + 1) * gs], w_codes[n][g * gs:(g + 1) * gs]) for g in range(K // gs)]
+            out.append(bf16(sum(Fraction(c) * a * w for c, a, w in zip(accs, sa[m], w_scales[n]))))
         y.append(out)
     return y, qa, sa
 

@@ -58,6 +58,9 @@ notes of the repository):
   interpolation between order statistics (numpy's default definition),
   evaluated as written in fp64 and rounded to fp32; s = t / qmax and the
   codes follow the min-max rule's code step, so magnitudes above t saturate.
+* bf16 I/O (the roadmap's automatic float16 / bfloat16 handling): bf16
+  activations and weights quantize by the same rule (their fp32 images are
+  exact); the output is the same exact dequant value rounded once to bf16.
 * decode MV: y = sum_k x[m,k] * (w_q[n,k] * s_w[n,g(k)]), the exact value
   rounded once to fp16 (evaluated in fp64: each product is exact, the sum's
   relative error is about K * 2^-53).
@@ -76,7 +79,8 @@ __all__ = [
     "pack_int4", "unpack_int4", "int_dot", "int_dot_groups", "dequant_per_channel",
     "dequant_per_group", "w8a8_linear", "w4a8_linear", "num_groups", "int8_mv",
     "dequant_token_group", "w8a8_linear_token_group", "percentile_threshold", "quantize_rows_clip",
-    "quantize_weight_clip",
+    "quantize_weight_clip", "bf16_to_f32", "f64_to_bf16", "quantize_rows_bf16", "quantize_weight_bf16",
+    "dequant_bf16", "w8a8_linear_bf16", "w4a8_linear_bf16",
 ]
 
 QMAX_INT8 = 127
@@ -106,7 +110,15 @@ def quantize_rows(X: np.ndarray, group_size: int, qmax: int):
     R, K = X.shape
     G = num_groups(K, group_size)
     gs = K if group_size == 0 else group_size
-    xg = X.astype(np.float32).reshape(R, G, gs)          # fp16 -> fp32 is exact
+    return _quantize_values(X.astype(np.float32), group_size, qmax)   # fp16 -> fp32 is exact
+
+
+def _quantize_values(Xf: np.ndarray, group_size: int, qmax: int):
+    """The min-max steps on fp32 values (exact images of fp16 or bf16 inputs)."""
+    R, K = Xf.shape
+    G = num_groups(K, group_size)
+    gs = K if group_size == 0 else group_size
+    xg = Xf.reshape(R, G, gs)
     amax = np.abs(xg).max(axis=2) if K else np.zeros((R, G), np.float32)
     s = (amax / np.float32(qmax)).astype(np.float32)      # one rounded fp32 division
     zero = s == 0
@@ -272,6 +284,84 @@ def w8a8_linear(x: np.ndarray, w_q: np.ndarray, s_w: np.ndarray, group_size: int
     else:
         y = dequant_per_group(int_dot_groups(q_a, w_q, group_size), s_a, s_w)
     return y, q_a, s_a
+
+
+# ------------------------------------------------------------------ bf16 I/O
+# The README's roadmap lists automatic float16 / bfloat16 handling: a bf16
+# model feeds bf16 activations (and weights) and gets bf16 outputs. numpy has
+# no bfloat16, so bf16 arrays are carried as uint16 bit patterns (the top half
+# of the fp32 pattern). The quantization rule is unchanged (bf16 -> fp32 is
+# exact); the dequantized output is rounded once to bf16 instead of fp16.
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """uint16 bf16 patterns -> the fp32 values they denote (exact)."""
+    b = np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32)
+
+
+def f64_to_bf16(v: np.ndarray) -> np.ndarray:
+    """Round fp64 values once to bfloat16 (nearest, ties to even; 8 significand
+    bits, exponents of fp32, gradual underflow below 2^-126, +-inf from
+    2^128 up). Returns uint16 bit patterns."""
+    v = np.asarray(v, np.float64)
+    a = np.abs(v)
+    _, e = np.frexp(a)                                  # 2^(e-1) <= a < 2^e
+    q = np.maximum(e - 1, -126) - 7                     # exponent of the bf16 spacing
+    val = np.ldexp(np.rint(np.ldexp(a, -q)), q)          # exact scalings; one rounding
+    val = np.where(val >= 2.0 ** 128, np.inf, val)
+    bits = (val.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    return np.where(np.signbit(v), bits | np.uint16(0x8000), bits).astype(np.uint16)
+
+
+def quantize_rows_bf16(Xbits: np.ndarray, group_size: int, qmax: int):
+    """quantize_rows for bf16 rows (uint16 patterns [R, K])."""
+    Xbits = np.asarray(Xbits)
+    if Xbits.dtype != np.uint16 or Xbits.ndim != 2:
+        raise TypeError("Xbits must be a 2-D uint16 array of bf16 patterns")
+    return _quantize_values(bf16_to_f32(Xbits), group_size, qmax)
+
+
+def quantize_weight_bf16(w_bits: np.ndarray, bits: int = 8, group_size: int = 0):
+    """quantize_weight for bf16 weights (same outputs and layouts)."""
+    if bits == 8:
+        q, s = quantize_rows_bf16(w_bits, group_size, QMAX_INT8)
+        return q, (s[:, 0] if group_size == 0 else s)
+    if bits == 4:
+        if group_size != 0:
+            raise ValueError("int4 weights are per output channel only")
+        q, s = quantize_rows_bf16(w_bits, 0, QMAX_INT4)
+        return pack_int4(q), s[:, 0]
+    raise ValueError("bits must be 8 or 4")
+
+
+def dequant_bf16(acc_g: np.ndarray, s_a: np.ndarray, s_w: np.ndarray) -> np.ndarray:
+    """Per-channel (acc [M, N], s_a [M], s_w [N]) or per-group (acc_g [G, M, N],
+    s_a [M, G], s_w [N, G]) dequant, the exact fp64 value rounded once to
+    bf16 (uint16 patterns [M, N])."""
+    if acc_g.ndim == 2:
+        t = acc_g.astype(np.float64) * s_a.astype(np.float64)[:, None]
+        return f64_to_bf16(t * s_w.astype(np.float64)[None, :])
+    y = np.zeros(acc_g.shape[1:], np.float64)
+    for g in range(acc_g.shape[0]):
+        t = acc_g[g].astype(np.float64) * s_a[:, g].astype(np.float64)[:, None]
+        y += t * s_w[:, g].astype(np.float64)[None, :]
+    return f64_to_bf16(y)
+
+
+def w8a8_linear_bf16(x_bits: np.ndarray, w_q: np.ndarray, s_w: np.ndarray, group_size: int = 0):
+    """w8a8_linear with bf16 activations in and bf16 output (uint16 patterns).
+    Returns (y [M, N], q_a, s_a)."""
+    q_a, s2 = quantize_rows_bf16(x_bits, group_size, QMAX_INT8)
+    if group_size == 0:
+        y = dequant_bf16(int_dot(q_a, w_q), s2[:, 0], s_w)
+        return y, q_a, s2[:, 0]
+    return dequant_bf16(int_dot_groups(q_a, w_q, group_size), s2, s_w), q_a, s2
+
+
+def w4a8_linear_bf16(x_bits: np.ndarray, w_packed: np.ndarray, s_w: np.ndarray):
+    """w4a8_linear with bf16 activations in and bf16 output."""
+    q_a, s2 = quantize_rows_bf16(x_bits, 0, QMAX_INT8)
+    return dequant_bf16(int_dot(q_a, unpack_int4(w_packed)), s2[:, 0], s_w), q_a, s2[:, 0]
 
 
 def w4a8_linear(x: np.ndarray, w_packed: np.ndarray, s_w: np.ndarray):

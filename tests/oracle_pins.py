@@ -528,6 +528,77 @@ def check_clip_reductions(impl, seed=20):
     assert np.array_equal(ts[-1], m.max(axis=-1))
 
 
+# ------------------------------------------------- bf16 I/O
+def _bf16_bits(h):
+    return np.array([int(h, 16)], np.uint16)
+
+
+def check_golden_bf16(impl):
+    d = _load("bf16.json")
+    for c in d["round"]:
+        got = int(impl.f64_to_bf16(np.array([c["v"]]))[0])
+        assert got == int(c["bits"], 16), (c, hex(got))
+        got = int(impl.f64_to_bf16(np.array([-c["v"]]))[0])
+        assert got == int(c["bits"], 16) ^ 0x8000, (c, "negated", hex(got))
+    for c in d["decode"]:
+        v = float(impl.bf16_to_f32(_bf16_bits(c["bits"]))[0])
+        assert v == float(c["v"]), (c, v)
+
+
+def check_brute_bf16_rounding(impl, seed=21):
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal(1500) * 10.0 ** rng.integers(-44, 39, 1500)
+    v = np.concatenate([v, rng.integers(-300, 300, 200) * 2.0 ** rng.integers(-140, 120, 200)])
+    got = impl.f64_to_bf16(v)
+    for x, b in zip(v, got):
+        ref = brute.bf16(Fraction(float(x)))
+        val = float(impl.bf16_to_f32(np.array([b], np.uint16))[0])
+        assert val == float(ref), (x, val, float(ref))
+
+
+def check_brute_linear_bf16(impl, trials=24, seed=22):
+    rng = np.random.default_rng(seed)
+    for t in range(trials):
+        M, N = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        gs = [0, 2, 4][t % 3]
+        K = (gs or 1) * int(rng.integers(1, 5)) if gs else int(rng.integers(1, 9))
+        xf = _rand_fp16(rng, (M, K), ["normal", "wide", "ties"][t % 3]).astype(np.float32)
+        xb = (xf.view(np.uint32) >> np.uint32(16)).astype(np.uint16)      # truncated to bf16
+        w = _rand_fp16(rng, (N, K), ["normal", "wide", "small"][t % 3])
+        qw, sw = impl.quantize_rows(w, gs, 127)
+        qa, sa = impl.quantize_rows_bf16(xb, gs, 127)
+        acc = impl.int_dot(qa, qw) if gs == 0 else impl.int_dot_groups(qa, qw, gs)
+        y = impl.dequant_bf16(acc, sa[:, 0] if gs == 0 else sa, sw[:, 0] if gs == 0 else sw)
+        xr = [[float(v) for v in row] for row in impl.bf16_to_f32(xb)]
+        by, bq, _ = brute.linear_bf16(xr, qw.astype(int).tolist(), [[Fraction(float(v)) for v in row] for row in sw], gs)
+        assert qa.astype(int).tolist() == bq, t
+        yv = impl.bf16_to_f32(y)
+        for m in range(M):
+            for n in range(N):
+                assert float(yv[m, n]) == float(by[m][n]), (t, m, n, float(yv[m, n]), float(by[m][n]))
+
+
+def check_bf16_reductions(impl, seed=23):
+    """bf16 rows whose values are fp16 values too quantize exactly as the fp16
+    rows do; a bf16 output equals the fp16 output wherever the exact value
+    fits both formats."""
+    rng = np.random.default_rng(seed)
+    xf = (rng.integers(-255, 256, (6, 128)) * 2.0 ** rng.integers(-8, 4, (6, 1))).astype(np.float32)
+    xb = (xf.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    assert np.array_equal(impl.bf16_to_f32(xb), xf)
+    for gs in (0, 64):
+        q1, s1 = impl.quantize_rows_bf16(xb, gs, 127)
+        q0, s0 = impl.quantize_rows(xf.astype(np.float16), gs, 127)
+        assert np.array_equal(q1, q0) and np.array_equal(s1, s0)
+    acc = rng.integers(-2 ** 14, 2 ** 14, (5, 7))
+    s_a = np.full(5, 2.0 ** -6, np.float32)
+    s_w = np.full(7, 2.0 ** -3, np.float32)
+    yb = impl.dequant_bf16(acc, s_a, s_w)
+    small = np.abs(acc) < 256                 # acc * 2^-9 has at most 8 significant bits
+    y16 = impl.dequant_per_channel(acc, s_a, s_w)
+    assert np.array_equal(impl.bf16_to_f32(yb)[small], y16.astype(np.float32)[small])
+
+
 ALL_CHECKS = [
     check_golden_quant, check_golden_division, check_golden_int4, check_golden_integer_gemm,
     check_closed_form_k10240, check_brute_quant, check_brute_linear,
@@ -537,4 +608,5 @@ ALL_CHECKS = [
     check_mv_pow2_scaling, check_mv_matches_lossless_w8a8, check_mv_exact_sum,
     check_golden_token_group, check_brute_token_group, check_token_group_reductions,
     check_golden_clip, check_brute_clip, check_clip_vs_numpy_percentile, check_clip_reductions,
+    check_golden_bf16, check_brute_bf16_rounding, check_brute_linear_bf16, check_bf16_reductions,
 ]

@@ -13,7 +13,8 @@ def _impl(**over):
     base = {name: getattr(O, name) for name in (
         "quantize_rows", "pack_int4", "unpack_int4", "int_dot", "int_dot_groups",
         "dequant_per_channel", "dequant_per_group", "int8_mv", "dequant_token_group",
-        "percentile_threshold", "quantize_rows_clip")}
+        "percentile_threshold", "quantize_rows_clip", "f64_to_bf16", "bf16_to_f32", "quantize_rows_bf16",
+        "dequant_bf16")}
     base.update(over)
     ns = types.SimpleNamespace(**base)
     return ns
@@ -175,6 +176,33 @@ def _clip_impl(kind):
     return _impl(percentile_threshold=t, quantize_rows_clip=q)
 
 
+def _bf16_variant(kind):
+    """(rounding, dequant, quantizer) with one planted bf16 mistake."""
+    def rnd(v):
+        v = np.asarray(v, np.float64)
+        if kind == "truncate":
+            return (v.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+        if kind == "via_fp32":
+            f = v.astype(np.float32).view(np.uint32)
+            r = (f + np.uint32(0x7FFF) + ((f >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+            return r.astype(np.uint16)
+        return O.f64_to_bf16(v)
+
+    def deq(acc_g, s_a, s_w):
+        if acc_g.ndim == 2:
+            return rnd(acc_g.astype(np.float64) * s_a.astype(np.float64)[:, None] * s_w.astype(np.float64)[None, :])
+        y = np.zeros(acc_g.shape[1:], np.float64)
+        for g in range(acc_g.shape[0]):
+            y += acc_g[g].astype(np.float64) * s_a[:, g].astype(np.float64)[:, None] * s_w[:, g].astype(np.float64)[None, :]
+        return rnd(y)
+
+    def quant(Xbits, group_size, qmax):
+        if kind == "as_fp16":
+            return O.quantize_rows(np.asarray(Xbits, np.uint16).view(np.float16), group_size, qmax)
+        return O.quantize_rows_bf16(Xbits, group_size, qmax)
+    return _impl(f64_to_bf16=rnd, dequant_bf16=deq, quantize_rows_bf16=quant)
+
+
 MUTANTS = {
     "round_half_up": _impl(quantize_rows=_quant_variant(rounding="up")),
     "scale_over_128": _impl(quantize_rows=_quant_variant(divisor_bias=1)),
@@ -204,6 +232,9 @@ MUTANTS = {
     "clip_ignores_percentile": _clip_impl("max"),
     "clip_signed_values": _clip_impl("signed"),
     "clip_no_saturation": _clip_impl("no_saturation"),
+    "bf16_truncation": _bf16_variant("truncate"),
+    "bf16_double_rounding_via_fp32": _bf16_variant("via_fp32"),
+    "bf16_rows_read_as_fp16": _bf16_variant("as_fp16"),
 }
 
 
