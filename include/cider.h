@@ -67,6 +67,15 @@ typedef enum {
   CIDER_ERROR_LAUNCH = 3,
 } cider_status_t;
 
+/* Element types of fp inputs and outputs (the README's roadmap: automatic
+ * float16 / bfloat16 handling). bf16 values quantize by the same rule (their
+ * fp32 images are exact); a bf16 output is the fp32 dequant value of the
+ * fp16 output's arithmetic rounded to bf16 (nearest, ties to even). */
+typedef enum {
+  CIDER_DTYPE_F16 = 0,
+  CIDER_DTYPE_BF16 = 1,
+} cider_dtype_t;
+
 /* 1 if the current HIP device is a gfx950 (MI355X-class) GPU, else 0.
  * Mirrors the README's is_available() gate (section "条件编译"). */
 int cider_is_available(void);
@@ -86,6 +95,9 @@ int cider_version(void);
  */
 cider_status_t cider_quant_act(const void* x_f16, int64_t M, int64_t K, int32_t group_size,
                                int8_t* x_q, float* x_scale, void* stream);
+/* The same for fp16 or bf16 rows (x_dtype, a cider_dtype_t). */
+cider_status_t cider_quant_act_dt(const void* x, int32_t x_dtype, int64_t M, int64_t K,
+                                  int32_t group_size, int8_t* x_q, float* x_scale, void* stream);
 
 /* Weight quantization (the README runs it offline in numpy; here it is a
  * device kernel with the same rule, not part of the timed linear).
@@ -96,6 +108,9 @@ cider_status_t cider_quant_act(const void* x_f16, int64_t M, int64_t K, int32_t 
  */
 cider_status_t cider_quant_weight(const void* w_f16, int64_t N, int64_t K, int32_t bits,
                                   int32_t group_size, void* w_q, float* w_scale, void* stream);
+/* The same for fp16 or bf16 weights (w_dtype, a cider_dtype_t). */
+cider_status_t cider_quant_weight_dt(const void* w, int32_t w_dtype, int64_t N, int64_t K, int32_t bits,
+                                     int32_t group_size, void* w_q, float* w_scale, void* stream);
 
 /* Weight quantization with percentile-clipped scales (the README's notes
  * section: scales by min-max by default, or by a percentile of the
@@ -108,11 +123,12 @@ cider_status_t cider_quant_weight(const void* w_f16, int64_t N, int64_t K, int32
  * max|w|, i.e. cider_quant_weight). s = t / qmax; codes as for
  * cider_quant_weight, so magnitudes above t saturate at +-qmax; s == 0
  * gives codes 0. Outputs and layouts as cider_quant_weight.
+ *   w_dtype    : CIDER_DTYPE_F16 or CIDER_DTYPE_BF16 (the weights' type).
  *   percentile : in [0, 100] (99.9 on the pages).
  * Sizes and errors as for cider_quant_weight; also N * (K/group_size) < 2^31.
  */
-cider_status_t cider_quant_weight_clip(const void* w_f16, int64_t N, int64_t K, int32_t bits,
-                                       int32_t group_size, double percentile, void* w_q,
+cider_status_t cider_quant_weight_clip(const void* w_f16, int32_t w_dtype, int64_t N, int64_t K,
+                                       int32_t bits, int32_t group_size, double percentile, void* w_q,
                                        float* w_scale, void* stream);
 
 /* W8A8 GEMM with fused dequant (pipeline step "matmul_fused_dequant"):
@@ -125,6 +141,12 @@ cider_status_t cider_quant_weight_clip(const void* w_f16, int64_t N, int64_t K, 
 cider_status_t cider_w8a8_gemm(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
                                const float* w_scale, int64_t M, int64_t N, int64_t K,
                                int32_t group_size, void* y_f16, void* stream);
+/* The same with the output type chosen by y_dtype (a cider_dtype_t):
+ * bf16: y = bf16(((float)acc * x_scale[m]) * w_scale[n]) (per group: the
+ * fp32 sum), i.e. the fp16 path's fp32 value rounded to bf16. */
+cider_status_t cider_w8a8_gemm_dt(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
+                                  const float* w_scale, int64_t M, int64_t N, int64_t K,
+                                  int32_t group_size, void* y, int32_t y_dtype, void* stream);
 
 /* W4A8 GEMM with fused dequant: the int4 weights are unpacked to int8 codes
  * (nibble - 8) inside the matmul's operand loads; per-channel scales only.
@@ -133,6 +155,10 @@ cider_status_t cider_w8a8_gemm(const int8_t* x_q, const float* x_scale, const in
 cider_status_t cider_w4a8_gemm(const int8_t* x_q, const float* x_scale, const uint8_t* w_packed,
                                const float* w_scale, int64_t M, int64_t N, int64_t K,
                                void* y_f16, void* stream);
+/* The same with the output type chosen by y_dtype (a cider_dtype_t). */
+cider_status_t cider_w4a8_gemm_dt(const int8_t* x_q, const float* x_scale, const uint8_t* w_packed,
+                                  const float* w_scale, int64_t M, int64_t N, int64_t K, void* y,
+                                  int32_t y_dtype, void* stream);
 
 /* The whole linear layer in one call, fp16 x in and fp16 y out (the README's
  * perchannel_linear / w4a8_linear take fp16 activations): the activation

@@ -80,7 +80,7 @@ __all__ = [
     "dequant_per_group", "w8a8_linear", "w4a8_linear", "num_groups", "int8_mv",
     "dequant_token_group", "w8a8_linear_token_group", "percentile_threshold", "quantize_rows_clip",
     "quantize_weight_clip", "bf16_to_f32", "f64_to_bf16", "quantize_rows_bf16", "quantize_weight_bf16",
-    "dequant_bf16", "w8a8_linear_bf16", "w4a8_linear_bf16",
+    "quantize_weight_clip_bf16", "dequant_bf16", "w8a8_linear_bf16", "w4a8_linear_bf16",
 ]
 
 QMAX_INT8 = 127
@@ -187,10 +187,15 @@ def quantize_rows_clip(X: np.ndarray, group_size: int, qmax: int, percentile: fl
         raise TypeError("X must be a 2-D float16 array")
     if not 0.0 <= percentile <= 100.0:
         raise ValueError("percentile must lie in [0, 100]")
-    R, K = X.shape
+    return _quantize_clip_values(X.astype(np.float32), group_size, qmax, percentile)
+
+
+def _quantize_clip_values(Xf: np.ndarray, group_size: int, qmax: int, percentile: float):
+    """The percentile-clipped steps on fp32 values (exact images of the inputs)."""
+    R, K = Xf.shape
     G = num_groups(K, group_size)
     gs = K if group_size == 0 else group_size
-    xg = X.astype(np.float32).reshape(R, G, gs)
+    xg = Xf.reshape(R, G, gs)
     t = percentile_threshold(np.abs(xg), percentile)
     s = (t / np.float32(qmax)).astype(np.float32)
     zero = s == 0
@@ -332,6 +337,19 @@ def quantize_weight_bf16(w_bits: np.ndarray, bits: int = 8, group_size: int = 0)
         q, s = quantize_rows_bf16(w_bits, 0, QMAX_INT4)
         return pack_int4(q), s[:, 0]
     raise ValueError("bits must be 8 or 4")
+
+
+def quantize_weight_clip_bf16(w_bits: np.ndarray, bits: int = 8, group_size: int = 0, percentile: float = 99.9):
+    """quantize_weight_clip for bf16 weights (uint16 patterns)."""
+    if not 0.0 <= percentile <= 100.0:
+        raise ValueError("percentile must lie in [0, 100]")
+    qmax = QMAX_INT8 if bits == 8 else QMAX_INT4
+    if bits == 4 and group_size != 0:
+        raise ValueError("int4 weights are per output channel only")
+    q, s = _quantize_clip_values(bf16_to_f32(np.asarray(w_bits, np.uint16)), group_size, qmax, percentile)
+    if bits == 4:
+        return pack_int4(q), s[:, 0]
+    return q, (s[:, 0] if group_size == 0 else s)
 
 
 def dequant_bf16(acc_g: np.ndarray, s_a: np.ndarray, s_w: np.ndarray) -> np.ndarray:

@@ -161,16 +161,33 @@ def test_linear_workspace_query_and_rejects():
 
 def test_quant_weight_clip_rejects():
     c = L.cider_quant_weight_clip
-    assert c(P, 4, 64, 8, 0, 100.5, P, P, NULL) == INV                  # percentile above 100
-    assert c(P, 4, 64, 8, 0, -0.1, P, P, NULL) == INV
-    assert c(P, 4, 64, 8, 0, float("nan"), P, P, NULL) == INV
-    assert c(P, 4, 64, 6, 0, 99.9, P, P, NULL) == INV                   # bits
-    assert c(P, 4, 64, 4, 64, 99.9, P, P, NULL) == INV                  # int4 is per-channel
-    assert c(P, 4, 48, 4, 0, 99.9, P, P, NULL) == INV                   # int4 needs K % 32
-    assert c(P, 4, 192, 8, 128, 99.9, P, P, NULL) == INV                # K % gs
-    assert c(P, 4, 64, 8, 0, 99.9, P, MIS, NULL) == INV
-    assert c(NULL, 4, 64, 8, 0, 99.9, P, P, NULL) == INV
-    assert c(NULL, 0, 64, 8, 0, 99.9, NULL, NULL, NULL) == 0              # empty work
+    assert c(P, 0, 4, 64, 8, 0, 100.5, P, P, NULL) == INV               # percentile above 100
+    assert c(P, 0, 4, 64, 8, 0, -0.1, P, P, NULL) == INV
+    assert c(P, 0, 4, 64, 8, 0, float("nan"), P, P, NULL) == INV
+    assert c(P, 2, 4, 64, 8, 0, 99.9, P, P, NULL) == INV                # dtype
+    assert c(P, 0, 4, 64, 6, 0, 99.9, P, P, NULL) == INV                # bits
+    assert c(P, 1, 4, 64, 4, 64, 99.9, P, P, NULL) == INV               # int4 is per-channel
+    assert c(P, 0, 4, 48, 4, 0, 99.9, P, P, NULL) == INV                # int4 needs K % 32
+    assert c(P, 0, 4, 192, 8, 128, 99.9, P, P, NULL) == INV             # K % gs
+    assert c(P, 0, 4, 64, 8, 0, 99.9, P, MIS, NULL) == INV
+    assert c(NULL, 0, 4, 64, 8, 0, 99.9, P, P, NULL) == INV
+    assert c(NULL, 1, 0, 64, 8, 0, 99.9, NULL, NULL, NULL) == 0           # empty work
+
+
+def test_dtype_entries_reject():
+    assert L.cider_quant_act_dt(P, 2, 4, 64, 0, P, P, NULL) == INV      # dtype
+    assert L.cider_quant_act_dt(P, -1, 4, 64, 0, P, P, NULL) == INV
+    assert L.cider_quant_act_dt(P, 1, 4, 40, 0, P, P, NULL) == INV      # K % 16
+    assert L.cider_quant_act_dt(NULL, 1, 0, 64, 0, NULL, NULL, NULL) == 0
+    assert L.cider_quant_weight_dt(P, 2, 4, 64, 8, 0, P, P, NULL) == INV
+    assert L.cider_quant_weight_dt(P, 1, 4, 64, 4, 64, P, P, NULL) == INV
+    assert L.cider_quant_weight_dt(NULL, 1, 0, 64, 8, 0, NULL, NULL, NULL) == 0
+    assert L.cider_w8a8_gemm_dt(P, P, P, P, 4, 4, 64, 0, P, 2, NULL) == INV
+    assert L.cider_w8a8_gemm_dt(P, P, P, P, 4, 4, 64, 0, MIS, 1, NULL) == INV
+    assert L.cider_w8a8_gemm_dt(NULL, NULL, NULL, NULL, 0, 4, 64, 0, NULL, 1, NULL) == 0
+    assert L.cider_w4a8_gemm_dt(P, P, P, P, 4, 4, 64, P, 7, NULL) == INV
+    assert L.cider_w4a8_gemm_dt(P, P, P, P, 4, 4, 48, P, 1, NULL) == INV
+    assert L.cider_w4a8_gemm_dt(NULL, NULL, NULL, NULL, 4, 0, 64, NULL, 1, NULL) == 0
 
 
 def test_not_available_without_gpu():

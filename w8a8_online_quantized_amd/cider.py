@@ -39,8 +39,12 @@ SIGNATURES = {
     "cider_linear_workspace_size": (ctypes.c_int64, [_c_i64, _c_i64, _c_i32, _c_i32]),
     "cider_linear": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_p, _c_i64, _c_p,
                                     _c_p]),
-    "cider_quant_weight_clip": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i32, _c_i32, ctypes.c_double, _c_p, _c_p,
-                                               _c_p]),
+    "cider_quant_weight_clip": (ctypes.c_int, [_c_p, _c_i32, _c_i64, _c_i64, _c_i32, _c_i32, ctypes.c_double, _c_p,
+                                               _c_p, _c_p]),
+    "cider_quant_act_dt": (ctypes.c_int, [_c_p, _c_i32, _c_i64, _c_i64, _c_i32, _c_p, _c_p, _c_p]),
+    "cider_quant_weight_dt": (ctypes.c_int, [_c_p, _c_i32, _c_i64, _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_p]),
+    "cider_w8a8_gemm_dt": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_i32, _c_p]),
+    "cider_w4a8_gemm_dt": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_i32, _c_p]),
     "cider_int8_mv": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p]),
     "cider_stack_workspace_layout": (ctypes.c_int64, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                                       ctypes.POINTER(ctypes.c_int64)]),
@@ -127,31 +131,46 @@ def cider_version() -> int:
     return int(lib().cider_version())
 
 
+CIDER_DTYPE_F16, CIDER_DTYPE_BF16 = 0, 1
+
+
+def _fp_code(t, name):
+    """cider_dtype_t of an fp16 / bf16 tensor."""
+    import torch
+    if t.dtype == torch.float16:
+        return CIDER_DTYPE_F16
+    if t.dtype == torch.bfloat16:
+        return CIDER_DTYPE_BF16
+    raise TypeError(f"{name} must be float16 or bfloat16, got {t.dtype}")
+
+
 def _scale_shape(rows, K, group_size):
     return (rows,) if group_size == 0 else (rows, K // group_size)
 
 
 def cider_quant_act(x, group_size: int = 0, x_q=None, x_scale=None, stream=None):
-    """fp16 [M, K] -> (int8 codes [M, K], fp32 scales [M] or [M, K/gs])."""
+    """fp16 or bf16 [M, K] -> (int8 codes [M, K], fp32 scales [M] or [M, K/gs])."""
     import torch
     M, K = x.shape
-    _need(x, torch.float16, (M, K), "x")
+    dt = _fp_code(x, "x")
+    _need(x, x.dtype, (M, K), "x")
     if x_q is None:
         x_q = torch.empty((M, K), dtype=torch.int8, device=x.device)
     if x_scale is None:
         x_scale = torch.empty(_scale_shape(M, K, group_size), dtype=torch.float32, device=x.device)
     _need(x_q, torch.int8, (M, K), "x_q")
     _need(x_scale, torch.float32, _scale_shape(M, K, group_size), "x_scale")
-    _check("cider_quant_act", lib().cider_quant_act(_ptr(x), M, K, group_size, _ptr(x_q), _ptr(x_scale),
-                                                    _stream(stream)))
+    _check("cider_quant_act_dt", lib().cider_quant_act_dt(_ptr(x), dt, M, K, group_size, _ptr(x_q), _ptr(x_scale),
+                                                          _stream(stream)))
     return x_q, x_scale
 
 
 def cider_quant_weight(w, bits: int = 8, group_size: int = 0, w_q=None, w_scale=None, stream=None):
-    """fp16 [N, K] -> (int8 [N, K] or packed uint8 [N, K/2], fp32 scales)."""
+    """fp16 or bf16 [N, K] -> (int8 [N, K] or packed uint8 [N, K/2], fp32 scales)."""
     import torch
     N, K = w.shape
-    _need(w, torch.float16, (N, K), "w")
+    dt = _fp_code(w, "w")
+    _need(w, w.dtype, (N, K), "w")
     qshape = (N, K) if bits == 8 else (N, K // 2)
     qdtype = torch.int8 if bits == 8 else torch.uint8
     if w_q is None:
@@ -160,8 +179,8 @@ def cider_quant_weight(w, bits: int = 8, group_size: int = 0, w_q=None, w_scale=
         w_scale = torch.empty(_scale_shape(N, K, group_size), dtype=torch.float32, device=w.device)
     _need(w_q, qdtype, qshape, "w_q")
     _need(w_scale, torch.float32, _scale_shape(N, K, group_size), "w_scale")
-    _check("cider_quant_weight", lib().cider_quant_weight(_ptr(w), N, K, bits, group_size, _ptr(w_q),
-                                                          _ptr(w_scale), _stream(stream)))
+    _check("cider_quant_weight_dt", lib().cider_quant_weight_dt(_ptr(w), dt, N, K, bits, group_size, _ptr(w_q),
+                                                                _ptr(w_scale), _stream(stream)))
     return w_q, w_scale
 
 
@@ -170,7 +189,8 @@ def cider_quant_weight_clip(w, bits: int = 8, group_size: int = 0, percentile: f
     """cider_quant_weight with percentile-clipped scales (same outputs)."""
     import torch
     N, K = w.shape
-    _need(w, torch.float16, (N, K), "w")
+    dt = _fp_code(w, "w")
+    _need(w, w.dtype, (N, K), "w")
     qshape = (N, K) if bits == 8 else (N, K // 2)
     qdtype = torch.int8 if bits == 8 else torch.uint8
     if w_q is None:
@@ -180,13 +200,14 @@ def cider_quant_weight_clip(w, bits: int = 8, group_size: int = 0, percentile: f
     _need(w_q, qdtype, qshape, "w_q")
     _need(w_scale, torch.float32, _scale_shape(N, K, group_size), "w_scale")
     _check("cider_quant_weight_clip",
-           lib().cider_quant_weight_clip(_ptr(w), N, K, bits, group_size, float(percentile), _ptr(w_q),
+           lib().cider_quant_weight_clip(_ptr(w), dt, N, K, bits, group_size, float(percentile), _ptr(w_q),
                                          _ptr(w_scale), _stream(stream)))
     return w_q, w_scale
 
 
-def cider_w8a8_gemm(x_q, x_scale, w_q, w_scale, group_size: int = 0, y=None, stream=None):
-    """int8 codes + scales -> fp16 y [M, N] (fused dequant)."""
+def cider_w8a8_gemm(x_q, x_scale, w_q, w_scale, group_size: int = 0, y=None, stream=None, out_dtype=None):
+    """int8 codes + scales -> y [M, N] (fused dequant): fp16, or bf16 when
+    out_dtype (or a given y) is bfloat16."""
     import torch
     M, K = x_q.shape
     N = w_q.shape[0]
@@ -197,10 +218,11 @@ def cider_w8a8_gemm(x_q, x_scale, w_q, w_scale, group_size: int = 0, y=None, str
     _need(x_scale, torch.float32, _scale_shape(M, K, group_size), "x_scale")
     _need(w_scale, torch.float32, _scale_shape(N, K, group_size), "w_scale")
     if y is None:
-        y = torch.empty((M, N), dtype=torch.float16, device=x_q.device)
-    _need(y, torch.float16, (M, N), "y")
-    _check("cider_w8a8_gemm", lib().cider_w8a8_gemm(_ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale),
-                                                    M, N, K, group_size, _ptr(y), _stream(stream)))
+        y = torch.empty((M, N), dtype=out_dtype or torch.float16, device=x_q.device)
+    dt = _fp_code(y, "y")
+    _need(y, y.dtype, (M, N), "y")
+    _check("cider_w8a8_gemm_dt", lib().cider_w8a8_gemm_dt(_ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale),
+                                                          M, N, K, group_size, _ptr(y), dt, _stream(stream)))
     return y
 
 
@@ -303,8 +325,8 @@ def cider_int8_mv(x, w_q, w_scale, group_size: int = 0, y=None, stream=None):
     return y
 
 
-def cider_w4a8_gemm(x_q, x_scale, w_packed, w_scale, y=None, stream=None):
-    """int8 activation codes x packed int4 weights -> fp16 y [M, N]."""
+def cider_w4a8_gemm(x_q, x_scale, w_packed, w_scale, y=None, stream=None, out_dtype=None):
+    """int8 activation codes x packed int4 weights -> y [M, N] (fp16 or bf16)."""
     import torch
     M, K = x_q.shape
     N = w_packed.shape[0]
@@ -313,10 +335,11 @@ def cider_w4a8_gemm(x_q, x_scale, w_packed, w_scale, y=None, stream=None):
     _need(x_scale, torch.float32, (M,), "x_scale")
     _need(w_scale, torch.float32, (N,), "w_scale")
     if y is None:
-        y = torch.empty((M, N), dtype=torch.float16, device=x_q.device)
-    _need(y, torch.float16, (M, N), "y")
-    _check("cider_w4a8_gemm", lib().cider_w4a8_gemm(_ptr(x_q), _ptr(x_scale), _ptr(w_packed), _ptr(w_scale),
-                                                    M, N, K, _ptr(y), _stream(stream)))
+        y = torch.empty((M, N), dtype=out_dtype or torch.float16, device=x_q.device)
+    dt = _fp_code(y, "y")
+    _need(y, y.dtype, (M, N), "y")
+    _check("cider_w4a8_gemm_dt", lib().cider_w4a8_gemm_dt(_ptr(x_q), _ptr(x_scale), _ptr(w_packed), _ptr(w_scale),
+                                                          M, N, K, _ptr(y), dt, _stream(stream)))
     return y
 
 
@@ -340,9 +363,10 @@ def cider_gemm_acc_i32(mode: int, x_q, w, group_size: int = 0, acc=None, stream=
 
 
 def w8a8_linear(x, w_q, w_scale, group_size: int = 0, stream=None):
-    """The README's per-channel / per-group linear: quantize x, then the fused GEMM."""
+    """The README's per-channel / per-group linear: quantize x, then the fused
+    GEMM; the output has x's type (fp16 or bf16)."""
     x_q, x_scale = cider_quant_act(x, group_size, stream=stream)
-    return cider_w8a8_gemm(x_q, x_scale, w_q, w_scale, group_size, stream=stream)
+    return cider_w8a8_gemm(x_q, x_scale, w_q, w_scale, group_size, stream=stream, out_dtype=x.dtype)
 
 
 def w8a8_linear_token_group(x, w_q, w_scale, group_size: int, stream=None):
@@ -352,9 +376,10 @@ def w8a8_linear_token_group(x, w_q, w_scale, group_size: int, stream=None):
 
 
 def w4a8_linear(x, w_packed, w_scale, stream=None):
-    """The README's W4A8 linear: per-token int8 activations times packed int4 weights."""
+    """The README's W4A8 linear: per-token int8 activations times packed int4
+    weights; the output has x's type (fp16 or bf16)."""
     x_q, x_scale = cider_quant_act(x, 0, stream=stream)
-    return cider_w4a8_gemm(x_q, x_scale, w_packed, w_scale, stream=stream)
+    return cider_w4a8_gemm(x_q, x_scale, w_packed, w_scale, stream=stream, out_dtype=x.dtype)
 
 
 def cider_stack_workspace_layout(M: int, hidden: int, q_dim: int, kv_dim: int, mlp_dim: int):

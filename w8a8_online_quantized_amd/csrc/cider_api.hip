@@ -77,19 +77,34 @@ int cider_is_available(void) {
   return device_is_gfx950() ? 1 : 0;
 }
 
-cider_status_t cider_quant_act(const void* x_f16, int64_t M, int64_t K, int32_t group_size, int8_t* x_q,
-                               float* x_scale, void* stream) {
+static bool valid_dtype(int32_t d) { return d == CIDER_DTYPE_F16 || d == CIDER_DTYPE_BF16; }
+
+cider_status_t cider_quant_act_dt(const void* x, int32_t x_dtype, int64_t M, int64_t K, int32_t group_size,
+                                  int8_t* x_q, float* x_scale, void* stream) {
+  if (!valid_dtype(x_dtype)) return CIDER_ERROR_INVALID_VALUE;
   if (M < 0 || !valid_gs(group_size) || !valid_k(K, 16, group_size)) return CIDER_ERROR_INVALID_VALUE;
   if (M == 0) return CIDER_SUCCESS;
-  if (!x_f16 || !x_q || !x_scale || !aligned16(x_f16) || !aligned16(x_q) || !aligned16(x_scale))
+  if (!x || !x_q || !x_scale || !aligned16(x) || !aligned16(x_q) || !aligned16(x_scale))
     return CIDER_ERROR_INVALID_VALUE;
   if (!device_is_gfx950()) return CIDER_ERROR_NOT_SUPPORTED;
-  return from_hip(cider::launch_quant_rows(x_f16, M, K, group_size, 127, x_q, x_scale,
-                                           static_cast<hipStream_t>(stream)));
+  return from_hip(cider::launch_quant_rows(x, M, K, group_size, 127, x_q, x_scale, static_cast<hipStream_t>(stream),
+                                           x_dtype == CIDER_DTYPE_BF16));
+}
+
+cider_status_t cider_quant_act(const void* x_f16, int64_t M, int64_t K, int32_t group_size, int8_t* x_q,
+                               float* x_scale, void* stream) {
+  return cider_quant_act_dt(x_f16, CIDER_DTYPE_F16, M, K, group_size, x_q, x_scale, stream);
 }
 
 cider_status_t cider_quant_weight(const void* w_f16, int64_t N, int64_t K, int32_t bits, int32_t group_size,
                                   void* w_q, float* w_scale, void* stream) {
+  return cider_quant_weight_dt(w_f16, CIDER_DTYPE_F16, N, K, bits, group_size, w_q, w_scale, stream);
+}
+
+cider_status_t cider_quant_weight_dt(const void* w, int32_t w_dtype, int64_t N, int64_t K, int32_t bits,
+                                     int32_t group_size, void* w_q, float* w_scale, void* stream) {
+  if (!valid_dtype(w_dtype)) return CIDER_ERROR_INVALID_VALUE;
+  const void* w_f16 = w;
   if (N < 0 || !valid_gs(group_size)) return CIDER_ERROR_INVALID_VALUE;
   if (bits == 8) {
     if (!valid_k(K, 16, group_size)) return CIDER_ERROR_INVALID_VALUE;
@@ -103,12 +118,13 @@ cider_status_t cider_quant_weight(const void* w_f16, int64_t N, int64_t K, int32
     return CIDER_ERROR_INVALID_VALUE;
   if (!device_is_gfx950()) return CIDER_ERROR_NOT_SUPPORTED;
   return from_hip(cider::launch_quant_rows(w_f16, N, K, group_size, bits == 8 ? 127 : 7, w_q, w_scale,
-                                           static_cast<hipStream_t>(stream)));
+                                           static_cast<hipStream_t>(stream), w_dtype == CIDER_DTYPE_BF16));
 }
 
-cider_status_t cider_quant_weight_clip(const void* w_f16, int64_t N, int64_t K, int32_t bits, int32_t group_size,
-                                       double percentile, void* w_q, float* w_scale, void* stream) {
-  if (N < 0 || !valid_gs(group_size)) return CIDER_ERROR_INVALID_VALUE;
+cider_status_t cider_quant_weight_clip(const void* w_f16, int32_t w_dtype, int64_t N, int64_t K, int32_t bits,
+                                       int32_t group_size, double percentile, void* w_q, float* w_scale,
+                                       void* stream) {
+  if (!valid_dtype(w_dtype) || N < 0 || !valid_gs(group_size)) return CIDER_ERROR_INVALID_VALUE;
   if (!(percentile >= 0.0 && percentile <= 100.0)) return CIDER_ERROR_INVALID_VALUE;   // NaN fails too
   if (bits == 8) {
     if (!valid_k(K, 16, group_size)) return CIDER_ERROR_INVALID_VALUE;
@@ -124,7 +140,8 @@ cider_status_t cider_quant_weight_clip(const void* w_f16, int64_t N, int64_t K, 
     return CIDER_ERROR_INVALID_VALUE;
   if (!device_is_gfx950()) return CIDER_ERROR_NOT_SUPPORTED;
   return from_hip(cider::launch_quant_rows_clip(w_f16, N, K, group_size, bits == 8 ? 127 : 7, percentile, w_q,
-                                                w_scale, static_cast<hipStream_t>(stream)));
+                                                w_scale, static_cast<hipStream_t>(stream),
+                                                w_dtype == CIDER_DTYPE_BF16));
 }
 
 static cider_status_t gemm_common(cider::GemmArgs& g, cider::WeightKind wk, cider::Epilogue epi,
@@ -140,6 +157,13 @@ static bool gemm_sizes_ok(int64_t M, int64_t N) {
 cider_status_t cider_w8a8_gemm(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
                                const float* w_scale, int64_t M, int64_t N, int64_t K, int32_t group_size,
                                void* y_f16, void* stream) {
+  return cider_w8a8_gemm_dt(x_q, x_scale, w_q, w_scale, M, N, K, group_size, y_f16, CIDER_DTYPE_F16, stream);
+}
+
+cider_status_t cider_w8a8_gemm_dt(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
+                                  const float* w_scale, int64_t M, int64_t N, int64_t K, int32_t group_size,
+                                  void* y_f16, int32_t y_dtype, void* stream) {
+  if (!valid_dtype(y_dtype)) return CIDER_ERROR_INVALID_VALUE;
   if (!gemm_sizes_ok(M, N) || !valid_gs(group_size) || !valid_k(K, 16, group_size))
     return CIDER_ERROR_INVALID_VALUE;
   if (M == 0 || N == 0) return CIDER_SUCCESS;
@@ -147,12 +171,19 @@ cider_status_t cider_w8a8_gemm(const int8_t* x_q, const float* x_scale, const in
   if (!aligned16(x_q) || !aligned16(x_scale) || !aligned16(w_q) || !aligned16(w_scale) || !aligned16(y_f16))
     return CIDER_ERROR_INVALID_VALUE;
   cider::GemmArgs g{x_q, x_scale, w_q, w_scale, M, N, K, group_size, y_f16, nullptr};
-  return gemm_common(g, cider::kWeightI8, cider::kEpiF16, stream);
+  return gemm_common(g, cider::kWeightI8, y_dtype == CIDER_DTYPE_BF16 ? cider::kEpiBF16 : cider::kEpiF16, stream);
 }
 
 cider_status_t cider_w4a8_gemm(const int8_t* x_q, const float* x_scale, const uint8_t* w_packed,
                                const float* w_scale, int64_t M, int64_t N, int64_t K, void* y_f16,
                                void* stream) {
+  return cider_w4a8_gemm_dt(x_q, x_scale, w_packed, w_scale, M, N, K, y_f16, CIDER_DTYPE_F16, stream);
+}
+
+cider_status_t cider_w4a8_gemm_dt(const int8_t* x_q, const float* x_scale, const uint8_t* w_packed,
+                                  const float* w_scale, int64_t M, int64_t N, int64_t K, void* y_f16,
+                                  int32_t y_dtype, void* stream) {
+  if (!valid_dtype(y_dtype)) return CIDER_ERROR_INVALID_VALUE;
   if (!gemm_sizes_ok(M, N) || !valid_k(K, 32, 0)) return CIDER_ERROR_INVALID_VALUE;
   if (M == 0 || N == 0) return CIDER_SUCCESS;
   if (!x_q || !x_scale || !w_packed || !w_scale || !y_f16) return CIDER_ERROR_INVALID_VALUE;
@@ -160,7 +191,7 @@ cider_status_t cider_w4a8_gemm(const int8_t* x_q, const float* x_scale, const ui
       !aligned16(y_f16))
     return CIDER_ERROR_INVALID_VALUE;
   cider::GemmArgs g{x_q, x_scale, w_packed, w_scale, M, N, K, 0, y_f16, nullptr};
-  return gemm_common(g, cider::kWeightI4, cider::kEpiF16, stream);
+  return gemm_common(g, cider::kWeightI4, y_dtype == CIDER_DTYPE_BF16 ? cider::kEpiBF16 : cider::kEpiF16, stream);
 }
 
 cider_status_t cider_w8a8_gemm_token_group(const int8_t* x_q, const float* x_scale, const int8_t* w_q,

@@ -79,6 +79,32 @@ __device__ __forceinline__ h4 dequant4(v4i acc, float sa, float4 sw) {
   return __builtin_convertvector(f4{t.x, t.y, t.z, t.w}, h4);
 }
 
+// The same two fp32 roundings with a bfloat16 output (round to nearest even).
+typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __bf16 dequant1_bf(int32_t acc, float sa, float sw) {
+  float t = (float)acc * sa;
+  t = t * sw;
+  asm("" : "+v"(t));
+  return (__bf16)t;
+}
+
+__device__ __forceinline__ bf4 dequant4_bf(v4i acc, float sa, float4 sw) {
+  float4 t;
+  t.x = ((float)acc.x * sa) * sw.x;
+  t.y = ((float)acc.y * sa) * sw.y;
+  t.z = ((float)acc.z * sa) * sw.z;
+  t.w = ((float)acc.w * sa) * sw.w;
+  asm("" : "+v"(t.x), "+v"(t.y), "+v"(t.z), "+v"(t.w));
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  return __builtin_convertvector(f4{t.x, t.y, t.z, t.w}, bf4);
+}
+
+// A finished fp32 value to bfloat16.
+__device__ __forceinline__ __bf16 to_bf16(float t) {
+  asm("" : "+v"(t));
+  return (__bf16)t;
+}
+
 // Reorder 16 activation codes (4 dwords, K order 0..15) into the order the
 // unpacked int4 weights come in: 0,2,4,6 | 1,3,5,7 | 8,10,12,14 | 9,11,13,15.
 __device__ __forceinline__ v4i even_odd_bytes(v4i v) {
@@ -200,7 +226,7 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int TM = WTM / 16, TN = WTN / 16;
   constexpr bool kI4 = WK == kWeightI4;
-  constexpr bool kF16 = EPI == kEpiF16 || EPI == kEpiF16Split;
+  constexpr bool kF16 = EPI == kEpiF16 || EPI == kEpiF16Split || EPI == kEpiBF16;
   constexpr int RBA = BK;                     // activation bytes per row per stage
   constexpr int RBW = kI4 ? BK / 2 : BK;      // weight bytes per row per stage
   constexpr int kStageBytes = BM * RBA + BN * RBW;
@@ -461,6 +487,16 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
           for (int r = 0; r < 4; ++r)
             if (n + r < N) dst[r] = acc[a][b][r];
         }
+      } else if constexpr (EPI == kEpiBF16) {
+        const bf4 o = dequant4_bf(acc[a][b], sam, *reinterpret_cast<const float4*>(lsw + nl));
+        __bf16* dst = reinterpret_cast<__bf16*>(Y) + (int64_t)m * N + n;
+        if (vec_ok && n + 3 < N) {
+          *reinterpret_cast<bf4*>(dst) = o;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) dst[r] = o[r];
+        }
       } else {
         const h4 o = dequant4(acc[a][b], sam, *reinterpret_cast<const float4*>(lsw + nl));   // s_w zero past N
         _Float16* dst = Y + (int64_t)m * N + n;
@@ -603,12 +639,21 @@ gemm_skinny_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, c
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (n + r < N) ACC[(int64_t)m * N + n + r] = t[r];
+    } else if constexpr (EPI == kEpiBF16) {
+      const float sam = SA[m];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n + r < N) reinterpret_cast<__bf16*>(Y)[(int64_t)m * N + n + r] = dequant1_bf(t[r], sam, SW[n + r]);
     } else {
       const float sam = SA[m];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (n + r < N) Y[(int64_t)m * N + n + r] = dequant1(t[r], sam, SW[n + r]);
     }
+  } else if constexpr (EPI == kEpiBF16) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (n + r < N) reinterpret_cast<__bf16*>(Y)[(int64_t)m * N + n + r] = to_bf16(t[r]);
   } else if constexpr (EPI == kEpiF16) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -796,6 +841,8 @@ gemm_gemv_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, con
         const int t = red[0][r][m] + red[1][r][m] + red[2][r][m] + red[3][r][m];
         if constexpr (EPI == kEpiAccI32) ACC[(int64_t)m * N + n] = t;
         else if constexpr (EPI == kEpiF16Linear) Y[(int64_t)m * N + n] = dequant1(t, srow[m], SW[n]);
+        else if constexpr (EPI == kEpiBF16)
+          reinterpret_cast<__bf16*>(Y)[(int64_t)m * N + n] = dequant1_bf(t, SA[m], SW[n]);
         else Y[(int64_t)m * N + n] = dequant1(t, SA[m], SW[n]);
       }
     }
@@ -1066,6 +1113,20 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
       for (int a = 0; a < TN; ++a) {
         const int n = n0 + wn + 16 * a + 4 * l4;
         if (n >= N) continue;
+        if constexpr (EPI == kEpiBF16) {
+          bf4 o;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] = to_bf16(facc[a][b][r]);
+          __bf16* dst = reinterpret_cast<__bf16*>(Y) + (int64_t)m * N + n;
+          if (vec_ok && n + 3 < N) {
+            *reinterpret_cast<bf4*>(dst) = o;
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (n + r < N) dst[r] = o[r];
+          }
+          continue;
+        }
         h4 o;
 #pragma unroll
         for (int r = 0; r < 4; ++r) o[r] = kTok ? scale1(facc[a][b][r], sam) : (_Float16)facc[a][b][r];
@@ -1247,6 +1308,7 @@ bool linear_is_one_launch(int64_t M, int64_t K, int group_size) {
 hipError_t launch_gemm(const GemmArgs& g, WeightKind wk, Epilogue epi, hipStream_t st) {
   // Tile table by M (the README's tile section also switches configs by M).
   if (epi == kEpiF16Tok) return launch_tok(g, st);
+  if (epi == kEpiBF16) return launch_epi<kEpiBF16>(g, wk, st);
   if (epi == kEpiF16Linear)   // g.a holds fp16 activations; linear_is_one_launch() holds
     return wk == kWeightI4 ? launch_gemv<kWeightI4, kEpiF16Linear>(g, st) : launch_gemv<kWeightI8, kEpiF16Linear>(g, st);
   if (epi == kEpiF16Split) {

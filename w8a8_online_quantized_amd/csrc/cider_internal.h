@@ -10,15 +10,16 @@ namespace cider {
 // Launches the activation / weight quantization kernel.
 //   x: fp16 [R, K]; qmax 127 (int8 codes into q8 [R, K]) or 7 (packed int4
 //   codes into q4 [R, K/2]); s: fp32 [R, G].
+//   bf16: the rows are bfloat16 instead of fp16.
 hipError_t launch_quant_rows(const void* x, int64_t R, int64_t K, int group_size, int qmax,
-                             void* q, float* s, hipStream_t stream);
+                             void* q, float* s, hipStream_t stream, bool bf16 = false);
 
 // The same with percentile-clipped scales: s = t / qmax, t = the percentile
 // (0..100) of the group's magnitudes (linear interpolation between order
 // statistics, fp64, rounded to fp32). R * K / group size groups, one
 // workgroup each.
 hipError_t launch_quant_rows_clip(const void* x, int64_t R, int64_t K, int group_size, int qmax,
-                                  double percentile, void* q, float* s, hipStream_t stream);
+                                  double percentile, void* q, float* s, hipStream_t stream, bool bf16 = false);
 
 // Epilogue kinds of the GEMM kernels. kEpiF16Tok: per-group weight scales
 // [N, G] with per-token activation scales [M] (int8 weights, gs 64 / 128).
@@ -26,7 +27,8 @@ hipError_t launch_quant_rows_clip(const void* x, int64_t R, int64_t K, int group
 // matrices (GemmArgs::split).
 // kEpiF16Linear: the GEMV kernel takes fp16 activations and quantizes them
 // itself (per token), then dequantizes as kEpiF16.
-enum Epilogue { kEpiF16 = 0, kEpiAccI32 = 1, kEpiF16Tok = 2, kEpiF16Split = 3, kEpiF16Linear = 4 };
+// kEpiBF16: as kEpiF16 with a bfloat16 output.
+enum Epilogue { kEpiF16 = 0, kEpiAccI32 = 1, kEpiF16Tok = 2, kEpiF16Split = 3, kEpiF16Linear = 4, kEpiBF16 = 5 };
 
 // Column split of a GEMM's output: columns [end[i-1], end[i]) (end[-1] = 0)
 // go to y[i], a row-major fp16 matrix of end[i] - end[i-1] columns. Unused

@@ -46,7 +46,7 @@ __device__ __forceinline__ void store_codes(void* q, int64_t row, int64_t K, int
 // segments of kSegChunks chunks along gridDim.y).
 constexpr int kSegChunks = 64 * 32;
 
-template <int CPL, int GS>
+template <int CPL, int GS, bool BF>
 __global__ __launch_bounds__(64 * kWaves) void quant_rows_reg(const uint4* __restrict__ x, int64_t R,
                                                               int64_t K, float qmax, bool pack4,
                                                               void* __restrict__ q,
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(64 * kWaves) void quant_rows_reg(const uint4* __res
     for (int i = 0; i < CPL; ++i) a = max(a, m[i]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) a = max(a, (uint32_t)__shfl_xor((int)a, off));
-    const float amax = half_bits_to_float(a);
+    const float amax = elem_to_float<BF>(a);
     const float sc = amax / qmax;
     if (lane == 0) s[row] = sc;
     const float inv = 1.0f / sc;
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(64 * kWaves) void quant_rows_reg(const uint4* __res
       const int c = c0 + lane + 64 * i;
       if (c < cend) {
         int cq[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (sc != 0.0f) codes_of_chunk(v[i], sc, inv, qmax, cq);
+        if (sc != 0.0f) codes_of_chunk<BF>(v[i], sc, inv, qmax, cq);
         store_codes(q, row, K, c, pack4, cq);
       }
     }
@@ -97,12 +97,12 @@ __global__ __launch_bounds__(64 * kWaves) void quant_rows_reg(const uint4* __res
       for (int off = kCpg / 2; off >= 1; off >>= 1) a = max(a, (uint32_t)__shfl_xor((int)a, off));
       const int c = c0 + lane + 64 * i;
       if (c < cend) {
-        const float amax = half_bits_to_float(a);
+        const float amax = elem_to_float<BF>(a);
         const float sc = amax / qmax;
         if ((lane & (kCpg - 1)) == 0) s[row * G + c / kCpg] = sc;
         const float inv = 1.0f / sc;
         int cq[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (sc != 0.0f) codes_of_chunk(v[i], sc, inv, qmax, cq);
+        if (sc != 0.0f) codes_of_chunk<BF>(v[i], sc, inv, qmax, cq);
         store_codes(q, row, K, c, pack4, cq);
       }
     }
@@ -111,6 +111,7 @@ __global__ __launch_bounds__(64 * kWaves) void quant_rows_reg(const uint4* __res
 
 // Rows longer than the register path holds (per-row scale only): one
 // workgroup per row reads the row twice, first for max|v|, then for codes.
+template <bool BF>
 __global__ __launch_bounds__(256) void quant_rows_two_pass(const uint4* __restrict__ x, int64_t K,
                                                            float qmax, bool pack4, void* __restrict__ q,
                                                            float* __restrict__ s) {
@@ -125,12 +126,12 @@ __global__ __launch_bounds__(256) void quant_rows_two_pass(const uint4* __restri
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
   __syncthreads();
   a = max(max(red[0], red[1]), max(red[2], red[3]));
-  const float sc = half_bits_to_float(a) / qmax;
+  const float sc = elem_to_float<BF>(a) / qmax;
   if (threadIdx.x == 0) s[row] = sc;
   const float inv = 1.0f / sc;
   for (int c = threadIdx.x; c < C; c += 256) {
     int cq[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (sc != 0.0f) codes_of_chunk(xr[c], sc, inv, qmax, cq);
+    if (sc != 0.0f) codes_of_chunk<BF>(xr[c], sc, inv, qmax, cq);
     store_codes(q, row, K, c, pack4, cq);
   }
 }
@@ -147,6 +148,7 @@ __global__ __launch_bounds__(256) void quant_rows_two_pass(const uint4* __restri
 // a 256-bin histogram of the high 8 bits finds each rank's bucket, a 128-bin
 // histogram of the low 7 bits inside it the exact pattern. The group is read
 // three times (two histograms, then the codes); weight quantization is offline.
+template <bool BF>
 __global__ __launch_bounds__(256) void quant_rows_clip(const uint4* __restrict__ x, int64_t K, int n, int G,
                                                        double pfrac, float qmax, bool pack4,
                                                        void* __restrict__ q, float* __restrict__ s) {
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(256) void quant_rows_clip(const uint4* __restrict__
       }
       sel[k] = ((uint32_t)pick[2 * k] << 7) | lo;
     }
-    const double ai = (double)half_bits_to_float(sel[0]), aj = (double)half_bits_to_float(sel[1]);
+    const double ai = (double)elem_to_float<BF>(sel[0]), aj = (double)elem_to_float<BF>(sel[1]);
     double prod = (h - (double)i) * (aj - ai);
     asm("" : "+v"(prod));                 // keep the product and the sum two roundings
     const float t = (float)(ai + prod);
@@ -223,46 +225,35 @@ __global__ __launch_bounds__(256) void quant_rows_clip(const uint4* __restrict__
   const float inv = 1.0f / sc;
   for (int c = threadIdx.x; c < C; c += 256) {
     int cq[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (sc != 0.0f) codes_of_chunk(xg[c], sc, inv, qmax, cq);
+    if (sc != 0.0f) codes_of_chunk<BF>(xg[c], sc, inv, qmax, cq);
     store_codes(q, row, K, g * C + c, pack4, cq);
   }
 }
 
-template <int GS>
+template <int GS, bool BF>
 hipError_t launch_reg(int cpl, int segs, const uint4* x, int64_t R, int64_t K, float qmax, bool pack4,
                       void* q, float* s, hipStream_t st) {
   const dim3 grid((unsigned)((R + kWaves - 1) / kWaves), (unsigned)segs), block(64 * kWaves);
   switch (cpl) {
-    case 1: quant_rows_reg<1, GS><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
-    case 2: quant_rows_reg<2, GS><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
-    case 4: quant_rows_reg<4, GS><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
-    case 8: quant_rows_reg<8, GS><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
-    case 16: quant_rows_reg<16, GS><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
-    default: quant_rows_reg<32, GS><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
+    case 1: quant_rows_reg<1, GS, BF><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
+    case 2: quant_rows_reg<2, GS, BF><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
+    case 4: quant_rows_reg<4, GS, BF><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
+    case 8: quant_rows_reg<8, GS, BF><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
+    case 16: quant_rows_reg<16, GS, BF><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
+    default: quant_rows_reg<32, GS, BF><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
   }
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_quant_rows_clip(const void* x, int64_t R, int64_t K, int group_size, int qmax,
-                                  double percentile, void* q, float* s, hipStream_t stream) {
-  const int n = group_size ? group_size : (int)K;
-  const int G = (int)(K / n);
-  quant_rows_clip<<<dim3((unsigned)(R * G)), dim3(256), 0, stream>>>(static_cast<const uint4*>(x), K, n, G,
-                                                                    percentile / 100.0, (float)qmax, qmax == 7,
-                                                                    q, s);
-  return hipGetLastError();
-}
-
-hipError_t launch_quant_rows(const void* x, int64_t R, int64_t K, int group_size, int qmax, void* q,
-                             float* s, hipStream_t stream) {
+template <bool BF>
+hipError_t launch_quant_t(const void* x, int64_t R, int64_t K, int group_size, int qmax, void* q, float* s,
+                          hipStream_t stream) {
   const uint4* xv = static_cast<const uint4*>(x);
   const bool pack4 = qmax == 7;
   const float fq = (float)qmax;
   const int64_t C = K / 8;
   if (group_size == 0 && C > kSegChunks) {
-    quant_rows_two_pass<<<dim3((unsigned)R), dim3(256), 0, stream>>>(xv, K, fq, pack4, q, s);
+    quant_rows_two_pass<BF><<<dim3((unsigned)R), dim3(256), 0, stream>>>(xv, K, fq, pack4, q, s);
     return hipGetLastError();
   }
   const int64_t segs = (C + kSegChunks - 1) / kSegChunks;
@@ -270,10 +261,31 @@ hipError_t launch_quant_rows(const void* x, int64_t R, int64_t K, int group_size
   int cpl = 1;
   while (64 * cpl < per_seg) cpl *= 2;
   switch (group_size) {
-    case 0: return launch_reg<0>(cpl, 1, xv, R, K, fq, pack4, q, s, stream);
-    case 64: return launch_reg<64>(cpl, (int)segs, xv, R, K, fq, pack4, q, s, stream);
-    default: return launch_reg<128>(cpl, (int)segs, xv, R, K, fq, pack4, q, s, stream);
+    case 0: return launch_reg<0, BF>(cpl, 1, xv, R, K, fq, pack4, q, s, stream);
+    case 64: return launch_reg<64, BF>(cpl, (int)segs, xv, R, K, fq, pack4, q, s, stream);
+    default: return launch_reg<128, BF>(cpl, (int)segs, xv, R, K, fq, pack4, q, s, stream);
   }
+}
+
+}  // namespace
+
+hipError_t launch_quant_rows_clip(const void* x, int64_t R, int64_t K, int group_size, int qmax,
+                                  double percentile, void* q, float* s, hipStream_t stream, bool bf16) {
+  const int n = group_size ? group_size : (int)K;
+  const int G = (int)(K / n);
+  const dim3 grid((unsigned)(R * G)), block(256);
+  const uint4* xv = static_cast<const uint4*>(x);
+  if (bf16)
+    quant_rows_clip<true><<<grid, block, 0, stream>>>(xv, K, n, G, percentile / 100.0, (float)qmax, qmax == 7, q, s);
+  else
+    quant_rows_clip<false><<<grid, block, 0, stream>>>(xv, K, n, G, percentile / 100.0, (float)qmax, qmax == 7, q, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows(const void* x, int64_t R, int64_t K, int group_size, int qmax, void* q,
+                             float* s, hipStream_t stream, bool bf16) {
+  return bf16 ? launch_quant_t<true>(x, R, K, group_size, qmax, q, s, stream)
+              : launch_quant_t<false>(x, R, K, group_size, qmax, q, s, stream);
 }
 
 }  // namespace cider

@@ -20,8 +20,8 @@ namespace cider {
 
 constexpr float kNearHalf = 0.4998779296875f;   // 0.5 - 2^-13
 
-// max |v| of 8 fp16 values as a 15-bit pattern: fp16 magnitudes compare like
-// their bit patterns (finite inputs).
+// max |v| of 8 fp16 (or bf16) values as a 15-bit pattern: the magnitudes of
+// both formats compare like their bit patterns (finite inputs).
 __device__ __forceinline__ uint32_t abs_max_bits(uint4 v) {
   uint32_t m = 0;
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -37,6 +37,14 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
   return (float)__builtin_bit_cast(_Float16, (unsigned short)bits);
 }
 
+// The fp32 value of a 16-bit element (low 16 bits of `bits`): fp16, or bf16
+// (the top half of an fp32 pattern). Exact either way.
+template <bool BF>
+__device__ __forceinline__ float elem_to_float(uint32_t bits) {
+  if constexpr (BF) return __builtin_bit_cast(float, (bits & 0xFFFFu) << 16);
+  else return half_bits_to_float(bits & 0xFFFFu);
+}
+
 // Code of one element given the group scale s (> 0) and inv = fl(1/s).
 __device__ __forceinline__ int code_of(float v, float s, float inv, float qmax) {
   const float r = v * inv;
@@ -46,13 +54,14 @@ __device__ __forceinline__ int code_of(float v, float s, float inv, float qmax) 
   return (int)t;
 }
 
-// 8 codes of one 16-byte chunk (8 fp16 values).
+// 8 codes of one 16-byte chunk (8 fp16, or bf16 when BF, values).
+template <bool BF = false>
 __device__ __forceinline__ void codes_of_chunk(uint4 v, float s, float inv, float qmax, int q[8]) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    q[2 * i] = code_of(half_bits_to_float(w[i] & 0xFFFFu), s, inv, qmax);
-    q[2 * i + 1] = code_of(half_bits_to_float(w[i] >> 16), s, inv, qmax);
+    q[2 * i] = code_of(elem_to_float<BF>(w[i]), s, inv, qmax);
+    q[2 * i + 1] = code_of(elem_to_float<BF>(w[i] >> 16), s, inv, qmax);
   }
 }
 
