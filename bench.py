@@ -34,15 +34,18 @@ sys.path.insert(0, ROOT)
 PEAK_INT8_TOPS = 5000.0        # MI355X dense INT8 MFMA, TOP/s
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PAGES_M5PRO_TOPS = 2 * 4096 * 10240 * 2560 / 4.41e-3 / 1e12   # README table: 4.41 ms on Apple M5 Pro
-KERNEL_SOURCES = ["cider_api.hip", "cider_quant.hip", "cider_gemm.hip", "cider_internal.h"]
+CSRC = os.path.join(ROOT, "w8a8_online_quantized_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_w8a8_gemm_m4096_n10240_k2560.json")
 
 
 def kernel_source_sha() -> str:
+    """Hash of every source the library is built from (csrc/*.hip, *.h)."""
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "w8a8_online_quantized_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
     return h.hexdigest()[:16]
 
 
