@@ -129,16 +129,19 @@ def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_byte
         sa = torch.empty((M,) if ags == 0 else (M, K // ags), dtype=torch.float32, device=dev)
         y = torch.empty((M, N), dtype=torch.float16, device=dev)
         sets.append((x, xq, sa, wq0.clone(), sw0.clone(), y))
+    # split-K workspace (scratch shared by the sets; calls run in stream order)
+    ws_bytes = 0 if mode == "w8a8_tokpg" else cider.cider_gemm_workspace_size(M, N, K, bits, gs)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
     def gemm(xq, sa, wq, sw, y):
         if mode == "w4a8":
-            cider.cider_w4a8_gemm(xq, sa, wq, sw, y, stream=stream)
+            cider.cider_w4a8_gemm(xq, sa, wq, sw, y, stream=stream, workspace=ws)
         elif mode == "w8a8_tokpg":
             cider.cider_w8a8_gemm_token_group(xq, sa, wq, sw, gs, y, stream=stream)
         else:
-            cider.cider_w8a8_gemm(xq, sa, wq, sw, gs, y, stream=stream)
+            cider.cider_w8a8_gemm(xq, sa, wq, sw, gs, y, stream=stream, workspace=ws)
 
     def timed(body):
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -165,7 +168,7 @@ def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_byte
     del sets
     torch.cuda.empty_cache()
     return {"ms_per_step": step_ms, "quant_ms": q_ms, "gemm_ms": g_ms, "ops": ops,
-            "gemm_bytes": gemm_bytes, "quant_bytes": quant_bytes, "sets": R}
+            "gemm_bytes": gemm_bytes, "quant_bytes": quant_bytes, "sets": R, "split_k_ws": ws_bytes}
 
 
 def measure_mv(cider, torch, x_h, w_h, M, N, K, gs, steps, warmup, R, ops, nbytes, mode="int8_mv"):
@@ -353,7 +356,8 @@ def main():
                          "gemm_us": round(rr["gemm_ms"] * 1e3, 2), "quant_us": round(rr["quant_ms"] * 1e3, 2),
                          "gemm_roofline": roofline_of(rr["ops"], rr["gemm_bytes"], rr["gemm_ms"]),
                          "quant_GBs": round(rr["quant_bytes"] / (rr["quant_ms"] * 1e-3) / 1e9, 1) if rr["quant_ms"] else None,
-                         "linear_TOPs": round(rr["ops"] / (rr["ms_per_step"] * 1e-3) / 1e12, 2)})
+                         "linear_TOPs": round(rr["ops"] / (rr["ms_per_step"] * 1e-3) / 1e12, 2),
+                         "split_k": bool(rr.get("split_k_ws"))})
             print(json.dumps({"sweep_row": rows[-1]}), file=sys.stderr, flush=True)
         out["sweep"] = rows
     if args.stack:

@@ -155,6 +155,27 @@ cider_status_t cider_w8a8_gemm_dt(const int8_t* x_q, const float* x_scale, const
 cider_status_t cider_w4a8_gemm(const int8_t* x_q, const float* x_scale, const uint8_t* w_packed,
                                const float* w_scale, int64_t M, int64_t N, int64_t K,
                                void* y_f16, void* stream);
+/* Split-K for medium M with long K (too few output tiles to fill the GPU):
+ * the _ex GEMMs take a caller workspace and, where the dispatch's plan says
+ * so, cut K into ranges whose exact int32 partial sums go to the workspace
+ * as [splits][M][N] slabs before a second kernel adds them (in split order:
+ * integer sums, so y is bit-identical to the unsplit GEMM) and dequantizes.
+ *   cider_gemm_workspace_size: the bytes the plan needs at this shape, 0 when
+ *   it does not split (bits 8 or 4; per-channel only: per-group gives 0),
+ *   -1 for invalid sizes. The library never allocates.
+ *   workspace may be NULL (no split); otherwise 16-byte aligned with at
+ *   least the queried bytes, else CIDER_ERROR_INVALID_VALUE. Its contents are
+ *   scratch; calls that share one workspace must not overlap in time.
+ * Everything else as for cider_w8a8_gemm_dt / cider_w4a8_gemm_dt. */
+int64_t cider_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t bits, int32_t group_size);
+cider_status_t cider_w8a8_gemm_ex(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
+                                  const float* w_scale, int64_t M, int64_t N, int64_t K,
+                                  int32_t group_size, void* y, int32_t y_dtype, void* workspace,
+                                  int64_t workspace_bytes, void* stream);
+cider_status_t cider_w4a8_gemm_ex(const int8_t* x_q, const float* x_scale, const uint8_t* w_packed,
+                                  const float* w_scale, int64_t M, int64_t N, int64_t K, void* y,
+                                  int32_t y_dtype, void* workspace, int64_t workspace_bytes, void* stream);
+
 /* The same with the output type chosen by y_dtype (a cider_dtype_t). */
 cider_status_t cider_w4a8_gemm_dt(const int8_t* x_q, const float* x_scale, const uint8_t* w_packed,
                                   const float* w_scale, int64_t M, int64_t N, int64_t K, void* y,
@@ -171,13 +192,14 @@ cider_status_t cider_w4a8_gemm_dt(const int8_t* x_q, const float* x_scale, const
  *   ONE kernel launch that quantizes the activations itself and needs no
  *   workspace. Otherwise the codes and
  *   scales go through `workspace` (device, 16-byte aligned, at least
- *   cider_linear_workspace_size(M, K, bits, group_size) bytes; its contents
- *   after the call are the activation codes [M, K] at offset 0 and the scales
- *   at the next 256-byte boundary).
+ *   cider_linear_workspace_size(M, N, K, bits, group_size) bytes; its
+ *   contents after the call are the activation codes [M, K] at offset 0 and
+ *   the scales at the next 256-byte boundary, then the GEMM's split-K slabs
+ *   when its shape uses them, see cider_gemm_workspace_size).
  * Sizes, alignment and errors as for cider_quant_act / cider_w8a8_gemm;
  * `workspace` may be NULL when the size query returns 0.
  */
-int64_t cider_linear_workspace_size(int64_t M, int64_t K, int32_t bits, int32_t group_size);
+int64_t cider_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t bits, int32_t group_size);
 cider_status_t cider_linear(const void* x_f16, const void* w, const float* w_scale, int64_t M, int64_t N,
                             int64_t K, int32_t bits, int32_t group_size, void* workspace,
                             int64_t workspace_bytes, void* y_f16, void* stream);

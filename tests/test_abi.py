@@ -140,14 +140,16 @@ def test_split_rejects():
 
 def test_linear_workspace_query_and_rejects():
     q = L.cider_linear_workspace_size
-    assert q(1, 2560, 8, 0) == 0 and q(2, 32768, 8, 0) == 0 and q(2, 2560, 4, 0) == 0   # one launch
-    assert q(2, 32768 + 256, 8, 0) == 2 * 33024 + 256                     # codes past the 64 KiB staging
-    assert q(3, 2560, 8, 0) == 3 * 2560 + 256                             # M = 3: separate quantization
-    assert q(5, 1024, 8, 0) == 5 * 1024 + 256
-    assert q(5, 1024, 8, 128) == 5 * 1024 + 256                           # 40 scale bytes
-    assert q(300, 1024, 8, 64) == 300 * 1024 + (4 * 300 * 16 + 255) // 256 * 256
-    assert q(0, 1024, 8, 0) == 0
-    assert q(4, 1024, 6, 0) == -1 and q(4, 1024, 4, 64) == -1 and q(4, 48, 4, 0) == -1 and q(-1, 64, 8, 0) == -1
+    assert q(1, 64, 2560, 8, 0) == 0 and q(2, 64, 32768, 8, 0) == 0 and q(2, 64, 2560, 4, 0) == 0   # one launch
+    assert q(2, 64, 32768 + 256, 8, 0) == 2 * 33024 + 256                 # codes past the 64 KiB staging
+    assert q(3, 64, 2560, 8, 0) == 3 * 2560 + 256                         # M = 3: separate quantization
+    assert q(5, 64, 1024, 8, 0) == 5 * 1024 + 256
+    assert q(5, 64, 1024, 8, 128) == 5 * 1024 + 256                       # 40 scale bytes
+    assert q(300, 64, 1024, 8, 64) == 300 * 1024 + (4 * 300 * 16 + 255) // 256 * 256
+    assert q(0, 64, 1024, 8, 0) == 0
+    assert q(128, 2560, 10240, 8, 0) == 128 * 10240 + 512 + 8 * 128 * 2560 * 4   # + split-K slabs
+    assert q(4, 64, 1024, 6, 0) == -1 and q(4, 64, 1024, 4, 64) == -1 and q(4, 64, 48, 4, 0) == -1
+    assert q(-1, 64, 64, 8, 0) == -1
     lin = L.cider_linear
     assert lin(P, P, P, 4, 8, 1024, 6, 0, NULL, 0, P, NULL) == INV        # bits
     assert lin(P, P, P, 4, 8, 40, 8, 0, NULL, 0, P, NULL) == INV          # K % 16
@@ -188,6 +190,27 @@ def test_dtype_entries_reject():
     assert L.cider_w4a8_gemm_dt(P, P, P, P, 4, 4, 64, P, 7, NULL) == INV
     assert L.cider_w4a8_gemm_dt(P, P, P, P, 4, 4, 48, P, 1, NULL) == INV
     assert L.cider_w4a8_gemm_dt(NULL, NULL, NULL, NULL, 4, 0, 64, NULL, 1, NULL) == 0
+
+
+def test_split_k_workspace_plan():
+    g = L.cider_gemm_workspace_size
+    assert g(128, 2560, 10240, 8, 0) == 8 * 128 * 2560 * 4        # 64x160 tiles, 8 K ranges
+    assert g(1024, 2560, 10240, 8, 0) == 4 * 1024 * 2560 * 4      # 128x320 tiles, 4 K ranges
+    assert g(128, 2560, 10240, 4, 0) == 8 * 128 * 2560 * 4        # W4A8: 128x128 tiles, 8 ranges
+    assert g(4096, 10240, 2560, 8, 0) == 0                        # enough tiles: no split
+    assert g(128, 10240, 2560, 8, 0) == 0                         # short K
+    assert g(128, 2560, 10240, 8, 128) == 0                       # per-group: no split
+    assert g(16, 2560, 10240, 8, 0) == 0                          # skinny path
+    assert g(0, 2560, 10240, 8, 0) == 0
+    assert g(4, 4, 40, 8, 0) == -1 and g(4, 4, 64, 4, 64) == -1 and g(4, 4, 64, 6, 0) == -1
+    ex = L.cider_w8a8_gemm_ex
+    assert ex(P, P, P, P, 128, 2560, 10240, 0, P, 0, P, 1024, NULL) == INV     # workspace too small
+    assert ex(P, P, P, P, 128, 2560, 10240, 0, P, 0, MIS, 1 << 30, NULL) == INV
+    assert ex(P, P, P, P, 128, 2560, 10240, 0, P, 3, NULL, 0, NULL) == INV     # dtype
+    assert ex(NULL, NULL, NULL, NULL, 0, 2560, 10240, 0, NULL, 0, NULL, 0, NULL) == 0
+    ex4 = L.cider_w4a8_gemm_ex
+    assert ex4(P, P, P, P, 128, 2560, 10240, P, 0, P, 1024, NULL) == INV
+    assert ex4(P, P, P, P, 128, 2560, 10240, P, 0, MIS, 1 << 30, NULL) == INV
 
 
 def test_not_available_without_gpu():

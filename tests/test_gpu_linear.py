@@ -32,7 +32,7 @@ def _two_calls(c, xd, wq, sw, bits, gs):
 @pytest.mark.parametrize("M,N,K", ONE_LAUNCH)
 def test_one_launch_linear(M, N, K, bits):
     c = cider()
-    assert c.cider_linear_workspace_size(M, K, bits, 0) == 0
+    assert c.cider_linear_workspace_size(M, N, K, bits, 0) == 0
     x = inputs.activations(M, K, seed=41)
     w = inputs.weights(N, K, seed=41)
     xd = dev(x)
@@ -49,7 +49,7 @@ def test_one_launch_linear(M, N, K, bits):
                                            (1024, 2560, 10240, 8, 128)])
 def test_workspace_linear(M, N, K, bits, gs):
     c = cider()
-    need = c.cider_linear_workspace_size(M, K, bits, gs)
+    need = c.cider_linear_workspace_size(M, N, K, bits, gs)
     assert need >= M * K
     x = inputs.activations(M, K, seed=42)
     w = inputs.weights(N, K, seed=42)

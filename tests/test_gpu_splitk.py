@@ -1,0 +1,86 @@
+"""Split-K (cider_w8a8_gemm_ex / cider_w4a8_gemm_ex with a workspace) for
+medium M with long K: outputs bit-identical to the unsplit GEMM (the int32
+partial sums are exact) and within the per-channel bar of the oracle on
+sampled rows; ragged N takes the scalar reduction; bf16 output and W4A8 too;
+a workspace reused by a second, smaller call stays correct.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from w8a8_online_quantized_amd import inputs
+from tests.test_gpu_parity import assert_y_close, cider, dev, host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+SHAPES = [(128, 2560, 10240), (256, 2560, 10240), (1024, 2560, 10240), (300, 650, 8192), (130, 2048, 6144),
+          (64, 4096, 16384)]
+
+
+def _ws(c, M, N, K, bits=8):
+    need = c.cider_gemm_workspace_size(M, N, K, bits, 0)
+    assert need > 0, f"{M}x{N}x{K} was expected to split"
+    return torch.empty(need, dtype=torch.uint8, device="cuda")
+
+
+def _rows(M):
+    return np.arange(M) if M <= 300 else np.unique(np.r_[0, M - 1, np.random.default_rng(M).integers(0, M, 24)])
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_split_k_bit_identical_and_oracle(M, N, K):
+    c = cider()
+    x = inputs.activations(M, K, seed=61)
+    w = inputs.weights(N, K, seed=61)
+    wq, sw = c.cider_quant_weight(dev(w), 8, 0)
+    xq, sa = c.cider_quant_act(dev(x), 0)
+    y0 = host(c.cider_w8a8_gemm(xq, sa, wq, sw, 0))
+    y1 = host(c.cider_w8a8_gemm(xq, sa, wq, sw, 0, workspace=_ws(c, M, N, K)))
+    assert np.array_equal(y0.view(np.uint16), y1.view(np.uint16))
+    rows = _rows(M)
+    wqo, swo = oracle.quantize_weight(w, 8, 0)
+    yo, _, _ = oracle.w8a8_linear(x[rows], wqo, swo, 0)
+    assert_y_close(y1[rows], yo, 1e-3, max_ulp=1, what=f"split-K {M}x{N}x{K}")
+
+
+def test_split_k_bf16_and_w4a8():
+    c = cider()
+    M, N, K = 128, 2560, 10240
+    x = inputs.activations(M, K, seed=62)
+    w = inputs.weights(N, K, seed=62)
+    xq, sa = c.cider_quant_act(dev(x), 0)
+    wq, sw = c.cider_quant_weight(dev(w), 8, 0)
+    b0 = c.cider_w8a8_gemm(xq, sa, wq, sw, 0, out_dtype=torch.bfloat16)
+    b1 = c.cider_w8a8_gemm(xq, sa, wq, sw, 0, out_dtype=torch.bfloat16, workspace=_ws(c, M, N, K))
+    torch.cuda.synchronize()
+    assert torch.equal(b0.view(torch.int16), b1.view(torch.int16))
+    wp, sw4 = c.cider_quant_weight(dev(w), 4, 0)
+    y0 = host(c.cider_w4a8_gemm(xq, sa, wp, sw4))
+    y1 = host(c.cider_w4a8_gemm(xq, sa, wp, sw4, workspace=_ws(c, M, N, K, bits=4)))
+    assert np.array_equal(y0.view(np.uint16), y1.view(np.uint16))
+    wpo, swo = oracle.quantize_weight(w, 4, 0)
+    yo, _, _ = oracle.w4a8_linear(x, wpo, swo)
+    assert_y_close(y1, yo, 1e-3, max_ulp=1, what="split-K W4A8")
+
+
+def test_split_k_workspace_reuse_and_linear():
+    c = cider()
+    big = (1024, 2560, 10240)
+    small = (130, 2048, 6144)
+    ws = _ws(c, *big)
+    assert ws.numel() >= c.cider_gemm_workspace_size(*small, 8, 0)
+    for (M, N, K) in (big, small):
+        x = inputs.activations(M, K, seed=63)
+        w = inputs.weights(N, K, seed=63)
+        xq, sa = c.cider_quant_act(dev(x), 0)
+        wq, sw = c.cider_quant_weight(dev(w), 8, 0)
+        y0 = host(c.cider_w8a8_gemm(xq, sa, wq, sw, 0))
+        y1 = host(c.cider_w8a8_gemm(xq, sa, wq, sw, 0, workspace=ws))
+        assert np.array_equal(y0.view(np.uint16), y1.view(np.uint16)), (M, N, K)
+        # the one-call linear sizes and uses the same slabs after its codes
+        need = c.cider_linear_workspace_size(M, N, K, 8, 0)
+        assert need > M * K
+        y2 = host(c.cider_linear(dev(x), wq, sw, 8, 0))
+        assert np.array_equal(y0.view(np.uint16), y2.view(np.uint16)), (M, N, K)

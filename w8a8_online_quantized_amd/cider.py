@@ -36,7 +36,12 @@ SIGNATURES = {
     "cider_w8a8_gemm_token_group": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p,
                                                    _c_p]),
     "cider_w8a8_gemm_split": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_p, _c_p, _c_p]),
-    "cider_linear_workspace_size": (ctypes.c_int64, [_c_i64, _c_i64, _c_i32, _c_i32]),
+    "cider_linear_workspace_size": (ctypes.c_int64, [_c_i64, _c_i64, _c_i64, _c_i32, _c_i32]),
+    "cider_gemm_workspace_size": (ctypes.c_int64, [_c_i64, _c_i64, _c_i64, _c_i32, _c_i32]),
+    "cider_w8a8_gemm_ex": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_i32, _c_p,
+                                         _c_i64, _c_p]),
+    "cider_w4a8_gemm_ex": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_i32, _c_p, _c_i64,
+                                         _c_p]),
     "cider_linear": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_p, _c_i64, _c_p,
                                     _c_p]),
     "cider_quant_weight_clip": (ctypes.c_int, [_c_p, _c_i32, _c_i64, _c_i64, _c_i32, _c_i32, ctypes.c_double, _c_p,
@@ -205,9 +210,25 @@ def cider_quant_weight_clip(w, bits: int = 8, group_size: int = 0, percentile: f
     return w_q, w_scale
 
 
-def cider_w8a8_gemm(x_q, x_scale, w_q, w_scale, group_size: int = 0, y=None, stream=None, out_dtype=None):
+def cider_gemm_workspace_size(M: int, N: int, K: int, bits: int = 8, group_size: int = 0) -> int:
+    """Split-K workspace bytes the GEMM dispatch uses at this shape (0: none)."""
+    n = int(lib().cider_gemm_workspace_size(M, N, K, bits, group_size))
+    if n < 0:
+        raise ValueError("invalid GEMM sizes")
+    return n
+
+
+def _ws_args(workspace):
+    if workspace is None:
+        return None, 0
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
+def cider_w8a8_gemm(x_q, x_scale, w_q, w_scale, group_size: int = 0, y=None, stream=None, out_dtype=None,
+                    workspace=None):
     """int8 codes + scales -> y [M, N] (fused dequant): fp16, or bf16 when
-    out_dtype (or a given y) is bfloat16."""
+    out_dtype (or a given y) is bfloat16. A workspace of at least
+    cider_gemm_workspace_size bytes enables split-K where the plan uses it."""
     import torch
     M, K = x_q.shape
     N = w_q.shape[0]
@@ -221,8 +242,10 @@ def cider_w8a8_gemm(x_q, x_scale, w_q, w_scale, group_size: int = 0, y=None, str
         y = torch.empty((M, N), dtype=out_dtype or torch.float16, device=x_q.device)
     dt = _fp_code(y, "y")
     _need(y, y.dtype, (M, N), "y")
-    _check("cider_w8a8_gemm_dt", lib().cider_w8a8_gemm_dt(_ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale),
-                                                          M, N, K, group_size, _ptr(y), dt, _stream(stream)))
+    wsp, wsb = _ws_args(workspace)
+    _check("cider_w8a8_gemm_ex", lib().cider_w8a8_gemm_ex(_ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale),
+                                                          M, N, K, group_size, _ptr(y), dt, wsp, wsb,
+                                                          _stream(stream)))
     return y
 
 
@@ -273,9 +296,9 @@ def cider_w8a8_gemm_split(x_q, x_scale, w_q, w_scale, part_n, ys=None, stream=No
     return ys
 
 
-def cider_linear_workspace_size(M: int, K: int, bits: int = 8, group_size: int = 0) -> int:
+def cider_linear_workspace_size(M: int, N: int, K: int, bits: int = 8, group_size: int = 0) -> int:
     """Workspace bytes cider_linear needs (0: one launch, no workspace)."""
-    n = int(lib().cider_linear_workspace_size(M, K, bits, group_size))
+    n = int(lib().cider_linear_workspace_size(M, N, K, bits, group_size))
     if n < 0:
         raise ValueError("invalid linear sizes")
     return n
@@ -293,7 +316,7 @@ def cider_linear(x, w, w_scale, bits: int = 8, group_size: int = 0, workspace=No
     else:
         _need(w, torch.uint8, (N, K // 2), "w")
     _need(w_scale, torch.float32, _scale_shape(N, K, group_size), "w_scale")
-    need = cider_linear_workspace_size(M, K, bits, group_size)
+    need = cider_linear_workspace_size(M, N, K, bits, group_size)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     if y is None:
@@ -325,7 +348,7 @@ def cider_int8_mv(x, w_q, w_scale, group_size: int = 0, y=None, stream=None):
     return y
 
 
-def cider_w4a8_gemm(x_q, x_scale, w_packed, w_scale, y=None, stream=None, out_dtype=None):
+def cider_w4a8_gemm(x_q, x_scale, w_packed, w_scale, y=None, stream=None, out_dtype=None, workspace=None):
     """int8 activation codes x packed int4 weights -> y [M, N] (fp16 or bf16)."""
     import torch
     M, K = x_q.shape
@@ -338,8 +361,9 @@ def cider_w4a8_gemm(x_q, x_scale, w_packed, w_scale, y=None, stream=None, out_dt
         y = torch.empty((M, N), dtype=out_dtype or torch.float16, device=x_q.device)
     dt = _fp_code(y, "y")
     _need(y, y.dtype, (M, N), "y")
-    _check("cider_w4a8_gemm_dt", lib().cider_w4a8_gemm_dt(_ptr(x_q), _ptr(x_scale), _ptr(w_packed), _ptr(w_scale),
-                                                          M, N, K, _ptr(y), dt, _stream(stream)))
+    wsp, wsb = _ws_args(workspace)
+    _check("cider_w4a8_gemm_ex", lib().cider_w4a8_gemm_ex(_ptr(x_q), _ptr(x_scale), _ptr(w_packed), _ptr(w_scale),
+                                                          M, N, K, _ptr(y), dt, wsp, wsb, _stream(stream)))
     return y
 
 

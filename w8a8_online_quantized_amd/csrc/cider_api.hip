@@ -160,9 +160,30 @@ cider_status_t cider_w8a8_gemm(const int8_t* x_q, const float* x_scale, const in
   return cider_w8a8_gemm_dt(x_q, x_scale, w_q, w_scale, M, N, K, group_size, y_f16, CIDER_DTYPE_F16, stream);
 }
 
+int64_t cider_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t bits, int32_t group_size) {
+  if (!gemm_sizes_ok(M, N) || !valid_gs(group_size) || (bits != 8 && bits != 4)) return -1;
+  if (bits == 4 && (group_size != 0 || !valid_k(K, 32, 0))) return -1;
+  if (bits == 8 && !valid_k(K, 16, group_size)) return -1;
+  if (M == 0 || N == 0) return 0;
+  return cider::gemm_split_workspace_bytes(M, N, K, bits == 4 ? cider::kWeightI4 : cider::kWeightI8, group_size);
+}
+
+// A caller workspace, when given, must hold the size query's bytes.
+static bool workspace_ok(const void* ws, int64_t ws_bytes, int64_t need) {
+  if (!ws) return true;
+  return aligned16(ws) && ws_bytes >= need;
+}
+
 cider_status_t cider_w8a8_gemm_dt(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
                                   const float* w_scale, int64_t M, int64_t N, int64_t K, int32_t group_size,
                                   void* y_f16, int32_t y_dtype, void* stream) {
+  return cider_w8a8_gemm_ex(x_q, x_scale, w_q, w_scale, M, N, K, group_size, y_f16, y_dtype, nullptr, 0, stream);
+}
+
+cider_status_t cider_w8a8_gemm_ex(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
+                                  const float* w_scale, int64_t M, int64_t N, int64_t K, int32_t group_size,
+                                  void* y_f16, int32_t y_dtype, void* workspace, int64_t workspace_bytes,
+                                  void* stream) {
   if (!valid_dtype(y_dtype)) return CIDER_ERROR_INVALID_VALUE;
   if (!gemm_sizes_ok(M, N) || !valid_gs(group_size) || !valid_k(K, 16, group_size))
     return CIDER_ERROR_INVALID_VALUE;
@@ -170,7 +191,11 @@ cider_status_t cider_w8a8_gemm_dt(const int8_t* x_q, const float* x_scale, const
   if (!x_q || !x_scale || !w_q || !w_scale || !y_f16) return CIDER_ERROR_INVALID_VALUE;
   if (!aligned16(x_q) || !aligned16(x_scale) || !aligned16(w_q) || !aligned16(w_scale) || !aligned16(y_f16))
     return CIDER_ERROR_INVALID_VALUE;
+  if (!workspace_ok(workspace, workspace_bytes, cider_gemm_workspace_size(M, N, K, 8, group_size)))
+    return CIDER_ERROR_INVALID_VALUE;
   cider::GemmArgs g{x_q, x_scale, w_q, w_scale, M, N, K, group_size, y_f16, nullptr};
+  g.ws = workspace;
+  g.ws_bytes = workspace ? workspace_bytes : 0;
   return gemm_common(g, cider::kWeightI8, y_dtype == CIDER_DTYPE_BF16 ? cider::kEpiBF16 : cider::kEpiF16, stream);
 }
 
@@ -183,6 +208,12 @@ cider_status_t cider_w4a8_gemm(const int8_t* x_q, const float* x_scale, const ui
 cider_status_t cider_w4a8_gemm_dt(const int8_t* x_q, const float* x_scale, const uint8_t* w_packed,
                                   const float* w_scale, int64_t M, int64_t N, int64_t K, void* y_f16,
                                   int32_t y_dtype, void* stream) {
+  return cider_w4a8_gemm_ex(x_q, x_scale, w_packed, w_scale, M, N, K, y_f16, y_dtype, nullptr, 0, stream);
+}
+
+cider_status_t cider_w4a8_gemm_ex(const int8_t* x_q, const float* x_scale, const uint8_t* w_packed,
+                                  const float* w_scale, int64_t M, int64_t N, int64_t K, void* y_f16,
+                                  int32_t y_dtype, void* workspace, int64_t workspace_bytes, void* stream) {
   if (!valid_dtype(y_dtype)) return CIDER_ERROR_INVALID_VALUE;
   if (!gemm_sizes_ok(M, N) || !valid_k(K, 32, 0)) return CIDER_ERROR_INVALID_VALUE;
   if (M == 0 || N == 0) return CIDER_SUCCESS;
@@ -190,7 +221,11 @@ cider_status_t cider_w4a8_gemm_dt(const int8_t* x_q, const float* x_scale, const
   if (!aligned16(x_q) || !aligned16(x_scale) || !aligned16(w_packed) || !aligned16(w_scale) ||
       !aligned16(y_f16))
     return CIDER_ERROR_INVALID_VALUE;
+  if (!workspace_ok(workspace, workspace_bytes, cider_gemm_workspace_size(M, N, K, 4, 0)))
+    return CIDER_ERROR_INVALID_VALUE;
   cider::GemmArgs g{x_q, x_scale, w_packed, w_scale, M, N, K, 0, y_f16, nullptr};
+  g.ws = workspace;
+  g.ws_bytes = workspace ? workspace_bytes : 0;
   return gemm_common(g, cider::kWeightI4, y_dtype == CIDER_DTYPE_BF16 ? cider::kEpiBF16 : cider::kEpiF16, stream);
 }
 
@@ -235,20 +270,26 @@ cider_status_t cider_w8a8_gemm_split(const int8_t* x_q, const float* x_scale, co
   return gemm_common(g, cider::kWeightI8, cider::kEpiF16Split, stream);
 }
 
-int64_t cider_linear_workspace_size(int64_t M, int64_t K, int32_t bits, int32_t group_size) {
-  if (M < 0 || !valid_gs(group_size) || (bits != 8 && bits != 4)) return -1;
-  if (bits == 4 && group_size != 0) return -1;
-  if (!valid_k(K, bits == 4 ? 32 : 16, group_size)) return -1;
-  if (M == 0 || cider::linear_is_one_launch(M, K, group_size)) return 0;
+// The one-call linear's workspace: the activation codes and scales (each
+// 256-byte aligned), then room for the GEMM's split-K slabs.
+static int64_t linear_quant_bytes(int64_t M, int64_t K, int32_t group_size) {
   const int64_t G = group_size ? K / group_size : 1;
   return (M * K + 255) / 256 * 256 + (4 * M * G + 255) / 256 * 256;
+}
+
+int64_t cider_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t bits, int32_t group_size) {
+  if (!gemm_sizes_ok(M, N) || !valid_gs(group_size) || (bits != 8 && bits != 4)) return -1;
+  if (bits == 4 && group_size != 0) return -1;
+  if (!valid_k(K, bits == 4 ? 32 : 16, group_size)) return -1;
+  if (M == 0 || N == 0 || cider::linear_is_one_launch(M, K, group_size)) return 0;
+  return linear_quant_bytes(M, K, group_size) + cider_gemm_workspace_size(M, N, K, bits, group_size);
 }
 
 cider_status_t cider_linear(const void* x_f16, const void* w, const float* w_scale, int64_t M, int64_t N,
                             int64_t K, int32_t bits, int32_t group_size, void* workspace,
                             int64_t workspace_bytes, void* y_f16, void* stream) {
-  const int64_t need = cider_linear_workspace_size(M, K, bits, group_size);
-  if (need < 0 || !gemm_sizes_ok(M, N)) return CIDER_ERROR_INVALID_VALUE;
+  const int64_t need = cider_linear_workspace_size(M, N, K, bits, group_size);
+  if (need < 0) return CIDER_ERROR_INVALID_VALUE;
   if (M == 0 || N == 0) return CIDER_SUCCESS;
   if (!x_f16 || !w || !w_scale || !y_f16) return CIDER_ERROR_INVALID_VALUE;
   if (!aligned16(x_f16) || !aligned16(w) || !aligned16(w_scale) || !aligned16(y_f16)) return CIDER_ERROR_INVALID_VALUE;
@@ -265,6 +306,11 @@ cider_status_t cider_linear(const void* x_f16, const void* w, const float* w_sca
   hipError_t e = cider::launch_quant_rows(x_f16, M, K, group_size, 127, xq, sa, st);
   if (e != hipSuccess) return from_hip(e);
   cider::GemmArgs g{xq, sa, w, w_scale, M, N, K, group_size, y_f16, nullptr};
+  const int64_t qb = linear_quant_bytes(M, K, group_size);
+  if (need > qb) {   // the split-K slabs follow the codes and scales
+    g.ws = static_cast<char*>(workspace) + qb;
+    g.ws_bytes = workspace_bytes - qb;
+  }
   return from_hip(cider::launch_gemm(g, wk, cider::kEpiF16, st));
 }
 

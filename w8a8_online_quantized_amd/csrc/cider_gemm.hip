@@ -221,7 +221,7 @@ template <int BM, int BN, int WGM, int WGN, int BK, int NS, int WK, int EPI, boo
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, const void* __restrict__ Wv,
                 const float* __restrict__ SW, int M, int N, int K, _Float16* __restrict__ Y,
-                int32_t* __restrict__ ACC, int splits, int32_t* __restrict__ WS, OutSplit osp) {
+                int32_t* __restrict__ ACC, int splits, OutSplit osp) {
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int TM = WTM / 16, TN = WTN / 16;
@@ -420,45 +420,10 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
   }
   wait_vmcnt<0>();
 
-  if constexpr (SPLIT) {
-    // Split-K: every unit writes its int32 partial tile to the workspace (in
-    // register order: one contiguous KiB per wave instruction), then bumps
-    // the tile's arrival counter. The last of the tile's `splits` units adds
-    // the others' partials (integer sums: exact in any order), resets the
-    // counter to zero for the next call and runs the store stage.
-    // Workspace: [total] int32 counters (256-byte padded), then
-    // [total][splits][BM * BN] int32 partials.
-    int32_t* const ctr = WS;
-    int32_t* const parts = WS + ((total + 63) & ~63);
-    constexpr int kTileInts = BM * BN;
-    int32_t* const mine = parts + ((int64_t)tile * splits + split) * kTileInts;
-#pragma unroll
-    for (int a = 0; a < TN; ++a)
-#pragma unroll
-      for (int b = 0; b < TM; ++b)
-        *reinterpret_cast<v4i*>(mine + ((a * TM + b) * NW * 64 + threadIdx.x) * 4) = acc[a][b];
-    __threadfence();   // publish this thread's partial at device scope
-    __shared__ int last_flag;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const int seen = __hip_atomic_fetch_add(ctr + tile, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      const bool last = seen == splits - 1;
-      if (last) __hip_atomic_store(ctr + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last_flag = last;
-    }
-    __syncthreads();
-    if (!last_flag) return;
-    __threadfence();   // acquire: the other units' partials are visible
-    for (int s = 0; s < splits; ++s) {
-      if (s == split) continue;
-      const int32_t* other = parts + ((int64_t)tile * splits + s) * kTileInts;
-#pragma unroll
-      for (int a = 0; a < TN; ++a)
-#pragma unroll
-        for (int b = 0; b < TM; ++b)
-          acc[a][b] += *reinterpret_cast<const v4i*>(other + ((a * TM + b) * NW * 64 + threadIdx.x) * 4);
-    }
-  }
+  // Split-K (SPLIT, with the int32 epilogue): each unit stores its partial
+  // sum over its K range to slab `split` of ACC ([splits][M][N]); a second
+  // kernel adds the slabs and dequantizes, so no unit waits for another.
+  static_assert(!SPLIT || EPI == kEpiAccI32, "split-K units store int32 partials");
 
   // ---- store stage: y = fp16((fp32(acc) * s_a[m]) * s_w[n]), or the raw int32.
   // Lane l holds column m = l % 16 of each 16x16 tile and the 4 consecutive
@@ -479,7 +444,7 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
       const int n = n0 + nl;
       if (n >= N) continue;
       if constexpr (!kF16) {
-        int32_t* dst = ACC + (int64_t)m * N + n;
+        int32_t* dst = ACC + (SPLIT ? (int64_t)split * M * N : 0) + (int64_t)m * N + n;
         if (vec_ok && n + 3 < N) {
           *reinterpret_cast<v4i*>(dst) = acc[a][b];
         } else {
@@ -1158,26 +1123,61 @@ hipError_t launch_dma(const GemmArgs& g, hipStream_t st) {
   const int64_t nbm = (g.M + BM - 1) / BM, nbn = (g.N + BN - 1) / BN;
   const dim3 grid((unsigned)(nbm * nbn)), block(WGM * WGN * 64);
   gemm_dma_kernel<BM, BN, WGM, WGN, BK, NS, WK, EPI><<<grid, block, 0, st>>>(
-      g.a, g.sa, g.w, g.sw, (int)g.M, (int)g.N, (int)g.K, static_cast<_Float16*>(g.y), g.acc, 1, nullptr, g.split);
+      g.a, g.sa, g.w, g.sw, (int)g.M, (int)g.N, (int)g.K, static_cast<_Float16*>(g.y), g.acc, 1, g.split);
   return hipGetLastError();
 }
 
-// Workspace bytes a split-K launch of BM x BN tiles needs: arrival counters
-// (256-byte padded) and one int32 partial tile per (tile, split).
-inline int64_t split_ws_bytes(int64_t M, int64_t N, int bm, int bn, int splits) {
-  const int64_t total = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
-  return ((total + 63) & ~int64_t(63)) * 4 + total * splits * (int64_t)bm * bn * 4;
+// Split-K reduction: y[m, n] = dequant(sum over the `splits` int32 slabs of
+// P [splits][M][N]), adding the slabs in order (integers: exact), with the
+// same store-stage arithmetic as the unsplit kernels (bit-identical y). Four
+// consecutive outputs per thread when N % 4 == 0, else one.
+template <int EPI, bool VEC>
+__global__ void __launch_bounds__(256)
+splitk_reduce_kernel(const int32_t* __restrict__ P, int splits, int M, int N, const float* __restrict__ SA,
+                     const float* __restrict__ SW, void* __restrict__ Y) {
+  constexpr int E = VEC ? 4 : 1;
+  const int64_t total = (int64_t)M * N / E;
+  const int64_t slab = (int64_t)M * N;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t e0 = i * E;
+    const int m = (int)(e0 / N), n = (int)(e0 % N);
+    if constexpr (VEC) {
+      v4i t = *reinterpret_cast<const v4i*>(P + e0);
+      for (int s = 1; s < splits; ++s) t += *reinterpret_cast<const v4i*>(P + s * slab + e0);
+      const float4 sw = *reinterpret_cast<const float4*>(SW + n);
+      if constexpr (EPI == kEpiBF16) *reinterpret_cast<bf4*>(static_cast<__bf16*>(Y) + e0) = dequant4_bf(t, SA[m], sw);
+      else *reinterpret_cast<h4*>(static_cast<_Float16*>(Y) + e0) = dequant4(t, SA[m], sw);
+    } else {
+      int t = P[e0];
+      for (int s = 1; s < splits; ++s) t += P[s * slab + e0];
+      if constexpr (EPI == kEpiBF16) static_cast<__bf16*>(Y)[e0] = dequant1_bf(t, SA[m], SW[n]);
+      else static_cast<_Float16*>(Y)[e0] = dequant1(t, SA[m], SW[n]);
+    }
+  }
 }
 
-// Split-K launch; g.ws must hold split_ws_bytes(...) bytes whose counter part
-// is zero (each launch leaves it zero again).
+// Workspace bytes of a split-K launch: the int32 slabs.
+inline int64_t split_ws_bytes(int64_t M, int64_t N, int splits) { return (int64_t)splits * M * N * 4; }
+
+// Split-K launch of BM x BN tiles over `splits` K ranges (whole stages; the
+// last range takes the rest), then the reduction. g.ws holds at least
+// split_ws_bytes(M, N, splits) bytes.
 template <int BM, int BN, int WGM, int WGN, int BK, int NS, int WK, int EPI>
 hipError_t launch_dma_split(const GemmArgs& g, int splits, hipStream_t st) {
   const int64_t nbm = (g.M + BM - 1) / BM, nbn = (g.N + BN - 1) / BN;
-  const dim3 grid((unsigned)(nbm * nbn * splits)), block(WGM * WGN * 64);
-  gemm_dma_kernel<BM, BN, WGM, WGN, BK, NS, WK, EPI, true><<<grid, block, 0, st>>>(
-      g.a, g.sa, g.w, g.sw, (int)g.M, (int)g.N, (int)g.K, static_cast<_Float16*>(g.y), g.acc, splits,
-      static_cast<int32_t*>(g.ws), g.split);
+  int32_t* parts = static_cast<int32_t*>(g.ws);
+  gemm_dma_kernel<BM, BN, WGM, WGN, BK, NS, WK, kEpiAccI32, true>
+      <<<dim3((unsigned)(nbm * nbn * splits)), dim3(WGM * WGN * 64), 0, st>>>(
+          g.a, nullptr, g.w, nullptr, (int)g.M, (int)g.N, (int)g.K, nullptr, parts, splits, g.split);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const bool vec = (g.N & 3) == 0;
+  const int64_t items = g.M * g.N / (vec ? 4 : 1);
+  const unsigned blocks = (unsigned)std::min<int64_t>((items + 255) / 256, 4096);
+  if (vec)
+    splitk_reduce_kernel<EPI, true><<<blocks, 256, 0, st>>>(parts, splits, (int)g.M, (int)g.N, g.sa, g.sw, g.y);
+  else
+    splitk_reduce_kernel<EPI, false><<<blocks, 256, 0, st>>>(parts, splits, (int)g.M, (int)g.N, g.sa, g.sw, g.y);
   return hipGetLastError();
 }
 
@@ -1199,7 +1199,7 @@ struct TileCost {
 };
 
 template <int NC>
-int cheapest_tile(const GemmArgs& g, const TileCost (&c)[NC]) {
+int cheapest_tile(const GemmArgs& g, const TileCost (&c)[NC], int64_t* est_out = nullptr) {
   int best = 0;
   int64_t best_est = 0;
   for (int i = 0; i < NC; ++i) {
@@ -1209,14 +1209,76 @@ int cheapest_tile(const GemmArgs& g, const TileCost (&c)[NC]) {
       best_est = est;
     }
   }
+  if (est_out) *est_out = best_est;
   return best;
 }
+
+// Per-channel / W4A8 tile tables (costs as described above).
+constexpr TileCost kTilesI8[] = {{256, 320, 62}, {128, 320, 92}, {128, 256, 102},
+                                 {128, 128, 105}, {64, 160, 167}, {64, 64, 194}};
+constexpr TileCost kTilesI4[] = {{256, 320, 62}, {128, 320, 92}, {128, 256, 102}, {128, 128, 105}, {64, 64, 194}};
+
+// Split-K plan for medium M with long K: too few output tiles to fill the
+// 256 CUs are cut along K into `splits` ranges (int32 partial slabs, then a
+// reduction). Candidates: 64x160 (int8 only), 128x128, 128x320, each with the
+// largest power-of-two split count <= min(8, 256 / tiles) (one round),
+// at least 4 and leaving >= 1024 codes per range; a block of a split launch
+// costs about BM * BN * cost * (K / splits) / 2560 by the same measured
+// costs. The cheapest candidate is used when it is below 0.6 x the unsplit
+// estimate (the margin pays for the reduction and the second launch).
+// Measured on MI355X (N=2560, K=10240): M=128 50.8 -> 18.2 us, M=256 50.9 ->
+// 24.1 us, M=1024 65.9 -> 46.6 us; outputs are bit-identical.
+struct SplitPlan {
+  int tile = -1;     // 0: 64x160, 1: 128x128, 2: 128x320; -1: no split
+  int splits = 0;
+};
+
+SplitPlan plan_split(const GemmArgs& g, WeightKind wk) {
+  SplitPlan plan;
+  if (g.group_size != 0 || g.M <= 16 || g.K < 4096) return plan;
+  int64_t est_plain = 0;
+  if (wk == kWeightI4) cheapest_tile(g, kTilesI4, &est_plain);
+  else cheapest_tile(g, kTilesI8, &est_plain);
+  static constexpr TileCost kCand[] = {{64, 160, 167}, {128, 128, 105}, {128, 320, 92}};
+  int64_t best = 0;
+  for (int i = wk == kWeightI4 ? 1 : 0; i < 3; ++i) {
+    const int64_t t = tiles_of(g, kCand[i].bm, kCand[i].bn);
+    int s = 8;
+    while (s > 1 && t * s > 256) s >>= 1;
+    if (s < 4 || g.K / s < 1024) continue;
+    const int64_t est = (int64_t)kCand[i].bm * kCand[i].bn * kCand[i].cost * (g.K / s) / 2560;
+    if (plan.tile < 0 || est < best) {
+      plan.tile = i;
+      plan.splits = s;
+      best = est;
+    }
+  }
+  const int64_t plain = est_plain * g.K / 2560;
+  if (plan.tile < 0 || best * 10 >= plain * 6) return SplitPlan{};
+  return plan;
+}
+
 
 // Wave tiles stay <= 128 x 80 (160 accumulator registers) with two waves per
 // SIMD: larger wave tiles (128 x 128) made the register allocator shuffle
 // accumulators between MFMAs.
 template <int WK, int EPI>
 hipError_t launch_pc(const GemmArgs& g, hipStream_t st) {
+  if constexpr (EPI == kEpiF16 || EPI == kEpiBF16) {
+    if (g.ws) {
+      const SplitPlan p = plan_split(g, (WeightKind)WK);
+      if (p.splits && g.ws_bytes >= split_ws_bytes(g.M, g.N, p.splits)) {
+        if constexpr (WK == kWeightI4) {
+          if (p.tile == 1) return launch_dma_split<128, 128, 2, 2, 128, 2, WK, EPI>(g, p.splits, st);
+          return launch_dma_split<128, 320, 2, 4, 128, 2, WK, EPI>(g, p.splits, st);
+        } else {
+          if (p.tile == 0) return launch_dma_split<64, 160, 2, 2, 128, 2, WK, EPI>(g, p.splits, st);
+          if (p.tile == 1) return launch_dma_split<128, 128, 2, 2, 64, 3, WK, EPI>(g, p.splits, st);
+          return launch_dma_split<128, 320, 2, 4, 128, 2, WK, EPI>(g, p.splits, st);
+        }
+      }
+    }
+  }
   if constexpr (WK == kWeightI4) {
     static constexpr TileCost kTiles[] = {
         {256, 320, 62}, {128, 320, 92}, {128, 256, 102}, {128, 128, 105}, {64, 64, 194}};
@@ -1297,6 +1359,16 @@ hipError_t launch_tok(const GemmArgs& g, hipStream_t st) {
 }
 
 }  // namespace
+
+int64_t gemm_split_workspace_bytes(int64_t M, int64_t N, int64_t K, WeightKind wk, int group_size) {
+  GemmArgs g{};
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.group_size = group_size;
+  const SplitPlan p = plan_split(g, wk);
+  return p.splits ? split_ws_bytes(M, N, p.splits) : 0;
+}
 
 bool linear_is_one_launch(int64_t M, int64_t K, int group_size) {
   GemmArgs g{};

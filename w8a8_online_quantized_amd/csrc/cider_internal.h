@@ -64,6 +64,9 @@ hipError_t launch_gemm(const GemmArgs& args, WeightKind wk, Epilogue epi, hipStr
 // separate quantization launch it saves.)
 bool linear_is_one_launch(int64_t M, int64_t K, int group_size);
 
+// Workspace bytes the GEMM dispatch uses for split-K at this shape (0: none).
+int64_t gemm_split_workspace_bytes(int64_t M, int64_t N, int64_t K, WeightKind wk, int group_size);
+
 struct MvArgs {
   const void* x;     // fp16 activations [M, K], 1 <= M <= 4
   const int8_t* w;   // int8 weight codes [N, K]
