@@ -376,7 +376,44 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
     issue(kt + NS - 1);   // past the end: out-of-range offsets, zero fill, never read
     const int8_t* sa_ = smem + (kt % NS) * kStageBytes;
     const int8_t* sw_ = sa_ + BM * RBA;
-    if constexpr (!kI4) {
+    if constexpr (!kI4 && BK == 128) {
+      // Two 64-code steps per stage. MFMAs run activation-fragment-major
+      // (group b = the TN MFMAs of fragment b), and each group is followed
+      // by reads issued ahead of use: step 0's fragment b+2, and step 1's
+      // fragments b (into the register group b just freed) and the weight
+      // fragment b. Step 1 then runs from registers, and a stage starts its
+      // MFMAs after TN + 2 reads instead of TN + TM. (The order of the
+      // MFMAs into one accumulator is unchanged: k ascending.)
+      v4i wf[TN], af[TM], nwf[TN], naf[TM];
+#pragma unroll
+      for (int a = 0; a < TN; ++a)
+        wf[a] = *reinterpret_cast<const v4i*>(sw_ + tile_off<RBW>(wn + 16 * a + l16, l4));
+#pragma unroll
+      for (int b = 0; b < 2 && b < TM; ++b)
+        af[b] = *reinterpret_cast<const v4i*>(sa_ + tile_off<RBA>(wm + 16 * b + l16, l4));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int b = 0; b < TM; ++b) {
+#pragma unroll
+        for (int a = 0; a < TN; ++a)
+          acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[a], af[b], acc[a][b], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (b + 2 < TM) af[b + 2] = *reinterpret_cast<const v4i*>(sa_ + tile_off<RBA>(wm + 16 * (b + 2) + l16, l4));
+        naf[b] = *reinterpret_cast<const v4i*>(sa_ + tile_off<RBA>(wm + 16 * b + l16, 4 + l4));
+        if (b < TN) nwf[b] = *reinterpret_cast<const v4i*>(sw_ + tile_off<RBW>(wn + 16 * b + l16, 4 + l4));
+        if (b == TM - 1) {
+#pragma unroll
+          for (int a = TM; a < TN; ++a)
+            nwf[a] = *reinterpret_cast<const v4i*>(sw_ + tile_off<RBW>(wn + 16 * a + l16, 4 + l4));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int b = 0; b < TM; ++b)
+#pragma unroll
+        for (int a = 0; a < TN; ++a)
+          acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(nwf[a], naf[b], acc[a][b], 0, 0, 0);
+    } else if constexpr (!kI4) {
 #pragma unroll
       for (int ks = 0; ks < BK / 64; ++ks) {
         v4i wf[TN], af[TM];
