@@ -373,7 +373,9 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
   for (int kt = 0; kt < KT; ++kt) {
     wait_vmcnt<(NS - 2) * LPS>();
     stage_barrier();
-    issue(kt + NS - 1);   // past the end: out-of-range offsets, zero fill, never read
+    // the next stage's DMA (past the end: out-of-range offsets, zero fill,
+    // never read); the 128-code int8 path issues it after its first reads
+    if constexpr (kI4 || BK != 128) issue(kt + NS - 1);
     const int8_t* sa_ = smem + (kt % NS) * kStageBytes;
     const int8_t* sw_ = sa_ + BM * RBA;
     if constexpr (!kI4 && BK == 128) {
@@ -391,6 +393,8 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
 #pragma unroll
       for (int b = 0; b < 2 && b < TM; ++b)
         af[b] = *reinterpret_cast<const v4i*>(sa_ + tile_off<RBA>(wm + 16 * b + l16, l4));
+      __builtin_amdgcn_sched_barrier(0);
+      issue(kt + NS - 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int b = 0; b < TM; ++b) {
