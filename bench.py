@@ -130,7 +130,7 @@ def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_byte
         y = torch.empty((M, N), dtype=torch.float16, device=dev)
         sets.append((x, xq, sa, wq0.clone(), sw0.clone(), y))
     # split-K workspace (scratch shared by the sets; calls run in stream order)
-    ws_bytes = 0 if mode == "w8a8_tokpg" else cider.cider_gemm_workspace_size(M, N, K, bits, gs)
+    ws_bytes = cider.cider_gemm_workspace_size(M, N, K, bits, gs)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
@@ -139,7 +139,7 @@ def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_byte
         if mode == "w4a8":
             cider.cider_w4a8_gemm(xq, sa, wq, sw, y, stream=stream, workspace=ws)
         elif mode == "w8a8_tokpg":
-            cider.cider_w8a8_gemm_token_group(xq, sa, wq, sw, gs, y, stream=stream)
+            cider.cider_w8a8_gemm_token_group(xq, sa, wq, sw, gs, y, stream=stream, workspace=ws)
         else:
             cider.cider_w8a8_gemm(xq, sa, wq, sw, gs, y, stream=stream, workspace=ws)
 

@@ -157,12 +157,15 @@ cider_status_t cider_w4a8_gemm(const int8_t* x_q, const float* x_scale, const ui
                                void* y_f16, void* stream);
 /* Split-K for medium M with long K (too few output tiles to fill the GPU):
  * the _ex GEMMs take a caller workspace and, where the dispatch's plan says
- * so, cut K into ranges whose exact int32 partial sums go to the workspace
- * as [splits][M][N] slabs before a second kernel adds them (in split order:
- * integer sums, so y is bit-identical to the unsplit GEMM) and dequantizes.
+ * so, cut K into ranges (whole 128-code stages) whose partial sums go to the
+ * workspace as [splits][M][N] slabs before a second kernel adds them in
+ * split order and stores y. Per-channel and W4A8 partials are exact int32
+ * sums, so y is bit-identical to the unsplit GEMM; per-group partials are
+ * the fp32 group sums of each range (without the per-token scale for
+ * cider_w8a8_gemm_token_group), so only the fp32 summation order changes
+ * (within the per-group error bound).
  *   cider_gemm_workspace_size: the bytes the plan needs at this shape, 0 when
- *   it does not split (bits 8 or 4; per-channel only: per-group gives 0),
- *   -1 for invalid sizes. The library never allocates.
+ *   it does not split, -1 for invalid sizes. The library never allocates.
  *   workspace may be NULL (no split); otherwise 16-byte aligned with at
  *   least the queried bytes, else CIDER_ERROR_INVALID_VALUE. Its contents are
  *   scratch; calls that share one workspace must not overlap in time.
@@ -215,11 +218,15 @@ cider_status_t cider_linear(const void* x_f16, const void* w, const float* w_sca
  *   w_scale[n,g]| plus the fp16 rounding; results are deterministic.
  *   x_q [M, K] int8 with x_scale fp32 [M] (cider_quant_act with group_size 0);
  *   w_q [N, K] int8 with w_scale fp32 [N, K/group_size]; group_size 64 or 128.
+ * workspace / workspace_bytes: an optional split-K workspace as for
+ * cider_w8a8_gemm_ex (size from cider_gemm_workspace_size(M, N, K, 8,
+ * group_size); NULL: no split).
  * K, alignment and errors as for cider_w8a8_gemm.
  */
 cider_status_t cider_w8a8_gemm_token_group(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
                                            const float* w_scale, int64_t M, int64_t N, int64_t K,
-                                           int32_t group_size, void* y_f16, void* stream);
+                                           int32_t group_size, void* y_f16, void* workspace,
+                                           int64_t workspace_bytes, void* stream);
 
 /* Same-input projections as one GEMM (the README's experimental SplitLinear
  * page prepares the input of the Q/K/V and gate/up projections once): the

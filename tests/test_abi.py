@@ -59,8 +59,8 @@ def test_empty_work_is_success_without_pointers():
     assert L.cider_gemm_acc_i32(0, NULL, NULL, 0, 4, 64, 0, NULL, NULL) == 0
     assert L.cider_int8_mv(NULL, NULL, NULL, 0, 16, 64, 0, NULL, NULL) == 0
     assert L.cider_int8_mv(NULL, NULL, NULL, 2, 0, 64, 0, NULL, NULL) == 0
-    assert L.cider_w8a8_gemm_token_group(NULL, NULL, NULL, NULL, 0, 16, 128, 64, NULL, NULL) == 0
-    assert L.cider_w8a8_gemm_token_group(NULL, NULL, NULL, NULL, 16, 0, 128, 128, NULL, NULL) == 0
+    assert L.cider_w8a8_gemm_token_group(NULL, NULL, NULL, NULL, 0, 16, 128, 64, NULL, NULL, 0, NULL) == 0
+    assert L.cider_w8a8_gemm_token_group(NULL, NULL, NULL, NULL, 16, 0, 128, 128, NULL, NULL, 0, NULL) == 0
 
 
 def test_quant_weight_rejects():
@@ -106,15 +106,15 @@ def test_int8_mv_rejects():
 
 def test_token_group_rejects():
     t = L.cider_w8a8_gemm_token_group
-    assert t(P, P, P, P, 4, 4, 128, 0, P, NULL) == INV                    # needs per-group weights
-    assert t(P, P, P, P, 4, 4, 128, 32, P, NULL) == INV
-    assert t(P, P, P, P, 4, 4, 192, 128, P, NULL) == INV                  # K % gs
-    assert t(P, P, P, P, -1, 4, 128, 64, P, NULL) == INV
-    assert t(P, P, P, P, 4, 4, 133120 + 128, 64, P, NULL) == INV          # int32 range guard
-    assert t(NULL, P, P, P, 4, 4, 128, 64, P, NULL) == INV
-    assert t(P, NULL, P, P, 4, 4, 128, 64, P, NULL) == INV
-    assert t(P, P, P, P, 4, 4, 128, 64, NULL, NULL) == INV
-    assert t(P, MIS, P, P, 4, 4, 128, 64, P, NULL) == INV
+    assert t(P, P, P, P, 4, 4, 128, 0, P, NULL, 0, NULL) == INV                    # needs per-group weights
+    assert t(P, P, P, P, 4, 4, 128, 32, P, NULL, 0, NULL) == INV
+    assert t(P, P, P, P, 4, 4, 192, 128, P, NULL, 0, NULL) == INV                  # K % gs
+    assert t(P, P, P, P, -1, 4, 128, 64, P, NULL, 0, NULL) == INV
+    assert t(P, P, P, P, 4, 4, 133120 + 128, 64, P, NULL, 0, NULL) == INV          # int32 range guard
+    assert t(NULL, P, P, P, 4, 4, 128, 64, P, NULL, 0, NULL) == INV
+    assert t(P, NULL, P, P, 4, 4, 128, 64, P, NULL, 0, NULL) == INV
+    assert t(P, P, P, P, 4, 4, 128, 64, NULL, NULL, 0, NULL) == INV
+    assert t(P, MIS, P, P, 4, 4, 128, 64, P, NULL, 0, NULL) == INV
 
 
 def test_split_rejects():
@@ -199,7 +199,8 @@ def test_split_k_workspace_plan():
     assert g(128, 2560, 10240, 4, 0) == 8 * 128 * 2560 * 4        # W4A8: 128x128 tiles, 8 ranges
     assert g(4096, 10240, 2560, 8, 0) == 0                        # enough tiles: no split
     assert g(128, 10240, 2560, 8, 0) == 0                         # short K
-    assert g(128, 2560, 10240, 8, 128) == 0                       # per-group: no split
+    assert g(128, 2560, 10240, 8, 128) == 4 * 128 * 2560 * 4      # per-group: 64x64 tiles, fp32 partials
+    assert g(1024, 2560, 10240, 8, 128) == 0                      # per-group with enough tiles
     assert g(16, 2560, 10240, 8, 0) == 0                          # skinny path
     assert g(0, 2560, 10240, 8, 0) == 0
     assert g(4, 4, 40, 8, 0) == -1 and g(4, 4, 64, 4, 64) == -1 and g(4, 4, 64, 6, 0) == -1

@@ -84,3 +84,67 @@ def test_split_k_workspace_reuse_and_linear():
         assert need > M * K
         y2 = host(c.cider_linear(dev(x), wq, sw, 8, 0))
         assert np.array_equal(y0.view(np.uint16), y2.view(np.uint16)), (M, N, K)
+
+
+# ---------------------------------------------------------------- per-group split-K (fp32 partial sums)
+from tests.test_gpu_parity import pg_sum_bound  # noqa: E402
+from tests.test_gpu_token_group import token_group_bound  # noqa: E402
+
+PG = [(128, 2560, 10240, 128), (128, 2560, 10240, 64), (130, 650, 8192, 128), (64, 1024, 16384, 64)]
+
+
+@pytest.mark.parametrize("M,N,K,gs", PG)
+def test_split_k_per_group(M, N, K, gs):
+    c = cider()
+    need = c.cider_gemm_workspace_size(M, N, K, 8, gs)
+    assert need > 0, f"{M}x{N}x{K} gs{gs} was expected to split"
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    x = inputs.activations(M, K, seed=64)
+    w = inputs.weights(N, K, seed=64)
+    wq, sw = c.cider_quant_weight(dev(w), 8, gs)
+    xq, sa = c.cider_quant_act(dev(x), gs)
+    y = host(c.cider_w8a8_gemm(xq, sa, wq, sw, gs, workspace=ws))
+    wqo, swo = oracle.quantize_weight(w, 8, gs)
+    yo, qo, sao = oracle.w8a8_linear(x, wqo, swo, gs)
+    e = pg_sum_bound(qo, sao, wqo, swo, gs, np.arange(M))
+    assert_y_close(y, yo, 2e-3, extra_atol=e, what=f"split-K pg{gs} {M}x{N}x{K}")
+    # deterministic: the same bits again
+    y2 = host(c.cider_w8a8_gemm(xq, sa, wq, sw, gs, workspace=ws))
+    assert np.array_equal(y.view(np.uint16), y2.view(np.uint16))
+
+
+@pytest.mark.parametrize("gs", [128, 64])
+def test_split_k_token_group(gs):
+    c = cider()
+    M, N, K = 128, 2560, 10240
+    ws = torch.empty(c.cider_gemm_workspace_size(M, N, K, 8, gs), dtype=torch.uint8, device="cuda")
+    assert ws.numel() > 0
+    x = inputs.activations(M, K, seed=65)
+    w = inputs.weights(N, K, seed=65)
+    wq, sw = c.cider_quant_weight(dev(w), 8, gs)
+    xq, sa = c.cider_quant_act(dev(x), 0)
+    y = host(c.cider_w8a8_gemm_token_group(xq, sa, wq, sw, gs, workspace=ws))
+    wqo, swo = oracle.quantize_weight(w, 8, gs)
+    yo, qo, sao = oracle.w8a8_linear_token_group(x, wqo, swo, gs)
+    e = token_group_bound(qo, sao, wqo, swo, gs)
+    assert_y_close(y, yo, 2e-3, extra_atol=e, what=f"split-K token x pg{gs}")
+
+
+def test_split_k_per_group_bf16():
+    c = cider()
+    M, N, K, gs = 128, 2560, 10240, 128
+    ws = torch.empty(c.cider_gemm_workspace_size(M, N, K, 8, gs), dtype=torch.uint8, device="cuda")
+    x32 = inputs.activations(M, K, seed=66).astype(np.float32)
+    xd = torch.from_numpy(x32).to(torch.bfloat16).cuda()
+    w = inputs.weights(N, K, seed=66)
+    wq, sw = c.cider_quant_weight(dev(w), 8, gs)
+    xq, sa = c.cider_quant_act(xd, gs)
+    y = c.cider_w8a8_gemm(xq, sa, wq, sw, gs, out_dtype=torch.bfloat16, workspace=ws)
+    torch.cuda.synchronize()
+    yb = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    xb = xd.view(torch.int16).cpu().numpy().view(np.uint16)
+    wqo, swo = oracle.quantize_weight(w, 8, gs)
+    yo, qo, sao = oracle.w8a8_linear_bf16(xb, wqo, swo, gs)
+    yv, ov = oracle.bf16_to_f32(yb).astype(np.float64), oracle.bf16_to_f32(yo).astype(np.float64)
+    e = pg_sum_bound(qo, sao, wqo, swo, gs, np.arange(M))
+    assert np.all(np.abs(yv - ov) <= 2.0 ** -7 * np.abs(ov) + e + 2.0 ** -133)

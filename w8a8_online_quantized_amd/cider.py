@@ -34,7 +34,7 @@ SIGNATURES = {
     "cider_w4a8_gemm": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p]),
     "cider_gemm_acc_i32": (ctypes.c_int, [_c_i32, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p]),
     "cider_w8a8_gemm_token_group": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p,
-                                                   _c_p]),
+                                                   _c_p, _c_i64, _c_p]),
     "cider_w8a8_gemm_split": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_p, _c_p, _c_p]),
     "cider_linear_workspace_size": (ctypes.c_int64, [_c_i64, _c_i64, _c_i64, _c_i32, _c_i32]),
     "cider_gemm_workspace_size": (ctypes.c_int64, [_c_i64, _c_i64, _c_i64, _c_i32, _c_i32]),
@@ -249,7 +249,7 @@ def cider_w8a8_gemm(x_q, x_scale, w_q, w_scale, group_size: int = 0, y=None, str
     return y
 
 
-def cider_w8a8_gemm_token_group(x_q, x_scale, w_q, w_scale, group_size: int, y=None, stream=None):
+def cider_w8a8_gemm_token_group(x_q, x_scale, w_q, w_scale, group_size: int, y=None, stream=None, workspace=None):
     """Per-token activation codes (x_scale [M]) times per-group weight codes
     (w_scale [N, K/group_size], group_size 64 or 128) -> fp16 y [M, N]."""
     import torch
@@ -266,7 +266,7 @@ def cider_w8a8_gemm_token_group(x_q, x_scale, w_q, w_scale, group_size: int, y=N
     _need(y, torch.float16, (M, N), "y")
     _check("cider_w8a8_gemm_token_group",
            lib().cider_w8a8_gemm_token_group(_ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale), M, N, K,
-                                             group_size, _ptr(y), _stream(stream)))
+                                             group_size, _ptr(y), *_ws_args(workspace), _stream(stream)))
     return y
 
 

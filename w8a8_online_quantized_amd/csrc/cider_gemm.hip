@@ -920,11 +920,11 @@ hipError_t launch_skinny(const GemmArgs& g, hipStream_t st) {
 // gathered, the fold is fp32(acc) * s_w[n,g-1] added with one fma, and s_a[m]
 // multiplies the finished fp32 sum in the store stage.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WGM, int WGN, int NS, int GS, int EPI>
+template <int BM, int BN, int WGM, int WGN, int NS, int GS, int EPI, bool SPLIT = false>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, const int8_t* __restrict__ W,
                    const float* __restrict__ SW, int M, int N, int K, _Float16* __restrict__ Y,
-                   int32_t* __restrict__ ACC) {
+                   int32_t* __restrict__ ACC, int splits = 1, float* __restrict__ PART = nullptr) {
   constexpr int BK = 128, RB = 128;
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
@@ -961,11 +961,16 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
 
   const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
   const int total = nbm * nbn;
-  int tile;
+  // work unit = (tile, K range); split-K launches number them tile-major
+  const int nsplit = SPLIT ? splits : 1;
+  int tile, split;
   {
+    const int units = total * nsplit;
     const int b = blockIdx.x, xcd = b & 7, idx = b >> 3;
-    const int per = total >> 3, rem = total & 7;
-    tile = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    const int per = units >> 3, rem = units & 7;
+    const int unit = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    tile = unit / nsplit;
+    split = unit - tile * nsplit;
   }
   constexpr int kGroupM = 8;
   const int group = tile / (kGroupM * nbn);
@@ -997,11 +1002,15 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
       for (int r = 0; r < 4; ++r) facc[a][b][r] = 0.0f;
     }
 
-  const int KT = (K + BK - 1) / BK;
+  // this unit's stages: [kt0, kt0 + KT) of the K loop (whole stages; a split
+  // past the end of K has none and stores zeros)
+  const int kc = ((K + nsplit - 1) / nsplit + BK - 1) / BK * BK;
+  const int kt0 = split * (kc / BK);
+  const int KT = max(0, min((K + BK - 1) / BK, kt0 + kc / BK) - kt0);
   auto issue = [&](int kt) {
     int8_t* st = smem + (kt % NS) * kCodeBytes;
-    dma_stage<BM, RB, NW>(ra, st, pad, wave, lane, ld, kt * RB, (int)ld);
-    dma_stage<BN, RB, NW>(rw, st + BM * RB, pad, wave, lane, ld, kt * RB, (int)ld);
+    dma_stage<BM, RB, NW>(ra, st, pad, wave, lane, ld, (kt0 + kt) * RB, (int)ld);
+    dma_stage<BN, RB, NW>(rw, st + BM * RB, pad, wave, lane, ld, (kt0 + kt) * RB, (int)ld);
     float* slot = ring + (kt % NSR) * kSlotFloats;
 #pragma unroll
     for (int i = 0; i < kScalePer; ++i) {
@@ -1011,7 +1020,7 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
         continue;
       }
       const int gi = j / (kSeg / 64), p = j % (kSeg / 64);
-      const int g = kt * GPS + gi;
+      const int g = (kt0 + kt) * GPS + gi;
       float* dst = slot + gi * kSeg + 64 * p;
       // rows past the tile's valid rows are past the descriptor's range: zero
       if (p < BMp / 64) {
@@ -1072,7 +1081,7 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
     for (int gi = 0; gi < GPS; ++gi) {
       // keep each group's fragment loads with its own MFMAs (bounds register use)
       if (gi > 0) __builtin_amdgcn_sched_barrier(0);
-      const int g = kt * GPS + gi;
+      const int g = (kt0 + kt) * GPS + gi;
       const float* psc = gi == 0 ? prev + (GPS - 1) * kSeg : cur + (gi - 1) * kSeg;
 #pragma unroll
       for (int s = 0; s < KPG; ++s) {
@@ -1099,8 +1108,8 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
     }
   }
   // the last group (its slot was not overwritten: later zero-fill stages used other slots)
-  {
-    const int g = KT * GPS - 1;
+  if (KT > 0) {
+    const int g = (kt0 + KT) * GPS - 1;
     const float* lsc = ring + ((KT - 1) % NSR) * kSlotFloats + (GPS - 1) * kSeg;
 #pragma unroll
     for (int a = 0; a < TN; ++a)
@@ -1108,6 +1117,32 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
       for (int b = 0; b < TM; ++b) fold_tile(a, b, lsc, g);
   }
   wait_vmcnt<0>();
+  if constexpr (SPLIT) {
+    // the unit's fp32 partial sums (without s_a[m] for per-token scales) to
+    // slab `split` of PART [splits][M][N]; a second kernel adds the slabs
+    static_assert(kF16, "split-K per-group units store fp32 partial sums");
+    const bool vec_ok = (N & 3) == 0;
+    float* const slab = PART + (int64_t)split * M * N;
+#pragma unroll
+    for (int b = 0; b < TM; ++b) {
+      const int m = m0 + wm + 16 * b + l16;
+      if (m >= M) continue;
+#pragma unroll
+      for (int a = 0; a < TN; ++a) {
+        const int n = n0 + wn + 16 * a + 4 * l4;
+        if (n >= N) continue;
+        float* dst = slab + (int64_t)m * N + n;
+        if (vec_ok && n + 3 < N) {
+          *reinterpret_cast<float4*>(dst) = make_float4(facc[a][b][0], facc[a][b][1], facc[a][b][2], facc[a][b][3]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) dst[r] = facc[a][b][r];
+        }
+      }
+    }
+    return;
+  }
   if constexpr (kF16) {
     const bool vec_ok = (N & 3) == 0;
 #pragma unroll
@@ -1156,6 +1191,54 @@ hipError_t launch_dma_pg(const GemmArgs& g, hipStream_t st) {
   gemm_dma_pg_kernel<BM, BN, WGM, WGN, NS, GS, EPI><<<grid, block, 0, st>>>(
       g.a, g.sa, static_cast<const int8_t*>(g.w), g.sw, (int)g.M, (int)g.N, (int)g.K,
       static_cast<_Float16*>(g.y), g.acc);
+  return hipGetLastError();
+}
+
+// Split-K reduction of fp32 per-group partial sums P [splits][M][N], added in
+// split order; per-token activation scales multiply the sum (fp32 product,
+// then fp16), as in the unsplit store stage.
+template <int EPI, bool VEC>
+__global__ void __launch_bounds__(256)
+splitk_reduce_f32_kernel(const float* __restrict__ P, int splits, int M, int N, const float* __restrict__ SA,
+                         void* __restrict__ Y) {
+  constexpr int E = VEC ? 4 : 1;
+  const int64_t total = (int64_t)M * N / E;
+  const int64_t slab = (int64_t)M * N;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t e0 = i * E;
+    const int m = (int)(e0 / N);
+    float t[E];
+#pragma unroll
+    for (int r = 0; r < E; ++r) t[r] = P[e0 + r];
+    for (int s = 1; s < splits; ++s)
+#pragma unroll
+      for (int r = 0; r < E; ++r) t[r] += P[s * slab + e0 + r];
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      if constexpr (EPI == kEpiBF16) static_cast<__bf16*>(Y)[e0 + r] = to_bf16(t[r]);
+      else if constexpr (EPI == kEpiF16Tok) static_cast<_Float16*>(Y)[e0 + r] = scale1(t[r], SA[m]);
+      else static_cast<_Float16*>(Y)[e0 + r] = (_Float16)t[r];
+    }
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN, int NS, int GS, int EPI>
+hipError_t launch_dma_pg_split(const GemmArgs& g, int splits, hipStream_t st) {
+  const int64_t nbm = (g.M + BM - 1) / BM, nbn = (g.N + BN - 1) / BN;
+  float* parts = static_cast<float*>(g.ws);
+  gemm_dma_pg_kernel<BM, BN, WGM, WGN, NS, GS, EPI, true>
+      <<<dim3((unsigned)(nbm * nbn * splits)), dim3(WGM * WGN * 64), 0, st>>>(
+          g.a, g.sa, static_cast<const int8_t*>(g.w), g.sw, (int)g.M, (int)g.N, (int)g.K, nullptr, nullptr, splits,
+          parts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const bool vec = (g.N & 3) == 0;
+  const int64_t items = g.M * g.N / (vec ? 4 : 1);
+  const unsigned blocks = (unsigned)std::min<int64_t>((items + 255) / 256, 4096);
+  if (vec)
+    splitk_reduce_f32_kernel<EPI, true><<<blocks, 256, 0, st>>>(parts, splits, (int)g.M, (int)g.N, g.sa, g.y);
+  else
+    splitk_reduce_f32_kernel<EPI, false><<<blocks, 256, 0, st>>>(parts, splits, (int)g.M, (int)g.N, g.sa, g.y);
   return hipGetLastError();
 }
 
@@ -1269,14 +1352,33 @@ constexpr TileCost kTilesI4[] = {{256, 320, 62}, {128, 320, 92}, {128, 256, 102}
 // estimate (the margin pays for the reduction and the second launch).
 // Measured on MI355X (N=2560, K=10240): M=128 50.8 -> 18.2 us, M=256 50.9 ->
 // 24.1 us, M=1024 65.9 -> 46.6 us; outputs are bit-identical.
+// Per-group (gs 64 / 128, both operands or per-token activations) splits on
+// 64x64 tiles, whose units store fp32 partial sums: 4 K ranges up to 160
+// tiles, 2 up to 320, none beyond (K >= 4096, >= 1024 codes per range).
+// Measured on MI355X, N=2560, K=10240, gs 128 / 64: M=128 60.7 / 69.3 ->
+// 24.3 / 28.0 us, M=256 61.7 / 70.5 -> 31.7 / 35.3 us, M=512 65.7 / 75.3 ->
+// 52.8 / 64.6 us; at M=1024 splitting lost (the tile-cost model above
+// mispredicts these small-M per-group launches, hence a table by tile count).
 struct SplitPlan {
-  int tile = -1;     // 0: 64x160, 1: 128x128, 2: 128x320; -1: no split
+  int tile = -1;     // per-channel 0: 64x160, 1: 128x128, 2: 128x320; per-group: 64x64
   int splits = 0;
 };
 
+SplitPlan plan_split_pg(const GemmArgs& g) {
+  SplitPlan plan;
+  if (g.M <= 16 || g.K < 4096) return plan;
+  const int64_t t = tiles_of(g, 64, 64);
+  const int s = t <= 160 ? 4 : (t <= 320 ? 2 : 0);
+  if (s == 0 || g.K / s < 1024) return plan;
+  plan.tile = 1;
+  plan.splits = s;
+  return plan;
+}
+
 SplitPlan plan_split(const GemmArgs& g, WeightKind wk) {
   SplitPlan plan;
-  if (g.group_size != 0 || g.M <= 16 || g.K < 4096) return plan;
+  if (g.group_size != 0) return wk == kWeightI8 ? plan_split_pg(g) : plan;
+  if (g.M <= 16 || g.K < 4096) return plan;
   int64_t est_plain = 0;
   if (wk == kWeightI4) cheapest_tile(g, kTilesI4, &est_plain);
   else cheapest_tile(g, kTilesI8, &est_plain);
@@ -1352,6 +1454,14 @@ hipError_t launch_pc(const GemmArgs& g, hipStream_t st) {
 // its registers spill.
 template <int GS, int EPI>
 hipError_t launch_pg(const GemmArgs& g, hipStream_t st) {
+  if constexpr (EPI != kEpiAccI32) {
+    if (g.ws) {
+      const SplitPlan p = plan_split_pg(g);
+      if (p.splits && g.ws_bytes >= split_ws_bytes(g.M, g.N, p.splits)) {
+        return launch_dma_pg_split<64, 64, 1, 4, 2, GS, EPI>(g, p.splits, st);
+      }
+    }
+  }
   if constexpr (GS == 128) {
     static constexpr TileCost kTiles[] = {{256, 160, 521}, {256, 128, 540}, {128, 128, 770}, {64, 64, 778}};
     switch (cheapest_tile(g, kTiles)) {
