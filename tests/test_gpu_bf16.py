@@ -90,7 +90,8 @@ def test_bf16_gemm_per_channel(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K,gs", [(3, 40, 1024, 128), (16, 70, 2560, 64), (130, 300, 1152, 64),
-                                      (520, 260, 2560, 128), (1024, 2560, 10240, 128)])
+                                      (520, 260, 2560, 128), (1024, 2560, 10240, 128),
+                                      (4000, 2500, 1280, 128), (2000, 2498, 1280, 64)])
 def test_bf16_gemm_per_group(M, N, K, gs):
     c = cider()
     x32 = act32(M, K, 54)

@@ -227,6 +227,29 @@ def test_w8a8_per_group_outputs(M, N, K, gs):
     assert_y_close(y, yo, 2e-3, extra_atol=e, what=f"pg{gs} {M}x{N}x{K}")
 
 
+# (M, N, K, gs) that select each per-group tile of the dispatch: 128x160
+# (ragged M and N, vector stores), 128x128 (N not a multiple of 4: scalar
+# stores), 128x128 at gs 64, 64x64 at gs 64 with four blocks per CU
+PG_TILE_SHAPES = [(4000, 2500, 1280, 128), (2000, 2498, 1280, 128), (2000, 2500, 1280, 64),
+                  (1000, 2498, 640, 64)]
+
+
+@pytest.mark.parametrize("M,N,K,gs", PG_TILE_SHAPES)
+def test_w8a8_per_group_tiles_sampled(M, N, K, gs):
+    c = cider()
+    x, w = _pc_case(M, N, K, seed=2)
+    wq, sw = c.cider_quant_weight(dev(w), 8, gs)
+    xq, sa = c.cider_quant_act(dev(x), gs)
+    y = host(c.cider_w8a8_gemm(xq, sa, wq, sw, gs))
+    rng = np.random.default_rng(M + N)
+    rows = np.unique(np.r_[0, M - 1, rng.integers(0, M, 40)])
+    wqo, swo = oracle.quantize_weight(w, 8, gs)
+    yo, qo, sao = oracle.w8a8_linear(x[rows], wqo, swo, gs)
+    assert np.array_equal(host(xq)[rows], qo)
+    e = pg_sum_bound(qo, sao, wqo, swo, gs, np.arange(len(rows)))
+    assert_y_close(y[rows], yo, 2e-3, extra_atol=e, what=f"pg{gs} tile {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 77, 64), (5, 3, 32), (40, 100, 1056), (300, 520, 2560)])
 def test_w4a8_outputs(M, N, K):
     c = cider()

@@ -49,8 +49,8 @@ def _run(M, N, K, gs, seed, rows=None):
     return c, x, y
 
 
-# (M, N, K, gs): skinny (M <= 16) with 4 / 8 / 16 waves, then the 64x64,
-# 128x128, 256x128 and (gs 128) 256x160 per-group tiles, ragged tails
+# (M, N, K, gs): skinny (M <= 16) with 4 / 8 / 16 waves, then the 64x64 and
+# 128x128 per-group tiles, ragged tails
 SMALL = [(1, 17, 128, 64), (3, 5, 128, 128), (16, 70, 2560, 64), (9, 300, 10240, 128), (1, 2560, 10240, 128),
          (33, 100, 1024, 128), (130, 300, 1152, 64), (520, 260, 2560, 128), (300, 650, 1280, 64),
          (257, 1000, 640, 128)]
@@ -59,6 +59,13 @@ SMALL = [(1, 17, 128, 64), (3, 5, 128, 128), (16, 70, 2560, 64), (9, 300, 10240,
 @pytest.mark.parametrize("M,N,K,gs", SMALL)
 def test_token_group_outputs(M, N, K, gs):
     _run(M, N, K, gs, seed=21)
+
+
+# 128x160 and 128x128 tiles at both group sizes, ragged M and N (2498: scalar stores)
+@pytest.mark.parametrize("M,N,K,gs", [(4000, 2500, 1280, 128), (2000, 2498, 1280, 128),
+                                      (4000, 2498, 1280, 64), (2000, 2500, 1280, 64)])
+def test_token_group_tiles_sampled(M, N, K, gs):
+    _run(M, N, K, gs, seed=26, rows=sampled(M))
 
 
 @pytest.mark.parametrize("M,N,K,gs", [(1024, 2560, 10240, 128), (4096, 2560, 10240, 128),

@@ -612,7 +612,7 @@ gemm_skinny_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, c
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float sw = SW[(int64_t)min(n0 + 4 * l4 + r, N - 1) * G + u];
-            facc[r] += ((float)acc[r] * sa) * sw;
+            facc[r] = __builtin_fmaf((float)acc[r] * sa, sw, facc[r]);
           }
         }
         acc = zero4();
@@ -921,7 +921,7 @@ hipError_t launch_skinny(const GemmArgs& g, hipStream_t st) {
 // multiplies the finished fp32 sum in the store stage.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int WGM, int WGN, int NS, int GS, int EPI, bool SPLIT = false>
-__global__ void __launch_bounds__(WGM * WGN * 64)
+__global__ void __launch_bounds__(WGM * WGN * 64, WGM * WGN == 4 ? 2 : 1)
 gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, const int8_t* __restrict__ W,
                    const float* __restrict__ SW, int M, int N, int K, _Float16* __restrict__ Y,
                    int32_t* __restrict__ ACC, int splits = 1, float* __restrict__ PART = nullptr) {
@@ -1042,12 +1042,13 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
       facc[a][b][2] = __builtin_fmaf((float)acc[a][b][2], s4.z, facc[a][b][2]);
       facc[a][b][3] = __builtin_fmaf((float)acc[a][b][3], s4.w, facc[a][b][3]);
     } else if constexpr (kF16) {
+      // fp32(acc) * s_a rounded, then one fma with s_w into the sum
       const float sam = gsc[wm + 16 * b + l16];
       const float4 s4 = *reinterpret_cast<const float4*>(gsc + BMp + wn + 16 * a + 4 * l4);
-      facc[a][b][0] += ((float)acc[a][b][0] * sam) * s4.x;
-      facc[a][b][1] += ((float)acc[a][b][1] * sam) * s4.y;
-      facc[a][b][2] += ((float)acc[a][b][2] * sam) * s4.z;
-      facc[a][b][3] += ((float)acc[a][b][3] * sam) * s4.w;
+      facc[a][b][0] = __builtin_fmaf((float)acc[a][b][0] * sam, s4.x, facc[a][b][0]);
+      facc[a][b][1] = __builtin_fmaf((float)acc[a][b][1] * sam, s4.y, facc[a][b][1]);
+      facc[a][b][2] = __builtin_fmaf((float)acc[a][b][2] * sam, s4.z, facc[a][b][2]);
+      facc[a][b][3] = __builtin_fmaf((float)acc[a][b][3] * sam, s4.w, facc[a][b][3]);
     } else {
       if (g < 0 || g >= G) return;
       const int m = m0 + wm + 16 * b + l16, n = n0 + wn + 16 * a + 4 * l4;
@@ -1094,16 +1095,15 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
         for (int b = 0; b < TM; ++b)
           af[b] = *reinterpret_cast<const v4i*>(sa_ + tile_off<RB>(wm + 16 * b + l16, 4 * ks + l4));
 #pragma unroll
-        for (int a = 0; a < TN; ++a)
-#pragma unroll
-          for (int b = 0; b < TM; ++b) {
-            if (s == 0) {
-              fold_tile(a, b, psc, g - 1);
-              acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[a], af[b], zero4(), 0, 0, 0);
-            } else {
-              acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[a], af[b], acc[a][b], 0, 0, 0);
-            }
+        for (int t = 0; t < TN * TM; ++t) {
+          const int a = t / TM, b = t % TM;
+          if (s == 0) {
+            fold_tile(a, b, psc, g - 1);
+            acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[a], af[b], zero4(), 0, 0, 0);
+          } else {
+            acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[a], af[b], acc[a][b], 0, 0, 0);
           }
+        }
       }
     }
   }
@@ -1309,17 +1309,18 @@ inline int64_t tiles_of(const GemmArgs& g, int bm, int bn) {
   return ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn);
 }
 
-// Per-channel and W4A8 tile choice. A launch of T tiles runs in about
-// ceil(T / 256) rounds of one block per CU, and a round of BM x BN tiles
-// costs about BM * BN * cost, where `cost` (time per output element per
-// round, relative) was measured on MI355X at K = 2560 with quantized
+// Tile choice. A launch of T tiles whose blocks fit `bpc` to a CU (LDS and
+// registers) runs in about ceil(T / (256 * bpc)) rounds, and a round of
+// BM x BN tiles costs about BM * BN * cost, where `cost` (time per output
+// element per round, relative) was measured on MI355X with quantized
 // Gaussian codes: large tiles reuse each staged byte over more MFMAs, small
 // tiles fill the 256 CUs when M or N is small. The candidate with the lowest
-// ceil(T / 256) * BM * BN * cost is launched (ties: the earlier one). With
-// these costs e.g. M=4096 N=10240 takes 256 x 320 (512 tiles: two full
-// rounds) and M=1024 N=10240 or M=4096 N=2560 take 128 x 320 (256 tiles).
+// rounds * BM * BN * cost is launched (ties: the earlier one). With the
+// per-channel costs (K = 2560, one block per CU) e.g. M=4096 N=10240 takes
+// 256 x 320 (512 tiles: two full rounds) and M=1024 N=10240 or M=4096
+// N=2560 take 128 x 320 (256 tiles).
 struct TileCost {
-  int bm, bn, cost;
+  int bm, bn, cost, bpc = 1;
 };
 
 template <int NC>
@@ -1327,7 +1328,8 @@ int cheapest_tile(const GemmArgs& g, const TileCost (&c)[NC], int64_t* est_out =
   int best = 0;
   int64_t best_est = 0;
   for (int i = 0; i < NC; ++i) {
-    const int64_t est = (tiles_of(g, c[i].bm, c[i].bn) + 255) / 256 * c[i].bm * c[i].bn * c[i].cost;
+    const int64_t slots = 256 * (int64_t)c[i].bpc;
+    const int64_t est = (tiles_of(g, c[i].bm, c[i].bn) + slots - 1) / slots * c[i].bm * c[i].bn * c[i].cost;
     if (i == 0 || est < best_est) {
       best = i;
       best_est = est;
@@ -1447,11 +1449,18 @@ hipError_t launch_pc(const GemmArgs& g, hipStream_t st) {
 }
 
 // Per-group tiles, chosen by the same round-count estimate with costs measured
-// on MI355X at K = 10240 (the fp32 fold after every group makes per-group
-// VALU-heavy, so its costs differ from the per-channel ones). Wave tiles stay
-// at 64 x 64 / 64 x 80: the fp32 sums double the accumulator registers.
-// 256 x 160 is used for gs 128 only: with gs 64 (a fold at every MFMA step)
-// its registers spill.
+// on MI355X at N = 2560, K = 10240 (the fp32 fold after every group makes
+// per-group VALU-heavy, so its costs differ from the per-channel ones). Wave
+// tiles stay at 64 x 64 / 64 x 80: the fp32 sums double the accumulator
+// registers. All per-group blocks have 4 waves and are built for two blocks
+// per CU (<= 256 registers, <= 80 KB of LDS; 64 x 64 fits four): the fold is
+// VALU work that all waves of a block reach at the same point of each stage,
+// and blocks at different points let a SIMD overlap one wave's fold with
+// another wave's MFMAs. Same-box A/B against the former 8-wave 256 x 160 /
+// 256 x 128 tiles: gs 128, M=4096 203 -> 167 us, M=2048 159 -> 118 us, M=8192
+// 375 -> 324 us; per-token activations M=4096 175 -> 142 us (gs 128) and
+// 270 -> 197 us (gs 64). 128 x 160 is left out for gs 64 with both operands
+// per-group: its s_a segments push it past 256 registers.
 template <int GS, int EPI>
 hipError_t launch_pg(const GemmArgs& g, hipStream_t st) {
   if constexpr (EPI != kEpiAccI32) {
@@ -1462,18 +1471,17 @@ hipError_t launch_pg(const GemmArgs& g, hipStream_t st) {
       }
     }
   }
-  if constexpr (GS == 128) {
-    static constexpr TileCost kTiles[] = {{256, 160, 521}, {256, 128, 540}, {128, 128, 770}, {64, 64, 778}};
-    switch (cheapest_tile(g, kTiles)) {
-      case 0: return launch_dma_pg<256, 160, 4, 2, 2, GS, EPI>(g, st);
-      case 1: return launch_dma_pg<256, 128, 4, 2, 2, GS, EPI>(g, st);
-      case 2: return launch_dma_pg<128, 128, 2, 2, 2, GS, EPI>(g, st);
-      default: return launch_dma_pg<64, 64, 1, 4, 2, GS, EPI>(g, st);
-    }
+  constexpr bool kTok = EPI == kEpiF16Tok;
+  if constexpr (GS == 64 && !kTok) {
+    static constexpr TileCost kTiles[] = {{128, 128, 985, 2}, {64, 64, 2500, 4}};
+    if (cheapest_tile(g, kTiles) == 0) return launch_dma_pg<128, 128, 2, 2, 2, GS, EPI>(g, st);
+    return launch_dma_pg<64, 64, 1, 4, 2, GS, EPI>(g, st);
   } else {
-    static constexpr TileCost kTiles[] = {{256, 128, 665}, {128, 128, 1125}, {64, 64, 877}};
-    switch (cheapest_tile(g, kTiles)) {
-      case 0: return launch_dma_pg<256, 128, 4, 2, 2, GS, EPI>(g, st);
+    static constexpr TileCost kPg128[] = {{128, 160, 851, 2}, {128, 128, 737, 2}, {64, 64, 2033, 4}};
+    static constexpr TileCost kTok128[] = {{128, 160, 722, 2}, {128, 128, 648, 2}, {64, 64, 1660, 4}};
+    static constexpr TileCost kTok64[] = {{128, 160, 1001, 2}, {128, 128, 762, 2}, {64, 64, 2110, 4}};
+    switch (cheapest_tile(g, !kTok ? kPg128 : (GS == 128 ? kTok128 : kTok64))) {
+      case 0: return launch_dma_pg<128, 160, 2, 2, 2, GS, EPI>(g, st);
       case 1: return launch_dma_pg<128, 128, 2, 2, 2, GS, EPI>(g, st);
       default: return launch_dma_pg<64, 64, 1, 4, 2, GS, EPI>(g, st);
     }
