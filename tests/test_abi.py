@@ -200,7 +200,10 @@ def test_split_k_workspace_plan():
     assert g(4096, 10240, 2560, 8, 0) == 0                        # enough tiles: no split
     assert g(128, 10240, 2560, 8, 0) == 0                         # short K
     assert g(128, 2560, 10240, 8, 128) == 4 * 128 * 2560 * 4      # per-group: 64x64 tiles, fp32 partials
-    assert g(1024, 2560, 10240, 8, 128) == 0                      # per-group with enough tiles
+    assert g(1024, 2560, 10240, 8, 128) == 3 * 1024 * 2560 * 4    # per-group: 128x128 tiles, 3 K ranges
+    assert g(2048, 2560, 10240, 8, 128) == 2 * 2048 * 2560 * 4    # gs 128: 128x160 tiles, 2 K ranges
+    assert g(2048, 2560, 10240, 8, 64) == 0                       # gs 64: 320 tiles of 128x128, no split
+    assert g(4096, 2560, 10240, 8, 128) == 0                      # per-group with enough tiles
     assert g(16, 2560, 10240, 8, 0) == 0                          # skinny path
     assert g(0, 2560, 10240, 8, 0) == 0
     assert g(4, 4, 40, 8, 0) == -1 and g(4, 4, 64, 4, 64) == -1 and g(4, 4, 64, 6, 0) == -1

@@ -22,10 +22,16 @@ ONE_LAUNCH = [(1, 10240, 2560), (2, 2560, 10240), (2, 300, 1056), (2, 130, 32768
 
 
 def _two_calls(c, xd, wq, sw, bits, gs):
+    """quant_act + GEMM, the GEMM with its own split-K workspace when it plans
+    one (the one-call linear takes the same split, so the same bits)."""
+    M, K = xd.shape
+    N = wq.shape[0]
     xq, sa = c.cider_quant_act(xd, gs)
+    need = c.cider_gemm_workspace_size(M, N, K, bits, gs)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
     if bits == 8:
-        return host(c.cider_w8a8_gemm(xq, sa, wq, sw, gs))
-    return host(c.cider_w4a8_gemm(xq, sa, wq, sw))
+        return host(c.cider_w8a8_gemm(xq, sa, wq, sw, gs, workspace=ws))
+    return host(c.cider_w4a8_gemm(xq, sa, wq, sw, workspace=ws))
 
 
 @pytest.mark.parametrize("bits", [8, 4])

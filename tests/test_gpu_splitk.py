@@ -90,7 +90,17 @@ def test_split_k_workspace_reuse_and_linear():
 from tests.test_gpu_parity import pg_sum_bound  # noqa: E402
 from tests.test_gpu_token_group import token_group_bound  # noqa: E402
 
-PG = [(128, 2560, 10240, 128), (128, 2560, 10240, 64), (130, 650, 8192, 128), (64, 1024, 16384, 64)]
+# 64x64 tiles with 4 / 2 K ranges, then 128x128 with 3 (M=1024; ragged at
+# gs 64) and, for gs 128, 128x160 with 2 (M=2048; ragged M, N = 2498: scalar
+# stores in the reduction)
+PG = [(128, 2560, 10240, 128), (128, 2560, 10240, 64), (130, 650, 8192, 128), (64, 1024, 16384, 64),
+      (1024, 2560, 10240, 128), (1000, 2500, 8192, 64), (2048, 2560, 10240, 128), (1800, 2498, 4096, 128)]
+
+
+def _rows(M):
+    if M <= 256:
+        return np.arange(M)
+    return np.unique(np.r_[0, M - 1, np.random.default_rng(M).integers(0, M, 32)])
 
 
 @pytest.mark.parametrize("M,N,K,gs", PG)
@@ -104,19 +114,20 @@ def test_split_k_per_group(M, N, K, gs):
     wq, sw = c.cider_quant_weight(dev(w), 8, gs)
     xq, sa = c.cider_quant_act(dev(x), gs)
     y = host(c.cider_w8a8_gemm(xq, sa, wq, sw, gs, workspace=ws))
+    rows = _rows(M)
     wqo, swo = oracle.quantize_weight(w, 8, gs)
-    yo, qo, sao = oracle.w8a8_linear(x, wqo, swo, gs)
-    e = pg_sum_bound(qo, sao, wqo, swo, gs, np.arange(M))
-    assert_y_close(y, yo, 2e-3, extra_atol=e, what=f"split-K pg{gs} {M}x{N}x{K}")
+    yo, qo, sao = oracle.w8a8_linear(x[rows], wqo, swo, gs)
+    e = pg_sum_bound(qo, sao, wqo, swo, gs, np.arange(len(rows)))
+    assert_y_close(y[rows], yo, 2e-3, extra_atol=e, what=f"split-K pg{gs} {M}x{N}x{K}")
     # deterministic: the same bits again
     y2 = host(c.cider_w8a8_gemm(xq, sa, wq, sw, gs, workspace=ws))
     assert np.array_equal(y.view(np.uint16), y2.view(np.uint16))
 
 
-@pytest.mark.parametrize("gs", [128, 64])
-def test_split_k_token_group(gs):
+@pytest.mark.parametrize("M,gs", [(128, 128), (128, 64), (1024, 64), (2048, 128)])
+def test_split_k_token_group(M, gs):
     c = cider()
-    M, N, K = 128, 2560, 10240
+    N, K = 2560, 10240
     ws = torch.empty(c.cider_gemm_workspace_size(M, N, K, 8, gs), dtype=torch.uint8, device="cuda")
     assert ws.numel() > 0
     x = inputs.activations(M, K, seed=65)
@@ -124,10 +135,11 @@ def test_split_k_token_group(gs):
     wq, sw = c.cider_quant_weight(dev(w), 8, gs)
     xq, sa = c.cider_quant_act(dev(x), 0)
     y = host(c.cider_w8a8_gemm_token_group(xq, sa, wq, sw, gs, workspace=ws))
+    rows = _rows(M)
     wqo, swo = oracle.quantize_weight(w, 8, gs)
-    yo, qo, sao = oracle.w8a8_linear_token_group(x, wqo, swo, gs)
+    yo, qo, sao = oracle.w8a8_linear_token_group(x[rows], wqo, swo, gs)
     e = token_group_bound(qo, sao, wqo, swo, gs)
-    assert_y_close(y, yo, 2e-3, extra_atol=e, what=f"split-K token x pg{gs}")
+    assert_y_close(y[rows], yo, 2e-3, extra_atol=e, what=f"split-K token x pg{gs} M={M}")
 
 
 def test_split_k_per_group_bf16():

@@ -1354,26 +1354,37 @@ constexpr TileCost kTilesI4[] = {{256, 320, 62}, {128, 320, 92}, {128, 256, 102}
 // estimate (the margin pays for the reduction and the second launch).
 // Measured on MI355X (N=2560, K=10240): M=128 50.8 -> 18.2 us, M=256 50.9 ->
 // 24.1 us, M=1024 65.9 -> 46.6 us; outputs are bit-identical.
-// Per-group (gs 64 / 128, both operands or per-token activations) splits on
-// 64x64 tiles, whose units store fp32 partial sums: 4 K ranges up to 160
-// tiles, 2 up to 320, none beyond (K >= 4096, >= 1024 codes per range).
-// Measured on MI355X, N=2560, K=10240, gs 128 / 64: M=128 60.7 / 69.3 ->
-// 24.3 / 28.0 us, M=256 61.7 / 70.5 -> 31.7 / 35.3 us, M=512 65.7 / 75.3 ->
-// 52.8 / 64.6 us; at M=1024 splitting lost (the tile-cost model above
-// mispredicts these small-M per-group launches, hence a table by tile count).
+// Per-group (gs 64 / 128, both operands or per-token activations) units
+// store fp32 partial sums. Plan by tile count (K >= 4096, >= 1024 codes per
+// range): 64x64 tiles with 4 K ranges up to 160 tiles and 2 up to 320; else
+// 128x128 tiles with 3 ranges when 3 x tiles fill at most one round of two
+// blocks per CU (512); else, for gs 128, 128x160 tiles with 2 ranges on the
+// same condition; none beyond. Measured on MI355X, N=2560, K=10240, gs 128 /
+// 64: M=128 60.7 / 69.3 -> 24.3 / 28.0 us, M=256 61.7 / 70.5 -> 31.7 / 35.3
+// us, M=512 65.7 / 75.3 -> 52.8 / 64.6 us (64x64); M=1024 81.2 / 92.6 ->
+// 67.3 / 86.1 us (128x128, 3 ranges); gs 128 M=2048 129.0 -> 106.8 us
+// (128x160, 2 ranges). The tile-cost model above mispredicts these
+// launches, hence a table by tile count.
 struct SplitPlan {
-  int tile = -1;     // per-channel 0: 64x160, 1: 128x128, 2: 128x320; per-group: 64x64
+  int tile = -1;     // per-channel 0: 64x160, 1: 128x128, 2: 128x320; per-group 0: 64x64, 1: 128x128, 2: 128x160
   int splits = 0;
 };
 
 SplitPlan plan_split_pg(const GemmArgs& g) {
   SplitPlan plan;
   if (g.M <= 16 || g.K < 4096) return plan;
-  const int64_t t = tiles_of(g, 64, 64);
-  const int s = t <= 160 ? 4 : (t <= 320 ? 2 : 0);
-  if (s == 0 || g.K / s < 1024) return plan;
-  plan.tile = 1;
-  plan.splits = s;
+  const int64_t t64 = tiles_of(g, 64, 64), t128 = tiles_of(g, 128, 128), t160 = tiles_of(g, 128, 160);
+  if (t64 <= 320) {
+    plan.tile = 0;
+    plan.splits = t64 <= 160 ? 4 : 2;
+  } else if (3 * t128 <= 512) {
+    plan.tile = 1;
+    plan.splits = 3;
+  } else if (g.group_size == 128 && 2 * t160 <= 512) {
+    plan.tile = 2;
+    plan.splits = 2;
+  }
+  if (plan.splits && g.K / plan.splits < 1024) plan = SplitPlan{};
   return plan;
 }
 
@@ -1467,7 +1478,11 @@ hipError_t launch_pg(const GemmArgs& g, hipStream_t st) {
     if (g.ws) {
       const SplitPlan p = plan_split_pg(g);
       if (p.splits && g.ws_bytes >= split_ws_bytes(g.M, g.N, p.splits)) {
-        return launch_dma_pg_split<64, 64, 1, 4, 2, GS, EPI>(g, p.splits, st);
+        if (p.tile == 0) return launch_dma_pg_split<64, 64, 1, 4, 2, GS, EPI>(g, p.splits, st);
+        if constexpr (GS == 128) {
+          if (p.tile == 2) return launch_dma_pg_split<128, 160, 2, 2, 2, GS, EPI>(g, p.splits, st);
+        }
+        return launch_dma_pg_split<128, 128, 2, 2, 2, GS, EPI>(g, p.splits, st);
       }
     }
   }
