@@ -276,6 +276,35 @@ SWEEP = ([("w8a8_pc", M, 10240, 2560, 0) for M in (1, 128, 1024, 4096, 8192)] +
          [("w8a8_linear", 1, 10240, 2560, 0), ("w8a8_linear", 1, 2560, 10240, 0), ("w8a8_linear", 4, 10240, 2560, 0)])
 
 
+def sweep_indices(spec):
+    """Sweep row indices from "3", "0-4,9" or "" (all rows)."""
+    if not spec:
+        return list(range(len(SWEEP)))
+    out = []
+    for part in spec.split(","):
+        a, _, b = part.partition("-")
+        out.extend(range(int(a), int(b or a) + 1))
+    if any(i < 0 or i >= len(SWEEP) for i in out):
+        raise SystemExit(f"--sweep-rows: indices must lie in 0..{len(SWEEP) - 1}")
+    return out
+
+
+def run_sweep(cider, torch, inputs, indices, steps):
+    """Times the selected sweep configurations, each with its own roofline."""
+    rows = []
+    for i in indices:
+        mode, m, n, k, gs = SWEEP[i]
+        rr = measure(cider, torch, inputs, mode, m, n, k, gs, max(10, steps // 2), 3)
+        rows.append({"row": i, "mode": mode, "M": m, "N": n, "K": k, "group_size": gs,
+                     "gemm_us": round(rr["gemm_ms"] * 1e3, 2), "quant_us": round(rr["quant_ms"] * 1e3, 2),
+                     "gemm_roofline": roofline_of(rr["ops"], rr["gemm_bytes"], rr["gemm_ms"]),
+                     "quant_GBs": round(rr["quant_bytes"] / (rr["quant_ms"] * 1e-3) / 1e9, 1) if rr["quant_ms"] else None,
+                     "linear_TOPs": round(rr["ops"] / (rr["ms_per_step"] * 1e-3) / 1e12, 2),
+                     "split_k": bool(rr.get("split_k_ws"))})
+        print(json.dumps({"sweep_row": rows[-1]}), file=sys.stderr, flush=True)
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -288,6 +317,11 @@ def main():
                     help="also time the 28-layer Qwen3-VL-2B-shaped linear stack at seq 1024")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--sweep-rows", default="",
+                    help="with --sweep / --sweep-only: indices of the sweep rows to run, e.g. 3 or 0-4,9")
+    ap.add_argument("--sweep-only", action="store_true",
+                    help="run only the sweep rows (no headline step, no CPU baseline): one JSON line "
+                         "with the rows, for per-configuration profiler runs")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -301,6 +335,11 @@ def main():
     if not torch.cuda.is_available() or not cider.cider_is_available():
         print("bench.py needs a gfx950 GPU and the built libcider.so", file=sys.stderr)
         sys.exit(3)
+
+    if args.sweep_only:
+        rows = run_sweep(cider, torch, inputs, sweep_indices(args.sweep_rows), args.steps)
+        print(json.dumps({"sweep": rows, "kernel_source_sha": kernel_source_sha()}), flush=True)
+        return
 
     M, N, K = 4096, 10240, 2560
     r = measure(cider, torch, inputs, "w8a8_pc", M, N, K, 0, args.steps, args.warmup)
@@ -349,17 +388,7 @@ def main():
         "kernel_source_sha": sha,
     }
     if args.sweep:
-        rows = []
-        for mode, m, n, k, gs in SWEEP:
-            rr = measure(cider, torch, inputs, mode, m, n, k, gs, max(10, args.steps // 2), 3)
-            rows.append({"mode": mode, "M": m, "N": n, "K": k, "group_size": gs,
-                         "gemm_us": round(rr["gemm_ms"] * 1e3, 2), "quant_us": round(rr["quant_ms"] * 1e3, 2),
-                         "gemm_roofline": roofline_of(rr["ops"], rr["gemm_bytes"], rr["gemm_ms"]),
-                         "quant_GBs": round(rr["quant_bytes"] / (rr["quant_ms"] * 1e-3) / 1e9, 1) if rr["quant_ms"] else None,
-                         "linear_TOPs": round(rr["ops"] / (rr["ms_per_step"] * 1e-3) / 1e12, 2),
-                         "split_k": bool(rr.get("split_k_ws"))})
-            print(json.dumps({"sweep_row": rows[-1]}), file=sys.stderr, flush=True)
-        out["sweep"] = rows
+        out["sweep"] = run_sweep(cider, torch, inputs, sweep_indices(args.sweep_rows), args.steps)
     if args.stack:
         out["stack"] = measure_stack(cider, torch, inputs, max(3, args.steps // 10), 1)
     if not args.no_cpu_baseline:
