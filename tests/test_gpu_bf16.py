@@ -41,7 +41,9 @@ def act32(M, K, seed, scale=1.0):
 
 @pytest.mark.parametrize("M,K,gs,scale", [(7, 64, 0, 1.0), (37, 2560, 0, 3.0e4), (5, 10240, 0, 1.0),
                                           (3, 32768, 0, 1.0e-20), (33, 1024, 128, 1.0), (9, 10240, 64, 7.0e6),
-                                          (4, 20480, 128, 1.0)])
+                                          (4, 20480, 128, 1.0),
+                                          # fp32-subnormal scales: 1/s overflows for the smallest groups
+                                          (6, 256, 0, 1.0e-39), (5, 512, 64, 1.0e-41)])
 def test_bf16_quant_act_bit_exact(M, K, gs, scale):
     c = cider()
     xd = to_bf16_dev(act32(M, K, 51, scale))

@@ -795,13 +795,13 @@ gemm_gemv_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, con
       if (m < M && c * 16 < K && sc != 0.0f) {
         const uint4* xp = reinterpret_cast<const uint4*>(X) + ((int64_t)m * K + c * 16) / 8;
         const float inv = 1.0f / sc;
-        int q[16];
-        codes_of_chunk(xp[0], sc, inv, 127.0f, q);
-        codes_of_chunk(xp[1], sc, inv, 127.0f, q + 8);
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-          v[d] = (q[4 * d] & 0xFF) | ((q[4 * d + 1] & 0xFF) << 8) | ((q[4 * d + 2] & 0xFF) << 16) |
-                 (int)((uint32_t)(q[4 * d + 3] & 0xFF) << 24);
+        // min-max scale: no clamp needed (see code_bytes_of_chunk)
+        const uint2 q0 = code_bytes_of_chunk<false, false>(xp[0], sc, inv, 127.0f);
+        const uint2 q1 = code_bytes_of_chunk<false, false>(xp[1], sc, inv, 127.0f);
+        v[0] = (int)q0.x;
+        v[1] = (int)q0.y;
+        v[2] = (int)q1.x;
+        v[3] = (int)q1.y;
       }
     } else {
       if (m < M && c * 16 < K) v = *reinterpret_cast<const v4i*>(X + (int64_t)m * K + c * 16);

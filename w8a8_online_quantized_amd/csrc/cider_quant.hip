@@ -24,18 +24,17 @@ namespace {
 
 constexpr int kWaves = 4;                 // waves (rows) per workgroup
 
+// Stores the 8 code bytes of one chunk (element j in byte j): as int8, or as
+// int4 nibbles (code + 8, low nibble of byte b = even k, high = odd k).
 __device__ __forceinline__ void store_codes(void* q, int64_t row, int64_t K, int chunk, bool pack4,
-                                            const int c[8]) {
+                                            uint2 c) {
   if (!pack4) {
-    uint2 o;
-    o.x = (c[0] & 0xFF) | ((c[1] & 0xFF) << 8) | ((c[2] & 0xFF) << 16) | ((uint32_t)(c[3] & 0xFF) << 24);
-    o.y = (c[4] & 0xFF) | ((c[5] & 0xFF) << 8) | ((c[6] & 0xFF) << 16) | ((uint32_t)(c[7] & 0xFF) << 24);
-    *reinterpret_cast<uint2*>(static_cast<int8_t*>(q) + row * K + (int64_t)chunk * 8) = o;
+    *reinterpret_cast<uint2*>(static_cast<int8_t*>(q) + row * K + (int64_t)chunk * 8) = c;
   } else {
-    // nibble j holds code j + 8: low nibble of byte b = even k, high = odd k
+    // the low nibble of a two's complement code in [-8, 7], xor 8, is code + 8
     uint32_t o = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o |= (uint32_t)(c[j] + 8) << (4 * j);
+    for (int j = 0; j < 8; ++j) o |= ((((j < 4 ? c.x : c.y) >> (8 * (j & 3))) & 0xFu) ^ 0x8u) << (4 * j);
     *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(q) + row * (K / 2) + (int64_t)chunk * 4) = o;
   }
 }
@@ -82,8 +81,7 @@ __global__ __launch_bounds__(64 * kWaves) void quant_rows_reg(const uint4* __res
     for (int i = 0; i < CPL; ++i) {
       const int c = c0 + lane + 64 * i;
       if (c < cend) {
-        int cq[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (sc != 0.0f) codes_of_chunk<BF>(v[i], sc, inv, qmax, cq);
+        const uint2 cq = sc != 0.0f ? code_bytes_of_chunk<BF, false>(v[i], sc, inv, qmax) : make_uint2(0, 0);
         store_codes(q, row, K, c, pack4, cq);
       }
     }
@@ -101,8 +99,7 @@ __global__ __launch_bounds__(64 * kWaves) void quant_rows_reg(const uint4* __res
         const float sc = amax / qmax;
         if ((lane & (kCpg - 1)) == 0) s[row * G + c / kCpg] = sc;
         const float inv = 1.0f / sc;
-        int cq[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (sc != 0.0f) codes_of_chunk<BF>(v[i], sc, inv, qmax, cq);
+        const uint2 cq = sc != 0.0f ? code_bytes_of_chunk<BF, false>(v[i], sc, inv, qmax) : make_uint2(0, 0);
         store_codes(q, row, K, c, pack4, cq);
       }
     }
@@ -130,8 +127,7 @@ __global__ __launch_bounds__(256) void quant_rows_two_pass(const uint4* __restri
   if (threadIdx.x == 0) s[row] = sc;
   const float inv = 1.0f / sc;
   for (int c = threadIdx.x; c < C; c += 256) {
-    int cq[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (sc != 0.0f) codes_of_chunk<BF>(xr[c], sc, inv, qmax, cq);
+    const uint2 cq = sc != 0.0f ? code_bytes_of_chunk<BF, false>(xr[c], sc, inv, qmax) : make_uint2(0, 0);
     store_codes(q, row, K, c, pack4, cq);
   }
 }
@@ -224,8 +220,7 @@ __global__ __launch_bounds__(256) void quant_rows_clip(const uint4* __restrict__
   const float sc = scale;
   const float inv = 1.0f / sc;
   for (int c = threadIdx.x; c < C; c += 256) {
-    int cq[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (sc != 0.0f) codes_of_chunk<BF>(xg[c], sc, inv, qmax, cq);
+    const uint2 cq = sc != 0.0f ? code_bytes_of_chunk<BF, true>(xg[c], sc, inv, qmax) : make_uint2(0, 0);
     store_codes(q, row, K, g * C + c, pack4, cq);
   }
 }

@@ -45,24 +45,53 @@ __device__ __forceinline__ float elem_to_float(uint32_t bits) {
   else return half_bits_to_float(bits & 0xFFFFu);
 }
 
-// Code of one element given the group scale s (> 0) and inv = fl(1/s).
-__device__ __forceinline__ int code_of(float v, float s, float inv, float qmax) {
-  const float r = v * inv;
-  float t = __builtin_rintf(r);
-  if (__builtin_fabsf(r - t) > kNearHalf) t = __builtin_rintf(v / s);
-  t = __builtin_fminf(__builtin_fmaxf(t, -qmax), qmax);
-  return (int)t;
-}
-
-// 8 codes of one 16-byte chunk (8 fp16, or bf16 when BF, values).
-template <bool BF = false>
-__device__ __forceinline__ void codes_of_chunk(uint4 v, float s, float inv, float qmax, int q[8]) {
+// 8 codes of one 16-byte chunk (8 fp16, or bf16 when BF, values) as int8
+// bytes, element j in byte j of the result, by the rule above.
+// The integer is rounded by adding 1.5 * 2^23: for |r| < 2^22 the sum lands
+// in [2^23, 2^24), where the fp32 spacing is 1, so the round-to-nearest-even
+// addition yields rint(r) (ties to even, as the addend is even) in the low
+// mantissa bits, and the low byte of the pattern is rint(r) as a two's
+// complement byte. The near-half test runs per element but the exact-division
+// path is entered once per chunk, only when some lane needs it.
+// CLAMP: the scale may lie below max|v| / qmax (clipped scales), so r is
+// clamped to +-qmax first (clamping to integer bounds commutes with rint).
+// With min-max scales (s = fl(amax / qmax), amax = max|v| of the group)
+// |v * fl(1/s)| <= qmax * (1 + 3 * 2^-24) < qmax + 1/2 and |fl(v / s)| <=
+// qmax * (1 + 2^-24), so the clamp cannot act and is left out. A scale whose
+// reciprocal is not finite (bf16 groups below ~3.7e-37) sends every element
+// through the division.
+template <bool BF, bool CLAMP>
+__device__ __forceinline__ uint2 code_bytes_of_chunk(uint4 v, float s, float inv, float qmax) {
+  constexpr float kMagic = 12582912.0f;   // 1.5 * 2^23
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float x[8], r[8], t[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    q[2 * i] = code_of(elem_to_float<BF>(w[i]), s, inv, qmax);
-    q[2 * i + 1] = code_of(elem_to_float<BF>(w[i] >> 16), s, inv, qmax);
+    x[2 * i] = elem_to_float<BF>(w[i]);
+    x[2 * i + 1] = elem_to_float<BF>(w[i] >> 16);
   }
+  float worst = __builtin_isfinite(inv) ? 0.0f : 1.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    r[j] = x[j] * inv;
+    if constexpr (CLAMP) r[j] = __builtin_fminf(__builtin_fmaxf(r[j], -qmax), qmax);
+    t[j] = r[j] + kMagic;
+    worst = __builtin_fmaxf(worst, __builtin_fabsf((t[j] - kMagic) - r[j]));
+  }
+  if (worst > kNearHalf) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (!(__builtin_fabsf((t[j] - kMagic) - r[j]) <= kNearHalf) || !__builtin_isfinite(inv))
+        t[j] = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(x[j] / s), -qmax), qmax) + kMagic;
+    }
+  }
+  uint32_t b[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) b[j] = __builtin_bit_cast(uint32_t, t[j]);
+  uint2 o;
+  o.x = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u) | __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu);
+  o.y = __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u) | __builtin_amdgcn_perm(b[7], b[6], 0x04000c0cu);
+  return o;
 }
 
 }  // namespace cider
