@@ -305,7 +305,10 @@ typedef struct {
  * offset: 0 codes int8 [M, max(hidden, q_dim, mlp_dim)], 1 scales fp32 [M],
  * 2 Q fp16 [M, q_dim], 3 K fp16 [M, kv_dim], 4 V fp16 [M, kv_dim],
  * 5 O fp16 [M, hidden], 6 G fp16 [M, mlp_dim], 7 U fp16 [M, mlp_dim],
- * 8 h fp16 [M, hidden] (layer output ping buffer).
+ * 8 h fp16 [M, hidden] (layer output ping buffer), then a region not listed
+ * in `offsets`: the int32 partial sums of the per-projection GEMMs whose K is
+ * split (as cider_gemm_workspace_size plans it; e.g. the down projection at
+ * M = 1024, mlp_dim = 6144), sized for the largest of them (may be empty).
  * Writes the 9 byte offsets into `offsets` (may be NULL) and returns the total
  * size in bytes (0 for invalid dims). Host-only, no HIP call. */
 int64_t cider_stack_workspace_layout(int64_t M, int64_t hidden, int64_t q_dim, int64_t kv_dim,

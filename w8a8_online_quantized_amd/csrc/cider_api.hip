@@ -344,26 +344,49 @@ cider_status_t cider_gemm_acc_i32(int32_t mode, const int8_t* x_q, const void* w
   return gemm_common(g, mode == 1 ? cider::kWeightI4 : cider::kWeightI8, cider::kEpiAccI32, stream);
 }
 
-int64_t cider_stack_workspace_layout(int64_t M, int64_t hidden, int64_t q_dim, int64_t kv_dim, int64_t mlp_dim,
-                                     int64_t* offsets) {
+}  // extern "C"
+
+// Stack workspace regions 0..8 (see include/cider.h) plus region 9: the int32
+// partial sums of a split-K GEMM (the largest the stack's per-projection GEMMs
+// need; 0 bytes when none splits). Returns the total, 0 for invalid dims.
+static int64_t stack_layout(int64_t M, int64_t hidden, int64_t q_dim, int64_t kv_dim, int64_t mlp_dim,
+                            int64_t off[10]) {
   if (M < 0 || hidden <= 0 || q_dim <= 0 || kv_dim <= 0 || mlp_dim <= 0) return 0;
   if (hidden % 16 || q_dim % 16 || kv_dim % 16 || mlp_dim % 16) return 0;
   const int64_t kmax = std::max(hidden, std::max(q_dim, mlp_dim));
-  const int64_t sizes[9] = {M * kmax, 4 * M, 2 * M * q_dim, 2 * M * kv_dim, 2 * M * kv_dim,
-                            2 * M * hidden, 2 * M * mlp_dim, 2 * M * mlp_dim, 2 * M * hidden};
-  int64_t off = 0;
-  for (int i = 0; i < 9; ++i) {
-    if (offsets) offsets[i] = off;
-    off += (sizes[i] + 255) / 256 * 256;
+  int64_t split = 0;
+  if (M > 0) {
+    const int64_t nk[4][2] = {{q_dim, hidden}, {kv_dim, hidden}, {hidden, q_dim}, {mlp_dim, hidden}};
+    for (const auto& p : nk)
+      split = std::max(split, cider::gemm_split_workspace_bytes(M, p[0], p[1], cider::kWeightI8, 0));
+    split = std::max(split, cider::gemm_split_workspace_bytes(M, hidden, mlp_dim, cider::kWeightI8, 0));
   }
-  return off;
+  const int64_t sizes[10] = {M * kmax, 4 * M, 2 * M * q_dim, 2 * M * kv_dim, 2 * M * kv_dim,
+                             2 * M * hidden, 2 * M * mlp_dim, 2 * M * mlp_dim, 2 * M * hidden, split};
+  int64_t o = 0;
+  for (int i = 0; i < 10; ++i) {
+    off[i] = o;
+    o += (sizes[i] + 255) / 256 * 256;
+  }
+  return o;
+}
+
+extern "C" {
+
+int64_t cider_stack_workspace_layout(int64_t M, int64_t hidden, int64_t q_dim, int64_t kv_dim, int64_t mlp_dim,
+                                     int64_t* offsets) {
+  int64_t off[10];
+  const int64_t total = stack_layout(M, hidden, q_dim, kv_dim, mlp_dim, off);
+  if (total && offsets)
+    for (int i = 0; i < 9; ++i) offsets[i] = off[i];
+  return total;
 }
 
 cider_status_t cider_stack_forward(const void* x_f16, int64_t M, int64_t hidden, int64_t q_dim, int64_t kv_dim,
                                    int64_t mlp_dim, int32_t n_layers, const cider_stack_layer_t* layers,
                                    void* workspace, int64_t workspace_bytes, void* y_f16, void* stream) {
-  int64_t off[9];
-  const int64_t need = cider_stack_workspace_layout(M, hidden, q_dim, kv_dim, mlp_dim, off);
+  int64_t off[10];
+  const int64_t need = stack_layout(M, hidden, q_dim, kv_dim, mlp_dim, off);
   if (need == 0 || n_layers < 0 || M >= (int64_t(1) << 31)) return CIDER_ERROR_INVALID_VALUE;
   if (std::max(hidden, std::max(q_dim, mlp_dim)) > CIDER_MAX_K) return CIDER_ERROR_INVALID_VALUE;
   if (M == 0 || n_layers == 0) return CIDER_SUCCESS;
@@ -390,6 +413,12 @@ cider_status_t cider_stack_forward(const void* x_f16, int64_t M, int64_t hidden,
   auto quant = [&](const void* in, int64_t K) { return cider::launch_quant_rows(in, M, K, 0, 127, xq, sa, st); };
   auto gemm = [&](const cider_stack_layer_t& L, int j, int64_t N, int64_t K, void* out) {
     cider::GemmArgs a{xq, sa, L.w[j], L.s[j], M, N, K, 0, out, nullptr};
+    // split-K partials (e.g. the long-K down projection); stream order keeps
+    // one GEMM's partials from overlapping the next one's
+    if (need > off[9]) {
+      a.ws = ws + off[9];
+      a.ws_bytes = need - off[9];
+    }
     return cider::launch_gemm(a, cider::kWeightI8, cider::kEpiF16, st);
   };
   // Projections j, j+1[, j+2] of one input as one GEMM when their codes and
