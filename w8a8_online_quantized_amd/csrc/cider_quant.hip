@@ -39,30 +39,41 @@ __device__ __forceinline__ void store_codes(void* q, int64_t row, int64_t K, int
   }
 }
 
-// One wave per row, row held in registers: CPL = 16-byte chunks per lane.
-// GS = 0 (one scale per row; the whole row, K <= 512 * CPL, is one segment)
-// or 64 / 128 (groups never straddle a segment, so long rows are split into
-// segments of kSegChunks chunks along gridDim.y).
+// Row held in registers: CPL = 16-byte chunks per lane. WPR = 1: one wave
+// per row (kWaves rows per workgroup), lane L owning chunks L + 64i. WPR = 4:
+// one workgroup of 4 waves per row segment (long rows), wave w owning chunks
+// 64w + L + 256i, so each wave holds a quarter of the row in a quarter of the
+// registers and more waves stay resident to overlap one row's loads with
+// another's codes; the row max then goes through LDS.
+// GS = 0 (one scale per row; the whole row, K <= 8 * 64 * WPR * CPL, is one
+// segment) or 64 / 128 (groups never straddle a segment, so long rows are
+// split into segments of kSegChunks chunks along gridDim.y; a group's chunks
+// are consecutive lanes of one wave either way).
 constexpr int kSegChunks = 64 * 32;
+constexpr int kWgMinChunks = 256;   // K >= 2048
 
-template <int CPL, int GS, bool BF>
+template <int CPL, int GS, bool BF, int WPR>
 __global__ __launch_bounds__(64 * kWaves) void quant_rows_reg(const uint4* __restrict__ x, int64_t R,
                                                               int64_t K, float qmax, bool pack4,
                                                               void* __restrict__ q,
                                                               float* __restrict__ s) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (row >= R) return;
+  static_assert(WPR == 1 || WPR == kWaves, "one row per wave or per workgroup");
+  static_assert(64 * WPR * CPL <= kSegChunks, "a segment fits the registers");
+  constexpr int kStride = 64 * WPR;                     // chunks between a lane's slots
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = WPR == 1 ? (int64_t)blockIdx.x * kWaves + wave : (int64_t)blockIdx.x;
+  if (row >= R) return;                                 // uniform per workgroup when WPR > 1
   const int C = (int)(K / 8);
   const int c0 = (int)blockIdx.y * kSegChunks;          // first chunk of this segment
   const int cend = min(C, c0 + kSegChunks);
+  const int cl = c0 + (WPR == 1 ? lane : 64 * wave + lane);   // this lane's first chunk
   const uint4* xr = x + row * C;
 
   uint4 v[CPL];
   uint32_t m[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
-    const int c = c0 + lane + 64 * i;
+    const int c = cl + kStride * i;
     v[i] = c < cend ? xr[c] : make_uint4(0, 0, 0, 0);
     m[i] = abs_max_bits(v[i]);
   }
@@ -73,13 +84,20 @@ __global__ __launch_bounds__(64 * kWaves) void quant_rows_reg(const uint4* __res
     for (int i = 0; i < CPL; ++i) a = max(a, m[i]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) a = max(a, (uint32_t)__shfl_xor((int)a, off));
+    if constexpr (WPR > 1) {
+      __shared__ uint32_t red[WPR];
+      if (lane == 0) red[wave] = a;
+      __syncthreads();
+#pragma unroll
+      for (int w = 0; w < WPR; ++w) a = max(a, red[w]);
+    }
     const float amax = elem_to_float<BF>(a);
     const float sc = amax / qmax;
-    if (lane == 0) s[row] = sc;
+    if (threadIdx.x == 0 || (WPR == 1 && lane == 0)) s[row] = sc;
     const float inv = 1.0f / sc;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-      const int c = c0 + lane + 64 * i;
+      const int c = cl + kStride * i;
       if (c < cend) {
         const uint2 cq = sc != 0.0f ? code_bytes_of_chunk<BF, false>(v[i], sc, inv, qmax) : make_uint2(0, 0);
         store_codes(q, row, K, c, pack4, cq);
@@ -93,7 +111,7 @@ __global__ __launch_bounds__(64 * kWaves) void quant_rows_reg(const uint4* __res
       uint32_t a = m[i];
 #pragma unroll
       for (int off = kCpg / 2; off >= 1; off >>= 1) a = max(a, (uint32_t)__shfl_xor((int)a, off));
-      const int c = c0 + lane + 64 * i;
+      const int c = cl + kStride * i;
       if (c < cend) {
         const float amax = elem_to_float<BF>(a);
         const float sc = amax / qmax;
@@ -225,17 +243,23 @@ __global__ __launch_bounds__(256) void quant_rows_clip(const uint4* __restrict__
   }
 }
 
-template <int GS, bool BF>
+template <int GS, bool BF, int WPR>
 hipError_t launch_reg(int cpl, int segs, const uint4* x, int64_t R, int64_t K, float qmax, bool pack4,
                       void* q, float* s, hipStream_t st) {
-  const dim3 grid((unsigned)((R + kWaves - 1) / kWaves), (unsigned)segs), block(64 * kWaves);
+  const int64_t blocks = WPR == 1 ? (R + kWaves - 1) / kWaves : R;
+  const dim3 grid((unsigned)blocks, (unsigned)segs), block(64 * kWaves);
   switch (cpl) {
-    case 1: quant_rows_reg<1, GS, BF><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
-    case 2: quant_rows_reg<2, GS, BF><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
-    case 4: quant_rows_reg<4, GS, BF><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
-    case 8: quant_rows_reg<8, GS, BF><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
-    case 16: quant_rows_reg<16, GS, BF><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
-    default: quant_rows_reg<32, GS, BF><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
+    case 1: quant_rows_reg<1, GS, BF, WPR><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
+    case 2: quant_rows_reg<2, GS, BF, WPR><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
+    case 4: quant_rows_reg<4, GS, BF, WPR><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
+    case 8: quant_rows_reg<8, GS, BF, WPR><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
+    case 16:
+      if constexpr (WPR == 1) { quant_rows_reg<16, GS, BF, 1><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break; }
+      [[fallthrough]];
+    default:
+      if constexpr (WPR == 1) quant_rows_reg<32, GS, BF, 1><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s);
+      else return hipErrorInvalidValue;
+      break;
   }
   return hipGetLastError();
 }
@@ -253,12 +277,18 @@ hipError_t launch_quant_t(const void* x, int64_t R, int64_t K, int group_size, i
   }
   const int64_t segs = (C + kSegChunks - 1) / kSegChunks;
   const int64_t per_seg = segs > 1 ? kSegChunks : C;
+  // segments of >= kWgMinChunks chunks (K >= 2048): a workgroup per segment
+  const bool wg = per_seg >= kWgMinChunks;
+  const int lanes = wg ? 64 * kWaves : 64;
   int cpl = 1;
-  while (64 * cpl < per_seg) cpl *= 2;
+  while (lanes * cpl < per_seg) cpl *= 2;
   switch (group_size) {
-    case 0: return launch_reg<0, BF>(cpl, 1, xv, R, K, fq, pack4, q, s, stream);
-    case 64: return launch_reg<64, BF>(cpl, (int)segs, xv, R, K, fq, pack4, q, s, stream);
-    default: return launch_reg<128, BF>(cpl, (int)segs, xv, R, K, fq, pack4, q, s, stream);
+    case 0: return wg ? launch_reg<0, BF, kWaves>(cpl, 1, xv, R, K, fq, pack4, q, s, stream)
+                      : launch_reg<0, BF, 1>(cpl, 1, xv, R, K, fq, pack4, q, s, stream);
+    case 64: return wg ? launch_reg<64, BF, kWaves>(cpl, (int)segs, xv, R, K, fq, pack4, q, s, stream)
+                       : launch_reg<64, BF, 1>(cpl, (int)segs, xv, R, K, fq, pack4, q, s, stream);
+    default: return wg ? launch_reg<128, BF, kWaves>(cpl, (int)segs, xv, R, K, fq, pack4, q, s, stream)
+                       : launch_reg<128, BF, 1>(cpl, (int)segs, xv, R, K, fq, pack4, q, s, stream);
   }
 }
 
