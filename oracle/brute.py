@@ -200,9 +200,11 @@ def mv(x_rows, w_codes, w_scales, group_size: int):
     return y
 
 
-def linear_token_group(x_rows, w_codes, w_scales, group_size: int):
+def linear_token_group(x_rows, w_codes, w_scales, group_size: int, out=None):
     """Per-token activation codes (one scale per row) against per-group weight
-    codes: y[m][n] = f16( sum_g acc_g * s_a[m] * s_w[n][g] ), exact."""
+    codes: y[m][n] = f16( sum_g acc_g * s_a[m] * s_w[n][g] ), exact; `out`
+    rounds the exact sum instead (bf16 for a bfloat16 output)."""
+    out_round = f16 if out is None else out
     K = len(x_rows[0]) if x_rows else 0
     y = []
     for row in x_rows:
@@ -212,6 +214,6 @@ def linear_token_group(x_rows, w_codes, w_scales, group_size: int):
             t = sum(Fraction(dot(c[g * group_size:(g + 1) * group_size],
                                  w_codes[n][g * group_size:(g + 1) * group_size])) * s[0] * w_scales[n][g]
                     for g in range(K // group_size))
-            out.append(f16(t))
+            out.append(out_round(t))
         y.append(out)
     return y

@@ -427,6 +427,25 @@ def dequant_token_group(acc_g: np.ndarray, s_a: np.ndarray, s_w: np.ndarray) -> 
         return y.astype(np.float16)
 
 
+def dequant_token_group_bf16(acc_g: np.ndarray, s_a: np.ndarray, s_w: np.ndarray) -> np.ndarray:
+    """dequant_token_group with a bfloat16 output: the same fp64 value
+    sum_g acc_g[g, m, n] * s_a[m] * s_w[n, g], rounded once to bf16 (uint16
+    patterns [M, N])."""
+    G = acc_g.shape[0]
+    sa = s_a.reshape(-1).astype(np.float64)[:, None]
+    y = np.zeros(acc_g.shape[1:], np.float64)
+    for g in range(G):
+        y += (acc_g[g].astype(np.float64) * sa) * s_w[:, g].astype(np.float64)[None, :]
+    return f64_to_bf16(y)
+
+
+def w8a8_linear_token_group_bf16(x_bits: np.ndarray, w_q: np.ndarray, s_w: np.ndarray, group_size: int):
+    """w8a8_linear_token_group with bf16 activations in (uint16 patterns) and
+    a bf16 output. Returns (y, q_a, s_a)."""
+    q_a, s2 = quantize_rows_bf16(x_bits, 0, QMAX_INT8)
+    return dequant_token_group_bf16(int_dot_groups(q_a, w_q, group_size), s2[:, 0], s_w), q_a, s2[:, 0]
+
+
 def w8a8_linear_token_group(x: np.ndarray, w_q: np.ndarray, s_w: np.ndarray, group_size: int):
     """Per-token activation codes (one scale per row of x) against per-group
     weight codes (group_size 64 or 128 along K). Returns (y, q_a, s_a)."""

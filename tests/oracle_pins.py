@@ -578,6 +578,29 @@ def check_brute_linear_bf16(impl, trials=24, seed=22):
                 assert float(yv[m, n]) == float(by[m][n]), (t, m, n, float(yv[m, n]), float(by[m][n]))
 
 
+def check_brute_token_group_bf16(impl, trials=18, seed=24):
+    """bf16 rows in, per-token codes against per-group weight codes, bf16 out,
+    against the exact-arithmetic reference rounded once to bf16."""
+    rng = np.random.default_rng(seed)
+    for t in range(trials):
+        M, N = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        gs = [2, 4, 8][t % 3]
+        K = gs * int(rng.integers(1, 4))
+        xf = _rand_fp16(rng, (M, K), ["normal", "wide", "ties"][t % 3]).astype(np.float32)
+        xb = (xf.view(np.uint32) >> np.uint32(16)).astype(np.uint16)      # truncated to bf16
+        w = _rand_fp16(rng, (N, K), ["normal", "wide", "small"][t % 3])
+        qw, sw = impl.quantize_rows(w, gs, 127)
+        qa, sa = impl.quantize_rows_bf16(xb, 0, 127)
+        y = impl.dequant_token_group_bf16(impl.int_dot_groups(qa, qw, gs), sa[:, 0], sw)
+        xr = [[float(v) for v in row] for row in impl.bf16_to_f32(xb)]
+        by = brute.linear_token_group(xr, qw.astype(int).tolist(), [[Fraction(float(v)) for v in row] for row in sw],
+                                      gs, out=brute.bf16)
+        yv = impl.bf16_to_f32(y)
+        for m in range(M):
+            for n in range(N):
+                assert float(yv[m, n]) == float(by[m][n]), (t, m, n, float(yv[m, n]), float(by[m][n]))
+
+
 def check_bf16_reductions(impl, seed=23):
     """bf16 rows whose values are fp16 values too quantize exactly as the fp16
     rows do; a bf16 output equals the fp16 output wherever the exact value
@@ -609,4 +632,5 @@ ALL_CHECKS = [
     check_golden_token_group, check_brute_token_group, check_token_group_reductions,
     check_golden_clip, check_brute_clip, check_clip_vs_numpy_percentile, check_clip_reductions,
     check_golden_bf16, check_brute_bf16_rounding, check_brute_linear_bf16, check_bf16_reductions,
+    check_brute_token_group_bf16,
 ]

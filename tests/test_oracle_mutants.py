@@ -14,7 +14,7 @@ def _impl(**over):
         "quantize_rows", "pack_int4", "unpack_int4", "int_dot", "int_dot_groups",
         "dequant_per_channel", "dequant_per_group", "int8_mv", "dequant_token_group",
         "percentile_threshold", "quantize_rows_clip", "f64_to_bf16", "bf16_to_f32", "quantize_rows_bf16",
-        "dequant_bf16")}
+        "dequant_bf16", "dequant_token_group_bf16")}
     base.update(over)
     ns = types.SimpleNamespace(**base)
     return ns
@@ -203,6 +203,10 @@ def _bf16_variant(kind):
     return _impl(f64_to_bf16=rnd, dequant_bf16=deq, quantize_rows_bf16=quant)
 
 
+def _tok_bf16_no_act_scale(acc_g, s_a, s_w):
+    return O.dequant_token_group_bf16(acc_g, np.ones_like(s_a), s_w)
+
+
 MUTANTS = {
     "round_half_up": _impl(quantize_rows=_quant_variant(rounding="up")),
     "scale_over_128": _impl(quantize_rows=_quant_variant(divisor_bias=1)),
@@ -235,6 +239,7 @@ MUTANTS = {
     "bf16_truncation": _bf16_variant("truncate"),
     "bf16_double_rounding_via_fp32": _bf16_variant("via_fp32"),
     "bf16_rows_read_as_fp16": _bf16_variant("as_fp16"),
+    "token_group_bf16_no_act_scale": _impl(dequant_token_group_bf16=_tok_bf16_no_act_scale),
 }
 
 
