@@ -227,6 +227,13 @@ cider_status_t cider_w8a8_gemm_token_group(const int8_t* x_q, const float* x_sca
                                            const float* w_scale, int64_t M, int64_t N, int64_t K,
                                            int32_t group_size, void* y_f16, void* workspace,
                                            int64_t workspace_bytes, void* stream);
+/* The same with the output type chosen by y_dtype (a cider_dtype_t): bf16
+ * rounds the same fp32 value x_scale[m] * sum to bfloat16 (nearest, ties to
+ * even) instead of fp16. */
+cider_status_t cider_w8a8_gemm_token_group_dt(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
+                                              const float* w_scale, int64_t M, int64_t N, int64_t K,
+                                              int32_t group_size, void* y, int32_t y_dtype, void* workspace,
+                                              int64_t workspace_bytes, void* stream);
 
 /* Same-input projections as one GEMM (the README's experimental SplitLinear
  * page prepares the input of the Q/K/V and gate/up projections once): the

@@ -81,6 +81,7 @@ __all__ = [
     "dequant_token_group", "w8a8_linear_token_group", "percentile_threshold", "quantize_rows_clip",
     "quantize_weight_clip", "bf16_to_f32", "f64_to_bf16", "quantize_rows_bf16", "quantize_weight_bf16",
     "quantize_weight_clip_bf16", "dequant_bf16", "w8a8_linear_bf16", "w4a8_linear_bf16",
+    "dequant_token_group_bf16", "w8a8_linear_token_group_bf16",
 ]
 
 QMAX_INT8 = 127

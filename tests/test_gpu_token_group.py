@@ -121,3 +121,32 @@ def test_token_group_deterministic_and_stream_ordered():
         y1 = c.cider_w8a8_gemm_token_group(xq, sa, wq, sw, gs, stream=s)
     s.synchronize()
     assert np.array_equal(y0.view(np.uint16), host(y1).view(np.uint16))
+
+
+# bf16 rows in, bf16 out (cider_w8a8_gemm_token_group_dt): the skinny kernel,
+# the 64x64 / 128x128 / 128x160 tiles with ragged tails, and both split-K plans
+@pytest.mark.parametrize("M,N,K,gs,split", [(3, 5, 128, 128, False), (16, 70, 2560, 64, False),
+                                            (130, 300, 1152, 64, False), (520, 260, 2560, 128, False),
+                                            (4000, 2500, 1280, 128, False), (2000, 2498, 1280, 64, False),
+                                            (128, 2560, 10240, 128, True), (1024, 2560, 10240, 64, True)])
+def test_token_group_bf16(M, N, K, gs, split):
+    from tests.test_gpu_bf16 import bits, to_bf16_dev
+    c = cider()
+    xd = to_bf16_dev(inputs.activations(M, K, seed=23).astype(np.float32))
+    w = inputs.weights(N, K, seed=23)
+    wq, sw = c.cider_quant_weight(dev(w), 8, gs)
+    xq, sa = c.cider_quant_act(xd, 0)
+    ws = None
+    if split:
+        wsb = c.cider_gemm_workspace_size(M, N, K, 8, gs)
+        assert wsb > 0
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    y = bits(c.cider_w8a8_gemm_token_group(xq, sa, wq, sw, gs, workspace=ws, out_dtype=torch.bfloat16))
+    rows = np.arange(M) if M <= 520 else sampled(M)
+    wqo, swo = oracle.quantize_weight(w, 8, gs)
+    yo, qo, sao = oracle.w8a8_linear_token_group_bf16(bits(xd)[rows], wqo, swo, gs)
+    assert np.array_equal(host(xq)[rows], qo) and np.array_equal(host(sa)[rows], sao)
+    e = token_group_bound(qo, sao, wqo, swo, gs)
+    yv, ov = oracle.bf16_to_f32(y[rows]).astype(np.float64), oracle.bf16_to_f32(yo).astype(np.float64)
+    # one bf16 ulp (at most 2^-7 |o|) plus the fp32 summation bound
+    assert np.all(np.abs(yv - ov) <= 2.0 ** -7 * np.abs(ov) + e + 2.0 ** -133), float(np.abs(yv - ov).max())

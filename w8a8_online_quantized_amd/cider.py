@@ -35,6 +35,8 @@ SIGNATURES = {
     "cider_gemm_acc_i32": (ctypes.c_int, [_c_i32, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p]),
     "cider_w8a8_gemm_token_group": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p,
                                                    _c_p, _c_i64, _c_p]),
+    "cider_w8a8_gemm_token_group_dt": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p,
+                                                      _c_i32, _c_p, _c_i64, _c_p]),
     "cider_w8a8_gemm_split": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_p, _c_p, _c_p]),
     "cider_linear_workspace_size": (ctypes.c_int64, [_c_i64, _c_i64, _c_i64, _c_i32, _c_i32]),
     "cider_gemm_workspace_size": (ctypes.c_int64, [_c_i64, _c_i64, _c_i64, _c_i32, _c_i32]),
@@ -249,9 +251,11 @@ def cider_w8a8_gemm(x_q, x_scale, w_q, w_scale, group_size: int = 0, y=None, str
     return y
 
 
-def cider_w8a8_gemm_token_group(x_q, x_scale, w_q, w_scale, group_size: int, y=None, stream=None, workspace=None):
+def cider_w8a8_gemm_token_group(x_q, x_scale, w_q, w_scale, group_size: int, y=None, stream=None, workspace=None,
+                                out_dtype=None):
     """Per-token activation codes (x_scale [M]) times per-group weight codes
-    (w_scale [N, K/group_size], group_size 64 or 128) -> fp16 y [M, N]."""
+    (w_scale [N, K/group_size], group_size 64 or 128) -> y [M, N]: fp16, or
+    bf16 when out_dtype (or a given y) is bfloat16."""
     import torch
     M, K = x_q.shape
     N = w_q.shape[0]
@@ -262,11 +266,12 @@ def cider_w8a8_gemm_token_group(x_q, x_scale, w_q, w_scale, group_size: int, y=N
     _need(x_scale, torch.float32, (M,), "x_scale")
     _need(w_scale, torch.float32, _scale_shape(N, K, group_size), "w_scale")
     if y is None:
-        y = torch.empty((M, N), dtype=torch.float16, device=x_q.device)
-    _need(y, torch.float16, (M, N), "y")
-    _check("cider_w8a8_gemm_token_group",
-           lib().cider_w8a8_gemm_token_group(_ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale), M, N, K,
-                                             group_size, _ptr(y), *_ws_args(workspace), _stream(stream)))
+        y = torch.empty((M, N), dtype=out_dtype or torch.float16, device=x_q.device)
+    dt = _fp_code(y, "y")
+    _need(y, y.dtype, (M, N), "y")
+    _check("cider_w8a8_gemm_token_group_dt",
+           lib().cider_w8a8_gemm_token_group_dt(_ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale), M, N, K,
+                                                group_size, _ptr(y), dt, *_ws_args(workspace), _stream(stream)))
     return y
 
 

@@ -229,22 +229,32 @@ cider_status_t cider_w4a8_gemm_ex(const int8_t* x_q, const float* x_scale, const
   return gemm_common(g, cider::kWeightI4, y_dtype == CIDER_DTYPE_BF16 ? cider::kEpiBF16 : cider::kEpiF16, stream);
 }
 
+cider_status_t cider_w8a8_gemm_token_group_dt(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
+                                              const float* w_scale, int64_t M, int64_t N, int64_t K,
+                                              int32_t group_size, void* y, int32_t y_dtype, void* workspace,
+                                              int64_t workspace_bytes, void* stream) {
+  if (!valid_dtype(y_dtype)) return CIDER_ERROR_INVALID_VALUE;
+  if (!gemm_sizes_ok(M, N) || (group_size != 64 && group_size != 128) || !valid_k(K, 16, group_size))
+    return CIDER_ERROR_INVALID_VALUE;
+  if (M == 0 || N == 0) return CIDER_SUCCESS;
+  if (!x_q || !x_scale || !w_q || !w_scale || !y) return CIDER_ERROR_INVALID_VALUE;
+  if (!aligned16(x_q) || !aligned16(x_scale) || !aligned16(w_q) || !aligned16(w_scale) || !aligned16(y))
+    return CIDER_ERROR_INVALID_VALUE;
+  if (!workspace_ok(workspace, workspace_bytes, cider_gemm_workspace_size(M, N, K, 8, group_size)))
+    return CIDER_ERROR_INVALID_VALUE;
+  cider::GemmArgs g{x_q, x_scale, w_q, w_scale, M, N, K, group_size, y, nullptr};
+  g.ws = workspace;
+  g.ws_bytes = workspace ? workspace_bytes : 0;
+  return gemm_common(g, cider::kWeightI8, y_dtype == CIDER_DTYPE_BF16 ? cider::kEpiBF16Tok : cider::kEpiF16Tok,
+                     stream);
+}
+
 cider_status_t cider_w8a8_gemm_token_group(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
                                            const float* w_scale, int64_t M, int64_t N, int64_t K,
                                            int32_t group_size, void* y_f16, void* workspace,
                                            int64_t workspace_bytes, void* stream) {
-  if (!gemm_sizes_ok(M, N) || (group_size != 64 && group_size != 128) || !valid_k(K, 16, group_size))
-    return CIDER_ERROR_INVALID_VALUE;
-  if (M == 0 || N == 0) return CIDER_SUCCESS;
-  if (!x_q || !x_scale || !w_q || !w_scale || !y_f16) return CIDER_ERROR_INVALID_VALUE;
-  if (!aligned16(x_q) || !aligned16(x_scale) || !aligned16(w_q) || !aligned16(w_scale) || !aligned16(y_f16))
-    return CIDER_ERROR_INVALID_VALUE;
-  if (!workspace_ok(workspace, workspace_bytes, cider_gemm_workspace_size(M, N, K, 8, group_size)))
-    return CIDER_ERROR_INVALID_VALUE;
-  cider::GemmArgs g{x_q, x_scale, w_q, w_scale, M, N, K, group_size, y_f16, nullptr};
-  g.ws = workspace;
-  g.ws_bytes = workspace ? workspace_bytes : 0;
-  return gemm_common(g, cider::kWeightI8, cider::kEpiF16Tok, stream);
+  return cider_w8a8_gemm_token_group_dt(x_q, x_scale, w_q, w_scale, M, N, K, group_size, y_f16, CIDER_DTYPE_F16,
+                                        workspace, workspace_bytes, stream);
 }
 
 cider_status_t cider_w8a8_gemm_split(const int8_t* x_q, const float* x_scale, const int8_t* w_q,

@@ -105,6 +105,13 @@ __device__ __forceinline__ __bf16 to_bf16(float t) {
   return (__bf16)t;
 }
 
+// bf16(fp32(t * s)): a finished fp32 sum times one scale, two roundings.
+__device__ __forceinline__ __bf16 scale1_bf(float t, float s) {
+  t = t * s;
+  asm("" : "+v"(t));
+  return (__bf16)t;
+}
+
 // Reorder 16 activation codes (4 dwords, K order 0..15) into the order the
 // unpacked int4 weights come in: 0,2,4,6 | 1,3,5,7 | 8,10,12,14 | 9,11,13,15.
 __device__ __forceinline__ v4i even_odd_bytes(v4i v) {
@@ -600,7 +607,7 @@ gemm_skinny_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, c
             for (int r = 0; r < 4; ++r)
               if (n + r < N) ACC[((int64_t)u * M + m) * N + n + r] = acc[r];
           }
-        } else if constexpr (EPI == kEpiF16Tok) {
+        } else if constexpr (EPI == kEpiF16Tok || EPI == kEpiBF16Tok) {
           // per-token activations: s_a[m] is applied once, in the store stage
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -669,6 +676,11 @@ gemm_skinny_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, c
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       if (n + r < N) Y[(int64_t)m * N + n + r] = scale1(t[r], sam);
+  } else if constexpr (EPI == kEpiBF16Tok) {
+    const float sam = SA[m];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (n + r < N) reinterpret_cast<__bf16*>(Y)[(int64_t)m * N + n + r] = scale1_bf(t[r], sam);
   }
 }
 
@@ -933,7 +945,7 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
   constexpr int KPG = GS / 64;                           // 64-code MFMA steps per group
   constexpr int kCodeBytes = (BM + BN) * RB;
   constexpr bool kF16 = EPI != kEpiAccI32;
-  constexpr bool kTok = EPI == kEpiF16Tok;
+  constexpr bool kTok = EPI == kEpiF16Tok || EPI == kEpiBF16Tok;
   // 4-byte DMA instructions per stage and per wave (spares load nothing). The
   // int32-accumulator variant has no scales (its scale pointers are null), so
   // it issues none.
@@ -1154,10 +1166,10 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
       for (int a = 0; a < TN; ++a) {
         const int n = n0 + wn + 16 * a + 4 * l4;
         if (n >= N) continue;
-        if constexpr (EPI == kEpiBF16) {
+        if constexpr (EPI == kEpiBF16 || EPI == kEpiBF16Tok) {
           bf4 o;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = to_bf16(facc[a][b][r]);
+          for (int r = 0; r < 4; ++r) o[r] = kTok ? scale1_bf(facc[a][b][r], sam) : to_bf16(facc[a][b][r]);
           __bf16* dst = reinterpret_cast<__bf16*>(Y) + (int64_t)m * N + n;
           if (vec_ok && n + 3 < N) {
             *reinterpret_cast<bf4*>(dst) = o;
@@ -1217,6 +1229,7 @@ splitk_reduce_f32_kernel(const float* __restrict__ P, int splits, int M, int N, 
     for (int r = 0; r < E; ++r) {
       if constexpr (EPI == kEpiBF16) static_cast<__bf16*>(Y)[e0 + r] = to_bf16(t[r]);
       else if constexpr (EPI == kEpiF16Tok) static_cast<_Float16*>(Y)[e0 + r] = scale1(t[r], SA[m]);
+      else if constexpr (EPI == kEpiBF16Tok) static_cast<__bf16*>(Y)[e0 + r] = scale1_bf(t[r], SA[m]);
       else static_cast<_Float16*>(Y)[e0 + r] = (_Float16)t[r];
     }
   }
@@ -1490,7 +1503,7 @@ hipError_t launch_pg(const GemmArgs& g, hipStream_t st) {
       }
     }
   }
-  constexpr bool kTok = EPI == kEpiF16Tok;
+  constexpr bool kTok = EPI == kEpiF16Tok || EPI == kEpiBF16Tok;
   if constexpr (GS == 64 && !kTok) {
     static constexpr TileCost kTiles[] = {{128, 128, 985, 2}, {64, 64, 2500, 4}};
     if (cheapest_tile(g, kTiles) == 0) return launch_dma_pg<128, 128, 2, 2, 2, GS, EPI>(g, st);
@@ -1529,11 +1542,11 @@ hipError_t launch_epi(const GemmArgs& g, WeightKind wk, hipStream_t st) {
 
 // Per-token activations x per-group int8 weights: the skinny kernel for
 // M <= 16, else the per-group pipeline (tile costs as for per-group scales).
+template <int EPI>
 hipError_t launch_tok(const GemmArgs& g, hipStream_t st) {
   if (g.M <= 16)
-    return g.group_size == 64 ? launch_skinny<kWeightI8, 64, kEpiF16Tok>(g, st)
-                              : launch_skinny<kWeightI8, 128, kEpiF16Tok>(g, st);
-  return g.group_size == 64 ? launch_pg<64, kEpiF16Tok>(g, st) : launch_pg<128, kEpiF16Tok>(g, st);
+    return g.group_size == 64 ? launch_skinny<kWeightI8, 64, EPI>(g, st) : launch_skinny<kWeightI8, 128, EPI>(g, st);
+  return g.group_size == 64 ? launch_pg<64, EPI>(g, st) : launch_pg<128, EPI>(g, st);
 }
 
 }  // namespace
@@ -1557,7 +1570,8 @@ bool linear_is_one_launch(int64_t M, int64_t K, int group_size) {
 
 hipError_t launch_gemm(const GemmArgs& g, WeightKind wk, Epilogue epi, hipStream_t st) {
   // Tile table by M (the README's tile section also switches configs by M).
-  if (epi == kEpiF16Tok) return launch_tok(g, st);
+  if (epi == kEpiF16Tok) return launch_tok<kEpiF16Tok>(g, st);
+  if (epi == kEpiBF16Tok) return launch_tok<kEpiBF16Tok>(g, st);
   if (epi == kEpiBF16) return launch_epi<kEpiBF16>(g, wk, st);
   if (epi == kEpiF16Linear)   // g.a holds fp16 activations; linear_is_one_launch() holds
     return wk == kWeightI4 ? launch_gemv<kWeightI4, kEpiF16Linear>(g, st) : launch_gemv<kWeightI8, kEpiF16Linear>(g, st);

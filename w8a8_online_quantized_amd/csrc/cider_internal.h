@@ -27,8 +27,11 @@ hipError_t launch_quant_rows_clip(const void* x, int64_t R, int64_t K, int group
 // matrices (GemmArgs::split).
 // kEpiF16Linear: the GEMV kernel takes fp16 activations and quantizes them
 // itself (per token), then dequantizes as kEpiF16.
-// kEpiBF16: as kEpiF16 with a bfloat16 output.
-enum Epilogue { kEpiF16 = 0, kEpiAccI32 = 1, kEpiF16Tok = 2, kEpiF16Split = 3, kEpiF16Linear = 4, kEpiBF16 = 5 };
+// kEpiBF16: as kEpiF16 with a bfloat16 output; kEpiBF16Tok: as kEpiF16Tok
+// with a bfloat16 output.
+enum Epilogue {
+  kEpiF16 = 0, kEpiAccI32 = 1, kEpiF16Tok = 2, kEpiF16Split = 3, kEpiF16Linear = 4, kEpiBF16 = 5, kEpiBF16Tok = 6
+};
 
 // Column split of a GEMM's output: columns [end[i-1], end[i]) (end[-1] = 0)
 // go to y[i], a row-major fp16 matrix of end[i] - end[i-1] columns. Unused
