@@ -206,6 +206,14 @@ int64_t cider_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t bit
 cider_status_t cider_linear(const void* x_f16, const void* w, const float* w_scale, int64_t M, int64_t N,
                             int64_t K, int32_t bits, int32_t group_size, void* workspace,
                             int64_t workspace_bytes, void* y_f16, void* stream);
+/* The same for bf16 activations and a bf16 output (dtype a cider_dtype_t,
+ * for both x and y): the codes are those of cider_quant_act_dt on the bf16
+ * rows and y is the GEMMs' bf16 output (cider_w8a8_gemm_dt /
+ * cider_w4a8_gemm_dt arithmetic); the one-launch rule and the workspace size
+ * are unchanged. */
+cider_status_t cider_linear_dt(const void* x, int32_t dtype, const void* w, const float* w_scale, int64_t M,
+                               int64_t N, int64_t K, int32_t bits, int32_t group_size, void* workspace,
+                               int64_t workspace_bytes, void* y, void* stream);
 
 /* W8A8 GEMM with per-token activation scales and per-group weight scales
  * (the README's "量化" table quantizes activations per token in every mode,

@@ -94,3 +94,39 @@ def test_one_launch_special_rows():
     y = host(c.cider_linear(xd, wq, sw, 8, 0))
     assert not y[1].any()
     assert np.array_equal(y.view(np.uint16), _two_calls(c, xd, wq, sw, 8, 0).view(np.uint16))
+
+
+# bf16 x -> bf16 y (cider_linear_dt): both routes, int8 and int4 weights; bit
+# for bit the two bf16 calls it stands for, and within one bf16 ulp of the
+# oracle's exactly rounded value (per group: plus the fp32 summation bound)
+@pytest.mark.parametrize("M,N,K,bits,gs", [(1, 10240, 2560, 8, 0), (2, 300, 1056, 8, 0), (1, 2560, 10240, 4, 0),
+                                           (2, 130, 32768, 4, 0), (300, 650, 2560, 8, 0), (16, 300, 2560, 4, 0),
+                                           (70, 260, 1152, 8, 64), (1024, 2560, 10240, 8, 128)])
+def test_linear_bf16(M, N, K, bits, gs):
+    from tests.test_gpu_bf16 import bf16_ulp_distance, bits as bf_bits, to_bf16_dev
+    c = cider()
+    xd = to_bf16_dev(inputs.activations(M, K, seed=43).astype(np.float32))
+    w = inputs.weights(N, K, seed=43)
+    wq, sw = c.cider_quant_weight(dev(w), bits, gs)
+    y = bf_bits(c.cider_linear(xd, wq, sw, bits, gs))
+    xq, sa = c.cider_quant_act(xd, gs)
+    need = c.cider_gemm_workspace_size(M, N, K, bits, gs)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+    if bits == 8:
+        y2 = c.cider_w8a8_gemm(xq, sa, wq, sw, gs, workspace=ws, out_dtype=torch.bfloat16)
+    else:
+        y2 = c.cider_w4a8_gemm(xq, sa, wq, sw, workspace=ws, out_dtype=torch.bfloat16)
+    assert np.array_equal(y, bf_bits(y2))
+    rows = np.arange(M) if M <= 300 else np.unique(np.r_[0, M - 1, np.random.default_rng(M).integers(0, M, 24)])
+    wqo, swo = oracle.quantize_weight(w, bits, gs)
+    xb = bf_bits(xd)[rows]
+    if bits == 4:
+        yo, qo, sao = oracle.w4a8_linear_bf16(xb, wqo, swo)
+    else:
+        yo, qo, sao = oracle.w8a8_linear_bf16(xb, wqo, swo, gs)
+    if gs == 0:
+        assert int(bf16_ulp_distance(y[rows], yo).max()) <= 1
+    else:
+        yv, ov = oracle.bf16_to_f32(y[rows]).astype(np.float64), oracle.bf16_to_f32(yo).astype(np.float64)
+        e = pg_sum_bound(qo, sao, wqo, swo, gs, np.arange(len(rows)))
+        assert np.all(np.abs(yv - ov) <= 2.0 ** -7 * np.abs(ov) + e + 2.0 ** -133), float(np.abs(yv - ov).max())

@@ -46,6 +46,8 @@ SIGNATURES = {
                                          _c_p]),
     "cider_linear": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_p, _c_i64, _c_p,
                                     _c_p]),
+    "cider_linear_dt": (ctypes.c_int, [_c_p, _c_i32, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_p,
+                                       _c_i64, _c_p, _c_p]),
     "cider_quant_weight_clip": (ctypes.c_int, [_c_p, _c_i32, _c_i64, _c_i64, _c_i32, _c_i32, ctypes.c_double, _c_p,
                                                _c_p, _c_p]),
     "cider_quant_act_dt": (ctypes.c_int, [_c_p, _c_i32, _c_i64, _c_i64, _c_i32, _c_p, _c_p, _c_p]),
@@ -310,12 +312,14 @@ def cider_linear_workspace_size(M: int, N: int, K: int, bits: int = 8, group_siz
 
 
 def cider_linear(x, w, w_scale, bits: int = 8, group_size: int = 0, workspace=None, y=None, stream=None):
-    """fp16 x [M, K] -> fp16 y [M, N] through the quantized linear (w: int8
-    codes [N, K] for bits 8, packed uint8 [N, K/2] for bits 4)."""
+    """x [M, K] -> y [M, N] of the same dtype (fp16 or bf16) through the
+    quantized linear (w: int8 codes [N, K] for bits 8, packed uint8 [N, K/2]
+    for bits 4)."""
     import torch
     M, K = x.shape
     N = w.shape[0]
-    _need(x, torch.float16, (M, K), "x")
+    dt = _fp_code(x, "x")
+    _need(x, x.dtype, (M, K), "x")
     if bits == 8:
         _need(w, torch.int8, (N, K), "w")
     else:
@@ -325,12 +329,12 @@ def cider_linear(x, w, w_scale, bits: int = 8, group_size: int = 0, workspace=No
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     if y is None:
-        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
-    _need(y, torch.float16, (M, N), "y")
+        y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    _need(y, x.dtype, (M, N), "y")
     wsp = _ptr(workspace) if workspace is not None else None
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check("cider_linear", lib().cider_linear(_ptr(x), _ptr(w), _ptr(w_scale), M, N, K, bits, group_size, wsp, wsb,
-                                              _ptr(y), _stream(stream)))
+    _check("cider_linear_dt", lib().cider_linear_dt(_ptr(x), dt, _ptr(w), _ptr(w_scale), M, N, K, bits, group_size,
+                                                    wsp, wsb, _ptr(y), _stream(stream)))
     return y
 
 

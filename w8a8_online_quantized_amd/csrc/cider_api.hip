@@ -300,9 +300,11 @@ int64_t cider_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t bit
   return linear_quant_bytes(M, K, group_size) + cider_gemm_workspace_size(M, N, K, bits, group_size);
 }
 
-cider_status_t cider_linear(const void* x_f16, const void* w, const float* w_scale, int64_t M, int64_t N,
-                            int64_t K, int32_t bits, int32_t group_size, void* workspace,
-                            int64_t workspace_bytes, void* y_f16, void* stream) {
+cider_status_t cider_linear_dt(const void* x_f16, int32_t dtype, const void* w, const float* w_scale, int64_t M,
+                               int64_t N, int64_t K, int32_t bits, int32_t group_size, void* workspace,
+                               int64_t workspace_bytes, void* y_f16, void* stream) {
+  if (!valid_dtype(dtype)) return CIDER_ERROR_INVALID_VALUE;
+  const bool bf = dtype == CIDER_DTYPE_BF16;
   const int64_t need = cider_linear_workspace_size(M, N, K, bits, group_size);
   if (need < 0) return CIDER_ERROR_INVALID_VALUE;
   if (M == 0 || N == 0) return CIDER_SUCCESS;
@@ -314,11 +316,11 @@ cider_status_t cider_linear(const void* x_f16, const void* w, const float* w_sca
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (need == 0) {   // one launch: the GEMV kernel quantizes its activations itself
     cider::GemmArgs g{static_cast<const int8_t*>(x_f16), nullptr, w, w_scale, M, N, K, 0, y_f16, nullptr};
-    return from_hip(cider::launch_gemm(g, wk, cider::kEpiF16Linear, st));
+    return from_hip(cider::launch_gemm(g, wk, bf ? cider::kEpiBF16Linear : cider::kEpiF16Linear, st));
   }
   int8_t* xq = static_cast<int8_t*>(workspace);
   float* sa = reinterpret_cast<float*>(static_cast<char*>(workspace) + (M * K + 255) / 256 * 256);
-  hipError_t e = cider::launch_quant_rows(x_f16, M, K, group_size, 127, xq, sa, st);
+  hipError_t e = cider::launch_quant_rows(x_f16, M, K, group_size, 127, xq, sa, st, bf);
   if (e != hipSuccess) return from_hip(e);
   cider::GemmArgs g{xq, sa, w, w_scale, M, N, K, group_size, y_f16, nullptr};
   const int64_t qb = linear_quant_bytes(M, K, group_size);
@@ -326,7 +328,14 @@ cider_status_t cider_linear(const void* x_f16, const void* w, const float* w_sca
     g.ws = static_cast<char*>(workspace) + qb;
     g.ws_bytes = workspace_bytes - qb;
   }
-  return from_hip(cider::launch_gemm(g, wk, cider::kEpiF16, st));
+  return from_hip(cider::launch_gemm(g, wk, bf ? cider::kEpiBF16 : cider::kEpiF16, st));
+}
+
+cider_status_t cider_linear(const void* x_f16, const void* w, const float* w_scale, int64_t M, int64_t N,
+                            int64_t K, int32_t bits, int32_t group_size, void* workspace,
+                            int64_t workspace_bytes, void* y_f16, void* stream) {
+  return cider_linear_dt(x_f16, CIDER_DTYPE_F16, w, w_scale, M, N, K, bits, group_size, workspace, workspace_bytes,
+                         y_f16, stream);
 }
 
 cider_status_t cider_int8_mv(const void* x_f16, const int8_t* w_q, const float* w_scale, int64_t M, int64_t N,

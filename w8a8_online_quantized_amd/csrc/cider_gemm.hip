@@ -773,10 +773,13 @@ gemm_gemv_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, con
   v4i wa[kBatch], wb[kBatch];
   load_batch(wa, wave);
 
-  // kEpiF16Linear: X holds fp16 rows; each row's scale s = max|x| / 127 is
-  // formed here (block-wide max) and the codes follow the quantizer's rule
+  // kEpiF16Linear / kEpiBF16Linear: X holds fp16 / bf16 rows; each row's
+  // scale s = max|x| / 127 is formed here (block-wide max) and the codes
+  // follow the quantizer's rule
   __shared__ float srow[MT];
-  if constexpr (EPI == kEpiF16Linear) {
+  constexpr bool kLin = EPI == kEpiF16Linear || EPI == kEpiBF16Linear;
+  constexpr bool kLinBF = EPI == kEpiBF16Linear;
+  if constexpr (kLin) {
     const uint4* xh = reinterpret_cast<const uint4*>(X);
     const int C = K / 8;
     __shared__ uint32_t wmax[4][MT];
@@ -793,7 +796,7 @@ gemm_gemv_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, con
     if (threadIdx.x < MT) {
       const int m = threadIdx.x;
       const uint32_t a = max(max(wmax[0][m], wmax[1][m]), max(wmax[2][m], wmax[3][m]));
-      srow[m] = half_bits_to_float(a) / 127.0f;
+      srow[m] = elem_to_float<kLinBF>(a) / 127.0f;
     }
     __syncthreads();
   }
@@ -802,14 +805,14 @@ gemm_gemv_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, con
   for (int i = threadIdx.x; i < MT * Kpad / 16; i += 256) {
     const int m = i / (Kpad / 16), c = i % (Kpad / 16);
     v4i v = zero4();
-    if constexpr (EPI == kEpiF16Linear) {
+    if constexpr (kLin) {
       const float sc = m < MT ? srow[m] : 0.0f;
       if (m < M && c * 16 < K && sc != 0.0f) {
         const uint4* xp = reinterpret_cast<const uint4*>(X) + ((int64_t)m * K + c * 16) / 8;
         const float inv = 1.0f / sc;
         // min-max scale: no clamp needed (see code_bytes_of_chunk)
-        const uint2 q0 = code_bytes_of_chunk<false, false>(xp[0], sc, inv, 127.0f);
-        const uint2 q1 = code_bytes_of_chunk<false, false>(xp[1], sc, inv, 127.0f);
+        const uint2 q0 = code_bytes_of_chunk<kLinBF, false>(xp[0], sc, inv, 127.0f);
+        const uint2 q1 = code_bytes_of_chunk<kLinBF, false>(xp[1], sc, inv, 127.0f);
         v[0] = (int)q0.x;
         v[1] = (int)q0.y;
         v[2] = (int)q1.x;
@@ -859,6 +862,8 @@ gemm_gemv_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, con
         const int t = red[0][r][m] + red[1][r][m] + red[2][r][m] + red[3][r][m];
         if constexpr (EPI == kEpiAccI32) ACC[(int64_t)m * N + n] = t;
         else if constexpr (EPI == kEpiF16Linear) Y[(int64_t)m * N + n] = dequant1(t, srow[m], SW[n]);
+        else if constexpr (EPI == kEpiBF16Linear)
+          reinterpret_cast<__bf16*>(Y)[(int64_t)m * N + n] = dequant1_bf(t, srow[m], SW[n]);
         else if constexpr (EPI == kEpiBF16)
           reinterpret_cast<__bf16*>(Y)[(int64_t)m * N + n] = dequant1_bf(t, SA[m], SW[n]);
         else Y[(int64_t)m * N + n] = dequant1(t, SA[m], SW[n]);
@@ -878,7 +883,8 @@ hipError_t launch_gemv_m(const GemmArgs& g, hipStream_t st) {
   // the self-quantizing mode repeats the activation quantization in every
   // block, so its grid is capped (each block then loops over row groups)
   const int64_t nrg = (g.N + 7) / 8;
-  const dim3 grid((unsigned)(EPI == kEpiF16Linear ? std::min<int64_t>(nrg, kLinearBlocks) : nrg)), block(256);
+  constexpr bool kLin = EPI == kEpiF16Linear || EPI == kEpiBF16Linear;
+  const dim3 grid((unsigned)(kLin ? std::min<int64_t>(nrg, kLinearBlocks) : nrg)), block(256);
   gemm_gemv_kernel<MT, WK, EPI><<<grid, block, lds, st>>>(g.a, g.sa, g.w, g.sw, (int)g.M, (int)g.N, (int)g.K,
                                                          static_cast<_Float16*>(g.y), g.acc);
   return hipGetLastError();
@@ -1575,6 +1581,8 @@ hipError_t launch_gemm(const GemmArgs& g, WeightKind wk, Epilogue epi, hipStream
   if (epi == kEpiBF16) return launch_epi<kEpiBF16>(g, wk, st);
   if (epi == kEpiF16Linear)   // g.a holds fp16 activations; linear_is_one_launch() holds
     return wk == kWeightI4 ? launch_gemv<kWeightI4, kEpiF16Linear>(g, st) : launch_gemv<kWeightI8, kEpiF16Linear>(g, st);
+  if (epi == kEpiBF16Linear)  // the same with bf16 activations and output
+    return wk == kWeightI4 ? launch_gemv<kWeightI4, kEpiBF16Linear>(g, st) : launch_gemv<kWeightI8, kEpiBF16Linear>(g, st);
   if (epi == kEpiF16Split) {
     if (g.M > 16) return launch_pc<kWeightI8, kEpiF16Split>(g, st);
     // small M: one launch per part over its rows of the weights (the same

@@ -28,9 +28,11 @@ hipError_t launch_quant_rows_clip(const void* x, int64_t R, int64_t K, int group
 // kEpiF16Linear: the GEMV kernel takes fp16 activations and quantizes them
 // itself (per token), then dequantizes as kEpiF16.
 // kEpiBF16: as kEpiF16 with a bfloat16 output; kEpiBF16Tok: as kEpiF16Tok
-// with a bfloat16 output.
+// with a bfloat16 output; kEpiBF16Linear: as kEpiF16Linear with bfloat16
+// activations and output.
 enum Epilogue {
-  kEpiF16 = 0, kEpiAccI32 = 1, kEpiF16Tok = 2, kEpiF16Split = 3, kEpiF16Linear = 4, kEpiBF16 = 5, kEpiBF16Tok = 6
+  kEpiF16 = 0, kEpiAccI32 = 1, kEpiF16Tok = 2, kEpiF16Split = 3, kEpiF16Linear = 4, kEpiBF16 = 5, kEpiBF16Tok = 6,
+  kEpiBF16Linear = 7
 };
 
 // Column split of a GEMM's output: columns [end[i-1], end[i]) (end[-1] = 0)
