@@ -338,6 +338,14 @@ cider_status_t cider_stack_forward(const void* x_f16, int64_t M, int64_t hidden,
                                    int64_t kv_dim, int64_t mlp_dim, int32_t n_layers,
                                    const cider_stack_layer_t* layers, void* workspace,
                                    int64_t workspace_bytes, void* y_f16, void* stream);
+/* The same chain in bf16 (dtype a cider_dtype_t): x, every intermediate
+ * region and y hold bfloat16; each quantization reads bf16 rows
+ * (cider_quant_act_dt) and each GEMM stores bf16 (cider_w8a8_gemm_dt
+ * arithmetic). The workspace layout is the same (2 bytes per element). */
+cider_status_t cider_stack_forward_dt(const void* x, int32_t dtype, int64_t M, int64_t hidden, int64_t q_dim,
+                                      int64_t kv_dim, int64_t mlp_dim, int32_t n_layers,
+                                      const cider_stack_layer_t* layers, void* workspace,
+                                      int64_t workspace_bytes, void* y, void* stream);
 
 #ifdef __cplusplus
 }

@@ -93,3 +93,41 @@ def test_stack_fused_projections_are_bit_identical(M, dims):
         b = host(c.stack_region(ws1, offs, n, M, *dims))
         assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), n
 
+
+
+@pytest.mark.parametrize("M,dims,n_layers", [(70, (256, 256, 128, 512), 2), (9, (256, 256, 128, 512), 1),
+                                             (1024, (2048, 2048, 1024, 6144), 1)])
+def test_stack_bf16(M, dims, n_layers):
+    """The bf16 chain (cider_stack_forward_dt): every GEMM of the last layer
+    within one bf16 ulp of the oracle fed the same bf16 input (read back from
+    the workspace), fused and unfused projections bit-identical, and the
+    layer hand-off as for fp16."""
+    from tests.test_gpu_bf16 import bf16_ulp_distance, bits, to_bf16_dev
+    c = cider()
+    hidden, q_dim, kv_dim, mlp_dim = dims
+    xd = to_bf16_dev(inputs.activations(M, hidden, seed=11).astype(np.float32))
+    layers, H = make_layers(c, n_layers, dims, seed0=7)
+    y, ws = c.cider_stack_forward(xd, layers, dims)
+    fused = [c.fuse_stack_layer(L) for L in layers]
+    y1, ws1 = c.cider_stack_forward(xd, fused, dims)
+    assert np.array_equal(bits(y), bits(y1))
+    _, offs = c.cider_stack_workspace_layout(M, *dims)
+    reg = {n: bits(c.stack_region(ws, offs, n, M, *dims, dtype=torch.bfloat16))
+           for n in ("q", "k", "v", "o", "gate", "up")}
+    for n in reg:
+        assert np.array_equal(reg[n], bits(c.stack_region(ws1, offs, n, M, *dims, dtype=torch.bfloat16))), n
+    rows = np.arange(M) if M <= 128 else np.unique(np.r_[0, M - 1, np.random.default_rng(2).integers(0, M, 32)])
+    if n_layers == 1:
+        inp = bits(xd)
+    else:
+        y_prev, _ = c.cider_stack_forward(xd, layers[:-1], dims)
+        inp = bits(c.stack_region(ws, offs, "h", M, *dims, dtype=torch.bfloat16))
+        assert np.array_equal(inp, bits(y_prev))
+    Hl = H[-1]
+    checks = [("q", inp, "q"), ("k", inp, "k"), ("v", inp, "v"), ("o", reg["q"], "o"),
+              ("gate", reg["o"], "gate"), ("up", reg["o"], "up")]
+    for out_name, xin, wname in checks:
+        yo, _, _ = oracle.w8a8_linear_bf16(xin[rows], *Hl[wname], 0)
+        assert int(bf16_ulp_distance(reg[out_name][rows], yo).max()) <= 1, out_name
+    yo, _, _ = oracle.w8a8_linear_bf16(reg["up"][rows], *Hl["down"], 0)
+    assert int(bf16_ulp_distance(bits(y)[rows], yo).max()) <= 1, "down"

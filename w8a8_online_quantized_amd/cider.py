@@ -59,6 +59,8 @@ SIGNATURES = {
                                                       ctypes.POINTER(ctypes.c_int64)]),
     "cider_stack_forward": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p,
                                            _c_i64, _c_p, _c_p]),
+    "cider_stack_forward_dt": (ctypes.c_int, [_c_p, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i32, _c_p,
+                                              _c_p, _c_i64, _c_p, _c_p]),
 }
 
 STACK_PROJECTIONS = ("q", "k", "v", "o", "gate", "up", "down")
@@ -422,13 +424,14 @@ def cider_stack_workspace_layout(M: int, hidden: int, q_dim: int, kv_dim: int, m
     return total, dict(zip(STACK_REGIONS, list(offs)))
 
 
-def stack_region(workspace, offsets, name, M, hidden, q_dim, kv_dim, mlp_dim):
-    """A torch view of one workspace region (for checking intermediates)."""
+def stack_region(workspace, offsets, name, M, hidden, q_dim, kv_dim, mlp_dim, dtype=None):
+    """A torch view of one workspace region (for checking intermediates);
+    dtype: torch.float16 (default) or torch.bfloat16 for a bf16 chain."""
     import torch
     dims = {"q": q_dim, "k": kv_dim, "v": kv_dim, "o": hidden, "gate": mlp_dim, "up": mlp_dim, "h": hidden}
     n = dims[name]
     start = offsets[name]
-    return workspace[start:start + 2 * M * n].view(torch.float16).view(M, n)
+    return workspace[start:start + 2 * M * n].view(dtype or torch.float16).view(M, n)
 
 
 def fuse_stack_layer(layer):
@@ -454,19 +457,21 @@ def cider_stack_forward(x, layers, dims, workspace=None, y=None, stream=None):
     import torch
     hidden, q_dim, kv_dim, mlp_dim = dims
     M = x.shape[0]
-    _need(x, torch.float16, (M, hidden), "x")
+    dt = _fp_code(x, "x")
+    _need(x, x.dtype, (M, hidden), "x")
     total, _ = cider_stack_workspace_layout(M, hidden, q_dim, kv_dim, mlp_dim)
     if workspace is None:
         workspace = torch.empty(total, dtype=torch.uint8, device=x.device)
     if y is None:
-        y = torch.empty((M, hidden), dtype=torch.float16, device=x.device)
+        y = torch.empty((M, hidden), dtype=x.dtype, device=x.device)
+    _need(y, x.dtype, (M, hidden), "y")
     arr = (StackLayer * len(layers))()
     for i, L in enumerate(layers):
         for j, name in enumerate(STACK_PROJECTIONS):
             wq, ws = L[name]
             arr[i].w[j] = wq.data_ptr()
             arr[i].s[j] = ws.data_ptr()
-    _check("cider_stack_forward", lib().cider_stack_forward(
-        _ptr(x), M, hidden, q_dim, kv_dim, mlp_dim, len(layers), ctypes.cast(arr, ctypes.c_void_p),
+    _check("cider_stack_forward_dt", lib().cider_stack_forward_dt(
+        _ptr(x), dt, M, hidden, q_dim, kv_dim, mlp_dim, len(layers), ctypes.cast(arr, ctypes.c_void_p),
         _ptr(workspace), workspace.numel(), _ptr(y), _stream(stream)))
     return y, workspace

@@ -401,9 +401,12 @@ int64_t cider_stack_workspace_layout(int64_t M, int64_t hidden, int64_t q_dim, i
   return total;
 }
 
-cider_status_t cider_stack_forward(const void* x_f16, int64_t M, int64_t hidden, int64_t q_dim, int64_t kv_dim,
-                                   int64_t mlp_dim, int32_t n_layers, const cider_stack_layer_t* layers,
-                                   void* workspace, int64_t workspace_bytes, void* y_f16, void* stream) {
+cider_status_t cider_stack_forward_dt(const void* x_f16, int32_t dtype, int64_t M, int64_t hidden, int64_t q_dim,
+                                      int64_t kv_dim, int64_t mlp_dim, int32_t n_layers,
+                                      const cider_stack_layer_t* layers, void* workspace, int64_t workspace_bytes,
+                                      void* y_f16, void* stream) {
+  if (!valid_dtype(dtype)) return CIDER_ERROR_INVALID_VALUE;
+  const bool bf = dtype == CIDER_DTYPE_BF16;
   int64_t off[10];
   const int64_t need = stack_layout(M, hidden, q_dim, kv_dim, mlp_dim, off);
   if (need == 0 || n_layers < 0 || M >= (int64_t(1) << 31)) return CIDER_ERROR_INVALID_VALUE;
@@ -429,7 +432,7 @@ cider_status_t cider_stack_forward(const void* x_f16, int64_t M, int64_t hidden,
   void* h = ws + off[8];
   hipStream_t st = static_cast<hipStream_t>(stream);
 
-  auto quant = [&](const void* in, int64_t K) { return cider::launch_quant_rows(in, M, K, 0, 127, xq, sa, st); };
+  auto quant = [&](const void* in, int64_t K) { return cider::launch_quant_rows(in, M, K, 0, 127, xq, sa, st, bf); };
   auto gemm = [&](const cider_stack_layer_t& L, int j, int64_t N, int64_t K, void* out) {
     cider::GemmArgs a{xq, sa, L.w[j], L.s[j], M, N, K, 0, out, nullptr};
     // split-K partials (e.g. the long-K down projection); stream order keeps
@@ -438,7 +441,7 @@ cider_status_t cider_stack_forward(const void* x_f16, int64_t M, int64_t hidden,
       a.ws = ws + off[9];
       a.ws_bytes = need - off[9];
     }
-    return cider::launch_gemm(a, cider::kWeightI8, cider::kEpiF16, st);
+    return cider::launch_gemm(a, cider::kWeightI8, bf ? cider::kEpiBF16 : cider::kEpiF16, st);
   };
   // Projections j, j+1[, j+2] of one input as one GEMM when their codes and
   // scales are adjacent in memory, in that order (columns split to `outs`).
@@ -458,7 +461,7 @@ cider_status_t cider_stack_forward(const void* x_f16, int64_t M, int64_t hidden,
       a.split.end[i] = (int)end;
     }
     a.N = end;
-    return cider::launch_gemm(a, cider::kWeightI8, cider::kEpiF16Split, st);
+    return cider::launch_gemm(a, cider::kWeightI8, bf ? cider::kEpiBF16Split : cider::kEpiF16Split, st);
   };
   const int64_t n_qkv[3] = {q_dim, kv_dim, kv_dim}, n_gu[2] = {mlp_dim, mlp_dim};
   const void* in = x_f16;
@@ -490,6 +493,13 @@ cider_status_t cider_stack_forward(const void* x_f16, int64_t M, int64_t hidden,
     in = out;   // stream order: the next layer's first quant reads h before h is rewritten
   }
   return CIDER_SUCCESS;
+}
+
+cider_status_t cider_stack_forward(const void* x_f16, int64_t M, int64_t hidden, int64_t q_dim, int64_t kv_dim,
+                                   int64_t mlp_dim, int32_t n_layers, const cider_stack_layer_t* layers,
+                                   void* workspace, int64_t workspace_bytes, void* y_f16, void* stream) {
+  return cider_stack_forward_dt(x_f16, CIDER_DTYPE_F16, M, hidden, q_dim, kv_dim, mlp_dim, n_layers, layers,
+                                workspace, workspace_bytes, y_f16, stream);
 }
 
 }  // extern "C"

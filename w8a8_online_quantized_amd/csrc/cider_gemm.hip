@@ -224,6 +224,16 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Address of output (m, n) in a column-split output: the part holding
+// columns n .. n+3 (part widths are multiples of 4), as 16-bit elements.
+__device__ __forceinline__ _Float16* split_dst(const OutSplit& osp, int m, int n) {
+  const bool p1 = n >= osp.end[0], p2 = n >= osp.end[1], p3 = n >= osp.end[2];
+  const int start = p3 ? osp.end[2] : p2 ? osp.end[1] : p1 ? osp.end[0] : 0;
+  const int stop = p3 ? osp.end[3] : p2 ? osp.end[2] : p1 ? osp.end[1] : osp.end[0];
+  _Float16* base = p3 ? osp.y[3] : p2 ? osp.y[2] : p1 ? osp.y[1] : osp.y[0];
+  return base + (int64_t)m * (stop - start) + (n - start);
+}
+
 template <int BM, int BN, int WGM, int WGN, int BK, int NS, int WK, int EPI, bool SPLIT = false>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, const void* __restrict__ Wv,
@@ -233,7 +243,8 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int TM = WTM / 16, TN = WTN / 16;
   constexpr bool kI4 = WK == kWeightI4;
-  constexpr bool kF16 = EPI == kEpiF16 || EPI == kEpiF16Split || EPI == kEpiBF16;
+  constexpr bool kF16 = EPI == kEpiF16 || EPI == kEpiF16Split || EPI == kEpiBF16 || EPI == kEpiBF16Split;
+  constexpr bool kSplitOut = EPI == kEpiF16Split || EPI == kEpiBF16Split;
   constexpr int RBA = BK;                     // activation bytes per row per stage
   constexpr int RBW = kI4 ? BK / 2 : BK;      // weight bytes per row per stage
   constexpr int kStageBytes = BM * RBA + BN * RBW;
@@ -500,9 +511,10 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
           for (int r = 0; r < 4; ++r)
             if (n + r < N) dst[r] = acc[a][b][r];
         }
-      } else if constexpr (EPI == kEpiBF16) {
+      } else if constexpr (EPI == kEpiBF16 || EPI == kEpiBF16Split) {
         const bf4 o = dequant4_bf(acc[a][b], sam, *reinterpret_cast<const float4*>(lsw + nl));
         __bf16* dst = reinterpret_cast<__bf16*>(Y) + (int64_t)m * N + n;
+        if constexpr (kSplitOut) dst = reinterpret_cast<__bf16*>(split_dst(osp, m, n));
         if (vec_ok && n + 3 < N) {
           *reinterpret_cast<bf4*>(dst) = o;
         } else {
@@ -513,14 +525,7 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
       } else {
         const h4 o = dequant4(acc[a][b], sam, *reinterpret_cast<const float4*>(lsw + nl));   // s_w zero past N
         _Float16* dst = Y + (int64_t)m * N + n;
-        if constexpr (EPI == kEpiF16Split) {
-          // the part holding columns n .. n+3 (part widths are multiples of 4)
-          const bool p1 = n >= osp.end[0], p2 = n >= osp.end[1], p3 = n >= osp.end[2];
-          const int start = p3 ? osp.end[2] : p2 ? osp.end[1] : p1 ? osp.end[0] : 0;
-          const int stop = p3 ? osp.end[3] : p2 ? osp.end[2] : p1 ? osp.end[1] : osp.end[0];
-          _Float16* base = p3 ? osp.y[3] : p2 ? osp.y[2] : p1 ? osp.y[1] : osp.y[0];
-          dst = base + (int64_t)m * (stop - start) + (n - start);
-        }
+        if constexpr (kSplitOut) dst = split_dst(osp, m, n);
         if (vec_ok && n + 3 < N) {
           *reinterpret_cast<h4*>(dst) = o;
         } else {
@@ -1583,8 +1588,9 @@ hipError_t launch_gemm(const GemmArgs& g, WeightKind wk, Epilogue epi, hipStream
     return wk == kWeightI4 ? launch_gemv<kWeightI4, kEpiF16Linear>(g, st) : launch_gemv<kWeightI8, kEpiF16Linear>(g, st);
   if (epi == kEpiBF16Linear)  // the same with bf16 activations and output
     return wk == kWeightI4 ? launch_gemv<kWeightI4, kEpiBF16Linear>(g, st) : launch_gemv<kWeightI8, kEpiBF16Linear>(g, st);
-  if (epi == kEpiF16Split) {
-    if (g.M > 16) return launch_pc<kWeightI8, kEpiF16Split>(g, st);
+  if (epi == kEpiF16Split || epi == kEpiBF16Split) {
+    const bool bf = epi == kEpiBF16Split;
+    if (g.M > 16) return bf ? launch_pc<kWeightI8, kEpiBF16Split>(g, st) : launch_pc<kWeightI8, kEpiF16Split>(g, st);
     // small M: one launch per part over its rows of the weights (the same
     // per-channel arithmetic, so the same bits as the fused launch)
     int start = 0;
@@ -1594,7 +1600,7 @@ hipError_t launch_gemm(const GemmArgs& g, WeightKind wk, Epilogue epi, hipStream
       p.sw = g.sw + start;
       p.N = g.split.end[i] - start;
       p.y = g.split.y[i];
-      const hipError_t e = launch_epi<kEpiF16>(p, kWeightI8, st);
+      const hipError_t e = bf ? launch_epi<kEpiBF16>(p, kWeightI8, st) : launch_epi<kEpiF16>(p, kWeightI8, st);
       if (e != hipSuccess) return e;
       start = g.split.end[i];
     }

@@ -29,14 +29,16 @@ hipError_t launch_quant_rows_clip(const void* x, int64_t R, int64_t K, int group
 // itself (per token), then dequantizes as kEpiF16.
 // kEpiBF16: as kEpiF16 with a bfloat16 output; kEpiBF16Tok: as kEpiF16Tok
 // with a bfloat16 output; kEpiBF16Linear: as kEpiF16Linear with bfloat16
-// activations and output.
+// activations and output; kEpiBF16Split: as kEpiF16Split with bfloat16
+// output matrices.
 enum Epilogue {
   kEpiF16 = 0, kEpiAccI32 = 1, kEpiF16Tok = 2, kEpiF16Split = 3, kEpiF16Linear = 4, kEpiBF16 = 5, kEpiBF16Tok = 6,
-  kEpiBF16Linear = 7
+  kEpiBF16Linear = 7, kEpiBF16Split = 8
 };
 
 // Column split of a GEMM's output: columns [end[i-1], end[i]) (end[-1] = 0)
-// go to y[i], a row-major fp16 matrix of end[i] - end[i-1] columns. Unused
+// go to y[i], a row-major fp16 (bf16 for kEpiBF16Split) matrix of
+// end[i] - end[i-1] columns. Unused
 // trailing parts repeat the last end and are never selected.
 constexpr int kMaxSplitParts = 4;
 struct OutSplit {
