@@ -106,7 +106,62 @@ def algorithmic(mode, M, N, K, gs):
     return 2.0 * M * N * K, gemm_bytes, quant_bytes
 
 
-def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_bytes=512 * 2 ** 20):
+def _sclk_sample():
+    """Mean shader clock (MHz) over the XCDs now, from amd-smi (else
+    rocm-smi); None when neither tool answers."""
+    import re
+    import shutil
+    import subprocess
+    tool = shutil.which("amd-smi")
+    try:
+        if tool:
+            out = subprocess.run([tool, "metric", "--clock", "--json"], capture_output=True, text=True,
+                                 timeout=10).stdout
+            d = json.loads(out)
+            gpus = d["gpu_data"] if isinstance(d, dict) else d
+            clk = gpus[0]["clock"]
+            vals = [float(v["clk"]["value"]) for k, v in clk.items() if k.startswith("gfx_")]
+            return sum(vals) / len(vals) if vals else None
+        tool = shutil.which("rocm-smi")
+        if tool:
+            out = subprocess.run([tool, "--showclocks", "--json"], capture_output=True, text=True, timeout=10).stdout
+            m = re.search(r"sclk clock speed:\W+\(?(\d+)\s*Mhz", out, re.I)
+            return float(m.group(1)) if m else None
+    except (OSError, ValueError, KeyError, IndexError, TypeError, subprocess.SubprocessError):
+        return None
+    return None
+
+
+def sample_sclk(torch, launch, seconds=1.5):
+    """Median shader clock (MHz) sampled while `launch` (one GEMM) runs back
+    to back for `seconds` - the sustained state of the timed loop."""
+    import threading
+    samples = []
+    stop = time.time() + seconds
+
+    def sampler():
+        time.sleep(0.3)
+        while time.time() < stop - 0.2:
+            v = _sclk_sample()
+            if v:
+                samples.append(v)
+            time.sleep(0.1)
+    t = threading.Thread(target=sampler)
+    t.start()
+    i = 0
+    while time.time() < stop:
+        for _ in range(20):
+            launch(i)
+            i += 1
+        torch.cuda.synchronize()
+    t.join()
+    if not samples:
+        return None
+    samples.sort()
+    return samples[len(samples) // 2]
+
+
+def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_bytes=512 * 2 ** 20, clock_s=0.0):
     """Times `steps` passes of quant_act + GEMM for one workload, rotating over
     enough buffer sets to keep the working set out of the 256 MB last-level
     cache. Returns the time per step and each kernel's average launch duration,
@@ -167,10 +222,12 @@ def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_byte
     # at a time, back to back between two events on the launch stream
     q_ms = timed(lambda x, xq, sa, wq, sw, y: cider.cider_quant_act(x, ags, xq, sa, stream=stream))
     g_ms = timed(lambda x, xq, sa, wq, sw, y: gemm(xq, sa, wq, sw, y))
+    sclk = sample_sclk(torch, lambda i: gemm(*sets[i % R][1:]), clock_s) if clock_s > 0 else None
     del sets
     torch.cuda.empty_cache()
     return {"ms_per_step": step_ms, "quant_ms": q_ms, "gemm_ms": g_ms, "ops": ops,
-            "gemm_bytes": gemm_bytes, "quant_bytes": quant_bytes, "sets": R, "split_k_ws": ws_bytes}
+            "gemm_bytes": gemm_bytes, "quant_bytes": quant_bytes, "sets": R, "split_k_ws": ws_bytes,
+            "sclk_mhz": sclk}
 
 
 def measure_mv(cider, torch, x_h, w_h, M, N, K, gs, steps, warmup, R, ops, nbytes, mode="int8_mv"):
@@ -347,7 +404,7 @@ def main():
         return
 
     M, N, K = 4096, 10240, 2560
-    r = measure(cider, torch, inputs, "w8a8_pc", M, N, K, 0, args.steps, args.warmup)
+    r = measure(cider, torch, inputs, "w8a8_pc", M, N, K, 0, args.steps, args.warmup, clock_s=1.5)
     ops = r["ops"]
     value = ops / (r["ms_per_step"] * 1e-3) / 1e12
     gemm_tops = ops / (r["gemm_ms"] * 1e-3) / 1e12
@@ -384,7 +441,12 @@ def main():
                      "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
                      "traffic": measured_traffic(sha),
                      "algorithmic_bytes": r["gemm_bytes"], "algorithmic_ops": ops,
-                     "avg_launch_ms": round(r["gemm_ms"], 5)},
+                     "avg_launch_ms": round(r["gemm_ms"], 5),
+                     # shader clock sampled (amd-smi) while the GEMM ran back to back after the
+                     # timed loops, and the fraction of the dense peak at that clock
+                     "sclk_mhz": round(r["sclk_mhz"]) if r["sclk_mhz"] else None,
+                     "frac_at_sclk": (round(gemm_tops / (PEAK_INT8_TOPS * r["sclk_mhz"] / 2400.0), 4)
+                                      if r["sclk_mhz"] else None)},
         "kernels": {"cider_quant_act": {"avg_ms": round(r["quant_ms"], 5),
                                         "GB/s": round(r["quant_bytes"] / (r["quant_ms"] * 1e-3) / 1e9, 1),
                                         "hbm_frac": round(r["quant_bytes"] / (r["quant_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
