@@ -388,6 +388,75 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
     __builtin_amdgcn_s_waitcnt(0xC07F);
   }
 
+  // Two-stage int8 pipeline for wave tiles under 160 accumulator registers:
+  // the next stage's wait, barrier, DMA issue (two stages ahead) and first
+  // fragment reads sit in the middle of the current stage's second 64-code
+  // step, which runs from registers, so its remaining MFMAs cover the barrier
+  // skew and the LDS read latency. (With 160 accumulators the extra live
+  // fragments spill; those tiles keep the loop below.) Same-box A/B: M=1024
+  // N=10240 K=2560 (256 x 192) 40.6 -> 39.9 us, M=4096 N=2560 K=10240
+  // (256 x 192) 114.3 -> 111.4 us, M=1024 N=2560 K=10240 (128 x 320, split
+  // K) 50.1 -> 48.8 us.
+  if constexpr (!kI4 && BK == 128 && NS == 2 && TM * TN * 4 < 160) {
+    v4i wf[TN], af[TM], nwf[TN], naf[TM];
+    wait_vmcnt<0>();
+    stage_barrier();
+#pragma unroll
+    for (int a = 0; a < TN; ++a)
+      wf[a] = *reinterpret_cast<const v4i*>(smem + BM * RBA + tile_off<RBW>(wn + 16 * a + l16, l4));
+#pragma unroll
+    for (int b = 0; b < 2 && b < TM; ++b)
+      af[b] = *reinterpret_cast<const v4i*>(smem + tile_off<RBA>(wm + 16 * b + l16, l4));
+    __builtin_amdgcn_sched_barrier(0);
+    issue(1);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int kt = 0; kt < KT; ++kt) {
+      const int8_t* sa_ = smem + (kt & 1) * kStageBytes;
+      const int8_t* sw_ = sa_ + BM * RBA;
+#pragma unroll
+      for (int b = 0; b < TM; ++b) {
+#pragma unroll
+        for (int a = 0; a < TN; ++a)
+          acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[a], af[b], acc[a][b], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (b + 2 < TM) af[b + 2] = *reinterpret_cast<const v4i*>(sa_ + tile_off<RBA>(wm + 16 * (b + 2) + l16, l4));
+        naf[b] = *reinterpret_cast<const v4i*>(sa_ + tile_off<RBA>(wm + 16 * b + l16, 4 + l4));
+        if (b < TN) nwf[b] = *reinterpret_cast<const v4i*>(sw_ + tile_off<RBW>(wn + 16 * b + l16, 4 + l4));
+        if (b == TM - 1) {
+#pragma unroll
+          for (int a = TM; a < TN; ++a)
+            nwf[a] = *reinterpret_cast<const v4i*>(sw_ + tile_off<RBW>(wn + 16 * a + l16, 4 + l4));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      constexpr int kHalf = TM / 2;
+#pragma unroll
+      for (int b = 0; b < kHalf; ++b)
+#pragma unroll
+        for (int a = 0; a < TN; ++a)
+          acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(nwf[a], naf[b], acc[a][b], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + 1 < KT) {
+        wait_vmcnt<0>();                        // stage kt+1 landed (own DMA)
+        __builtin_amdgcn_s_waitcnt(0xC07F);     // own reads of stage kt returned
+        stage_barrier();                        // everyone's: stage kt+1 ready, stage kt free
+        issue(kt + 2);                          // into stage kt's buffer (past the end: zero fill)
+        const int8_t* sb_ = smem + ((kt + 1) & 1) * kStageBytes;
+#pragma unroll
+        for (int a = 0; a < TN; ++a)
+          wf[a] = *reinterpret_cast<const v4i*>(sb_ + BM * RBA + tile_off<RBW>(wn + 16 * a + l16, l4));
+#pragma unroll
+        for (int b = 0; b < 2 && b < TM; ++b)
+          af[b] = *reinterpret_cast<const v4i*>(sb_ + tile_off<RBA>(wm + 16 * b + l16, l4));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int b = kHalf; b < TM; ++b)
+#pragma unroll
+        for (int a = 0; a < TN; ++a)
+          acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(nwf[a], naf[b], acc[a][b], 0, 0, 0);
+    }
+  } else
   for (int kt = 0; kt < KT; ++kt) {
     wait_vmcnt<(NS - 2) * LPS>();
     stage_barrier();
