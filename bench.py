@@ -132,9 +132,10 @@ def _sclk_sample():
     return None
 
 
-def sample_sclk(torch, launch, seconds=1.5):
-    """Median shader clock (MHz) sampled while `launch` (one GEMM) runs back
-    to back for `seconds` - the sustained state of the timed loop."""
+def sample_sclk(torch, launch, seconds=3.0):
+    """Shader clock (MHz) sampled while `launch` (one GEMM) runs back to back
+    for `seconds` - the sustained state of the timed loop: (median, min, max,
+    number of samples), or None."""
     import threading
     samples = []
     stop = time.time() + seconds
@@ -158,7 +159,7 @@ def sample_sclk(torch, launch, seconds=1.5):
     if not samples:
         return None
     samples.sort()
-    return samples[len(samples) // 2]
+    return samples[len(samples) // 2], samples[0], samples[-1], len(samples)
 
 
 def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_bytes=512 * 2 ** 20, clock_s=0.0):
@@ -404,7 +405,7 @@ def main():
         return
 
     M, N, K = 4096, 10240, 2560
-    r = measure(cider, torch, inputs, "w8a8_pc", M, N, K, 0, args.steps, args.warmup, clock_s=1.5)
+    r = measure(cider, torch, inputs, "w8a8_pc", M, N, K, 0, args.steps, args.warmup, clock_s=3.0)
     ops = r["ops"]
     value = ops / (r["ms_per_step"] * 1e-3) / 1e12
     gemm_tops = ops / (r["gemm_ms"] * 1e-3) / 1e12
@@ -442,10 +443,13 @@ def main():
                      "traffic": measured_traffic(sha),
                      "algorithmic_bytes": r["gemm_bytes"], "algorithmic_ops": ops,
                      "avg_launch_ms": round(r["gemm_ms"], 5),
-                     # shader clock sampled (amd-smi) while the GEMM ran back to back after the
-                     # timed loops, and the fraction of the dense peak at that clock
-                     "sclk_mhz": round(r["sclk_mhz"]) if r["sclk_mhz"] else None,
-                     "frac_at_sclk": (round(gemm_tops / (PEAK_INT8_TOPS * r["sclk_mhz"] / 2400.0), 4)
+                     # shader clock sampled (amd-smi, mean of the XCDs) while the GEMM ran back
+                     # to back for 3 s after the timed loops: median, min, max, samples; and the
+                     # fraction of the dense peak at the median clock (the samples spread widely)
+                     "sclk_mhz": ({"median": round(r["sclk_mhz"][0]), "min": round(r["sclk_mhz"][1]),
+                                   "max": round(r["sclk_mhz"][2]), "samples": r["sclk_mhz"][3]}
+                                  if r["sclk_mhz"] else None),
+                     "frac_at_sclk": (round(gemm_tops / (PEAK_INT8_TOPS * r["sclk_mhz"][0] / 2400.0), 4)
                                       if r["sclk_mhz"] else None)},
         "kernels": {"cider_quant_act": {"avg_ms": round(r["quant_ms"], 5),
                                         "GB/s": round(r["quant_bytes"] / (r["quant_ms"] * 1e-3) / 1e9, 1),
