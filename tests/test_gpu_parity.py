@@ -200,8 +200,8 @@ def _pc_case(M, N, K, seed=0):
 
 @pytest.mark.parametrize("M,N,K", [(1, 10240, 2560), (3, 5, 16), (33, 100, 1040), (128, 1024, 2560),
                                    (300, 520, 1040), (700, 900, 2048), (64, 63, 10240),
-                                   # 256 x 192 tiles with ragged M, N and K
-                                   (1000, 12200, 320)])
+                                   # 256 x 192 tiles with ragged M, N and K; one K stage (full, partial)
+                                   (1000, 12200, 320), (1000, 12200, 128), (1000, 12200, 64)])
 def test_w8a8_per_channel_outputs(M, N, K):
     c = cider()
     x, w = _pc_case(M, N, K)
