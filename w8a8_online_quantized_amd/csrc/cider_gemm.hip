@@ -1550,7 +1550,13 @@ hipError_t launch_pc(const GemmArgs& g, hipStream_t st) {
       case 2: return launch_dma<128, 256, 2, 4, 128, 2, WK, EPI>(g, st);
       case 3: return launch_dma<128, 128, 2, 2, 64, 3, WK, EPI>(g, st);
       case 4: return launch_dma<64, 160, 2, 2, 128, 2, WK, EPI>(g, st);
-      case 5: return launch_dma<64, 64, 1, 4, 64, 3, WK, EPI>(g, st);
+      case 5:
+        // more than one round of 64 x 64 tiles: two 128-code stages (the
+        // mid-step schedule) ran 17.9 vs 20.6 us at M=128 N=10240 K=2560 (320
+        // tiles) and 21.3 vs 27.2 us at M=256, but 2.8-3.5% slower at 80-256
+        // tiles (M=64 or N <= 4096), which keep three 64-code stages
+        if (tiles_of(g, 64, 64) > 256) return launch_dma<64, 64, 1, 4, 128, 2, WK, EPI>(g, st);
+        return launch_dma<64, 64, 1, 4, 64, 3, WK, EPI>(g, st);
       default: return launch_dma<256, 192, 2, 4, 128, 2, WK, EPI>(g, st);
     }
   }
