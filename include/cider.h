@@ -261,6 +261,12 @@ cider_status_t cider_w8a8_gemm_token_group_dt(const int8_t* x_q, const float* x_
 cider_status_t cider_w8a8_gemm_split(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
                                      const float* w_scale, int64_t M, int64_t K, int32_t n_parts,
                                      const int64_t* part_n, void* const* y_parts, void* stream);
+/* The same with the outputs' type chosen by y_dtype (a cider_dtype_t): bf16
+ * parts hold what cider_w8a8_gemm_dt stores for each part alone. */
+cider_status_t cider_w8a8_gemm_split_dt(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
+                                        const float* w_scale, int64_t M, int64_t K, int32_t n_parts,
+                                        const int64_t* part_n, void* const* y_parts, int32_t y_dtype,
+                                        void* stream);
 
 /* Decode matrix-vector product, the README's int8_mv (section "架构 / Metal
  * Kernel 流水线", Decode (M = 1): the activations are not quantized; the int8

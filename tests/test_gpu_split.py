@@ -59,3 +59,28 @@ def test_split_leaves_memory_outside_the_parts_alone():
     untouched[M * 128:M * 128 + M * 64] = False
     untouched[2 * M * 128:2 * M * 128 + M * 32] = False
     assert np.all(b[untouched] == -7.0)
+
+
+@pytest.mark.parametrize("M,K,parts", [(5, 1024, (256, 128, 128)), (300, 640, (16, 32, 48, 64)),
+                                       (1024, 2048, (2048, 1024, 1024))])
+def test_split_bf16_parts_match_their_own_bf16_gemm(M, K, parts):
+    """bf16 outputs (cider_w8a8_gemm_split_dt): every part equals, bit for bit,
+    the bf16 GEMM of that part alone, and lies within one bf16 ulp of the
+    oracle's exactly rounded value."""
+    from tests.test_gpu_bf16 import bf16_ulp_distance, bits
+    c = cider()
+    x = inputs.activations(M, K, seed=32)
+    ws = [inputs.weights(n, K, seed=32 + i) for i, n in enumerate(parts)]
+    q = [c.cider_quant_weight(dev(w), 8, 0) for w in ws]
+    wcat = torch.cat([a for a, _ in q])
+    scat = torch.cat([b for _, b in q])
+    xq, sa = c.cider_quant_act(dev(x), 0)
+    ys = [bits(y) for y in c.cider_w8a8_gemm_split(xq, sa, wcat, scat, parts, out_dtype=torch.bfloat16)]
+    rows = np.arange(M) if M <= 300 else np.unique(np.r_[0, M - 1, np.random.default_rng(M).integers(0, M, 24)])
+    qo = host(xq)[rows]
+    so = host(sa)[rows]
+    for i, (w, (wq, sw)) in enumerate(zip(ws, q)):
+        alone = bits(c.cider_w8a8_gemm(xq, sa, wq, sw, 0, out_dtype=torch.bfloat16))
+        assert np.array_equal(ys[i], alone), f"part {i} differs from its own bf16 GEMM"
+        yo = oracle.dequant_bf16(oracle.int_dot(qo, host(wq)), so, host(sw))
+        assert int(bf16_ulp_distance(ys[i][rows], yo).max()) <= 1, i

@@ -38,6 +38,8 @@ SIGNATURES = {
     "cider_w8a8_gemm_token_group_dt": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p,
                                                       _c_i32, _c_p, _c_i64, _c_p]),
     "cider_w8a8_gemm_split": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_p, _c_p, _c_p]),
+    "cider_w8a8_gemm_split_dt": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_p, _c_p, _c_i32,
+                                                _c_p]),
     "cider_linear_workspace_size": (ctypes.c_int64, [_c_i64, _c_i64, _c_i64, _c_i32, _c_i32]),
     "cider_gemm_workspace_size": (ctypes.c_int64, [_c_i64, _c_i64, _c_i64, _c_i32, _c_i32]),
     "cider_w8a8_gemm_ex": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_i32, _c_p,
@@ -279,9 +281,10 @@ def cider_w8a8_gemm_token_group(x_q, x_scale, w_q, w_scale, group_size: int, y=N
     return y
 
 
-def cider_w8a8_gemm_split(x_q, x_scale, w_q, w_scale, part_n, ys=None, stream=None):
+def cider_w8a8_gemm_split(x_q, x_scale, w_q, w_scale, part_n, ys=None, stream=None, out_dtype=None):
     """Per-channel GEMM of x_q against row-concatenated weights w_q [sum(part_n), K];
-    returns one fp16 [M, part_n[i]] output per part."""
+    returns one [M, part_n[i]] output per part: fp16, or bf16 when out_dtype
+    (or the given ys) is bfloat16."""
     import torch
     M, K = x_q.shape
     N = w_q.shape[0]
@@ -293,15 +296,16 @@ def cider_w8a8_gemm_split(x_q, x_scale, w_q, w_scale, part_n, ys=None, stream=No
     _need(x_scale, torch.float32, (M,), "x_scale")
     _need(w_scale, torch.float32, (N,), "w_scale")
     if ys is None:
-        ys = [torch.empty((M, n), dtype=torch.float16, device=x_q.device) for n in part_n]
+        ys = [torch.empty((M, n), dtype=out_dtype or torch.float16, device=x_q.device) for n in part_n]
+    dt = _fp_code(ys[0], "ys[0]")
     for i, (y, n) in enumerate(zip(ys, part_n)):
-        _need(y, torch.float16, (M, n), f"ys[{i}]")
+        _need(y, ys[0].dtype, (M, n), f"ys[{i}]")
     arr_n = (ctypes.c_int64 * len(part_n))(*part_n)
     arr_y = (ctypes.c_void_p * len(ys))(*[y.data_ptr() for y in ys])
-    _check("cider_w8a8_gemm_split",
-           lib().cider_w8a8_gemm_split(_ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale), M, K, len(part_n),
-                                       ctypes.cast(arr_n, ctypes.c_void_p), ctypes.cast(arr_y, ctypes.c_void_p),
-                                       _stream(stream)))
+    _check("cider_w8a8_gemm_split_dt",
+           lib().cider_w8a8_gemm_split_dt(_ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale), M, K, len(part_n),
+                                          ctypes.cast(arr_n, ctypes.c_void_p), ctypes.cast(arr_y, ctypes.c_void_p),
+                                          dt, _stream(stream)))
     return ys
 
 

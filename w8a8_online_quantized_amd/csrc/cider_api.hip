@@ -257,9 +257,11 @@ cider_status_t cider_w8a8_gemm_token_group(const int8_t* x_q, const float* x_sca
                                         workspace, workspace_bytes, stream);
 }
 
-cider_status_t cider_w8a8_gemm_split(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
-                                     const float* w_scale, int64_t M, int64_t K, int32_t n_parts,
-                                     const int64_t* part_n, void* const* y_parts, void* stream) {
+cider_status_t cider_w8a8_gemm_split_dt(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
+                                        const float* w_scale, int64_t M, int64_t K, int32_t n_parts,
+                                        const int64_t* part_n, void* const* y_parts, int32_t y_dtype,
+                                        void* stream) {
+  if (!valid_dtype(y_dtype)) return CIDER_ERROR_INVALID_VALUE;
   if (M < 0 || M >= (int64_t(1) << 31) || !valid_k(K, 16, 0)) return CIDER_ERROR_INVALID_VALUE;
   if (n_parts < 1 || n_parts > CIDER_SPLIT_MAX_PARTS || !part_n || !y_parts) return CIDER_ERROR_INVALID_VALUE;
   cider::OutSplit sp{};
@@ -282,7 +284,15 @@ cider_status_t cider_w8a8_gemm_split(const int8_t* x_q, const float* x_scale, co
     if (!y_parts[i] || !aligned16(y_parts[i])) return CIDER_ERROR_INVALID_VALUE;
   cider::GemmArgs g{x_q, x_scale, w_q, w_scale, M, N, K, 0, sp.y[0], nullptr};
   g.split = sp;
-  return gemm_common(g, cider::kWeightI8, cider::kEpiF16Split, stream);
+  return gemm_common(g, cider::kWeightI8, y_dtype == CIDER_DTYPE_BF16 ? cider::kEpiBF16Split : cider::kEpiF16Split,
+                     stream);
+}
+
+cider_status_t cider_w8a8_gemm_split(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
+                                     const float* w_scale, int64_t M, int64_t K, int32_t n_parts,
+                                     const int64_t* part_n, void* const* y_parts, void* stream) {
+  return cider_w8a8_gemm_split_dt(x_q, x_scale, w_q, w_scale, M, K, n_parts, part_n, y_parts, CIDER_DTYPE_F16,
+                                  stream);
 }
 
 // The one-call linear's workspace: the activation codes and scales (each
