@@ -106,9 +106,9 @@ def algorithmic(mode, M, N, K, gs):
     return 2.0 * M * N * K, gemm_bytes, quant_bytes
 
 
-def _sclk_sample():
-    """Mean shader clock (MHz) over the XCDs now, from amd-smi (else
-    rocm-smi); None when neither tool answers."""
+def _clock_sample():
+    """(mean shader clock over the XCDs, memory clock) in MHz now, from
+    amd-smi (else rocm-smi); None when neither tool answers."""
     import re
     import shutil
     import subprocess
@@ -121,12 +121,14 @@ def _sclk_sample():
             gpus = d["gpu_data"] if isinstance(d, dict) else d
             clk = gpus[0]["clock"]
             vals = [float(v["clk"]["value"]) for k, v in clk.items() if k.startswith("gfx_")]
-            return sum(vals) / len(vals) if vals else None
+            mem = [float(v["clk"]["value"]) for k, v in clk.items() if k.startswith("mem_") and isinstance(v, dict)]
+            return (sum(vals) / len(vals), mem[0] if mem else None) if vals else None
         tool = shutil.which("rocm-smi")
         if tool:
             out = subprocess.run([tool, "--showclocks", "--json"], capture_output=True, text=True, timeout=10).stdout
             m = re.search(r"sclk clock speed:\W+\(?(\d+)\s*Mhz", out, re.I)
-            return float(m.group(1)) if m else None
+            mm = re.search(r"mclk clock speed:\W+\(?(\d+)\s*Mhz", out, re.I)
+            return (float(m.group(1)), float(mm.group(1)) if mm else None) if m else None
     except (OSError, ValueError, KeyError, IndexError, TypeError, subprocess.SubprocessError):
         return None
     return None
@@ -135,7 +137,7 @@ def _sclk_sample():
 def sample_sclk(torch, launch, seconds=3.0):
     """Shader clock (MHz) sampled while `launch` (one GEMM) runs back to back
     for `seconds` - the sustained state of the timed loop: (median, min, max,
-    number of samples), or None."""
+    number of samples, median memory clock), or None."""
     import threading
     samples = []
     stop = time.time() + seconds
@@ -143,7 +145,7 @@ def sample_sclk(torch, launch, seconds=3.0):
     def sampler():
         time.sleep(0.3)
         while time.time() < stop - 0.2:
-            v = _sclk_sample()
+            v = _clock_sample()
             if v:
                 samples.append(v)
             time.sleep(0.1)
@@ -158,8 +160,9 @@ def sample_sclk(torch, launch, seconds=3.0):
     t.join()
     if not samples:
         return None
-    samples.sort()
-    return samples[len(samples) // 2], samples[0], samples[-1], len(samples)
+    sc = sorted(v[0] for v in samples)
+    mc = sorted(v[1] for v in samples if v[1])
+    return sc[len(sc) // 2], sc[0], sc[-1], len(sc), (mc[len(mc) // 2] if mc else None)
 
 
 def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_bytes=512 * 2 ** 20, clock_s=0.0):
@@ -449,6 +452,7 @@ def main():
                      "sclk_mhz": ({"median": round(r["sclk_mhz"][0]), "min": round(r["sclk_mhz"][1]),
                                    "max": round(r["sclk_mhz"][2]), "samples": r["sclk_mhz"][3]}
                                   if r["sclk_mhz"] else None),
+                     "mclk_mhz": (round(r["sclk_mhz"][4]) if r["sclk_mhz"] and r["sclk_mhz"][4] else None),
                      "frac_at_sclk": (round(gemm_tops / (PEAK_INT8_TOPS * r["sclk_mhz"][0] / 2400.0), 4)
                                       if r["sclk_mhz"] else None)},
         "kernels": {"cider_quant_act": {"avg_ms": round(r["quant_ms"], 5),
