@@ -251,7 +251,9 @@ hipError_t launch_reg(int cpl, int segs, const uint4* x, int64_t R, int64_t K, f
   switch (cpl) {
     case 1: quant_rows_reg<1, GS, BF, WPR><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
     case 2: quant_rows_reg<2, GS, BF, WPR><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
+    case 3: quant_rows_reg<3, GS, BF, WPR><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
     case 4: quant_rows_reg<4, GS, BF, WPR><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
+    case 5: quant_rows_reg<5, GS, BF, WPR><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
     case 8: quant_rows_reg<8, GS, BF, WPR><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break;
     case 16:
       if constexpr (WPR == 1) { quant_rows_reg<16, GS, BF, 1><<<grid, block, 0, st>>>(x, R, K, qmax, pack4, q, s); break; }
@@ -280,8 +282,11 @@ hipError_t launch_quant_t(const void* x, int64_t R, int64_t K, int group_size, i
   // segments of >= kWgMinChunks chunks (K >= 2048): a workgroup per segment
   const bool wg = per_seg >= kWgMinChunks;
   const int lanes = wg ? 64 * kWaves : 64;
+  // chunks per lane: the smallest of 1, 2, 3, 4, 5, 8, 16, 32 that covers the
+  // segment (3 and 5 fit K = 6144 and 10240 exactly in a workgroup, so no
+  // register slots sit idle)
   int cpl = 1;
-  while (lanes * cpl < per_seg) cpl *= 2;
+  while (lanes * cpl < per_seg) cpl = cpl < 5 ? cpl + 1 : (cpl == 5 ? 8 : cpl * 2);
   switch (group_size) {
     case 0: return wg ? launch_reg<0, BF, kWaves>(cpl, 1, xv, R, K, fq, pack4, q, s, stream)
                       : launch_reg<0, BF, 1>(cpl, 1, xv, R, K, fq, pack4, q, s, stream);
