@@ -141,7 +141,7 @@ def test_quant_weight_bit_exact(N, K, bits, gs):
 
 # ------------------------------------------------------------------ accumulators
 ACC_SHAPES = [(1, 1, 16), (3, 5, 48), (17, 33, 80), (64, 64, 64), (65, 63, 1040), (300, 520, 1040),
-              (129, 257, 2560), (600, 700, 512), (1030, 770, 320)]
+              (129, 257, 2560), (600, 700, 512), (1030, 770, 320), (100, 9990, 2000)]
 
 
 def _codes(rng, shape):
@@ -201,7 +201,9 @@ def _pc_case(M, N, K, seed=0):
 @pytest.mark.parametrize("M,N,K", [(1, 10240, 2560), (3, 5, 16), (33, 100, 1040), (128, 1024, 2560),
                                    (300, 520, 1040), (700, 900, 2048), (64, 63, 10240),
                                    # 256 x 192 tiles with ragged M, N and K; one K stage (full, partial)
-                                   (1000, 12200, 320), (1000, 12200, 128), (1000, 12200, 64)])
+                                   (1000, 12200, 320), (1000, 12200, 128), (1000, 12200, 64),
+                                   # 64 x 80 tiles (one round where 64 x 64 needs two): exact and ragged
+                                   (128, 10240, 2560), (100, 9990, 2000)])
 def test_w8a8_per_channel_outputs(M, N, K):
     c = cider()
     x, w = _pc_case(M, N, K)

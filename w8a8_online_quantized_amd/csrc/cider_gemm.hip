@@ -1438,8 +1438,16 @@ int cheapest_tile(const GemmArgs& g, const TileCost (&c)[NC], int64_t* est_out =
 // N=12288 K=2048 (exactly 256 tiles) 33.4 us against 43.8 us for the 156 tiles
 // of 256 x 320, M=4096 N=2560 K=10240 (224 tiles) 112 us against 122 us for
 // 128 x 320, M=1024 N=10240 K=2560 a tie (41.5 / 40.5 us).
+// 64 x 64 and 64 x 80 keep four 128-code stages in flight (64 / 72 KB of
+// LDS): at small M the weight stream is HBM-bound and two stages leave too few
+// bytes in flight per CU. Same-box A/B against two-stage 64 x 64 tiles
+// (three 64-code stages at <= 256 tiles): M=128 N=10240 K=2560 18.0 -> 12.8
+// us (64 x 80: 256 tiles, one round), M=64 N=10240 K=2560 17.0 -> 11.6 us,
+// M=1024 N=1024 K=2048 13.3 -> 8.6 us, M=1024 N=2048 K=2048 14.8 -> 12.8 us;
+// and, with the lower 64 x 64 cost, unsplit 64 x 64 beats split-K 128 x 128
+// at M=256 N=4096 K=4096 (19.8 -> 13.2 us) and M=512 (27.8 -> 21.6 us).
 constexpr TileCost kTilesI8[] = {{256, 320, 62}, {128, 320, 92}, {128, 256, 102},
-                                 {128, 128, 105}, {64, 160, 167}, {64, 64, 194}, {256, 192, 76}};
+                                 {128, 128, 105}, {64, 160, 167}, {64, 64, 150}, {256, 192, 76}, {64, 80, 185}};
 constexpr TileCost kTilesI4[] = {{256, 320, 62}, {128, 320, 92}, {128, 256, 102}, {128, 128, 105}, {64, 64, 194}};
 
 // Split-K plan for medium M with long K: too few output tiles to fill the
@@ -1550,14 +1558,9 @@ hipError_t launch_pc(const GemmArgs& g, hipStream_t st) {
       case 2: return launch_dma<128, 256, 2, 4, 128, 2, WK, EPI>(g, st);
       case 3: return launch_dma<128, 128, 2, 2, 64, 3, WK, EPI>(g, st);
       case 4: return launch_dma<64, 160, 2, 2, 128, 2, WK, EPI>(g, st);
-      case 5:
-        // more than one round of 64 x 64 tiles: two 128-code stages (the
-        // mid-step schedule) ran 17.9 vs 20.6 us at M=128 N=10240 K=2560 (320
-        // tiles) and 21.3 vs 27.2 us at M=256, but 2.8-3.5% slower at 80-256
-        // tiles (M=64 or N <= 4096), which keep three 64-code stages
-        if (tiles_of(g, 64, 64) > 256) return launch_dma<64, 64, 1, 4, 128, 2, WK, EPI>(g, st);
-        return launch_dma<64, 64, 1, 4, 64, 3, WK, EPI>(g, st);
-      default: return launch_dma<256, 192, 2, 4, 128, 2, WK, EPI>(g, st);
+      case 5: return launch_dma<64, 64, 1, 4, 128, 4, WK, EPI>(g, st);
+      case 6: return launch_dma<256, 192, 2, 4, 128, 2, WK, EPI>(g, st);
+      default: return launch_dma<64, 80, 4, 1, 128, 4, WK, EPI>(g, st);
     }
   }
 }
