@@ -1446,6 +1446,8 @@ int cheapest_tile(const GemmArgs& g, const TileCost (&c)[NC], int64_t* est_out =
 // M=1024 N=1024 K=2048 13.3 -> 8.6 us, M=1024 N=2048 K=2048 14.8 -> 12.8 us;
 // and, with the lower 64 x 64 cost, unsplit 64 x 64 beats split-K 128 x 128
 // at M=256 N=4096 K=4096 (19.8 -> 13.2 us) and M=512 (27.8 -> 21.6 us).
+// 64 x 160 (also as the split-K tile) has four stages too (112 KB): M=128
+// N=2560 K=10240 19.4 -> 17.6 us, M=64 18.6 -> 16.5 us.
 constexpr TileCost kTilesI8[] = {{256, 320, 62}, {128, 320, 92}, {128, 256, 102},
                                  {128, 128, 105}, {64, 160, 167}, {64, 64, 150}, {256, 192, 76}, {64, 80, 185}};
 constexpr TileCost kTilesI4[] = {{256, 320, 62}, {128, 320, 92}, {128, 256, 102}, {128, 128, 105}, {64, 64, 194}};
@@ -1499,8 +1501,16 @@ SplitPlan plan_split(const GemmArgs& g, WeightKind wk) {
   if (g.group_size != 0) return wk == kWeightI8 ? plan_split_pg(g) : plan;
   if (g.M <= 16 || g.K < 4096) return plan;
   int64_t est_plain = 0;
-  if (wk == kWeightI4) cheapest_tile(g, kTilesI4, &est_plain);
-  else cheapest_tile(g, kTilesI8, &est_plain);
+  const int pick = wk == kWeightI4 ? cheapest_tile(g, kTilesI4, &est_plain) : cheapest_tile(g, kTilesI8, &est_plain);
+  // a plain launch of fewer than 256 tiles leaves CUs idle that split-K
+  // units would use: its estimate is scaled by 256 / tiles. Same-box A/B,
+  // M=256 N=2560 K=10240 (160 tiles of 64 x 64): split-K 22.2 us against
+  // 27.3 us plain; at 256 tiles (M=256 N=4096 K=4096) plain wins, 13.3 / 19.7 us.
+  {
+    const TileCost& c = wk == kWeightI4 ? kTilesI4[pick] : kTilesI8[pick];
+    const int64_t t = tiles_of(g, c.bm, c.bn);
+    if (t < 256) est_plain = est_plain * 256 / t;
+  }
   static constexpr TileCost kCand[] = {{64, 160, 167}, {128, 128, 105}, {128, 320, 92}};
   int64_t best = 0;
   for (int i = wk == kWeightI4 ? 1 : 0; i < 3; ++i) {
@@ -1536,7 +1546,7 @@ hipError_t launch_pc(const GemmArgs& g, hipStream_t st) {
           if (p.tile == 1) return launch_dma_split<128, 128, 2, 2, 128, 2, WK, EPI>(g, p.splits, st);
           return launch_dma_split<128, 320, 2, 4, 128, 2, WK, EPI>(g, p.splits, st);
         } else {
-          if (p.tile == 0) return launch_dma_split<64, 160, 2, 2, 128, 2, WK, EPI>(g, p.splits, st);
+          if (p.tile == 0) return launch_dma_split<64, 160, 2, 2, 128, 4, WK, EPI>(g, p.splits, st);
           if (p.tile == 1) return launch_dma_split<128, 128, 2, 2, 64, 3, WK, EPI>(g, p.splits, st);
           return launch_dma_split<128, 320, 2, 4, 128, 2, WK, EPI>(g, p.splits, st);
         }
@@ -1557,7 +1567,7 @@ hipError_t launch_pc(const GemmArgs& g, hipStream_t st) {
       case 1: return launch_dma<128, 320, 2, 4, 128, 2, WK, EPI>(g, st);
       case 2: return launch_dma<128, 256, 2, 4, 128, 2, WK, EPI>(g, st);
       case 3: return launch_dma<128, 128, 2, 2, 64, 3, WK, EPI>(g, st);
-      case 4: return launch_dma<64, 160, 2, 2, 128, 2, WK, EPI>(g, st);
+      case 4: return launch_dma<64, 160, 2, 2, 128, 4, WK, EPI>(g, st);
       case 5: return launch_dma<64, 64, 1, 4, 128, 4, WK, EPI>(g, st);
       case 6: return launch_dma<256, 192, 2, 4, 128, 2, WK, EPI>(g, st);
       default: return launch_dma<64, 80, 4, 1, 128, 4, WK, EPI>(g, st);
