@@ -19,7 +19,10 @@ Inputs are seeded synthetic tensors (w8a8_online_quantized_amd.inputs): x
 weights and activations out of the 256 MB last-level cache between steps the
 timed loop rotates over several buffer sets (>= 512 MB in total). The default
 100 untimed steps let the GPU reach its sustained clock before the 200 timed
-ones (it ramps up over the first ~10 ms of load after idling).
+ones (it ramps up over the first ~10 ms of load after idling); before them,
+--settle-ms of untimed steps (default 200 ms) let the clock ramp finish even
+when few warm-up steps are asked for. No process is spawned once the GPU is
+in use: the shader clock is read from sysfs in-process.
 """
 from __future__ import annotations
 
@@ -64,17 +67,39 @@ def measured_traffic(sha: str):
     return t.get("bytes_per_launch")
 
 
+def host_cpu_model() -> str:
+    """The host CPU's model name, read from /proc/cpuinfo (no process spawned)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_info():
+    """(BLAS vendor / library, threads) of numpy's BLAS from threadpoolctl."""
+    try:
+        from threadpoolctl import threadpool_info
+        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"] or threadpool_info()
+        if pools:
+            p = pools[0]
+            name = f"{p.get('internal_api', '?')} {p.get('version', '')}".strip()
+            return name, int(max(q.get("num_threads", 1) for q in pools))
+    except Exception:  # pragma: no cover
+        pass
+    return "unknown", os.cpu_count() or 1
+
+
 def cpu_baseline(M, N, K, budget_s=12.0):
     """The CPU oracle (never tuned) on the same workload for about budget_s
     seconds of host time (whole 256-row chunks, wrapping over the rows)."""
-    import numpy as np
+    import numpy as np  # noqa: F401
     import oracle
     from w8a8_online_quantized_amd import inputs
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    blas, threads = blas_info()
     w = inputs.weights(N, K, seed=0)
     wq, sw = oracle.quantize_weight(w, 8, 0)
     x = inputs.activations(M, K, seed=0)
@@ -90,7 +115,10 @@ def cpu_baseline(M, N, K, budget_s=12.0):
     return {"value": round(ops / dt / 1e12, 6), "unit": "TOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{rows_done} rows ({rows_done / M:.2f} passes over the M={M} rows, chunks of {chunk}) "
                       f"of the same N={N}, K={K} per-channel linear: numpy quantize + exact fp64 integer "
-                      f"matmul + fp64 dequant, {dt:.1f} s"}
+                      f"matmul + fp64 dequant, {dt:.1f} s",
+            "ms_per_step_equiv": round(dt / (rows_done / M) * 1e3, 2),
+            "cpu_model": host_cpu_model(), "os_cpu_count": os.cpu_count(), "blas": blas,
+            "blas_threads": int(threads)}
 
 
 def algorithmic(mode, M, N, K, gs):
@@ -106,49 +134,76 @@ def algorithmic(mode, M, N, K, gs):
     return 2.0 * M * N * K, gemm_bytes, quant_bytes
 
 
-def _clock_sample():
-    """(mean shader clock over the XCDs, memory clock) in MHz now, from
-    amd-smi (else rocm-smi); None when neither tool answers."""
+def _sysfs_clock_files():
+    """The amdgpu sysfs files that report the current shader clock: the
+    DPM table (current level marked '*') and the hwmon frequency input, for
+    every card the driver exposes. Read in-process: nothing is spawned."""
+    import glob
+    dpm = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    hw = sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/freq1_input"))
+    mem = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_mclk"))
+    return dpm, hw, mem
+
+
+def _read_dpm_mhz(path):
+    """MHz of the level marked current ('*') in a pp_dpm_* table, else None."""
     import re
-    import shutil
-    import subprocess
-    tool = shutil.which("amd-smi")
     try:
-        if tool:
-            out = subprocess.run([tool, "metric", "--clock", "--json"], capture_output=True, text=True,
-                                 timeout=10).stdout
-            d = json.loads(out)
-            gpus = d["gpu_data"] if isinstance(d, dict) else d
-            clk = gpus[0]["clock"]
-            vals = [float(v["clk"]["value"]) for k, v in clk.items() if k.startswith("gfx_")]
-            mem = [float(v["clk"]["value"]) for k, v in clk.items() if k.startswith("mem_") and isinstance(v, dict)]
-            return (sum(vals) / len(vals), mem[0] if mem else None) if vals else None
-        tool = shutil.which("rocm-smi")
-        if tool:
-            out = subprocess.run([tool, "--showclocks", "--json"], capture_output=True, text=True, timeout=10).stdout
-            m = re.search(r"sclk clock speed:\W+\(?(\d+)\s*Mhz", out, re.I)
-            mm = re.search(r"mclk clock speed:\W+\(?(\d+)\s*Mhz", out, re.I)
-            return (float(m.group(1)), float(mm.group(1)) if mm else None) if m else None
-    except (OSError, ValueError, KeyError, IndexError, TypeError, subprocess.SubprocessError):
+        with open(path) as f:
+            for line in f:
+                if "*" in line:
+                    m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                    if m:
+                        return float(m.group(1))
+    except OSError:
         return None
     return None
 
 
-def sample_sclk(torch, launch, seconds=3.0):
-    """Shader clock (MHz) sampled while `launch` (one GEMM) runs back to back
-    for `seconds` - the sustained state of the timed loop: (median, min, max,
-    number of samples, median memory clock), or None."""
+def _clock_sample(files):
+    """(shader clock, memory clock) in MHz now, from sysfs; None if unreadable."""
+    dpm, hw, mem = files
+    sc = None
+    for p in hw:
+        try:
+            with open(p) as f:
+                sc = float(f.read().strip()) / 1e6
+            break
+        except (OSError, ValueError):
+            continue
+    if sc is None:
+        for p in dpm:
+            sc = _read_dpm_mhz(p)
+            if sc is not None:
+                break
+    mc = next((v for v in (_read_dpm_mhz(p) for p in mem) if v is not None), None)
+    return (sc, mc) if sc is not None else None
+
+
+def profiler_attached() -> bool:
+    """True under rocprofv3 (its tool library is preloaded / its env is set)."""
+    pre = os.environ.get("LD_PRELOAD", "")
+    return "rocprof" in pre or any(k.startswith("ROCPROF") for k in os.environ)
+
+
+def sample_sclk(torch, launch, seconds=1.0):
+    """Shader clock (MHz) sampled from sysfs in a helper thread while `launch`
+    (one GEMM) runs back to back for `seconds`: (median, min, max, number of
+    samples, median memory clock), or None when sysfs reports no clock."""
     import threading
+    files = _sysfs_clock_files()
+    if not any(files[:2]):
+        return None
     samples = []
     stop = time.time() + seconds
 
     def sampler():
-        time.sleep(0.3)
-        while time.time() < stop - 0.2:
-            v = _clock_sample()
+        time.sleep(0.1)
+        while time.time() < stop - 0.05:
+            v = _clock_sample(files)
             if v:
                 samples.append(v)
-            time.sleep(0.1)
+            time.sleep(0.02)
     t = threading.Thread(target=sampler)
     t.start()
     i = 0
@@ -165,12 +220,19 @@ def sample_sclk(torch, launch, seconds=3.0):
     return sc[len(sc) // 2], sc[0], sc[-1], len(sc), (mc[len(mc) // 2] if mc else None)
 
 
-def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_bytes=512 * 2 ** 20, clock_s=0.0):
+def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_bytes=512 * 2 ** 20, clock_s=0.0,
+            settle_s=0.0):
     """Times `steps` passes of quant_act + GEMM for one workload, rotating over
     enough buffer sets to keep the working set out of the 256 MB last-level
     cache. Returns the time per step and each kernel's average launch duration,
     all from HIP events on the launch stream (events only around each timed
-    loop, so no event sits between two timed launches)."""
+    loop, so no event sits between two timed launches).
+
+    Order: `settle_s` seconds of untimed steps (the shader clock ramps up over
+    the first ~10 ms of load after the GPU idles), `warmup` untimed steps, the
+    `steps` timed steps, then the same number of GEMM-only launches (the
+    roofline's average launch duration), quant-only launches, and GEMM-only
+    launches on one buffer set (warm: operands cached between launches)."""
     dev = torch.device("cuda:0")
     x_h = torch.from_numpy(inputs.activations(M, K, seed=0))
     w_h = torch.from_numpy(inputs.weights(N, K, seed=0))
@@ -217,6 +279,14 @@ def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_byte
         cider.cider_quant_act(x, ags, xq, sa, stream=stream)
         gemm(xq, sa, wq, sw, y)
 
+    settle_steps = 0
+    if settle_s > 0:
+        t_end = time.perf_counter() + settle_s
+        while time.perf_counter() < t_end:
+            for _ in range(16):
+                step(*sets[settle_steps % R])
+                settle_steps += 1
+            torch.cuda.synchronize()
     for i in range(warmup):
         step(*sets[i % R])
     torch.cuda.synchronize()
@@ -224,14 +294,22 @@ def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_byte
     step_ms = timed(step)
     # each kernel's average launch duration: the same launches, one kernel kind
     # at a time, back to back between two events on the launch stream
-    q_ms = timed(lambda x, xq, sa, wq, sw, y: cider.cider_quant_act(x, ags, xq, sa, stream=stream))
     g_ms = timed(lambda x, xq, sa, wq, sw, y: gemm(xq, sa, wq, sw, y))
+    q_ms = timed(lambda x, xq, sa, wq, sw, y: cider.cider_quant_act(x, ags, xq, sa, stream=stream))
+    warm = sets[0]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        gemm(*warm[1:])
+    end.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = start.elapsed_time(end) / steps
     sclk = sample_sclk(torch, lambda i: gemm(*sets[i % R][1:]), clock_s) if clock_s > 0 else None
-    del sets
+    del sets, warm
     torch.cuda.empty_cache()
-    return {"ms_per_step": step_ms, "quant_ms": q_ms, "gemm_ms": g_ms, "ops": ops,
+    return {"ms_per_step": step_ms, "quant_ms": q_ms, "gemm_ms": g_ms, "gemm_warm_ms": warm_ms, "ops": ops,
             "gemm_bytes": gemm_bytes, "quant_bytes": quant_bytes, "sets": R, "split_k_ws": ws_bytes,
-            "sclk_mhz": sclk}
+            "sclk_mhz": sclk, "settle_steps": settle_steps}
 
 
 def measure_mv(cider, torch, x_h, w_h, M, N, K, gs, steps, warmup, R, ops, nbytes, mode="int8_mv"):
@@ -371,11 +449,19 @@ def run_sweep(cider, torch, inputs, indices, steps):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # defaults: ~11 ms of untimed steps, then ~23 ms timed - the shader clock
-    # ramps up over the first ~10 ms of sustained load after an idle GPU, and
-    # 5 warm-up steps timed that ramp (step 130 us instead of 113 us)
+    # defaults: ~11 ms of untimed steps, then ~23 ms timed. The shader clock
+    # ramps up over the first ~10 ms of sustained load after an idle GPU, so
+    # every run first settles for --settle-ms of untimed steps (5 warm-up
+    # steps alone timed that ramp: step 130 us instead of 113 us)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed steps run for this long before the warm-up steps (clock ramp)")
+    ap.add_argument("--clock-s", type=float, default=1.0,
+                    help="seconds of back-to-back GEMMs during which the shader clock is read from "
+                         "sysfs after the timed loops (0: no sampling)")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the shader-clock sampling (also skipped automatically under rocprofv3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="also time every per-channel / per-group / W4A8 configuration")
@@ -408,7 +494,9 @@ def main():
         return
 
     M, N, K = 4096, 10240, 2560
-    r = measure(cider, torch, inputs, "w8a8_pc", M, N, K, 0, args.steps, args.warmup, clock_s=3.0)
+    clock_s = 0.0 if (args.no_clock or profiler_attached()) else args.clock_s
+    r = measure(cider, torch, inputs, "w8a8_pc", M, N, K, 0, args.steps, args.warmup, clock_s=clock_s,
+                settle_s=args.settle_ms * 1e-3)
     ops = r["ops"]
     value = ops / (r["ms_per_step"] * 1e-3) / 1e12
     gemm_tops = ops / (r["gemm_ms"] * 1e-3) / 1e12
@@ -436,6 +524,8 @@ def main():
         "vs_baseline": round(value / PAGES_M5PRO_TOPS, 3),
         "dtype": "i8",
         "data": "synthetic",
+        "settle": {"ms": args.settle_ms, "steps": r["settle_steps"],
+                   "note": "untimed steps before the warm-up steps while the shader clock ramps up"},
         "config": {"workload": f"w8a8 per-channel online-quantized linear, M={M} N={N} K={K}, "
                                f"quant_act + fused GEMM per step",
                    "M": M, "N": N, "K": K, "group_size": 0, "x_dtype": "fp16", "y_dtype": "fp16",
@@ -446,9 +536,14 @@ def main():
                      "traffic": measured_traffic(sha),
                      "algorithmic_bytes": r["gemm_bytes"], "algorithmic_ops": ops,
                      "avg_launch_ms": round(r["gemm_ms"], 5),
-                     # shader clock sampled (amd-smi, mean of the XCDs) while the GEMM ran back
-                     # to back for 3 s after the timed loops: median, min, max, samples; and the
-                     # fraction of the dense peak at the median clock (the samples spread widely)
+                     "avg_launch_source": f"HIP events around {args.steps} back-to-back cider_w8a8_gemm "
+                                          f"launches (rotating {r['sets']} buffer sets) on the launch stream, "
+                                          f"right after the timed steps",
+                     "warm_launch_ms": round(r["gemm_warm_ms"], 5),
+                     "warm_note": "the same GEMM relaunched on one buffer set (operands stay cached): warm",
+                     # shader clock read from sysfs (no process spawned) while the GEMM ran back
+                     # to back after the timed loops: median, min, max, samples; and the
+                     # fraction of the dense peak at the median clock
                      "sclk_mhz": ({"median": round(r["sclk_mhz"][0]), "min": round(r["sclk_mhz"][1]),
                                    "max": round(r["sclk_mhz"][2]), "samples": r["sclk_mhz"][3]}
                                   if r["sclk_mhz"] else None),

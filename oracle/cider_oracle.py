@@ -44,14 +44,20 @@ notes of the repository):
 * int4: codes in [-7, 7] stored as nibble u = code + 8; two codes per byte,
   the even K index in the low nibble; weight rows are [N, K/2] bytes.
 * dequant: the exact product acc * s_a * s_w (summed over groups for
-  per-group) rounded once to fp16 (round to nearest even). This is the plain
-  definition of the formula; it is evaluated in fp64, where acc * s_a is
-  exact (at most 52 significant bits) and only the last product and the
-  group sum round.
+  per-group) rounded to fp16 (round to nearest even). Per-channel, this is
+  the plain definition rounded exactly once: the fp64 route is used where it
+  provably gives that result (|acc| < 2^29, so acc * s_a is exact in fp64,
+  and the fp64 product is not a midpoint of the output format, so its second
+  rounding cannot land on the wrong side), and every other element is
+  computed with exact rationals. Per-group sums are evaluated in fp64: each
+  term acc_g * s_a * s_w is rounded once to fp64 (|acc_g| < 2^29 for the
+  group sizes accepted) and the sum over G groups carries at most about
+  G * 2^-53 * sum_g |term_g| of error before the final fp16 rounding; the
+  GPU's fp32 sums are held to a much wider bound.
 
 * per-token activations x per-group weights (the quantization table's
   per-token activations with per-group weights): y = sum_g acc_g * s_a[m] *
-  s_w[n,g], in fp64, rounded once to fp16.
+  s_w[n,g], evaluated in fp64 as the per-group sum is, then rounded to fp16.
 * percentile-clipped weight scales (the notes name a "99th percentile"
   method with clip_percentile=99.9; the parameter's value is taken): the
   group's clip threshold t is the percentile of its magnitudes by linear
@@ -71,6 +77,9 @@ is below 2**53 for every K this module accepts, so each fp64 operation
 (whatever the BLAS blocking order or FMA use) is exact.
 """
 from __future__ import annotations
+
+import math
+from fractions import Fraction
 
 import numpy as np
 
@@ -263,15 +272,72 @@ def int_dot_groups(qa: np.ndarray, qw: np.ndarray, group_size: int) -> np.ndarra
                      for g in range(G)])
 
 
+# Output formats of the dequant: (significand bits including the hidden one,
+# smallest normal exponent, largest exponent).
+_F16 = (11, -14, 15)
+_BF16 = (8, -126, 127)
+
+
+def _round_rational(v: Fraction, fmt) -> float:
+    """The exact rational v rounded once to the binary format fmt (nearest,
+    ties to the even significand, gradual underflow, +-inf once the rounded
+    magnitude reaches 2^(emax+1)), as a Python float."""
+    p, emin, emax = fmt
+    if v == 0:
+        return 0.0
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()   # 2^(e-1) < a < 2^(e+1)
+    if a < Fraction(2) ** e:
+        e -= 1
+    step = Fraction(2) ** (max(e, emin) - (p - 1))              # spacing of the format at a
+    n, rem = divmod(a, step)
+    if 2 * rem > step or (2 * rem == step and n % 2 == 1):
+        n += 1
+    r = n * step
+    out = math.inf if r >= Fraction(2) ** (emax + 1) else float(r)
+    return -out if v < 0 else out
+
+
+def _is_midpoint(p: np.ndarray, fmt) -> np.ndarray:
+    """True where the fp64 value p lies exactly halfway between two
+    neighbours of the format (where rounding p again could differ from
+    rounding the exact value it came from)."""
+    bits, emin, _ = fmt
+    a = np.abs(p)
+    _, e = np.frexp(a)                                   # 2^(e-1) <= a < 2^e
+    q = np.maximum(e - 1, emin) - (bits - 1)              # exponent of the spacing
+    n = np.ldexp(a, -q)                                   # exact: a power-of-two scaling
+    return (a != 0) & (n - np.floor(n) == 0.5)
+
+
+def _product_rounded(acc: np.ndarray, s_a: np.ndarray, s_w: np.ndarray, fmt, to_fmt):
+    """acc[m, n] * s_a[m] * s_w[n] rounded once to fmt: fp64 where that is
+    provably the same, exact rationals elsewhere. Returns to_fmt(values)."""
+    acc = np.asarray(acc)
+    sa64 = s_a.astype(np.float64)[:, None]
+    sw64 = s_w.astype(np.float64)[None, :]
+    with np.errstate(over="ignore"):
+        t = acc.astype(np.float64) * sa64                  # exact while |acc| < 2^29
+        v = t * sw64
+    redo = (np.abs(acc) >= 2 ** 29) | _is_midpoint(v, fmt) | ~np.isfinite(v)
+    for m, n in zip(*np.nonzero(redo)):
+        exact = Fraction(int(acc[m, n])) * Fraction(float(s_a[m])) * Fraction(float(s_w[n]))
+        v[m, n] = _round_rational(exact, fmt)
+    return to_fmt(v)
+
+
 def dequant_per_channel(acc: np.ndarray, s_a: np.ndarray, s_w: np.ndarray) -> np.ndarray:
-    """y[m, n] = fp16(acc[m, n] * s_a[m] * s_w[n]); fp64 product, one fp16 rounding."""
-    t = acc.astype(np.float64) * s_a.astype(np.float64)[:, None]   # exact (<= 52 bits)
-    t = t * s_w.astype(np.float64)[None, :]
-    return t.astype(np.float16)
+    """y[m, n] = fp16(acc[m, n] * s_a[m] * s_w[n]): the exact product rounded once
+    to fp16. (Where the fp64 route is used the value handed to the fp16 cast
+    is either the exact product or lies strictly on the same side of every
+    fp16 rounding boundary as it, so the cast gives the single rounding.)"""
+    with np.errstate(over="ignore"):
+        return _product_rounded(acc, s_a, s_w, _F16, lambda v: v.astype(np.float16))
 
 
 def dequant_per_group(acc_g: np.ndarray, s_a: np.ndarray, s_w: np.ndarray) -> np.ndarray:
-    """y[m, n] = fp16(sum_g acc_g[g, m, n] * s_a[m, g] * s_w[n, g]) in fp64."""
+    """y[m, n] = fp16(sum_g acc_g[g, m, n] * s_a[m, g] * s_w[n, g]), the sum in fp64
+    (each term rounded once to fp64; see the module notes for its error)."""
     G = acc_g.shape[0]
     y = np.zeros(acc_g.shape[1:], np.float64)
     for g in range(G):
@@ -358,8 +424,7 @@ def dequant_bf16(acc_g: np.ndarray, s_a: np.ndarray, s_w: np.ndarray) -> np.ndar
     s_a [M, G], s_w [N, G]) dequant, the exact fp64 value rounded once to
     bf16 (uint16 patterns [M, N])."""
     if acc_g.ndim == 2:
-        t = acc_g.astype(np.float64) * s_a.astype(np.float64)[:, None]
-        return f64_to_bf16(t * s_w.astype(np.float64)[None, :])
+        return _product_rounded(acc_g, s_a, s_w, _BF16, f64_to_bf16)
     y = np.zeros(acc_g.shape[1:], np.float64)
     for g in range(acc_g.shape[0]):
         t = acc_g[g].astype(np.float64) * s_a[:, g].astype(np.float64)[:, None]
@@ -418,7 +483,9 @@ def dequant_token_group(acc_g: np.ndarray, s_a: np.ndarray, s_w: np.ndarray) -> 
     """Per-token activation scale times per-group weight scales (the README's
     quantization table: activations symmetric INT8 per token in every mode,
     weights per-channel or per-group): y[m, n] = fp16( sum_g acc_g[g, m, n] *
-    s_a[m] * s_w[n, g] ), evaluated in fp64 (acc * s_a exact), rounded once."""
+    s_a[m] * s_w[n, g] ), evaluated in fp64 (acc_g * s_a exact, each term then
+    rounded once to fp64, the sum carrying at most about G * 2^-53 of the
+    terms' magnitude), then rounded to fp16."""
     G = acc_g.shape[0]
     sa = s_a.reshape(-1).astype(np.float64)[:, None]
     y = np.zeros(acc_g.shape[1:], np.float64)

@@ -1,16 +1,18 @@
 """Checks that pin the CPU oracle to facts fixed outside itself.
 
-Each check takes an implementation namespace with the oracle's primitive
-functions (quantize_rows, pack_int4, unpack_int4, int_dot, int_dot_groups,
-dequant_per_channel, dequant_per_group, int8_mv, dequant_token_group) and raises AssertionError when the
-implementation disagrees with:
+Each check takes an implementation namespace with the oracle's functions
+(the primitives quantize_rows, pack_int4, unpack_int4, int_dot,
+int_dot_groups, the dequants, int8_mv, the percentile and bf16 helpers, and
+the composite entry points built from them) and raises AssertionError when
+the implementation disagrees with:
 
 * hand-derived worked examples stored under tests/golden/ (closed forms);
 * the exact-rational brute force in oracle/brute.py on tiny inputs;
 * invariants of the definition (2^k scaling, sign symmetry, range, K
   permutation, gs = K reducing to per-channel);
 * the deterministic error bound of symmetric min-max quantization against the
-  unquantized fp64 product, and cosine floors on the synthetic workload.
+  unquantized fp64 product, and cosine floors on the synthetic workload;
+* the composition of the primitives, for every composite entry point.
 
 The same checks run against deliberately broken copies of the oracle in
 test_oracle_mutants.py, to show that each plausible mistake is caught.
@@ -622,6 +624,225 @@ def check_bf16_reductions(impl, seed=23):
     assert np.array_equal(impl.bf16_to_f32(yb)[small], y16.astype(np.float32)[small])
 
 
+# ------------------------------------------------- long K: exact single rounding
+def _double_rounding_cases(count=4):
+    """Per-channel (acc, s_a, s_w) whose exact product lies 2^-63 above or below
+    a midpoint of fp16 while the fp64 product acc * s_a rounds onto that
+    midpoint: acc * m = H +- 1 with H = (2j+1) * 2^43 (an fp16 midpoint once
+    scaled by 2^-63), s_a = m * 2^-23 (m odd, 24 bits), s_w = 2^-40, |acc| near
+    2^31 (K well past 33k). Pure integer search: m must divide H +- 1, and
+    2j+1 is taken 1 mod 4 for +1 (3 mod 4 for -1) so that the exact value's
+    side of the midpoint is away from the even neighbour."""
+    out = []
+    for sign in (1, -1):
+        m = 2 ** 23 + 1
+        while len([c for c in out if c[3] == sign]) < count // 2:
+            inv = pow(2 ** 43, -1, m)
+            r = (-sign * inv) % m          # (2j+1) * 2^43 + sign == 0 (mod m)
+            if r % 4 == (1 if sign > 0 else 3) and 2 ** 11 <= r < 2 ** 12:
+                h = r * 2 ** 43
+                acc = (h + sign) // m
+                if acc < 2 ** 31:
+                    out.append((acc, m, h, sign))
+            m += 2
+    return out
+
+
+def check_dequant_long_k_exact(impl):
+    """|acc| near 2^31 (reachable for K up to the library's limit): the
+    per-channel dequant is the exact product rounded once, also where the
+    fp64 product acc * s_a is inexact and rounds onto an fp16 midpoint, so a
+    second rounding of it would go to the even neighbour whatever the side
+    the exact value lies on."""
+    cases = _double_rounding_cases()
+    sw_list = []
+    for acc_i, m, h, sign in cases:
+        sa = np.float32(m * 2.0 ** -23)
+        assert float(sa) == m * 2.0 ** -23                      # exactly representable
+        v = impl.dequant_per_channel(np.array([[acc_i]], np.int64), np.array([sa], np.float32),
+                                     np.array([2.0 ** -40], np.float32))
+        exact = brute.f16(Fraction(acc_i) * Fraction(float(sa)) * Fraction(2) ** -40)
+        assert float(v[0, 0]) == float(exact), (acc_i, m, sign, float(v[0, 0]), float(exact))
+        naive = np.float16((np.float64(acc_i) * np.float64(sa)) * 2.0 ** -40)
+        sw_list.append(float(naive) != float(exact))
+    assert all(sw_list), "a case did not exercise a double rounding"
+    # random accumulators up to the int32 limit against the brute force
+    rng = np.random.default_rng(31)
+    acc = rng.integers(-(2 ** 31) + 1, 2 ** 31, (6, 7))
+    s_a = (rng.uniform(1, 2, 6) * 2.0 ** rng.integers(-20, -6, 6)).astype(np.float32)
+    s_w = (rng.uniform(1, 2, 7) * 2.0 ** rng.integers(-12, -4, 7)).astype(np.float32)
+    with np.errstate(over="ignore"):
+        y = impl.dequant_per_channel(acc, s_a, s_w)
+    for m in range(6):
+        for n in range(7):
+            ref = brute.f16(Fraction(int(acc[m, n])) * Fraction(float(s_a[m])) * Fraction(float(s_w[n])))
+            assert float(y[m, n]) == float(ref), (m, n, float(y[m, n]), float(ref))
+
+
+# ------------------------------------------------- composite entry points
+# The public composites (weight quantizers, bf16 and per-token x per-group
+# linears) must equal their composition of the primitives pinned above, bit
+# for bit, and the exact-rational brute force on tiny shapes.
+def _pack_ref(codes):
+    """Two codes per byte, the even K index (plus 8) in the low nibble."""
+    return [(codes[2 * j] + 8) | ((codes[2 * j + 1] + 8) << 4) for j in range(len(codes) // 2)]
+
+
+def _unpack_ref(row):
+    out = []
+    for b in row:
+        out += [(int(b) & 15) - 8, (int(b) >> 4) - 8]
+    return out
+
+
+def _to_bf16_bits(xf):
+    """fp32 values that are bf16 values -> their uint16 patterns (exact)."""
+    return (np.asarray(xf, np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def check_weight_quantizers_compose(impl, seed=40):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((6, 128)) * 0.05).astype(np.float16)
+    w[2, 17] = np.float16(1.5)                                   # an outlier to clip
+    wb = _to_bf16_bits(w.astype(np.float32))                    # fp16 values with <= 8 bits? not always
+    wb_vals = impl.bf16_to_f32(wb)
+    for gs in (0, 64):
+        q, s = impl.quantize_weight(w, 8, gs)
+        q0, s0 = impl.quantize_rows(w, gs, 127)
+        assert np.array_equal(q, q0) and np.array_equal(s.reshape(6, -1), s0)
+        for p in (99.9, 50.0):
+            q, s = impl.quantize_weight_clip(w, 8, gs, p)
+            q0, s0 = impl.quantize_rows_clip(w, gs, 127, p)
+            assert np.array_equal(q, q0) and np.array_equal(s.reshape(6, -1), s0), (gs, p)
+        q, s = impl.quantize_weight_bf16(wb, 8, gs)
+        q0, s0 = impl.quantize_rows_bf16(wb, gs, 127)
+        assert np.array_equal(q, q0) and np.array_equal(s.reshape(6, -1), s0)
+    q, s = impl.quantize_weight(w, 4, 0)
+    q0, s0 = impl.quantize_rows(w, 0, 7)
+    assert np.array_equal(q, impl.pack_int4(q0)) and np.array_equal(s, s0[:, 0])
+    q, s = impl.quantize_weight_clip(w, 4, 0, 99.0)
+    q0, s0 = impl.quantize_rows_clip(w, 0, 7, 99.0)
+    assert q.shape == (6, 64) and np.array_equal(q, impl.pack_int4(q0)) and np.array_equal(s, s0[:, 0])
+    q, s = impl.quantize_weight_bf16(wb, 4, 0)
+    q0, s0 = impl.quantize_rows_bf16(wb, 0, 7)
+    assert np.array_equal(q, impl.pack_int4(q0)) and np.array_equal(s, s0[:, 0])
+    # bf16 rows whose values are also fp16 values: the bf16 clip quantizer is
+    # the fp16 one on the same values
+    exact16 = np.all(wb_vals.astype(np.float16).astype(np.float32) == wb_vals, axis=1)
+    assert exact16.any()
+    rows = np.nonzero(exact16)[0]
+    for bits, gs in ((8, 0), (8, 64), (4, 0)):
+        q, s = impl.quantize_weight_clip_bf16(wb[rows], bits, gs, 90.0)
+        q0, s0 = impl.quantize_weight_clip(wb_vals[rows].astype(np.float16), bits, gs, 90.0)
+        assert np.array_equal(q, q0) and np.array_equal(s, s0), (bits, gs)
+
+
+def check_weight_quantizers_brute(impl, trials=24, seed=41):
+    """Every weight quantizer against the exact-rational brute force and the
+    nibble layout written out here."""
+    rng = np.random.default_rng(seed)
+    for t in range(trials):
+        bits = 8 if t % 2 else 4
+        gs = 0 if bits == 4 else [0, 2, 4][t % 3]
+        K = (gs or 2) * int(rng.integers(1, 4))
+        N = int(rng.integers(1, 4))
+        w = _rand_fp16(rng, (N, K), ["normal", "wide", "ties", "small"][t % 4])
+        wf = w.astype(np.float32)
+        wb = _to_bf16_bits(wf)                                    # truncation: a bf16 value
+        wbf = impl.bf16_to_f32(wb)
+        p = [99.9, 50.0, 0.0, 75.0][t % 4]
+        qmax = 127 if bits == 8 else 7
+        for fn, vals, args in ((impl.quantize_weight, wf, ()), (impl.quantize_weight_clip, wf, (p,)),
+                               (impl.quantize_weight_bf16, wbf, ()), (impl.quantize_weight_clip_bf16, wbf, (p,))):
+            src = w if fn in (impl.quantize_weight, impl.quantize_weight_clip) else wb
+            q, s = fn(src, bits, gs, *args)
+            s2 = np.asarray(s).reshape(N, -1)
+            for n in range(N):
+                row = [float(v) for v in vals[n]]
+                if args:
+                    bq, bs = brute.quantize_row_clip(row, gs, qmax, p)
+                else:
+                    bq, bs = brute.quantize_row(row, gs, qmax)
+                got = q[n].tolist()
+                want = _pack_ref(bq) if bits == 4 else bq
+                assert got == want, (fn.__name__, t, n, got, want)
+                assert [float(v) for v in s2[n]] == [float(v) for v in bs], (fn.__name__, t, n)
+
+
+def check_linear_composites_compose(impl, seed=42):
+    """The linears equal their primitive compositions bit for bit."""
+    from w8a8_online_quantized_amd import inputs
+    x = inputs.activations(8, 256, seed=seed)
+    w = inputs.weights(12, 256, seed=seed)
+    xb = _to_bf16_bits(x.astype(np.float32))
+    for gs in (0, 64, 128):
+        wq, sw = impl.quantize_weight(w, 8, gs)
+        sw2 = sw[:, None] if gs == 0 else sw
+        y, qa, sa = impl.w8a8_linear(x, wq, sw, gs)
+        assert np.array_equal(y.view(np.uint16), _linear(impl, x, wq, sw2, gs).view(np.uint16)), gs
+        yb, qb, sb = impl.w8a8_linear_bf16(xb, wq, sw, gs)
+        q0, s0 = impl.quantize_rows_bf16(xb, gs, 127)
+        assert np.array_equal(qb, q0) and np.array_equal(np.asarray(sb).reshape(8, -1), s0), gs
+        acc = impl.int_dot(q0, wq) if gs == 0 else impl.int_dot_groups(q0, wq, gs)
+        want = impl.dequant_bf16(acc, s0[:, 0] if gs == 0 else s0, sw)
+        assert np.array_equal(yb, want), gs
+    p, s4 = impl.quantize_weight(w, 4, 0)
+    y4, _, _ = impl.w4a8_linear(x, p, s4)
+    y8, _, _ = impl.w8a8_linear(x, impl.unpack_int4(p), s4, 0)
+    assert np.array_equal(y4.view(np.uint16), y8.view(np.uint16))
+    y4b, q4b, s4b = impl.w4a8_linear_bf16(xb, p, s4)
+    y8b, _, _ = impl.w8a8_linear_bf16(xb, impl.unpack_int4(p), s4, 0)
+    assert np.array_equal(y4b, y8b)
+    for gs in (64, 128):
+        wq, sw = impl.quantize_weight(w, 8, gs)
+        y, qa, sa = impl.w8a8_linear_token_group(x, wq, sw, gs)
+        q0, s0 = impl.quantize_rows(x, 0, 127)
+        assert np.array_equal(qa, q0) and np.array_equal(sa, s0[:, 0])
+        want = impl.dequant_token_group(impl.int_dot_groups(q0, wq, gs), s0[:, 0], sw)
+        assert np.array_equal(y.view(np.uint16), want.view(np.uint16)), gs
+        yb, qb, sb = impl.w8a8_linear_token_group_bf16(xb, wq, sw, gs)
+        q0, s0 = impl.quantize_rows_bf16(xb, 0, 127)
+        assert np.array_equal(qb, q0) and np.array_equal(sb, s0[:, 0])
+        assert np.array_equal(yb, impl.dequant_token_group_bf16(impl.int_dot_groups(q0, wq, gs), s0[:, 0], sw)), gs
+
+
+def check_linear_composites_brute(impl, trials=18, seed=43):
+    """bf16, W4A8-bf16 and per-token x per-group linears against the brute force."""
+    rng = np.random.default_rng(seed)
+    for t in range(trials):
+        M, N = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        gs = [2, 4][t % 2]
+        K = 4 * int(rng.integers(1, 4))
+        x = _rand_fp16(rng, (M, K), ["normal", "wide", "ties"][t % 3])
+        xb = _to_bf16_bits(x.astype(np.float32))
+        xr = [[float(v) for v in row] for row in impl.bf16_to_f32(xb)]
+        x16 = [[float(v) for v in row] for row in x]
+        w = _rand_fp16(rng, (N, K), ["normal", "wide", "small"][t % 3])
+        # per-token x per-group, fp16 and bf16
+        wq, sw = impl.quantize_rows(w, gs, 127)
+        wc = wq.astype(int).tolist()
+        wsc = [[Fraction(float(v)) for v in row] for row in sw]
+        with np.errstate(over="ignore"):
+            y, qa, _ = impl.w8a8_linear_token_group(x, wq, sw, gs)
+        by = brute.linear_token_group(x16, wc, wsc, gs)
+        assert [[float(v) for v in r] for r in y] == [[float(v) for v in r] for r in by], ("tok", t)
+        yb, _, _ = impl.w8a8_linear_token_group_bf16(xb, wq, sw, gs)
+        byb = brute.linear_token_group(xr, wc, wsc, gs, out=brute.bf16)
+        assert impl.bf16_to_f32(yb).tolist() == [[float(v) for v in r] for r in byb], ("tok bf16", t)
+        # bf16 linear (per-group codes along the same groups)
+        yb, qb, _ = impl.w8a8_linear_bf16(xb, wq, sw, gs)
+        byb, bq, _ = brute.linear_bf16(xr, wc, wsc, gs)
+        assert qb.astype(int).tolist() == bq
+        assert impl.bf16_to_f32(yb).tolist() == [[float(v) for v in r] for r in byb], ("bf16", t)
+        # W4A8 with bf16 rows: the packed bytes unpacked by the layout written here
+        q4, s4 = impl.quantize_rows(w, 0, 7)
+        p = impl.pack_int4(q4)
+        yb, _, _ = impl.w4a8_linear_bf16(xb, p, s4[:, 0])
+        codes = [_unpack_ref(row) for row in p.tolist()]
+        byb, _, _ = brute.linear_bf16(xr, codes, [[Fraction(float(r[0]))] for r in s4], 0)
+        assert impl.bf16_to_f32(yb).tolist() == [[float(v) for v in r] for r in byb], ("w4a8 bf16", t)
+
+
 ALL_CHECKS = [
     check_golden_quant, check_golden_division, check_golden_int4, check_golden_integer_gemm,
     check_closed_form_k10240, check_brute_quant, check_brute_linear,
@@ -632,5 +853,6 @@ ALL_CHECKS = [
     check_golden_token_group, check_brute_token_group, check_token_group_reductions,
     check_golden_clip, check_brute_clip, check_clip_vs_numpy_percentile, check_clip_reductions,
     check_golden_bf16, check_brute_bf16_rounding, check_brute_linear_bf16, check_bf16_reductions,
-    check_brute_token_group_bf16,
+    check_brute_token_group_bf16, check_dequant_long_k_exact, check_weight_quantizers_compose,
+    check_weight_quantizers_brute, check_linear_composites_compose, check_linear_composites_brute,
 ]

@@ -1,0 +1,94 @@
+"""The boundary's own symbols, called through ctypes with raw device pointers.
+
+The binding routes to the _dt / _ex forms of the calls; this file calls the
+plain entry points the boundary is specified by (cider_quant_act,
+cider_quant_weight, cider_w8a8_gemm at group sizes 0 / 64 / 128,
+cider_w4a8_gemm, cider_gemm_acc_i32) directly, on torch-allocated device
+buffers and torch's current HIP stream, and holds them to the oracle: codes,
+scales, packed bytes and accumulators bit for bit, outputs within the
+per-channel (1e-3) or per-group (2e-3 plus the fp32 summation bound) bar.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+from w8a8_online_quantized_amd import inputs
+from tests.test_gpu_parity import assert_y_close, cider, dev, host, pg_sum_bound
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def P(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def S():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ok(status, what):
+    assert status == 0, f"{what}: status {status}"
+
+
+CASES = [(1, 300, 2560, 0), (37, 250, 1024, 0), (300, 520, 2048, 0), (130, 700, 1024, 64),
+         (64, 260, 2560, 128), (1024, 1024, 4096, 128)]
+
+
+@pytest.mark.parametrize("M,N,K,gs", CASES)
+def test_literal_w8a8(M, N, K, gs):
+    c = cider()
+    L = c.lib()
+    x = inputs.activations(M, K, seed=91)
+    w = inputs.weights(N, K, seed=91)
+    xd, wd = dev(x), dev(w)
+    G = 1 if gs == 0 else K // gs
+    xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    sa = torch.empty((M, G), dtype=torch.float32, device="cuda")
+    wq = torch.empty((N, K), dtype=torch.int8, device="cuda")
+    sw = torch.empty((N, G), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    _ok(L.cider_quant_weight(P(wd), N, K, 8, gs, P(wq), P(sw), S()), "cider_quant_weight")
+    _ok(L.cider_quant_act(P(xd), M, K, gs, P(xq), P(sa), S()), "cider_quant_act")
+    _ok(L.cider_w8a8_gemm(P(xq), P(sa), P(wq), P(sw), M, N, K, gs, P(y), S()), "cider_w8a8_gemm")
+    wqo, swo = oracle.quantize_weight(w, 8, gs)
+    yo, qo, sao = oracle.w8a8_linear(x, wqo, swo, gs)
+    assert np.array_equal(host(wq), wqo) and np.array_equal(host(sw).reshape(swo.shape), swo)
+    assert np.array_equal(host(xq), qo) and np.array_equal(host(sa).reshape(sao.shape), sao)
+    if gs == 0:
+        assert_y_close(host(y), yo, 1e-3, max_ulp=1, what=f"literal pc {M}x{N}x{K}")
+    else:
+        e = pg_sum_bound(qo, sao, wqo, swo, gs, np.arange(M))
+        assert_y_close(host(y), yo, 2e-3, extra_atol=e, what=f"literal pg{gs} {M}x{N}x{K}")
+    acc = torch.empty((G, M, N) if gs else (M, N), dtype=torch.int32, device="cuda")
+    _ok(L.cider_gemm_acc_i32(0, P(xq), P(wq), M, N, K, gs, P(acc), S()), "cider_gemm_acc_i32")
+    ref = oracle.int_dot(qo, wqo) if gs == 0 else oracle.int_dot_groups(qo, wqo, gs)
+    assert np.array_equal(host(acc), ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 300, 2560), (3, 77, 1024), (130, 520, 2048), (512, 1000, 4096)])
+def test_literal_w4a8(M, N, K):
+    c = cider()
+    L = c.lib()
+    x = inputs.activations(M, K, seed=92)
+    w = inputs.weights(N, K, seed=92)
+    xd, wd = dev(x), dev(w)
+    xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    sa = torch.empty((M,), dtype=torch.float32, device="cuda")
+    wp = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda")
+    sw = torch.empty((N,), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    _ok(L.cider_quant_weight(P(wd), N, K, 4, 0, P(wp), P(sw), S()), "cider_quant_weight(4)")
+    _ok(L.cider_quant_act(P(xd), M, K, 0, P(xq), P(sa), S()), "cider_quant_act")
+    _ok(L.cider_w4a8_gemm(P(xq), P(sa), P(wp), P(sw), M, N, K, P(y), S()), "cider_w4a8_gemm")
+    wpo, swo = oracle.quantize_weight(w, 4, 0)
+    yo, qo, _ = oracle.w4a8_linear(x, wpo, swo)
+    assert np.array_equal(host(wp), wpo) and np.array_equal(host(sw), swo)
+    assert np.array_equal(host(xq), qo)
+    assert_y_close(host(y), yo, 1e-3, max_ulp=1, what=f"literal w4a8 {M}x{N}x{K}")
+    acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    _ok(L.cider_gemm_acc_i32(1, P(xq), P(wp), M, N, K, 0, P(acc), S()), "cider_gemm_acc_i32(1)")
+    assert np.array_equal(host(acc), oracle.int_dot(qo, oracle.unpack_int4(wpo)))

@@ -14,7 +14,9 @@ def _impl(**over):
         "quantize_rows", "pack_int4", "unpack_int4", "int_dot", "int_dot_groups",
         "dequant_per_channel", "dequant_per_group", "int8_mv", "dequant_token_group",
         "percentile_threshold", "quantize_rows_clip", "f64_to_bf16", "bf16_to_f32", "quantize_rows_bf16",
-        "dequant_bf16", "dequant_token_group_bf16")}
+        "dequant_bf16", "dequant_token_group_bf16", "quantize_weight", "quantize_weight_clip",
+        "quantize_weight_bf16", "quantize_weight_clip_bf16", "w8a8_linear", "w4a8_linear", "w8a8_linear_bf16",
+        "w4a8_linear_bf16", "w8a8_linear_token_group", "w8a8_linear_token_group_bf16")}
     base.update(over)
     ns = types.SimpleNamespace(**base)
     return ns
@@ -207,6 +209,53 @@ def _tok_bf16_no_act_scale(acc_g, s_a, s_w):
     return O.dequant_token_group_bf16(acc_g, np.ones_like(s_a), s_w)
 
 
+def _dequant_fp64_two_roundings(acc, s_a, s_w):
+    # the product rounded to fp64 and then to fp16: wrong at constructed midpoints
+    t = acc.astype(np.float64) * s_a.astype(np.float64)[:, None]
+    return (t * s_w.astype(np.float64)[None, :]).astype(np.float16)
+
+
+def _clip_int4_unpacked(w, bits=8, group_size=0, percentile=99.9):
+    if bits == 4:   # the int4 codes returned without packing them
+        q, s = O.quantize_rows_clip(w, 0, 7, percentile)
+        return q, s[:, 0]
+    return O.quantize_weight_clip(w, bits, group_size, percentile)
+
+
+def _weight_bf16_as_fp16(w_bits, bits=8, group_size=0):
+    return O.quantize_weight(np.asarray(w_bits, np.uint16).view(np.float16), bits, group_size)
+
+
+def _clip_bf16_min_max(w_bits, bits=8, group_size=0, percentile=99.9):
+    return O.quantize_weight_bf16(w_bits, bits, group_size)
+
+
+def _linear_bf16_act_per_token(x_bits, w_q, s_w, group_size=0):
+    # per-group weights, but the activations quantized per token
+    if group_size == 0:
+        return O.w8a8_linear_bf16(x_bits, w_q, s_w, 0)
+    q_a, s2 = O.quantize_rows_bf16(x_bits, 0, 127)
+    sa = np.repeat(s2, s_w.shape[1], axis=1)
+    return O.dequant_bf16(O.int_dot_groups(q_a, w_q, group_size), sa, s_w), q_a, sa
+
+
+def _w4a8_bf16_swapped_nibbles(x_bits, w_packed, s_w):
+    p = np.asarray(w_packed, np.uint8)
+    return O.w4a8_linear_bf16(x_bits, ((p >> 4) | (p << 4)).astype(np.uint8), s_w)
+
+
+def _token_group_act_per_group(x, w_q, s_w, group_size):
+    q_a, s_a = O.quantize_rows(x, group_size, 127)   # per-group activation codes
+    y = O.dequant_per_group(O.int_dot_groups(q_a, w_q, group_size), s_a, s_w)
+    return y, q_a, s_a[:, 0]
+
+
+def _token_group_bf16_fp16_output(x_bits, w_q, s_w, group_size):
+    y, q_a, s_a = O.w8a8_linear_token_group_bf16(x_bits, w_q, s_w, group_size)
+    f = O.bf16_to_f32(y)
+    return f.astype(np.float16).view(np.uint16), q_a, s_a
+
+
 MUTANTS = {
     "round_half_up": _impl(quantize_rows=_quant_variant(rounding="up")),
     "scale_over_128": _impl(quantize_rows=_quant_variant(divisor_bias=1)),
@@ -240,6 +289,14 @@ MUTANTS = {
     "bf16_double_rounding_via_fp32": _bf16_variant("via_fp32"),
     "bf16_rows_read_as_fp16": _bf16_variant("as_fp16"),
     "token_group_bf16_no_act_scale": _impl(dequant_token_group_bf16=_tok_bf16_no_act_scale),
+    "dequant_fp64_double_rounding": _impl(dequant_per_channel=_dequant_fp64_two_roundings),
+    "clip_int4_not_packed": _impl(quantize_weight_clip=_clip_int4_unpacked),
+    "weight_bf16_read_as_fp16": _impl(quantize_weight_bf16=_weight_bf16_as_fp16),
+    "clip_bf16_ignores_percentile": _impl(quantize_weight_clip_bf16=_clip_bf16_min_max),
+    "linear_bf16_per_token_activations": _impl(w8a8_linear_bf16=_linear_bf16_act_per_token),
+    "w4a8_bf16_swapped_nibbles": _impl(w4a8_linear_bf16=_w4a8_bf16_swapped_nibbles),
+    "token_group_quantizes_per_group": _impl(w8a8_linear_token_group=_token_group_act_per_group),
+    "token_group_bf16_fp16_output": _impl(w8a8_linear_token_group_bf16=_token_group_bf16_fp16_output),
 }
 
 

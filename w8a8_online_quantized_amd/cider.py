@@ -8,7 +8,9 @@ gfx950, the call raises instead of computing anything some other way.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import functools
 import os
 import re
 
@@ -120,6 +122,23 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on_stream(fn):
+    """Run the wrapped call with `stream` (when given) as torch's current
+    stream, so that every output and temporary it allocates belongs to the
+    stream its kernels run on: torch's caching allocator then reuses a freed
+    temporary only for later work on that same stream, never while a kernel
+    of the call may still read it."""
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kw):
+        if stream is None:
+            return fn(*args, **kw)
+        import torch
+        ctx = torch.cuda.stream(stream) if stream != torch.cuda.current_stream() else contextlib.nullcontext()
+        with ctx:
+            return fn(*args, stream=stream, **kw)
+    return wrapper
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -161,6 +180,7 @@ def _scale_shape(rows, K, group_size):
     return (rows,) if group_size == 0 else (rows, K // group_size)
 
 
+@_on_stream
 def cider_quant_act(x, group_size: int = 0, x_q=None, x_scale=None, stream=None):
     """fp16 or bf16 [M, K] -> (int8 codes [M, K], fp32 scales [M] or [M, K/gs])."""
     import torch
@@ -178,6 +198,7 @@ def cider_quant_act(x, group_size: int = 0, x_q=None, x_scale=None, stream=None)
     return x_q, x_scale
 
 
+@_on_stream
 def cider_quant_weight(w, bits: int = 8, group_size: int = 0, w_q=None, w_scale=None, stream=None):
     """fp16 or bf16 [N, K] -> (int8 [N, K] or packed uint8 [N, K/2], fp32 scales)."""
     import torch
@@ -197,6 +218,7 @@ def cider_quant_weight(w, bits: int = 8, group_size: int = 0, w_q=None, w_scale=
     return w_q, w_scale
 
 
+@_on_stream
 def cider_quant_weight_clip(w, bits: int = 8, group_size: int = 0, percentile: float = 99.9, w_q=None,
                             w_scale=None, stream=None):
     """cider_quant_weight with percentile-clipped scales (same outputs)."""
@@ -232,6 +254,7 @@ def _ws_args(workspace):
     return _ptr(workspace), workspace.numel() * workspace.element_size()
 
 
+@_on_stream
 def cider_w8a8_gemm(x_q, x_scale, w_q, w_scale, group_size: int = 0, y=None, stream=None, out_dtype=None,
                     workspace=None):
     """int8 codes + scales -> y [M, N] (fused dequant): fp16, or bf16 when
@@ -257,6 +280,7 @@ def cider_w8a8_gemm(x_q, x_scale, w_q, w_scale, group_size: int = 0, y=None, str
     return y
 
 
+@_on_stream
 def cider_w8a8_gemm_token_group(x_q, x_scale, w_q, w_scale, group_size: int, y=None, stream=None, workspace=None,
                                 out_dtype=None):
     """Per-token activation codes (x_scale [M]) times per-group weight codes
@@ -281,6 +305,7 @@ def cider_w8a8_gemm_token_group(x_q, x_scale, w_q, w_scale, group_size: int, y=N
     return y
 
 
+@_on_stream
 def cider_w8a8_gemm_split(x_q, x_scale, w_q, w_scale, part_n, ys=None, stream=None, out_dtype=None):
     """Per-channel GEMM of x_q against row-concatenated weights w_q [sum(part_n), K];
     returns one [M, part_n[i]] output per part: fp16, or bf16 when out_dtype
@@ -317,6 +342,7 @@ def cider_linear_workspace_size(M: int, N: int, K: int, bits: int = 8, group_siz
     return n
 
 
+@_on_stream
 def cider_linear(x, w, w_scale, bits: int = 8, group_size: int = 0, workspace=None, y=None, stream=None):
     """x [M, K] -> y [M, N] of the same dtype (fp16 or bf16) through the
     quantized linear (w: int8 codes [N, K] for bits 8, packed uint8 [N, K/2]
@@ -344,6 +370,7 @@ def cider_linear(x, w, w_scale, bits: int = 8, group_size: int = 0, workspace=No
     return y
 
 
+@_on_stream
 def cider_int8_mv(x, w_q, w_scale, group_size: int = 0, y=None, stream=None):
     """Decode MV: fp16 x [M, K] (M <= 4) times int8 weights dequantized on the
     fly -> fp16 y [M, N]; no activation quantization."""
@@ -363,6 +390,7 @@ def cider_int8_mv(x, w_q, w_scale, group_size: int = 0, y=None, stream=None):
     return y
 
 
+@_on_stream
 def cider_w4a8_gemm(x_q, x_scale, w_packed, w_scale, y=None, stream=None, out_dtype=None, workspace=None):
     """int8 activation codes x packed int4 weights -> y [M, N] (fp16 or bf16)."""
     import torch
@@ -382,6 +410,7 @@ def cider_w4a8_gemm(x_q, x_scale, w_packed, w_scale, y=None, stream=None, out_dt
     return y
 
 
+@_on_stream
 def cider_gemm_acc_i32(mode: int, x_q, w, group_size: int = 0, acc=None, stream=None):
     """int32 accumulators of the GEMM main loop: [M, N], or [G, M, N] per group."""
     import torch
@@ -401,6 +430,7 @@ def cider_gemm_acc_i32(mode: int, x_q, w, group_size: int = 0, acc=None, stream=
     return acc
 
 
+@_on_stream
 def w8a8_linear(x, w_q, w_scale, group_size: int = 0, stream=None):
     """The README's per-channel / per-group linear: quantize x, then the fused
     GEMM; the output has x's type (fp16 or bf16)."""
@@ -408,12 +438,14 @@ def w8a8_linear(x, w_q, w_scale, group_size: int = 0, stream=None):
     return cider_w8a8_gemm(x_q, x_scale, w_q, w_scale, group_size, stream=stream, out_dtype=x.dtype)
 
 
+@_on_stream
 def w8a8_linear_token_group(x, w_q, w_scale, group_size: int, stream=None):
     """Per-token activation quantization, then the per-group-weight GEMM."""
     x_q, x_scale = cider_quant_act(x, 0, stream=stream)
     return cider_w8a8_gemm_token_group(x_q, x_scale, w_q, w_scale, group_size, stream=stream)
 
 
+@_on_stream
 def w4a8_linear(x, w_packed, w_scale, stream=None):
     """The README's W4A8 linear: per-token int8 activations times packed int4
     weights; the output has x's type (fp16 or bf16)."""
@@ -455,6 +487,7 @@ def fuse_stack_layer(layer):
     return out
 
 
+@_on_stream
 def cider_stack_forward(x, layers, dims, workspace=None, y=None, stream=None):
     """Runs the chained linear stack. `layers`: list of dicts {name: (codes, scales)}
     for the seven projections; dims = (hidden, q_dim, kv_dim, mlp_dim)."""
