@@ -65,6 +65,7 @@ typedef enum {
   CIDER_ERROR_INVALID_VALUE = 1,
   CIDER_ERROR_NOT_SUPPORTED = 2,
   CIDER_ERROR_LAUNCH = 3,
+  CIDER_ERROR_SCRATCH_LIMIT = 4, /* cider_w8a8_gemm_noalloc: the shape needs more scratch */
 } cider_status_t;
 
 /* Element types of fp inputs and outputs (the README's roadmap: automatic
@@ -178,6 +179,29 @@ cider_status_t cider_w8a8_gemm_ex(const int8_t* x_q, const float* x_scale, const
 cider_status_t cider_w4a8_gemm_ex(const int8_t* x_q, const float* x_scale, const uint8_t* w_packed,
                                   const float* w_scale, int64_t M, int64_t N, int64_t K, void* y,
                                   int32_t y_dtype, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * GEMM as cider_w8a8_gemm_ex (per-channel or per-group, fp16 or bf16 y, the
+ * same dispatch and the same bits), with the split-K scratch taken from a
+ * library-owned device array of CIDER_NOALLOC_SCRATCH_BYTES instead of a
+ * caller workspace. The call allocates nothing (no hipMalloc / hipFree, no
+ * allocating library routine); on a device's first call it looks up the
+ * array's device address (hipGetSymbolAddress) and keeps it.
+ *   - Every GPU that runs the library holds its own array until the process
+ *     ends. All calls on one GPU share it, so calls that overlap in time on
+ *     one GPU (different streams, or several host threads) race and must be
+ *     serialized by the caller; calls in one stream's order are safe.
+ *   - A shape whose split-K plan needs more than the array holds
+ *     (cider_gemm_workspace_size(M, N, K, 8, group_size) >
+ *     CIDER_NOALLOC_SCRATCH_BYTES) returns CIDER_ERROR_SCRATCH_LIMIT and
+ *     enqueues nothing; every plan of the current dispatch needs at most
+ *     42 MiB. Shapes that do not split use no scratch.
+ * Arguments, sizes and other errors as for cider_w8a8_gemm_dt. */
+#define CIDER_NOALLOC_SCRATCH_BYTES (48ll * 1024 * 1024)
+cider_status_t cider_w8a8_gemm_noalloc(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
+                                       const float* w_scale, int64_t M, int64_t N, int64_t K,
+                                       int32_t group_size, void* y, int32_t y_dtype, void* stream);
 
 /* The same with the output type chosen by y_dtype (a cider_dtype_t). */
 cider_status_t cider_w4a8_gemm_dt(const int8_t* x_q, const float* x_scale, const uint8_t* w_packed,

@@ -22,6 +22,8 @@ CIDER_SUCCESS = 0
 CIDER_ERROR_INVALID_VALUE = 1
 CIDER_ERROR_NOT_SUPPORTED = 2
 CIDER_ERROR_LAUNCH = 3
+CIDER_ERROR_SCRATCH_LIMIT = 4
+NOALLOC_SCRATCH_BYTES = 48 * 1024 * 1024
 
 _c_i64, _c_i32, _c_p = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
 
@@ -46,6 +48,8 @@ SIGNATURES = {
     "cider_gemm_workspace_size": (ctypes.c_int64, [_c_i64, _c_i64, _c_i64, _c_i32, _c_i32]),
     "cider_w8a8_gemm_ex": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_i32, _c_p,
                                          _c_i64, _c_p]),
+    "cider_w8a8_gemm_noalloc": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_i32,
+                                              _c_p]),
     "cider_w4a8_gemm_ex": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_i32, _c_p, _c_i64,
                                          _c_p]),
     "cider_linear": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_p, _c_i64, _c_p,
@@ -277,6 +281,29 @@ def cider_w8a8_gemm(x_q, x_scale, w_q, w_scale, group_size: int = 0, y=None, str
     _check("cider_w8a8_gemm_ex", lib().cider_w8a8_gemm_ex(_ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale),
                                                           M, N, K, group_size, _ptr(y), dt, wsp, wsb,
                                                           _stream(stream)))
+    return y
+
+
+@_on_stream
+def cider_w8a8_gemm_noalloc(x_q, x_scale, w_q, w_scale, group_size: int = 0, y=None, stream=None, out_dtype=None):
+    """cider_w8a8_gemm with the split-K scratch in the library's own device
+    array (the C call allocates nothing; pass y to allocate nothing here
+    either). Calls that overlap in time on one GPU race on that array."""
+    import torch
+    M, K = x_q.shape
+    N = w_q.shape[0]
+    _need(x_q, torch.int8, (M, K), "x_q")
+    _need(w_q, torch.int8, (N, K), "w_q")
+    if group_size and K % group_size:
+        raise ValueError("K must be a multiple of group_size")
+    _need(x_scale, torch.float32, _scale_shape(M, K, group_size), "x_scale")
+    _need(w_scale, torch.float32, _scale_shape(N, K, group_size), "w_scale")
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype or torch.float16, device=x_q.device)
+    dt = _fp_code(y, "y")
+    _need(y, y.dtype, (M, N), "y")
+    _check("cider_w8a8_gemm_noalloc", lib().cider_w8a8_gemm_noalloc(_ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale),
+                                                                    M, N, K, group_size, _ptr(y), dt, _stream(stream)))
     return y
 
 

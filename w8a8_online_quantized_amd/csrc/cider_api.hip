@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "cider_internal.h"
 
@@ -55,6 +56,34 @@ bool device_is_gfx950() {
 
 cider_status_t from_hip(hipError_t e) { return e == hipSuccess ? CIDER_SUCCESS : CIDER_ERROR_LAUNCH; }
 
+// Split-K scratch of cider_w8a8_gemm_noalloc (for callers that cannot
+// allocate). Every GPU that loads the library holds its own copy of this
+// array until the process ends; in host code its name is only a stand-in, so
+// the kernels get the device address looked up below, never the name.
+static __device__ __align__(256) int8_t scratch[CIDER_NOALLOC_SCRATCH_BYTES];
+
+// This device's address of `scratch`, looked up on the device's first
+// no-allocation call (with the device current) and kept; null if the lookup
+// fails.
+std::atomic<void*> g_scratch[kMaxDevices];
+std::atomic<int> g_scratch_state[kMaxDevices];   // 0 = not looked up, 1 = ok, 2 = failed
+std::mutex g_scratch_mu;
+
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  if (g_scratch_state[dev].load(std::memory_order_acquire) == 0) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_state[dev].load(std::memory_order_relaxed) == 0) {
+      void* ptr = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      g_scratch[dev].store(e == hipSuccess ? ptr : nullptr, std::memory_order_relaxed);
+      g_scratch_state[dev].store(e == hipSuccess && ptr ? 1 : 2, std::memory_order_release);
+    }
+  }
+  return g_scratch_state[dev].load(std::memory_order_acquire) == 1 ? g_scratch[dev].load() : nullptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -67,6 +96,9 @@ const char* cider_status_string(cider_status_t s) {
     case CIDER_ERROR_INVALID_VALUE: return "invalid argument (null/misaligned pointer, bad size or group size)";
     case CIDER_ERROR_NOT_SUPPORTED: return "not supported (no gfx950 device is current)";
     case CIDER_ERROR_LAUNCH: return "kernel launch failed";
+    case CIDER_ERROR_SCRATCH_LIMIT:
+      return "the shape's split-K plan needs more scratch than cider_w8a8_gemm_noalloc holds "
+             "(CIDER_NOALLOC_SCRATCH_BYTES = 48 MiB)";
   }
   return "unknown status";
 }
@@ -197,6 +229,32 @@ cider_status_t cider_w8a8_gemm_ex(const int8_t* x_q, const float* x_scale, const
   g.ws = workspace;
   g.ws_bytes = workspace ? workspace_bytes : 0;
   return gemm_common(g, cider::kWeightI8, y_dtype == CIDER_DTYPE_BF16 ? cider::kEpiBF16 : cider::kEpiF16, stream);
+}
+
+cider_status_t cider_w8a8_gemm_noalloc(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
+                                       const float* w_scale, int64_t M, int64_t N, int64_t K, int32_t group_size,
+                                       void* y, int32_t y_dtype, void* stream) {
+  if (!valid_dtype(y_dtype)) return CIDER_ERROR_INVALID_VALUE;
+  if (!gemm_sizes_ok(M, N) || !valid_gs(group_size) || !valid_k(K, 16, group_size))
+    return CIDER_ERROR_INVALID_VALUE;
+  if (M == 0 || N == 0) return CIDER_SUCCESS;
+  if (!x_q || !x_scale || !w_q || !w_scale || !y) return CIDER_ERROR_INVALID_VALUE;
+  if (!aligned16(x_q) || !aligned16(x_scale) || !aligned16(w_q) || !aligned16(w_scale) || !aligned16(y))
+    return CIDER_ERROR_INVALID_VALUE;
+  const int64_t need = cider_gemm_workspace_size(M, N, K, 8, group_size);
+  if (need > CIDER_NOALLOC_SCRATCH_BYTES) return CIDER_ERROR_SCRATCH_LIMIT;
+  if (!device_is_gfx950()) return CIDER_ERROR_NOT_SUPPORTED;
+  cider::GemmArgs g{x_q, x_scale, w_q, w_scale, M, N, K, group_size, y, nullptr};
+  if (need > 0) {
+    // every slab element the reduction reads is written first by the same
+    // call's split kernel, so nothing in the scratch needs clearing
+    g.ws = scratch_address();
+    if (!g.ws) return CIDER_ERROR_LAUNCH;
+    g.ws_bytes = CIDER_NOALLOC_SCRATCH_BYTES;
+  }
+  return from_hip(cider::launch_gemm(g, cider::kWeightI8,
+                                     y_dtype == CIDER_DTYPE_BF16 ? cider::kEpiBF16 : cider::kEpiF16,
+                                     static_cast<hipStream_t>(stream)));
 }
 
 cider_status_t cider_w4a8_gemm(const int8_t* x_q, const float* x_scale, const uint8_t* w_packed,
