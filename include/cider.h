@@ -43,9 +43,17 @@
  *   - Zero-sized work (M == 0 or N == 0) returns CIDER_SUCCESS and launches
  *     nothing; the pointers may then be NULL. Size queries (int64_t results)
  *     return -1 for invalid arguments.
- *   - K must be a positive multiple of 16 (of 32 for int4 weights) and at most
- *     CIDER_MAX_K, which keeps |acc| = |sum of K products of codes| <= 127*127*K
- *     below 2^31. Per-group calls need K % group_size == 0.
+ *   - K is at most CIDER_MAX_K, which keeps |acc| = |sum of K products of
+ *     codes| <= 127*127*K below 2^31. The per-channel calls (cider_quant_act
+ *     and cider_quant_weight with group_size 0, cider_w8a8_gemm[_dt/_ex/
+ *     _noalloc] and cider_gemm_acc_i32 with group_size 0, cider_linear[_dt]
+ *     with group_size 0) accept any K >= 1 for int8 codes and any even K for
+ *     packed int4 weights; rows whose length is not a multiple of 16 code
+ *     bytes (32 codes for int4) start at unaligned addresses and take a
+ *     general, slower path with the same results. Per-group calls need
+ *     K % group_size == 0. cider_int8_mv, cider_w8a8_gemm_token_group[_dt],
+ *     cider_w8a8_gemm_split[_dt], cider_quant_weight_clip and the stack
+ *     driver need K a multiple of 16 (32 for int4 weights).
  *   - Calls are reentrant; concurrent calls on different streams do not share
  *     any library state (there is none beyond a cached device-architecture flag).
  */
@@ -103,7 +111,7 @@ cider_status_t cider_quant_act_dt(const void* x, int32_t x_dtype, int64_t M, int
 /* Weight quantization (the README runs it offline in numpy; here it is a
  * device kernel with the same rule, not part of the timed linear).
  *   w_f16   : fp16 [N, K] weights, row = output channel.
- *   bits    : 8 or 4. bits 4 requires group_size 0 and K % 32 == 0.
+ *   bits    : 8 or 4. bits 4 requires group_size 0 and an even K.
  *   w_q     : bits 8: int8 [N, K] codes; bits 4: uint8 [N, K/2] packed nibbles.
  *   w_scale : fp32 [N] (group_size 0) or [N, K/group_size].
  */
@@ -151,7 +159,7 @@ cider_status_t cider_w8a8_gemm_dt(const int8_t* x_q, const float* x_scale, const
 
 /* W4A8 GEMM with fused dequant: the int4 weights are unpacked to int8 codes
  * (nibble - 8) inside the matmul's operand loads; per-channel scales only.
- *   w_packed uint8 [N, K/2] (K % 32 == 0), w_scale fp32 [N]; the rest as above.
+ *   w_packed uint8 [N, K/2] (K even), w_scale fp32 [N]; the rest as above.
  */
 cider_status_t cider_w4a8_gemm(const int8_t* x_q, const float* x_scale, const uint8_t* w_packed,
                                const float* w_scale, int64_t M, int64_t N, int64_t K,
@@ -214,8 +222,9 @@ cider_status_t cider_w4a8_gemm_dt(const int8_t* x_q, const float* x_scale, const
  * cider_w4a8_gemm (bits 4), with identical results.
  *   w : bits 8: int8 [N, K] codes, w_scale fp32 [N] or [N, K/group_size];
  *       bits 4: packed uint8 [N, K/2], w_scale fp32 [N] (group_size 0).
- *   For group_size 0 and M <= 2 (when the M activation rows' codes fit the
- *   GEMV kernel's 64 KiB staging area: M * ceil(K/256)*256 <= 65536) it is
+ *   For group_size 0, M <= 2 and K a multiple of 16 (32 for bits 4), when
+ *   the M activation rows' codes fit the GEMV kernel's 64 KiB staging area
+ *   (M * ceil(K/256)*256 <= 65536), it is
  *   ONE kernel launch that quantizes the activations itself and needs no
  *   workspace. Otherwise the codes and
  *   scales go through `workspace` (device, 16-byte aligned, at least

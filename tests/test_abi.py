@@ -36,8 +36,8 @@ NULL = None
 INV = cider.CIDER_ERROR_INVALID_VALUE
 
 
-@pytest.mark.parametrize("M,K,gs", [(-1, 64, 0), (4, 0, 0), (4, 8, 0), (4, 24, 0), (4, 96, 64),
-                                    (4, 128, 32), (4, 133120 + 128, 0)])
+@pytest.mark.parametrize("M,K,gs", [(-1, 64, 0), (4, 0, 0), (4, -8, 0), (4, 96, 64),
+                                    (4, 128, 32), (4, 133120 + 128, 0), (4, 100, 64)])
 def test_quant_act_rejects_bad_sizes(M, K, gs):
     assert L.cider_quant_act(P, M, K, gs, P, P, NULL) == INV
 
@@ -66,7 +66,7 @@ def test_empty_work_is_success_without_pointers():
 def test_quant_weight_rejects():
     assert L.cider_quant_weight(P, 4, 64, 6, 0, P, P, NULL) == INV        # bits
     assert L.cider_quant_weight(P, 4, 64, 4, 64, P, P, NULL) == INV       # int4 is per-channel
-    assert L.cider_quant_weight(P, 4, 48, 4, 0, P, P, NULL) == INV        # int4 needs K % 32
+    assert L.cider_quant_weight(P, 4, 47, 4, 0, P, P, NULL) == INV        # int4 needs an even K
     assert L.cider_quant_weight(P, 4, 192, 8, 128, P, P, NULL) == INV     # K % gs
     assert L.cider_quant_weight(P, 4, 64, 8, 0, P, MIS, NULL) == INV
 
@@ -75,7 +75,7 @@ def test_gemm_rejects():
     g = L.cider_w8a8_gemm
     assert g(P, P, P, P, -1, 4, 64, 0, P, NULL) == INV
     assert g(P, P, P, P, 4, -1, 64, 0, P, NULL) == INV
-    assert g(P, P, P, P, 4, 4, 40, 0, P, NULL) == INV
+    assert g(P, P, P, P, 4, 4, 0, 0, P, NULL) == INV
     assert g(P, P, P, P, 4, 4, 192, 128, P, NULL) == INV
     assert g(P, P, P, P, 4, 4, 128, 100, P, NULL) == INV
     assert g(P, P, P, P, 4, 4, 1 << 20, 0, P, NULL) == INV               # int32 range guard
@@ -83,7 +83,7 @@ def test_gemm_rejects():
     assert g(P, P, P, P, 4, 4, 64, 0, NULL, NULL) == INV
     assert g(P, P, P, MIS, 4, 4, 64, 0, P, NULL) == INV
     h = L.cider_w4a8_gemm
-    assert h(P, P, P, P, 4, 4, 48, P, NULL) == INV
+    assert h(P, P, P, P, 4, 4, 47, P, NULL) == INV                      # int4 needs an even K
     assert h(P, P, MIS, P, 4, 4, 64, P, NULL) == INV
     a = L.cider_gemm_acc_i32
     assert a(2, P, P, 4, 4, 64, 0, P, NULL) == INV
@@ -148,11 +148,14 @@ def test_linear_workspace_query_and_rejects():
     assert q(300, 64, 1024, 8, 64) == 300 * 1024 + (4 * 300 * 16 + 255) // 256 * 256
     assert q(0, 64, 1024, 8, 0) == 0
     assert q(128, 2560, 10240, 8, 0) == 128 * 10240 + 512 + 8 * 128 * 2560 * 4   # + split-K slabs
-    assert q(4, 64, 1024, 6, 0) == -1 and q(4, 64, 1024, 4, 64) == -1 and q(4, 64, 48, 4, 0) == -1
+    assert q(4, 64, 1024, 6, 0) == -1 and q(4, 64, 1024, 4, 64) == -1 and q(4, 64, 47, 4, 0) == -1
+    # unaligned K: never the one-launch path, codes + scales through the workspace
+    assert q(1, 64, 40, 8, 0) == 256 + 256 and q(2, 64, 34, 4, 0) == 256 + 256 and q(3, 64, 2568, 8, 0) == 7936 + 256
     assert q(-1, 64, 64, 8, 0) == -1
     lin = L.cider_linear
     assert lin(P, P, P, 4, 8, 1024, 6, 0, NULL, 0, P, NULL) == INV        # bits
-    assert lin(P, P, P, 4, 8, 40, 8, 0, NULL, 0, P, NULL) == INV          # K % 16
+    assert lin(P, P, P, 4, 8, 47, 4, 0, NULL, 0, P, NULL) == INV          # int4 needs an even K
+    assert lin(P, P, P, 1, 8, 40, 8, 0, NULL, 0, P, NULL) == INV          # unaligned K needs the workspace
     assert lin(P, P, P, 5, 8, 1024, 8, 0, NULL, 0, P, NULL) == INV        # workspace needed
     assert lin(P, P, P, 5, 8, 1024, 8, 0, P, 100, P, NULL) == INV         # workspace too small
     assert lin(P, P, P, 5, 8, 1024, 8, 0, MIS, 1 << 20, P, NULL) == INV
@@ -179,7 +182,7 @@ def test_quant_weight_clip_rejects():
 def test_dtype_entries_reject():
     assert L.cider_quant_act_dt(P, 2, 4, 64, 0, P, P, NULL) == INV      # dtype
     assert L.cider_quant_act_dt(P, -1, 4, 64, 0, P, P, NULL) == INV
-    assert L.cider_quant_act_dt(P, 1, 4, 40, 0, P, P, NULL) == INV      # K % 16
+    assert L.cider_quant_act_dt(P, 1, 4, 0, 0, P, P, NULL) == INV       # K >= 1
     assert L.cider_quant_act_dt(NULL, 1, 0, 64, 0, NULL, NULL, NULL) == 0
     assert L.cider_quant_weight_dt(P, 2, 4, 64, 8, 0, P, P, NULL) == INV
     assert L.cider_quant_weight_dt(P, 1, 4, 64, 4, 64, P, P, NULL) == INV
@@ -188,7 +191,7 @@ def test_dtype_entries_reject():
     assert L.cider_w8a8_gemm_dt(P, P, P, P, 4, 4, 64, 0, MIS, 1, NULL) == INV
     assert L.cider_w8a8_gemm_dt(NULL, NULL, NULL, NULL, 0, 4, 64, 0, NULL, 1, NULL) == 0
     assert L.cider_w4a8_gemm_dt(P, P, P, P, 4, 4, 64, P, 7, NULL) == INV
-    assert L.cider_w4a8_gemm_dt(P, P, P, P, 4, 4, 48, P, 1, NULL) == INV
+    assert L.cider_w4a8_gemm_dt(P, P, P, P, 4, 4, 47, P, 1, NULL) == INV
     assert L.cider_w4a8_gemm_dt(NULL, NULL, NULL, NULL, 4, 0, 64, NULL, 1, NULL) == 0
 
 
@@ -206,7 +209,9 @@ def test_split_k_workspace_plan():
     assert g(4096, 2560, 10240, 8, 128) == 0                      # per-group with enough tiles
     assert g(16, 2560, 10240, 8, 0) == 0                          # skinny path
     assert g(0, 2560, 10240, 8, 0) == 0
-    assert g(4, 4, 40, 8, 0) == -1 and g(4, 4, 64, 4, 64) == -1 and g(4, 4, 64, 6, 0) == -1
+    assert g(4, 4, 0, 8, 0) == -1 and g(4, 4, 64, 4, 64) == -1 and g(4, 4, 64, 6, 0) == -1
+    assert g(4, 4, 47, 4, 0) == -1 and g(4, 4, 40, 8, 64) == -1
+    assert g(4, 4, 40, 8, 0) == 0 and g(1024, 2560, 10248, 8, 0) == 0   # unaligned K never splits
     ex = L.cider_w8a8_gemm_ex
     assert ex(P, P, P, P, 128, 2560, 10240, 0, P, 0, P, 1024, NULL) == INV     # workspace too small
     assert ex(P, P, P, P, 128, 2560, 10240, 0, P, 0, MIS, 1 << 30, NULL) == INV

@@ -7,6 +7,7 @@ cider_w4a8_gemm, cider_gemm_acc_i32) directly, on torch-allocated device
 buffers and torch's current HIP stream, and holds them to the oracle: codes,
 scales, packed bytes and accumulators bit for bit, outputs within the
 per-channel (1e-3) or per-group (2e-3 plus the fp32 summation bound) bar.
+K includes values that are not multiples of 16 (int8) or 32 (int4).
 """
 import ctypes
 
@@ -35,7 +36,9 @@ def _ok(status, what):
 
 
 CASES = [(1, 300, 2560, 0), (37, 250, 1024, 0), (300, 520, 2048, 0), (130, 700, 1024, 64),
-         (64, 260, 2560, 128), (1024, 1024, 4096, 128)]
+         (64, 260, 2560, 128), (1024, 1024, 4096, 128),
+         # K not a multiple of 16: unaligned rows
+         (1, 40, 1, 0), (5, 33, 15, 0), (17, 100, 40, 0), (70, 260, 2568, 0)]
 
 
 @pytest.mark.parametrize("M,N,K,gs", CASES)
@@ -69,7 +72,8 @@ def test_literal_w8a8(M, N, K, gs):
     assert np.array_equal(host(acc), ref)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 300, 2560), (3, 77, 1024), (130, 520, 2048), (512, 1000, 4096)])
+@pytest.mark.parametrize("M,N,K", [(1, 300, 2560), (3, 77, 1024), (130, 520, 2048), (512, 1000, 4096),
+                                   (1, 9, 2), (7, 40, 34), (33, 70, 2570)])
 def test_literal_w4a8(M, N, K):
     c = cider()
     L = c.lib()

@@ -19,8 +19,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool valid_gs(int32_t gs) { return gs == 0 || gs == 64 || gs == 128; }
 
-// K must be a positive multiple of `mult`, at most CIDER_MAX_K, and a multiple
-// of the group size.
+// K must be a positive multiple of `mult` (1 for int8 codes, 2 for packed
+// int4, 16 where a kernel family needs aligned rows), at most CIDER_MAX_K,
+// and a multiple of the group size.
 bool valid_k(int64_t K, int64_t mult, int32_t gs) {
   if (K <= 0 || K > CIDER_MAX_K || K % mult) return false;
   return gs == 0 || K % gs == 0;
@@ -114,7 +115,7 @@ static bool valid_dtype(int32_t d) { return d == CIDER_DTYPE_F16 || d == CIDER_D
 cider_status_t cider_quant_act_dt(const void* x, int32_t x_dtype, int64_t M, int64_t K, int32_t group_size,
                                   int8_t* x_q, float* x_scale, void* stream) {
   if (!valid_dtype(x_dtype)) return CIDER_ERROR_INVALID_VALUE;
-  if (M < 0 || !valid_gs(group_size) || !valid_k(K, 16, group_size)) return CIDER_ERROR_INVALID_VALUE;
+  if (M < 0 || !valid_gs(group_size) || !valid_k(K, 1, group_size)) return CIDER_ERROR_INVALID_VALUE;
   if (M == 0) return CIDER_SUCCESS;
   if (!x || !x_q || !x_scale || !aligned16(x) || !aligned16(x_q) || !aligned16(x_scale))
     return CIDER_ERROR_INVALID_VALUE;
@@ -139,9 +140,9 @@ cider_status_t cider_quant_weight_dt(const void* w, int32_t w_dtype, int64_t N, 
   const void* w_f16 = w;
   if (N < 0 || !valid_gs(group_size)) return CIDER_ERROR_INVALID_VALUE;
   if (bits == 8) {
-    if (!valid_k(K, 16, group_size)) return CIDER_ERROR_INVALID_VALUE;
+    if (!valid_k(K, 1, group_size)) return CIDER_ERROR_INVALID_VALUE;
   } else if (bits == 4) {
-    if (group_size != 0 || !valid_k(K, 32, 0)) return CIDER_ERROR_INVALID_VALUE;
+    if (group_size != 0 || !valid_k(K, 2, 0)) return CIDER_ERROR_INVALID_VALUE;
   } else {
     return CIDER_ERROR_INVALID_VALUE;
   }
@@ -194,8 +195,8 @@ cider_status_t cider_w8a8_gemm(const int8_t* x_q, const float* x_scale, const in
 
 int64_t cider_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t bits, int32_t group_size) {
   if (!gemm_sizes_ok(M, N) || !valid_gs(group_size) || (bits != 8 && bits != 4)) return -1;
-  if (bits == 4 && (group_size != 0 || !valid_k(K, 32, 0))) return -1;
-  if (bits == 8 && !valid_k(K, 16, group_size)) return -1;
+  if (bits == 4 && (group_size != 0 || !valid_k(K, 2, 0))) return -1;
+  if (bits == 8 && !valid_k(K, 1, group_size)) return -1;
   if (M == 0 || N == 0) return 0;
   return cider::gemm_split_workspace_bytes(M, N, K, bits == 4 ? cider::kWeightI4 : cider::kWeightI8, group_size);
 }
@@ -217,7 +218,7 @@ cider_status_t cider_w8a8_gemm_ex(const int8_t* x_q, const float* x_scale, const
                                   void* y_f16, int32_t y_dtype, void* workspace, int64_t workspace_bytes,
                                   void* stream) {
   if (!valid_dtype(y_dtype)) return CIDER_ERROR_INVALID_VALUE;
-  if (!gemm_sizes_ok(M, N) || !valid_gs(group_size) || !valid_k(K, 16, group_size))
+  if (!gemm_sizes_ok(M, N) || !valid_gs(group_size) || !valid_k(K, 1, group_size))
     return CIDER_ERROR_INVALID_VALUE;
   if (M == 0 || N == 0) return CIDER_SUCCESS;
   if (!x_q || !x_scale || !w_q || !w_scale || !y_f16) return CIDER_ERROR_INVALID_VALUE;
@@ -235,7 +236,7 @@ cider_status_t cider_w8a8_gemm_noalloc(const int8_t* x_q, const float* x_scale, 
                                        const float* w_scale, int64_t M, int64_t N, int64_t K, int32_t group_size,
                                        void* y, int32_t y_dtype, void* stream) {
   if (!valid_dtype(y_dtype)) return CIDER_ERROR_INVALID_VALUE;
-  if (!gemm_sizes_ok(M, N) || !valid_gs(group_size) || !valid_k(K, 16, group_size))
+  if (!gemm_sizes_ok(M, N) || !valid_gs(group_size) || !valid_k(K, 1, group_size))
     return CIDER_ERROR_INVALID_VALUE;
   if (M == 0 || N == 0) return CIDER_SUCCESS;
   if (!x_q || !x_scale || !w_q || !w_scale || !y) return CIDER_ERROR_INVALID_VALUE;
@@ -273,7 +274,7 @@ cider_status_t cider_w4a8_gemm_ex(const int8_t* x_q, const float* x_scale, const
                                   const float* w_scale, int64_t M, int64_t N, int64_t K, void* y_f16,
                                   int32_t y_dtype, void* workspace, int64_t workspace_bytes, void* stream) {
   if (!valid_dtype(y_dtype)) return CIDER_ERROR_INVALID_VALUE;
-  if (!gemm_sizes_ok(M, N) || !valid_k(K, 32, 0)) return CIDER_ERROR_INVALID_VALUE;
+  if (!gemm_sizes_ok(M, N) || !valid_k(K, 2, 0)) return CIDER_ERROR_INVALID_VALUE;
   if (M == 0 || N == 0) return CIDER_SUCCESS;
   if (!x_q || !x_scale || !w_packed || !w_scale || !y_f16) return CIDER_ERROR_INVALID_VALUE;
   if (!aligned16(x_q) || !aligned16(x_scale) || !aligned16(w_packed) || !aligned16(w_scale) ||
@@ -363,8 +364,8 @@ static int64_t linear_quant_bytes(int64_t M, int64_t K, int32_t group_size) {
 int64_t cider_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t bits, int32_t group_size) {
   if (!gemm_sizes_ok(M, N) || !valid_gs(group_size) || (bits != 8 && bits != 4)) return -1;
   if (bits == 4 && group_size != 0) return -1;
-  if (!valid_k(K, bits == 4 ? 32 : 16, group_size)) return -1;
-  if (M == 0 || N == 0 || cider::linear_is_one_launch(M, K, group_size)) return 0;
+  if (!valid_k(K, bits == 4 ? 2 : 1, group_size)) return -1;
+  if (M == 0 || N == 0 || cider::linear_is_one_launch(M, K, group_size, bits == 4 ? cider::kWeightI4 : cider::kWeightI8)) return 0;
   return linear_quant_bytes(M, K, group_size) + cider_gemm_workspace_size(M, N, K, bits, group_size);
 }
 
@@ -423,8 +424,8 @@ cider_status_t cider_gemm_acc_i32(int32_t mode, const int8_t* x_q, const void* w
                                   int64_t K, int32_t group_size, int32_t* acc, void* stream) {
   if (mode != 0 && mode != 1) return CIDER_ERROR_INVALID_VALUE;
   if (!gemm_sizes_ok(M, N) || !valid_gs(group_size)) return CIDER_ERROR_INVALID_VALUE;
-  if (mode == 1 && (group_size != 0 || !valid_k(K, 32, 0))) return CIDER_ERROR_INVALID_VALUE;
-  if (mode == 0 && !valid_k(K, 16, group_size)) return CIDER_ERROR_INVALID_VALUE;
+  if (mode == 1 && (group_size != 0 || !valid_k(K, 2, 0))) return CIDER_ERROR_INVALID_VALUE;
+  if (mode == 0 && !valid_k(K, 1, group_size)) return CIDER_ERROR_INVALID_VALUE;
   if (M == 0 || N == 0) return CIDER_SUCCESS;
   if (!x_q || !w || !acc || !aligned16(x_q) || !aligned16(w) || !aligned16(acc)) return CIDER_ERROR_INVALID_VALUE;
   cider::GemmArgs g{x_q, nullptr, w, nullptr, M, N, K, group_size, nullptr, acc};

@@ -996,6 +996,168 @@ hipError_t launch_skinny(const GemmArgs& g, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
+// Ragged K, per-channel: int8 rows whose length is not a multiple of 16
+// codes, or packed int4 rows (K even) not a multiple of 32. A row then starts
+// at an arbitrary byte offset, so a lane's fragment bytes are assembled from
+// 4-byte-aligned dword loads and v_alignbyte (byte loads where the 4-byte
+// window would leave the tile's rows). Activation codes at k >= K are
+// zeroed, so whatever bytes the weight fragment holds there add nothing; rows
+// past M or N load as zero (the buffer range ends at the tile's last row). A
+// block of S waves owns one 16 x 16 output tile at a time (grid-stride over
+// the tiles), the waves take alternate 64-code units of K, and their exact
+// int32 sums are added through LDS in wave order before the store stage.
+// This is the general path for unaligned rows; aligned K keeps the tiled
+// kernels above.
+// ---------------------------------------------------------------------------
+
+// `nbytes` (8 or 16) bytes at byte offset `off` of a buffer whose range is
+// `total` bytes (4-aligned base), as 2 or 4 dwords; bytes past the range are 0.
+template <int NB>
+__device__ __forceinline__ v4i load_unaligned(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t total) {
+  constexpr int ND = NB / 4;
+  const uint32_t base = off & ~3u, sh = off & 3u;
+  uint32_t d[ND + 1];
+  if (base + 4 * (ND + 1) <= total) {
+#pragma unroll
+    for (int i = 0; i <= ND; ++i) d[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, base + 4 * i, 0, 0);
+  } else {
+    // the window would cross the end of the range: one byte at a time
+#pragma unroll
+    for (int i = 0; i <= ND; ++i) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const uint32_t o = base + 4 * i + b;
+        const uint32_t byte = o < total ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, o, 0, 0) : 0u;
+        v |= byte << (8 * b);
+      }
+      d[i] = v;
+    }
+  }
+  v4i out = zero4();
+#pragma unroll
+  for (int i = 0; i < ND; ++i) out[i] = (int)__builtin_amdgcn_alignbyte(d[i + 1], d[i], sh);
+  return out;
+}
+
+// Buffer over `rows` rows of `ld` bytes starting at row `r0` of `base`: the
+// descriptor starts at the 4-byte boundary at or below the first byte (the
+// base array is 16-byte aligned); `lead` is the first byte's offset in it.
+struct RowRange {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t lead, total;
+};
+
+__device__ __forceinline__ RowRange row_range(const void* base, int64_t r0, int rows, uint32_t ld) {
+  const int64_t first = r0 * (int64_t)ld;
+  const int64_t start = first & ~(int64_t)3;
+  RowRange rr;
+  rr.lead = (uint32_t)(first - start);
+  rr.total = rr.lead + (uint32_t)rows * ld;
+  rr.rsrc = make_rsrc(static_cast<const int8_t*>(base) + start, rr.total);
+  return rr;
+}
+
+template <int S, int WK, int EPI>
+__global__ void __launch_bounds__(S * 64)
+gemm_ragged_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, const void* __restrict__ Wv,
+                   const float* __restrict__ SW, int M, int N, int K, _Float16* __restrict__ Y,
+                   int32_t* __restrict__ ACC, int tiles_n, int64_t tiles) {
+  constexpr bool kI4 = WK == kWeightI4;
+  constexpr int kBatch = 4;                    // 64-code units in flight per wave
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, l4 = lane >> 4;
+  const uint32_t ldw = kI4 ? (uint32_t)K / 2 : (uint32_t)K;
+  const int KU = (K + 63) / 64;
+  __shared__ int red[S][4][64];
+  for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+    const int m0 = (int)(t / tiles_n) * 16, n0 = (int)(t % tiles_n) * 16;
+    const RowRange ra = row_range(X, m0, min(16, M - m0), (uint32_t)K);
+    const RowRange rw = row_range(Wv, n0, min(16, N - n0), ldw);
+    v4i acc = zero4();
+    for (int base = wave; base < KU; base += kBatch * S) {
+      v4i xf[kBatch], wf[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int u = base + i * S;
+        const int k = u * 64 + 16 * l4;           // first code of this lane's 16
+        xf[i] = zero4();
+        wf[i] = zero4();
+        if (u < KU && k < K) {
+          xf[i] = load_unaligned<16>(ra.rsrc, ra.lead + (uint32_t)l16 * (uint32_t)K + (uint32_t)k, ra.total);
+          if constexpr (kI4)
+            wf[i] = load_unaligned<8>(rw.rsrc, rw.lead + (uint32_t)l16 * ldw + (uint32_t)k / 2, rw.total);
+          else
+            wf[i] = load_unaligned<16>(rw.rsrc, rw.lead + (uint32_t)l16 * ldw + (uint32_t)k, rw.total);
+          // activation codes at k + j >= K (the next row's bytes) become 0
+          const int valid = K - k;
+          if (valid < 16) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              const int vb = min(max(valid - 4 * d, 0), 4);
+              const uint32_t mask = vb >= 4 ? 0xFFFFFFFFu : ((1u << (8 * vb)) - 1u);
+              xf[i][d] = (int)((uint32_t)xf[i][d] & mask);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (base + i * S >= KU) break;
+        v4i w = wf[i], x = xf[i];
+        if constexpr (kI4) {
+          w = unpack_int4(make_uint2((uint32_t)w.x, (uint32_t)w.y));
+          x = even_odd_bytes(x);
+        }
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(w, x, acc, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][r][lane] = acc[r];
+    __syncthreads();
+    if (wave == 0) {
+      const int m = m0 + l16, n = n0 + 4 * l4;
+      if (m < M) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (n + r >= N) break;
+          int v = red[0][r][lane];
+#pragma unroll
+          for (int w2 = 1; w2 < S; ++w2) v += red[w2][r][lane];
+          const int64_t o = (int64_t)m * N + n + r;
+          if constexpr (EPI == kEpiAccI32) ACC[o] = v;
+          else if constexpr (EPI == kEpiBF16) reinterpret_cast<__bf16*>(Y)[o] = dequant1_bf(v, SA[m], SW[n + r]);
+          else Y[o] = dequant1(v, SA[m], SW[n + r]);
+        }
+      }
+    }
+    __syncthreads();   // red is rewritten by the next tile
+  }
+}
+
+template <int WK, int EPI>
+hipError_t launch_ragged_t(const GemmArgs& g, hipStream_t st) {
+  const int64_t tn = (g.N + 15) / 16, tiles = ((g.M + 15) / 16) * tn;
+  const unsigned blocks = (unsigned)std::min<int64_t>(tiles, 8192);
+  gemm_ragged_kernel<4, WK, EPI><<<dim3(blocks), dim3(256), 0, st>>>(
+      g.a, g.sa, g.w, g.sw, (int)g.M, (int)g.N, (int)g.K, static_cast<_Float16*>(g.y), g.acc, (int)tn, tiles);
+  return hipGetLastError();
+}
+
+template <int WK>
+hipError_t launch_ragged_wk(const GemmArgs& g, Epilogue epi, hipStream_t st) {
+  switch (epi) {
+    case kEpiF16: return launch_ragged_t<WK, kEpiF16>(g, st);
+    case kEpiBF16: return launch_ragged_t<WK, kEpiBF16>(g, st);
+    case kEpiAccI32: return launch_ragged_t<WK, kEpiAccI32>(g, st);
+    default: return hipErrorInvalidValue;   // the other epilogues need aligned K
+  }
+}
+
+// K whose rows the tiled kernels cannot load (16-byte operand chunks).
+inline bool ragged_k(int64_t K, WeightKind wk) { return K % (wk == kWeightI4 ? 32 : 16) != 0; }
+
+// ---------------------------------------------------------------------------
 // Per-group variant of the direct-to-LDS pipeline (gs = 64 or 128 along K, for
 // both operands). Each 128-code stage also gathers its group scales into LDS
 // with 4-byte DMA loads (lane L fetches the scale of tile row 64p+L), so the
@@ -1498,6 +1660,7 @@ SplitPlan plan_split_pg(const GemmArgs& g) {
 
 SplitPlan plan_split(const GemmArgs& g, WeightKind wk) {
   SplitPlan plan;
+  if (ragged_k(g.K, wk)) return plan;
   if (g.group_size != 0) return wk == kWeightI8 ? plan_split_pg(g) : plan;
   if (g.M <= 16 || g.K < 4096) return plan;
   int64_t est_plain = 0;
@@ -1660,14 +1823,18 @@ int64_t gemm_split_workspace_bytes(int64_t M, int64_t N, int64_t K, WeightKind w
   return p.splits ? split_ws_bytes(M, N, p.splits) : 0;
 }
 
-bool linear_is_one_launch(int64_t M, int64_t K, int group_size) {
+bool linear_is_one_launch(int64_t M, int64_t K, int group_size, WeightKind wk) {
   GemmArgs g{};
   g.M = M;
   g.K = K;
-  return group_size == 0 && M >= 1 && M <= 2 && gemv_fits(g);
+  return group_size == 0 && M >= 1 && M <= 2 && !ragged_k(K, wk) && gemv_fits(g);
 }
 
 hipError_t launch_gemm(const GemmArgs& g, WeightKind wk, Epilogue epi, hipStream_t st) {
+  // Unaligned rows (per-channel only; the entry points keep every other
+  // kind at aligned K) take the general kernel.
+  if (ragged_k(g.K, wk))
+    return wk == kWeightI4 ? launch_ragged_wk<kWeightI4>(g, epi, st) : launch_ragged_wk<kWeightI8>(g, epi, st);
   // Tile table by M (the README's tile section also switches configs by M).
   if (epi == kEpiF16Tok) return launch_tok<kEpiF16Tok>(g, st);
   if (epi == kEpiBF16Tok) return launch_tok<kEpiBF16Tok>(g, st);

@@ -65,11 +65,11 @@ struct GemmArgs {
 
 hipError_t launch_gemm(const GemmArgs& args, WeightKind wk, Epilogue epi, hipStream_t stream);
 
-// True when the one-launch linear applies: per-channel, M <= 2 and the
-// activation codes fit the GEMV kernel's LDS staging. (From M = 3 on, the
-// activation quantization that every block repeats costs more than the
-// separate quantization launch it saves.)
-bool linear_is_one_launch(int64_t M, int64_t K, int group_size);
+// True when the one-launch linear applies: per-channel, M <= 2, K a multiple
+// of 16 (32 for int4 weights) and the activation codes fit the GEMV kernel's
+// LDS staging. (From M = 3 on, the activation quantization that every block
+// repeats costs more than the separate quantization launch it saves.)
+bool linear_is_one_launch(int64_t M, int64_t K, int group_size, WeightKind wk);
 
 // Workspace bytes the GEMM dispatch uses for split-K at this shape (0: none).
 int64_t gemm_split_workspace_bytes(int64_t M, int64_t N, int64_t K, WeightKind wk, int group_size);

@@ -150,6 +150,53 @@ __global__ __launch_bounds__(256) void quant_rows_two_pass(const uint4* __restri
   }
 }
 
+// Rows whose length is not a multiple of 8 elements (per-row scale, any
+// K >= 1; even K for int4): a row then starts only 2-byte aligned, so its
+// elements are loaded one at a time. One wave per row: the max pass, then
+// 8-element chunks (padded with zeros past K, which give code 0 and are not
+// stored) through the same element rule, stored byte by byte.
+template <bool BF>
+__global__ __launch_bounds__(64 * kWaves) void quant_rows_ragged(const uint16_t* __restrict__ x, int64_t R,
+                                                                  int64_t K, float qmax, bool pack4,
+                                                                  void* __restrict__ q, float* __restrict__ s) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * kWaves + wave;
+  if (row >= R) return;
+  const uint16_t* xr = x + row * K;
+  uint32_t a = 0;
+  for (int64_t k = lane; k < K; k += 64) a = max(a, (uint32_t)(xr[k] & 0x7FFFu));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) a = max(a, (uint32_t)__shfl_xor((int)a, off));
+  const float sc = elem_to_float<BF>(a) / qmax;
+  if (lane == 0) s[row] = sc;
+  const float inv = 1.0f / sc;
+  const int64_t C = (K + 7) / 8;
+  for (int64_t c = lane; c < C; c += 64) {
+    uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (8 * c + j < K) w[j >> 1] |= (uint32_t)xr[8 * c + j] << (16 * (j & 1));
+    const uint2 cq =
+        sc != 0.0f ? code_bytes_of_chunk<BF, false>(make_uint4(w[0], w[1], w[2], w[3]), sc, inv, qmax) : make_uint2(0, 0);
+    if (!pack4) {
+      int8_t* dst = static_cast<int8_t*>(q) + row * K + 8 * c;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (8 * c + j < K) dst[j] = (int8_t)(((j < 4 ? cq.x : cq.y) >> (8 * (j & 3))) & 0xFFu);
+    } else {
+      // byte b of the chunk holds codes 2b (low nibble) and 2b + 1, each + 8
+      uint8_t* dst = static_cast<uint8_t*>(q) + row * (K / 2) + 4 * c;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if (8 * c + 2 * b >= K) break;
+        const uint32_t word = b < 2 ? cq.x : cq.y;
+        const uint32_t lo = (word >> (16 * (b & 1))) & 0xFu, hi = (word >> (16 * (b & 1) + 8)) & 0xFu;
+        dst[b] = (uint8_t)((lo ^ 0x8u) | ((hi ^ 0x8u) << 4));
+      }
+    }
+  }
+}
+
 // Percentile-clipped scales (the README's notes section names a percentile
 // rule, clip_percentile=99.9, beside the default min-max): one workgroup per
 // group (a row, or gs elements of it). The clip threshold is the percentile of
@@ -272,6 +319,11 @@ hipError_t launch_quant_t(const void* x, int64_t R, int64_t K, int group_size, i
   const uint4* xv = static_cast<const uint4*>(x);
   const bool pack4 = qmax == 7;
   const float fq = (float)qmax;
+  if (K % 8 != 0) {   // per-row scales only (group sizes divide K)
+    const dim3 grid((unsigned)((R + kWaves - 1) / kWaves)), block(64 * kWaves);
+    quant_rows_ragged<BF><<<grid, block, 0, stream>>>(static_cast<const uint16_t*>(x), R, K, fq, pack4, q, s);
+    return hipGetLastError();
+  }
   const int64_t C = K / 8;
   if (group_size == 0 && C > kSegChunks) {
     quant_rows_two_pass<BF><<<dim3((unsigned)R), dim3(256), 0, stream>>>(xv, K, fq, pack4, q, s);
