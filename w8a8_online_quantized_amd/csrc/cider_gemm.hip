@@ -760,44 +760,51 @@ gemm_skinny_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, c
 
 // ---------------------------------------------------------------------------
 // GEMV path, M <= 4, per-channel and W4A8: a pure weight stream. A block owns
-// 8 weight rows; each wave instruction loads 8 rows x 128 contiguous bytes
-// (full cache lines), lane L taking 16 bytes of row L / 8. The block's four
-// waves take alternate 128-byte steps along each row. The M activation rows
-// are staged once in LDS (for W4A8 already in the even/odd code order the
-// unpacked nibbles come in), and v_dot4_i32_i8 accumulates exact int32 sums,
-// reduced across the 8 lanes of a row and then across the waves in order.
+// RI weight rows (RI = 8, 4 or 2: chosen so that the grid covers the 256 CUs
+// evenly); each wave instruction loads RI rows x (1024 / RI) contiguous bytes
+// (whole cache lines), lane L taking 16 bytes of row L / (64 / RI). The
+// block's four waves take alternate steps along each row. The M activation
+// rows are staged once in LDS (for W4A8 already in the even/odd code order
+// the unpacked nibbles come in), and v_dot4_i32_i8 accumulates exact int32
+// sums, reduced across the lanes of a row and then across the waves in order.
 // ---------------------------------------------------------------------------
-template <int MT, int WK, int EPI>
+template <int MT, int WK, int EPI, int RI>
 __global__ void __launch_bounds__(256)
 gemm_gemv_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, const void* __restrict__ Wv,
                  const float* __restrict__ SW, int M, int N, int K, _Float16* __restrict__ Y,
                  int32_t* __restrict__ ACC) {
   constexpr bool kI4 = WK == kWeightI4;
-  constexpr int kCodes = kI4 ? 256 : 128;     // codes per 128-byte weight step
-  constexpr int kBatch = 8;                   // steps in flight per wave
+  constexpr int kLanesPerRow = 64 / RI;
+  constexpr int kStepBytes = 16 * kLanesPerRow;        // weight bytes per row per wave instruction
+  constexpr int kCodes = kI4 ? 2 * kStepBytes : kStepBytes;   // codes per step
+  constexpr int kBatch = RI == 8 ? 8 : 4;              // steps in flight per wave
+  static_assert(RI == 8 || RI == 4 || RI == 2, "rows per instruction");
   extern __shared__ __attribute__((aligned(16))) int8_t xs[];   // [MT][Kpad]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int Kpad = (K + kCodes - 1) / kCodes * kCodes;
 
-  // block b owns row groups b, b + gridDim.x, ... of 8 weight rows (one per
+  // block b owns row groups b, b + gridDim.x, ... of RI weight rows (one per
   // block except in the self-quantizing mode, whose grid is capped)
-  int n0 = blockIdx.x * 8;
-  const int row = lane >> 3, sub = lane & 7;
-  int rows_w = min(8, N - n0);
+  int n0 = blockIdx.x * RI;
+  const int row = lane / kLanesPerRow, sub = lane % kLanesPerRow;
+  int rows_w = min(RI, N - n0);
   const uint32_t ldw = kI4 ? (uint32_t)K / 2 : (uint32_t)K;
   __amdgpu_buffer_rsrc_t rw =
       make_rsrc(static_cast<const int8_t*>(Wv) + (int64_t)n0 * ldw, (uint32_t)rows_w * ldw);
   const int steps = Kpad / kCodes;
+  constexpr bool kLin = EPI == kEpiF16Linear || EPI == kEpiBF16Linear;
+  constexpr bool kLinBF = EPI == kEpiBF16Linear;
   int acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = 0;
 
-  // a batch = this wave's next kBatch 128-byte steps (steps base, base+4, ...)
+  // a batch = this wave's next kBatch steps (steps base, base+4, ...); steps
+  // past the row load zeros, so every batch is kBatch loads (fixed wait counts)
   auto load_batch = [&](v4i (&wv)[kBatch], int base) {
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int st = base + 4 * i;
-      const uint32_t kb = (uint32_t)st * 128 + 16 * sub;        // byte offset within the row
+      const uint32_t kb = (uint32_t)st * kStepBytes + 16 * sub;   // byte offset within the row
       const bool in = st < steps && kb < ldw;
       wv[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, in ? (uint32_t)row * ldw + kb : 0x80000000u, 0, 0);
     }
@@ -808,14 +815,18 @@ gemm_gemv_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, con
       const int st = base + 4 * i;
       if (st >= steps) break;
       if constexpr (kI4) {
-        // 16 packed bytes = codes st*256 + 32*sub .. +31, in 2 x 16 unpacked bytes
+        // 16 packed bytes = codes st*kCodes + 32*sub .. +31, in 2 x 16 unpacked bytes
         const v4i lo = unpack_int4(make_uint2((uint32_t)wv[i].x, (uint32_t)wv[i].y));
         const v4i hi = unpack_int4(make_uint2((uint32_t)wv[i].z, (uint32_t)wv[i].w));
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          const int8_t* xp = xs + m * Kpad + st * 256 + 32 * sub;
-          const v4i x0 = *reinterpret_cast<const v4i*>(xp);
-          const v4i x1 = *reinterpret_cast<const v4i*>(xp + 16);
+          const int8_t* xp = xs + m * Kpad + st * kCodes + 32 * sub;
+          v4i x0 = *reinterpret_cast<const v4i*>(xp);
+          v4i x1 = *reinterpret_cast<const v4i*>(xp + 16);
+          if constexpr (!kLin) {   // staged by DMA in natural order
+            x0 = even_odd_bytes(x0);
+            x1 = even_odd_bytes(x1);
+          }
           int a = acc[m];
           a = __builtin_amdgcn_sdot4(lo.x, x0.x, a, false);
           a = __builtin_amdgcn_sdot4(lo.y, x0.y, a, false);
@@ -830,7 +841,7 @@ gemm_gemv_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, con
       } else {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          const v4i x = *reinterpret_cast<const v4i*>(xs + m * Kpad + st * 128 + 16 * sub);
+          const v4i x = *reinterpret_cast<const v4i*>(xs + m * Kpad + st * kCodes + 16 * sub);
           int a = acc[m];
           a = __builtin_amdgcn_sdot4(wv[i].x, x.x, a, false);
           a = __builtin_amdgcn_sdot4(wv[i].y, x.y, a, false);
@@ -842,17 +853,35 @@ gemm_gemv_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, con
     }
   };
 
-  // the first weight batch goes out before x is staged, so the weight stream
-  // and the x loads overlap; later batches load one batch ahead
+  // Activation codes (not self-quantizing): DMA'd straight into LDS before
+  // any weight load, so waiting for them (vmcnt counts in issue order) does
+  // not wait for the weight stream. Every wave issues the same number of
+  // 1 KiB DMA instructions; chunks past the rows or past K load zeros, and
+  // the LDS area is padded to whole 4 KiB rounds of the block.
   v4i wa[kBatch], wb[kBatch];
-  load_batch(wa, wave);
+  if constexpr (!kLin) {
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (uint32_t)M * (uint32_t)K);
+    const int chunks = MT * Kpad / 16, rounds = (chunks + 255) / 256;
+    for (int j = 0; j < rounds; ++j) {
+      const int i = j * 256 + wave * 64 + lane;
+      const int m = i / (Kpad / 16), c = i % (Kpad / 16);
+      const uint32_t off = (i < chunks && m < M && c * 16 < K) ? (uint32_t)m * (uint32_t)K + (uint32_t)c * 16
+                                                                : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(xs + (j * 256 + wave * 64) * 16), 16, off, 0, 0, 0);
+    }
+    load_batch(wa, wave);
+    wait_vmcnt<kBatch>();      // this wave's activation DMA landed (the weight batch may still fly)
+    __syncthreads();           // everyone's
+  } else {
+    // the first weight batch goes out before x is quantized and staged, so
+    // the weight stream and the x loads overlap
+    load_batch(wa, wave);
+  }
 
   // kEpiF16Linear / kEpiBF16Linear: X holds fp16 / bf16 rows; each row's
   // scale s = max|x| / 127 is formed here (block-wide max) and the codes
   // follow the quantizer's rule
   __shared__ float srow[MT];
-  constexpr bool kLin = EPI == kEpiF16Linear || EPI == kEpiBF16Linear;
-  constexpr bool kLinBF = EPI == kEpiBF16Linear;
   if constexpr (kLin) {
     const uint4* xh = reinterpret_cast<const uint4*>(X);
     const int C = K / 8;
@@ -875,11 +904,12 @@ gemm_gemv_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, con
     __syncthreads();
   }
 
-  // stage x (rows >= M and codes >= K as zero)
+  // self-quantizing modes: stage the codes of x (rows >= M and codes >= K as zero)
+  if constexpr (kLin) {
   for (int i = threadIdx.x; i < MT * Kpad / 16; i += 256) {
     const int m = i / (Kpad / 16), c = i % (Kpad / 16);
     v4i v = zero4();
-    if constexpr (kLin) {
+    {
       const float sc = m < MT ? srow[m] : 0.0f;
       if (m < M && c * 16 < K && sc != 0.0f) {
         const uint4* xp = reinterpret_cast<const uint4*>(X) + ((int64_t)m * K + c * 16) / 8;
@@ -892,21 +922,20 @@ gemm_gemv_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, con
         v[2] = (int)q1.x;
         v[3] = (int)q1.y;
       }
-    } else {
-      if (m < M && c * 16 < K) v = *reinterpret_cast<const v4i*>(X + (int64_t)m * K + c * 16);
     }
     if constexpr (kI4) v = even_odd_bytes(v);
     *reinterpret_cast<v4i*>(xs + m * Kpad + c * 16) = v;
   }
   __syncthreads();
+  }
 
   constexpr int kStride = 4 * kBatch;          // steps between a wave's batches
-  __shared__ int red[4][8][MT];
-  const int nrg = (N + 7) / 8;
+  __shared__ int red[4][RI][MT];
+  const int nrg = (N + RI - 1) / RI;
   for (int rg = blockIdx.x; rg < nrg; rg += gridDim.x) {
     if (rg != (int)blockIdx.x) {
-      n0 = rg * 8;
-      rows_w = min(8, N - n0);
+      n0 = rg * RI;
+      rows_w = min(RI, N - n0);
       rw = make_rsrc(static_cast<const int8_t*>(Wv) + (int64_t)n0 * ldw, (uint32_t)rows_w * ldw);
 #pragma unroll
       for (int m = 0; m < MT; ++m) acc[m] = 0;
@@ -919,17 +948,17 @@ gemm_gemv_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, con
       if (base + 2 * kStride < steps) load_batch(wa, base + 2 * kStride);
       process(wb, base + kStride);
     }
-    // sum the 8 lanes of each row (integer: order does not matter)
+    // sum the lanes of each row (integer: order does not matter)
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int off = 1; off < 8; off <<= 1) acc[m] += __shfl_xor(acc[m], off);
+      for (int off = 1; off < kLanesPerRow; off <<= 1) acc[m] += __shfl_xor(acc[m], off);
     if (sub == 0) {
 #pragma unroll
       for (int m = 0; m < MT; ++m) red[wave][row][m] = acc[m];
     }
     __syncthreads();
-    if (threadIdx.x < 8 * MT) {
+    if (threadIdx.x < RI * MT) {
       const int r = threadIdx.x / MT, m = threadIdx.x % MT;
       const int n = n0 + r;
       if (m < M && n < N) {
@@ -949,25 +978,53 @@ gemm_gemv_kernel(const int8_t* __restrict__ X, const float* __restrict__ SA, con
 
 constexpr int64_t kLinearBlocks = 512;   // two per CU
 
-template <int MT, int WK, int EPI>
-hipError_t launch_gemv_m(const GemmArgs& g, hipStream_t st) {
-  constexpr int kCodes = WK == kWeightI4 ? 256 : 128;
+// Rows per block: 8 while that gives >= 1024 blocks (four per CU), else 4,
+// else 2 (at least 4 for 4 activation rows, whose dot products make a block's
+// work per byte higher), so that small N still spreads over the CUs. Same-box
+// A/B against 8 rows everywhere (HIP events, rotating buffers): M=1 N=2560
+// K=10240 9.06 -> 7.39 us (2 rows: 1280 blocks instead of 320, which ran as
+// two rounds on a quarter of the CUs), W4A8 7.66 -> 5.62 us, M=4 N=2560
+// K=10240 13.1 -> 9.3 us (4 rows). The self-quantizing mode keeps 8 (its
+// grid is capped anyway).
+inline int gemv_rows(int64_t N, int64_t M, bool self_quant) {
+  if (self_quant || (N + 7) / 8 >= 1024) return 8;
+  return ((N + 3) / 4 >= 1024 || M > 2) ? 4 : 2;
+}
+
+template <int MT, int WK, int EPI, int RI>
+hipError_t launch_gemv_ri(const GemmArgs& g, hipStream_t st) {
+  constexpr int kCodes = (WK == kWeightI4 ? 2 : 1) * 16 * (64 / RI);
   const int64_t kpad = (g.K + kCodes - 1) / kCodes * kCodes;
-  const size_t lds = (size_t)MT * kpad;
+  const size_t lds = ((size_t)MT * kpad + 4095) / 4096 * 4096;   // whole DMA rounds of the block
   // the self-quantizing mode repeats the activation quantization in every
   // block, so its grid is capped (each block then loops over row groups)
-  const int64_t nrg = (g.N + 7) / 8;
+  const int64_t nrg = (g.N + RI - 1) / RI;
   constexpr bool kLin = EPI == kEpiF16Linear || EPI == kEpiBF16Linear;
   const dim3 grid((unsigned)(kLin ? std::min<int64_t>(nrg, kLinearBlocks) : nrg)), block(256);
-  gemm_gemv_kernel<MT, WK, EPI><<<grid, block, lds, st>>>(g.a, g.sa, g.w, g.sw, (int)g.M, (int)g.N, (int)g.K,
-                                                         static_cast<_Float16*>(g.y), g.acc);
+  gemm_gemv_kernel<MT, WK, EPI, RI><<<grid, block, lds, st>>>(g.a, g.sa, g.w, g.sw, (int)g.M, (int)g.N, (int)g.K,
+                                                             static_cast<_Float16*>(g.y), g.acc);
   return hipGetLastError();
 }
 
-// M <= 4 with the staged activations fitting in LDS (<= 64 KiB).
+template <int MT, int WK, int EPI>
+hipError_t launch_gemv_m(const GemmArgs& g, hipStream_t st) {
+  constexpr bool kLin = EPI == kEpiF16Linear || EPI == kEpiBF16Linear;
+  if constexpr (kLin) {
+    return launch_gemv_ri<MT, WK, EPI, 8>(g, st);
+  } else {
+    switch (gemv_rows(g.N, g.M, false)) {
+      case 8: return launch_gemv_ri<MT, WK, EPI, 8>(g, st);
+      case 4: return launch_gemv_ri<MT, WK, EPI, 4>(g, st);
+      default: return launch_gemv_ri<MT, WK, EPI, 2>(g, st);
+    }
+  }
+}
+
+// M <= 4 with the staged activations fitting in LDS (<= 64 KiB; the padding
+// of the widest step, 1024 codes for int4 with 2 rows per block, bounds Kpad).
 inline bool gemv_fits(const GemmArgs& g) {
   const int64_t mt = g.M <= 1 ? 1 : (g.M <= 2 ? 2 : 4);
-  return g.M <= 4 && mt * ((g.K + 255) / 256 * 256) <= 65536;
+  return g.M <= 4 && mt * ((g.K + 1023) / 1024 * 1024) <= 65536;
 }
 
 template <int WK, int EPI>
