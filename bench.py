@@ -347,6 +347,34 @@ def measure_mv(cider, torch, x_h, w_h, M, N, K, gs, steps, warmup, R, ops, nbyte
             "quant_bytes": 0, "sets": R}
 
 
+def measure_read_ceiling(cider, torch, nbytes=10240 * 2560, steps=200, min_set_bytes=512 * 2 ** 20):
+    """The single-launch HBM read ceiling for an `nbytes` stream: cider_read_probe
+    (one cold pass over a buffer, 16-byte loads, contiguous per workgroup)
+    back to back over rotating buffers (>= 512 MB, so no pass finds its data
+    in the 256 MB last-level cache), events around the loop."""
+    dev = torch.device("cuda:0")
+    R = max(2, -(-min_set_bytes // nbytes))
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(R)]
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    for i in range(3 * R):
+        cider.cider_read_probe(bufs[i % R], sink, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        cider.cider_read_probe(bufs[i % R], sink, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del bufs
+    torch.cuda.empty_cache()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"bytes": nbytes, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+            "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4), "kernel": "cider_read_probe",
+            "note": "one launch per cold pass, back to back over rotating buffers"}
+
+
 def roofline_of(ops, nbytes, ms):
     """Bound by the roof the algorithmic work hits first at peak rates."""
     t_mfma = ops / (PEAK_INT8_TOPS * 1e12)
@@ -430,6 +458,23 @@ def sweep_indices(spec):
     return out
 
 
+VALU_LANE_OPS_PER_S = 256 * 64 * 2.4e9   # non-packed fp32 VALU: 64 lane-ops per clock per CU
+
+
+def pg_coroof(mode, M, N, K, gs, ops, us):
+    """Per-group's second roof: the fp32 fold after every group is VALU work
+    the matrix cores do not do: cvt + mul + fma per output element and group
+    (both scales per group), cvt + fma with per-token activation scales. The
+    co-roof is max(MFMA time, fold VALU time) at peak rates."""
+    G = K // gs
+    fold = (3 if mode == "w8a8_pg" else 2) * M * N * G
+    t_valu = fold / VALU_LANE_OPS_PER_S * 1e6
+    t_mfma = ops / (PEAK_INT8_TOPS * 1e12) * 1e6
+    co = max(t_valu, t_mfma)
+    return {"fold_lane_ops": fold, "t_valu_us": round(t_valu, 2), "t_mfma_us": round(t_mfma, 2),
+            "co_roof_us": round(co, 2), "frac_of_co_roof": round(co / us, 4)}
+
+
 def run_sweep(cider, torch, inputs, indices, steps):
     """Times the selected sweep configurations, each with its own roofline."""
     rows = []
@@ -442,6 +487,8 @@ def run_sweep(cider, torch, inputs, indices, steps):
                      "quant_GBs": round(rr["quant_bytes"] / (rr["quant_ms"] * 1e-3) / 1e9, 1) if rr["quant_ms"] else None,
                      "linear_TOPs": round(rr["ops"] / (rr["ms_per_step"] * 1e-3) / 1e12, 2),
                      "split_k": bool(rr.get("split_k_ws"))})
+        if mode in ("w8a8_pg", "w8a8_tokpg"):
+            rows[-1]["valu_co_roof"] = pg_coroof(mode, m, n, k, gs, rr["ops"], rr["gemm_ms"] * 1e3)
         print(json.dumps({"sweep_row": rows[-1]}), file=sys.stderr, flush=True)
     return rows
 
@@ -471,6 +518,9 @@ def main():
                     help="also run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--sweep-rows", default="",
                     help="with --sweep / --sweep-only: indices of the sweep rows to run, e.g. 3 or 0-4,9")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="also measure the single-launch HBM read ceiling of a 26.2 MB stream "
+                         "(the M=1 weight stream), also done with --sweep")
     ap.add_argument("--sweep-only", action="store_true",
                     help="run only the sweep rows (no headline step, no CPU baseline): one JSON line "
                          "with the rows, for per-configuration profiler runs")
@@ -490,7 +540,10 @@ def main():
 
     if args.sweep_only:
         rows = run_sweep(cider, torch, inputs, sweep_indices(args.sweep_rows), args.steps)
-        print(json.dumps({"sweep": rows, "kernel_source_sha": kernel_source_sha()}), flush=True)
+        res = {"sweep": rows, "kernel_source_sha": kernel_source_sha()}
+        if args.read_ceiling:
+            res["read_ceiling"] = measure_read_ceiling(cider, torch)
+        print(json.dumps(res), flush=True)
         return
 
     M, N, K = 4096, 10240, 2560
@@ -559,6 +612,8 @@ def main():
     }
     if args.sweep:
         out["sweep"] = run_sweep(cider, torch, inputs, sweep_indices(args.sweep_rows), args.steps)
+    if args.sweep or args.read_ceiling:
+        out["read_ceiling"] = measure_read_ceiling(cider, torch)
     if args.stack:
         out["stack"] = measure_stack(cider, torch, inputs, max(3, args.steps // 10), 3)
     if not args.no_cpu_baseline:

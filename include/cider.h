@@ -330,6 +330,15 @@ cider_status_t cider_gemm_acc_i32(int32_t mode, const int8_t* x_q, const void* w
                                   int64_t N, int64_t K, int32_t group_size, int32_t* acc,
                                   void* stream);
 
+/* Measurement helper (not part of the method): reads `bytes` (a multiple of
+ * 16) of the device buffer `buf` once, in one launch, the way a pure weight
+ * stream would (16-byte loads, contiguous per workgroup). Its duration on a
+ * buffer that is not cache resident is the single-launch HBM read ceiling
+ * the bandwidth-bound small-M kernels are held against. `sink` (device,
+ * 16-byte aligned, 4 bytes) is written only for an impossible data pattern.
+ * Errors as for the other calls. */
+cider_status_t cider_read_probe(const void* buf, int64_t bytes, int32_t* sink, void* stream);
+
 /* ---- Linear-stack driver ----------------------------------------------------
  * The prefill linear layers of a decoder stack shaped like the Qwen3-VL-2B
  * model of the README's end-to-end VLM section, chained so that each layer's

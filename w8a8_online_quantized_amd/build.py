@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libcider.so")
-SOURCES = ["cider_api.hip", "cider_quant.hip", "cider_gemm.hip", "cider_mv.hip"]
+SOURCES = ["cider_api.hip", "cider_quant.hip", "cider_gemm.hip", "cider_mv.hip", "cider_probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -62,6 +62,7 @@ SIGNATURES = {
     "cider_quant_weight_dt": (ctypes.c_int, [_c_p, _c_i32, _c_i64, _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_p]),
     "cider_w8a8_gemm_dt": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_i32, _c_p]),
     "cider_w4a8_gemm_dt": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_i32, _c_p]),
+    "cider_read_probe": (ctypes.c_int, [_c_p, _c_i64, _c_p, _c_p]),
     "cider_int8_mv": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p]),
     "cider_stack_workspace_layout": (ctypes.c_int64, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                                       ctypes.POINTER(ctypes.c_int64)]),
@@ -415,6 +416,17 @@ def cider_int8_mv(x, w_q, w_scale, group_size: int = 0, y=None, stream=None):
     _check("cider_int8_mv", lib().cider_int8_mv(_ptr(x), _ptr(w_q), _ptr(w_scale), M, N, K, group_size,
                                                 _ptr(y), _stream(stream)))
     return y
+
+
+def cider_read_probe(buf, sink, stream=None):
+    """One pass over a device buffer (measurement helper: the single-launch
+    read ceiling); `sink` is a small int32 device tensor."""
+    import torch
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    _need(sink, torch.int32, tuple(sink.shape), "sink")
+    _check("cider_read_probe", lib().cider_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                                      _stream(stream)))
 
 
 @_on_stream

@@ -420,6 +420,14 @@ cider_status_t cider_int8_mv(const void* x_f16, const int8_t* w_q, const float* 
   return from_hip(cider::launch_mv(a, static_cast<hipStream_t>(stream)));
 }
 
+cider_status_t cider_read_probe(const void* buf, int64_t bytes, int32_t* sink, void* stream) {
+  if (bytes < 0 || bytes % 16) return CIDER_ERROR_INVALID_VALUE;
+  if (bytes == 0) return CIDER_SUCCESS;
+  if (!buf || !sink || !aligned16(buf) || !aligned16(sink)) return CIDER_ERROR_INVALID_VALUE;
+  if (!device_is_gfx950()) return CIDER_ERROR_NOT_SUPPORTED;
+  return from_hip(cider::launch_read_probe(buf, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
 cider_status_t cider_gemm_acc_i32(int32_t mode, const int8_t* x_q, const void* w, int64_t M, int64_t N,
                                   int64_t K, int32_t group_size, int32_t* acc, void* stream) {
   if (mode != 0 && mode != 1) return CIDER_ERROR_INVALID_VALUE;

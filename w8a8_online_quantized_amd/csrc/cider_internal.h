@@ -86,4 +86,8 @@ struct MvArgs {
 // Decode matrix-vector product (no activation quantization).
 hipError_t launch_mv(const MvArgs& args, hipStream_t stream);
 
+// One pass over bytes (a multiple of 16) of buf; sink receives nothing
+// (written only for an impossible data pattern).
+hipError_t launch_read_probe(const void* buf, int64_t bytes, int32_t* sink, hipStream_t stream);
+
 }  // namespace cider
