@@ -1221,13 +1221,12 @@ inline bool ragged_k(int64_t K, WeightKind wk) { return K % (wk == kWeightI4 ? 3
 // scales arrive with the codes under the same vmcnt wait; they go to a ring of
 // NS+1 scale slots, one deeper than the code stages, so a stage's scales stay
 // valid while the next stage runs.
-// Each 16x16 tile's int32 sum of group g is folded into the fp32 sum,
-// fp32(acc) * s_a[m,g] * s_w[n,g], between its last MFMA of group g and its
-// first MFMA of group g+1 (which starts from a zero accumulator): half the
-// tiles in group g's last 64-code step, half in group g+1's first, each fold
-// next to an independent MFMA, so the SIMD overlaps the fold's VALU work with
-// the matrix cores evenly over both steps. (Group -1 is a zero accumulator
-// with zero scales.)
+// Group g's first MFMA step visits each 16x16 tile once: it folds the tile's
+// int32 sum of group g-1 into the fp32 sum, fp32(acc) * s_a[m,g-1] *
+// s_w[n,g-1], and then starts the tile's group-g sum with a zero-accumulator
+// MFMA. The fold's VALU work thus sits between independent MFMAs, which the
+// SIMD overlaps with the matrix cores, instead of waiting for a group's MFMAs
+// to drain. (Group -1 is a zero accumulator with zero scales.)
 // With per-token activation scales (kEpiF16Tok) only the s_w segments are
 // gathered, the fold is fp32(acc) * s_w[n,g-1] added with one fma, and s_a[m]
 // multiplies the finished fp32 sum in the store stage.
@@ -1243,13 +1242,6 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
   constexpr int TM = WTM / 16, TN = WTN / 16;
   constexpr int GPS = BK / GS;                           // groups per stage
   constexpr int KPG = GS / 64;                           // 64-code MFMA steps per group
-  // Fold schedule: a 16x16 tile's finished group sum may be folded any time
-  // between its last MFMA of the group and its first MFMA of the next group.
-  // Tiles 0 .. kT-kH-1 fold during the group's last step, kH MFMAs after their
-  // own, and tiles kT-kH .. kT-1 during the next group's first step, before
-  // their own; so both steps carry the same share of the fold's VALU work,
-  // next to independent MFMAs, instead of all of it in the first step.
-  constexpr int kT = (BM / WGM / 16) * (BN / WGN / 16), kH = kT / 2;
   constexpr int kCodeBytes = (BM + BN) * RB;
   constexpr bool kF16 = EPI != kEpiAccI32;
   constexpr bool kTok = EPI == kEpiF16Tok || EPI == kEpiBF16Tok;
@@ -1403,7 +1395,6 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
       if (gi > 0) __builtin_amdgcn_sched_barrier(0);
       const int g = (kt0 + kt) * GPS + gi;
       const float* psc = gi == 0 ? prev + (GPS - 1) * kSeg : cur + (gi - 1) * kSeg;
-      const float* csc = cur + gi * kSeg;
 #pragma unroll
       for (int s = 0; s < KPG; ++s) {
         const int ks = gi * KPG + s;
@@ -1415,28 +1406,26 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
         for (int b = 0; b < TM; ++b)
           af[b] = *reinterpret_cast<const v4i*>(sa_ + tile_off<RB>(wm + 16 * b + l16, 4 * ks + l4));
 #pragma unroll
-        for (int t = 0; t < kT; ++t) {
+        for (int t = 0; t < TN * TM; ++t) {
           const int a = t / TM, b = t % TM;
-          // first step of a group: fold tile t + (kT - kH) of the previous
-          // group (its sum was finished kT - kH MFMAs ago and its first MFMA
-          // of this group comes later in this step)
-          if (s == 0 && t < kH) fold_tile((t + kT - kH) / TM, (t + kT - kH) % TM, psc, g - 1);
-          if (s == 0) acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[a], af[b], zero4(), 0, 0, 0);
-          else acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[a], af[b], acc[a][b], 0, 0, 0);
-          // last step of a group: fold tile t - kH of this group, whose last
-          // MFMA was issued kH MFMAs ago
-          if (s == KPG - 1 && t >= kH) fold_tile((t - kH) / TM, (t - kH) % TM, csc, g);
+          if (s == 0) {
+            fold_tile(a, b, psc, g - 1);
+            acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[a], af[b], zero4(), 0, 0, 0);
+          } else {
+            acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[a], af[b], acc[a][b], 0, 0, 0);
+          }
         }
       }
     }
   }
-  // the last group's tiles kT - kH .. kT - 1 (its slot was not overwritten:
-  // later zero-fill stages used other slots)
+  // the last group (its slot was not overwritten: later zero-fill stages used other slots)
   if (KT > 0) {
     const int g = (kt0 + KT) * GPS - 1;
     const float* lsc = ring + ((KT - 1) % NSR) * kSlotFloats + (GPS - 1) * kSeg;
 #pragma unroll
-    for (int t = kT - kH; t < kT; ++t) fold_tile(t / TM, t % TM, lsc, g);
+    for (int a = 0; a < TN; ++a)
+#pragma unroll
+      for (int b = 0; b < TM; ++b) fold_tile(a, b, lsc, g);
   }
   wait_vmcnt<0>();
   if constexpr (SPLIT) {
