@@ -9,13 +9,15 @@
 // with per-channel (one s_w per row) or per-group (gs 64 / 128) scales.
 //
 // The weight stream is the whole cost (N*K bytes), so the kernel is shaped for
-// HBM: a block owns 8 weight rows; a wave instruction loads 8 rows x 128
-// contiguous bytes (lane L: 16 bytes of row L / 8); the block's waves (4, or 8
-// for small N) take alternate 128-byte steps of each row, a batch of steps in flight at a time,
-// the next batch loading while the current one is consumed. The activations
-// are staged once per block in LDS (when M * K * 2 bytes fit in 64 KiB), with
-// the first weight batch already in flight; otherwise each lane reads its
-// activation chunks through the caches next to each weight chunk.
+// HBM: a block owns RI = 8, 4 or 2 weight rows (chosen so that the grid
+// covers the 256 CUs evenly); a wave instruction loads RI rows x (1024 / RI)
+// contiguous bytes (lane L: 16 bytes of row L / (64 / RI)); the block's four
+// waves take alternate steps of each row, a batch of steps in flight at a
+// time, the next batch loading while the current one is consumed. The
+// activations (and per-group, the block's scales) are DMA'd into LDS once per
+// block before the first weight batch (when they fit in 64 KiB); otherwise
+// each lane reads its activation chunks through the caches next to each
+// weight chunk.
 //
 // Arithmetic: int8 codes become fp16 exactly (bias by 128, place the byte
 // under the fp16 exponent of 1024 with v_perm_b32, subtract 1152 in packed
@@ -23,7 +25,7 @@
 // an fp16 activation and an 8-bit code are exact in fp32). Per-channel keeps one
 // fp32 sum per lane and applies s_w once at the end (fp32 product, then fp16);
 // per-group forms each lane's 16-code partial and adds partial * s_w[n, g]
-// (one group per partial: gs >= 16). The 8 lanes of a row are summed by a
+// (one group per partial: gs >= 16). The lanes of a row are summed by a
 // fixed butterfly and the waves in wave order, so results are
 // deterministic.
 #include "cider_internal.h"
@@ -58,21 +60,42 @@ __device__ __forceinline__ _Float16 scale_to_f16(float t, float s) {
   return (_Float16)p;
 }
 
-template <int MT, int GS, bool XL, int NWV>
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4]=7 | lgkmcnt[11:8]=15 | vmcnt[5:4] at [15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// LDS bytes of the staged activations [MT][Kpad] (whole rounds of the block's
+// 16-byte DMA) and of the per-group scales [RI][G] (whole rounds of 4-byte DMA).
+__host__ __device__ constexpr int64_t mv_x_lds(int64_t mt, int64_t kpad, int nwv) {
+  return (mt * kpad / 8 + nwv * 64 - 1) / (nwv * 64) * (nwv * 64) * 16;
+}
+__host__ __device__ constexpr int64_t mv_s_lds(int64_t ri, int64_t g, int nwv) {
+  return (ri * g + nwv * 64 - 1) / (nwv * 64) * (nwv * 64) * 4;
+}
+
+template <int MT, int GS, bool XL, int NWV, int RI>
 __global__ void __launch_bounds__(NWV * 64)
 mv_kernel(const _Float16* __restrict__ X, const int8_t* __restrict__ W, const float* __restrict__ SW,
           int M, int N, int K, _Float16* __restrict__ Y) {
-  constexpr int kBatch = XL ? 8 : (MT == 1 ? 8 : (MT == 2 ? 4 : 2));   // 128-byte steps in flight per wave
+  constexpr int kBatch = XL ? 8 : (MT == 1 ? 8 : (MT == 2 ? 4 : 2));   // steps in flight per wave
   constexpr int kStride = NWV * kBatch;                      // steps between a wave's batches
+  constexpr int kLanesPerRow = 64 / RI;
+  constexpr int kStep = 16 * kLanesPerRow;                   // codes (bytes) per row per step
   static_assert(GS == 0 || GS >= 16, "a lane's 16 codes must lie in one group");
+  static_assert(RI == 8 || RI == 4 || RI == 2, "rows per block");
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n0 = blockIdx.x * 8;
-  const int row = lane >> 3, sub = lane & 7;
-  const int rows_w = min(8, N - n0);
+  const int n0 = blockIdx.x * RI;
+  const int row = lane / kLanesPerRow, sub = lane % kLanesPerRow;
+  const int rows_w = min(RI, N - n0);
   const __amdgpu_buffer_rsrc_t rw = mv_rsrc(W + (int64_t)n0 * K, (uint32_t)rows_w * (uint32_t)K);
   // rows of x past M, and codes past K, read as zero
   const __amdgpu_buffer_rsrc_t rx = mv_rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
-  const int steps = (K + 127) / 128;
+  const int steps = (K + kStep - 1) / kStep;
   const int G = GS ? K / GS : 1;
   const float* swr = SW + (int64_t)min(n0 + row, N - 1) * G;
 
@@ -80,10 +103,10 @@ mv_kernel(const _Float16* __restrict__ X, const int8_t* __restrict__ W, const fl
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
 
-  // XL: [MT][Kpad] activations, then (per-group) the block's [8][G] scales
+  // XL: [MT][Kpad] activations, then (per-group) the block's [RI][G] scales
   extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
-  const int Kpad = steps * 128;
-  const float* scl = reinterpret_cast<const float*>(xs + MT * Kpad);
+  const int Kpad = steps * kStep;
+  const float* scl = reinterpret_cast<const float*>(reinterpret_cast<const int8_t*>(xs) + mv_x_lds(MT, Kpad, NWV));
   struct Batch {
     v4i w[kBatch];
     v4i x[XL ? 1 : kBatch][XL ? 1 : MT][2];
@@ -93,7 +116,7 @@ mv_kernel(const _Float16* __restrict__ X, const int8_t* __restrict__ W, const fl
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int st = base + NWV * i;
-      const uint32_t kb = (uint32_t)st * 128u + 16u * (uint32_t)sub;   // code index of the lane's chunk
+      const uint32_t kb = (uint32_t)st * kStep + 16u * (uint32_t)sub;   // code index of the lane's chunk
       const bool in = st < steps && kb < (uint32_t)K;
       b.w[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, in ? (uint32_t)row * (uint32_t)K + kb : 0x80000000u, 0, 0);
       if constexpr (!XL) {
@@ -114,7 +137,7 @@ mv_kernel(const _Float16* __restrict__ X, const int8_t* __restrict__ W, const fl
       h2 c[8];
 #pragma unroll
       for (int d = 0; d < 4; ++d) codes_to_h2((uint32_t)b.w[i][d], c[2 * d], c[2 * d + 1]);
-      const int kb = (base + NWV * i) * 128 + 16 * sub;
+      const int kb = (base + NWV * i) * kStep + 16 * sub;
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         float p = GS == 0 ? acc[m] : 0.0f;
@@ -138,23 +161,35 @@ mv_kernel(const _Float16* __restrict__ X, const int8_t* __restrict__ W, const fl
   };
 
   Batch ba, bb;
-  load(ba, wave);
   if constexpr (XL) {
-    // stage x (rows >= M and codes >= K as zero) while the first batch flies
-    for (int i = threadIdx.x; i < MT * Kpad / 8; i += NWV * 64) {
+    // Activations (rows >= M and codes >= K as zero) and the block's scales
+    // are DMA'd into LDS before any weight load, so waiting for them (vmcnt
+    // counts in issue order) does not wait for the weight stream; every wave
+    // issues the same number of DMA instructions (whole rounds of the block).
+    const int chunks = MT * Kpad / 8, xr = (chunks + NWV * 64 - 1) / (NWV * 64);
+    for (int j = 0; j < xr; ++j) {
+      const int i = (j * NWV + wave) * 64 + lane;
       const int m = i / (Kpad / 8), c = i % (Kpad / 8);
-      v4i v = {0, 0, 0, 0};
-      if (m < M && c * 8 < K) v = *reinterpret_cast<const v4i*>(X + (int64_t)m * K + c * 8);
-      *reinterpret_cast<v4i*>(xs + m * Kpad + c * 8) = v;
+      const uint32_t off = (i < chunks && m < M && c * 8 < K) ? ((uint32_t)m * (uint32_t)K + (uint32_t)c * 8) * 2u
+                                                              : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(reinterpret_cast<int8_t*>(xs) + (j * NWV + wave) * 1024),
+                                               16, off, 0, 0, 0);
     }
     if constexpr (GS != 0) {
-      float* sdst = reinterpret_cast<float*>(xs + MT * Kpad);
-      for (int i = threadIdx.x; i < 8 * G; i += NWV * 64) {
-        const int r = i / G;
-        sdst[i] = n0 + r < N ? SW[(int64_t)(n0 + r) * G + i % G] : 0.0f;
+      const __amdgpu_buffer_rsrc_t rs = mv_rsrc(SW + (int64_t)n0 * G, (uint32_t)rows_w * (uint32_t)G * 4u);
+      const int sr = (RI * G + NWV * 64 - 1) / (NWV * 64);
+      int8_t* sbase = reinterpret_cast<int8_t*>(xs) + mv_x_lds(MT, Kpad, NWV);
+      for (int j = 0; j < sr; ++j) {
+        const int i = (j * NWV + wave) * 64 + lane;   // scale (r = i / G, g = i % G) of the block
+        const uint32_t off = i < RI * G ? (uint32_t)i * 4u : 0x80000000u;   // rows past N: past the range
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(sbase + (j * NWV + wave) * 256), 4, off, 0, 0, 0);
       }
     }
-    __syncthreads();
+    load(ba, wave);
+    wait_vmcnt<kBatch>();   // this wave's DMA landed (its weight batch may still fly)
+    __syncthreads();        // everyone's
+  } else {
+    load(ba, wave);
   }
   for (int base = wave; base < steps; base += 2 * kStride) {
     if (base + kStride < steps) load(bb, base + kStride);
@@ -164,18 +199,18 @@ mv_kernel(const _Float16* __restrict__ X, const int8_t* __restrict__ W, const fl
     consume(bb, base + kStride);
   }
 
-  // the 8 lanes of a row (fixed butterfly), then the waves in order
+  // the lanes of a row (fixed butterfly), then the waves in order
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int off = 1; off < 8; off <<= 1) acc[m] += __shfl_xor(acc[m], off);
-  __shared__ float red[NWV][8][MT];
+    for (int off = 1; off < kLanesPerRow; off <<= 1) acc[m] += __shfl_xor(acc[m], off);
+  __shared__ float red[NWV][RI][MT];
   if (sub == 0) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) red[wave][row][m] = acc[m];
   }
   __syncthreads();
-  if (threadIdx.x >= 8 * MT) return;
+  if (threadIdx.x >= RI * MT) return;
   const int r = threadIdx.x / MT, m = threadIdx.x % MT;
   const int n = n0 + r;
   if (m >= M || n >= N) return;
@@ -185,26 +220,32 @@ mv_kernel(const _Float16* __restrict__ X, const int8_t* __restrict__ W, const fl
   Y[(int64_t)m * N + n] = GS == 0 ? scale_to_f16(t, SW[n]) : (_Float16)t;
 }
 
-template <int MT, int GS, int NWV>
+template <int MT, int GS, int NWV, int RI>
 hipError_t launch_mv_w(const MvArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)((a.N + 7) / 8)), block(NWV * 64);
-  const size_t lds = (size_t)MT * (size_t)((a.K + 127) / 128 * 128) * 2 + (GS ? 8 * (size_t)(a.K / GS) * 4 : 0);
+  constexpr int kStep = 16 * (64 / RI);
+  const dim3 grid((unsigned)((a.N + RI - 1) / RI)), block(NWV * 64);
+  const int64_t kpad = (a.K + kStep - 1) / kStep * kStep;
+  const size_t lds = (size_t)(mv_x_lds(MT, kpad, NWV) + (GS ? mv_s_lds(RI, a.K / (GS ? GS : 1), NWV) : 0));
   if (lds <= 64 * 1024) {
-    mv_kernel<MT, GS, true, NWV><<<grid, block, lds, st>>>(static_cast<const _Float16*>(a.x), a.w, a.sw, (int)a.M,
-                                                      (int)a.N, (int)a.K, static_cast<_Float16*>(a.y));
+    mv_kernel<MT, GS, true, NWV, RI><<<grid, block, lds, st>>>(static_cast<const _Float16*>(a.x), a.w, a.sw,
+                                                               (int)a.M, (int)a.N, (int)a.K,
+                                                               static_cast<_Float16*>(a.y));
   } else {
-    mv_kernel<MT, GS, false, NWV><<<grid, block, 0, st>>>(static_cast<const _Float16*>(a.x), a.w, a.sw, (int)a.M,
-                                                     (int)a.N, (int)a.K, static_cast<_Float16*>(a.y));
+    mv_kernel<MT, GS, false, NWV, RI><<<grid, block, 0, st>>>(static_cast<const _Float16*>(a.x), a.w, a.sw,
+                                                              (int)a.M, (int)a.N, (int)a.K,
+                                                              static_cast<_Float16*>(a.y));
   }
   return hipGetLastError();
 }
 
-// Eight waves per block when the grid (one block per 8 rows) is small, so
-// each block keeps more of the weight stream in flight.
+// Rows per block: 8 while that gives >= 1024 blocks (four per CU), else 4
+// (also for more than two activation rows), else 2, so that small N still
+// spreads over the 256 CUs; four waves per block.
 template <int MT, int GS>
 hipError_t launch_mv_t(const MvArgs& a, hipStream_t st) {
-  if ((a.N + 7) / 8 < 1024) return launch_mv_w<MT, GS, 8>(a, st);
-  return launch_mv_w<MT, GS, 4>(a, st);
+  if ((a.N + 7) / 8 >= 1024) return launch_mv_w<MT, GS, 4, 8>(a, st);
+  if ((a.N + 3) / 4 >= 1024 || MT > 2) return launch_mv_w<MT, GS, 4, 4>(a, st);
+  return launch_mv_w<MT, GS, 4, 2>(a, st);
 }
 
 template <int GS>
