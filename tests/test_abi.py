@@ -253,3 +253,12 @@ def test_stack_layout_and_validation():
     assert L.cider_stack_forward(P, 64, 256, 256, 128, 512, 1, ct.cast(layers, ct.c_void_p), P, total, P,
                                  NULL) == INV
     assert L.cider_stack_forward(P, 64, 256, 256, 128, 512, 0, NULL, NULL, 0, NULL, NULL) == 0
+
+
+def test_prepared_call_marshals_once_and_raises_on_error():
+    ok = cider.prepared("cider_int8_mv", NULL, NULL, NULL, 0, 16, 64, 0, NULL, NULL)
+    ok()
+    ok()
+    bad = cider.prepared("cider_int8_mv", P, P, P, 5, 4, 64, 0, P, NULL)
+    with pytest.raises(Exception, match="cider_int8_mv"):
+        bad()

@@ -160,6 +160,33 @@ def _need(t, dtype, shape, name):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _carg(a):
+    """A call argument in C form: a tensor as its device pointer, a stream as
+    its handle, anything else as given (ctypes converts ints and None)."""
+    import torch
+    if isinstance(a, torch.Tensor):
+        return ctypes.c_void_p(a.data_ptr())
+    if isinstance(a, torch.cuda.Stream):
+        return ctypes.c_void_p(a.cuda_stream)
+    return a
+
+
+def prepared(fn_name: str, *args):
+    """A zero-argument callable that calls the C entry point `fn_name` with
+    its arguments already in C form (tensors as device pointers, the stream
+    as its handle) and raises on a non-zero status. Timing loops use it so
+    that back-to-back launches of short kernels are not paced by Python-side
+    argument checking; the caller keeps the tensors alive."""
+    f = getattr(lib(), fn_name)
+    cargs = tuple(_carg(a) for a in args)
+
+    def call():
+        st = f(*cargs)
+        if st != CIDER_SUCCESS:
+            _check(fn_name, st)
+    return call
+
+
 def cider_is_available() -> bool:
     return bool(lib().cider_is_available())
 
