@@ -47,6 +47,10 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ v4i zero4() { return v4i{0, 0, 0, 0}; }
 
+// The lane index recomputed where it is used (mbcnt), so that no register
+// holds it across a long loop.
+__device__ __forceinline__ int lane_id() { return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
 // Per-channel dequant of one element: fp16(fp32(fp32(acc) * s_a) * s_w), each
 // product rounded to fp32 before the round-to-nearest-even fp16 conversion.
 // The empty asm pins the second product as an fp32 register value: without it
@@ -559,6 +563,66 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
   const bool vec_ok = (N & 3) == 0;
   const float* const lsa = lsc;
   const float* const lsw = lsc + BM;
+
+  // fp16 / bf16 output with N % 8 == 0: the dequantized tile goes through LDS
+  // (the operand stages are free once every wave is past its last MFMA) in
+  // slabs of R rows, and is written back as whole 16-byte row chunks,
+  // consecutive lanes on consecutive chunks, with nontemporal stores: every
+  // store instruction fills whole 128-byte lines and the output stream does
+  // not displace the operand panels from L2. Written straight from the
+  // accumulator layout, each instruction covers 32 bytes of 16 rows. Same-box
+  // A/B (outputs bit-identical): M=4096 N=10240 K=2560 102.9 -> 89.3 us,
+  // M=8192 201.9 -> 176.3 us, M=1024 37.9 -> 32.4 us, M=1024 N=12288 K=2048
+  // 32.8 -> 26.9 us; nontemporal stores straight from the accumulator layout
+  // were slower (M=4096: 149 us).
+  if constexpr (kF16) {
+    if ((N & 7) == 0) {
+      constexpr int kRowB = BN * 2 + 16;   // 16 bytes of padding spread the row starts over the banks
+      constexpr int kAvail = NS * kStageBytes;
+      constexpr int R = BM * kRowB <= kAvail ? BM : (BM / 2) * kRowB <= kAvail ? BM / 2 : BM / 4;
+      static_assert(R % 16 == 0 && R * kRowB <= kAvail, "store slab fits the operand stages");
+      constexpr int CPR = BN / 8;          // 16-byte chunks per tile row
+      constexpr int kIt = (R * CPR + NW * 64 - 1) / (NW * 64);
+      stage_barrier();                     // every wave is done reading the operand stages
+      // lane coordinates recomputed here rather than kept live across the loop
+      const int s16 = lane_id() & 15, s4 = lane_id() >> 4;
+#pragma unroll
+      for (int p = 0; p < BM / R; ++p) {
+#pragma unroll
+        for (int b = 0; b < TM; ++b) {
+          const int r0 = wm + 16 * b - p * R;   // wave-uniform
+          if (r0 >= 0 && r0 < R) {
+            const float sam = lsa[wm + 16 * b + s16];
+#pragma unroll
+            for (int a = 0; a < TN; ++a) {
+              const int nl = wn + 16 * a + 4 * s4;
+              int8_t* d = smem + (r0 + s16) * kRowB + nl * 2;
+              const float4 sw4 = *reinterpret_cast<const float4*>(lsw + nl);   // zero past N
+              if constexpr (EPI == kEpiBF16 || EPI == kEpiBF16Split)
+                *reinterpret_cast<bf4*>(d) = dequant4_bf(acc[a][b], sam, sw4);
+              else
+                *reinterpret_cast<h4*>(d) = dequant4(acc[a][b], sam, sw4);
+            }
+          }
+        }
+        stage_barrier();
+#pragma unroll
+        for (int i = 0; i < kIt; ++i) {
+          const int f = (i * NW + wave) * 64 + lane_id();
+          const int row = f / CPR, ch = f - row * CPR;
+          const int m = m0 + p * R + row, n = n0 + ch * 8;
+          if (f < R * CPR && m < M && n < N) {
+            const v4i v = *reinterpret_cast<const v4i*>(smem + row * kRowB + ch * 16);
+            _Float16* dst = Y + (int64_t)m * N + n;
+            if constexpr (kSplitOut) dst = split_dst(osp, m, n);   // parts are multiples of 16 wide
+            __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(dst));
+          }
+        }
+        if (p + 1 < BM / R) stage_barrier();   // the slab is rewritten by the next pass
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int b = 0; b < TM; ++b) {
     const int ml = wm + 16 * b + l16;
@@ -1455,6 +1519,57 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
     return;
   }
   if constexpr (kF16) {
+    // N % 8 == 0: through LDS as whole 16-byte row chunks with nontemporal
+    // stores, as in gemm_dma_kernel (the code stages are free after the loop)
+    if ((N & 7) == 0) {
+      constexpr int kRowB = BN * 2 + 16;
+      constexpr int kAvail = NS * kCodeBytes;
+      constexpr int R = BM * kRowB <= kAvail ? BM : (BM / 2) * kRowB <= kAvail ? BM / 2 : BM / 4;
+      static_assert(R % 16 == 0 && R * kRowB <= kAvail, "store slab fits the code stages");
+      constexpr int CPR = BN / 8;
+      constexpr int kIt = (R * CPR + NW * 64 - 1) / (NW * 64);
+      stage_barrier();
+      const int s16 = lane_id() & 15, s4 = lane_id() >> 4;
+#pragma unroll
+      for (int p = 0; p < BM / R; ++p) {
+#pragma unroll
+        for (int b = 0; b < TM; ++b) {
+          const int r0 = wm + 16 * b - p * R;
+          if (r0 >= 0 && r0 < R) {
+            const int m = m0 + wm + 16 * b + s16;
+            const float sam = kTok && m < M ? SA[m] : 1.0f;
+#pragma unroll
+            for (int a = 0; a < TN; ++a) {
+              int8_t* d = smem + (r0 + s16) * kRowB + (wn + 16 * a + 4 * s4) * 2;
+              if constexpr (EPI == kEpiBF16 || EPI == kEpiBF16Tok) {
+                bf4 o;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[r] = kTok ? scale1_bf(facc[a][b][r], sam) : to_bf16(facc[a][b][r]);
+                *reinterpret_cast<bf4*>(d) = o;
+              } else {
+                h4 o;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[r] = kTok ? scale1(facc[a][b][r], sam) : (_Float16)facc[a][b][r];
+                *reinterpret_cast<h4*>(d) = o;
+              }
+            }
+          }
+        }
+        stage_barrier();
+#pragma unroll
+        for (int i = 0; i < kIt; ++i) {
+          const int f = (i * NW + wave) * 64 + lane_id();
+          const int row = f / CPR, ch = f - row * CPR;
+          const int m = m0 + p * R + row, n = n0 + ch * 8;
+          if (f < R * CPR && m < M && n < N) {
+            const v4i v = *reinterpret_cast<const v4i*>(smem + row * kRowB + ch * 16);
+            __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(Y + (int64_t)m * N + n));
+          }
+        }
+        if (p + 1 < BM / R) stage_barrier();
+      }
+      return;
+    }
     const bool vec_ok = (N & 3) == 0;
 #pragma unroll
     for (int b = 0; b < TM; ++b) {
