@@ -20,7 +20,8 @@ REPEATS = 20
 
 # (name, mode, M, N, K, group_size, use_workspace): the shape picks the family
 FAMILIES = [
-    ("256x320 tile", "pc", 4096, 10240, 2560, 0, False),
+    ("256x320 persistent", "pc", 4096, 10240, 2560, 0, False),
+    ("256x320 one round", "pc", 2048, 10240, 2560, 0, False),
     ("256x192 tile", "pc", 1024, 12288, 2048, 0, False),
     ("128x320 tile", "pc", 1024, 10240, 2560, 0, False),
     ("64x80 tile", "pc", 128, 10240, 2560, 0, False),

@@ -44,6 +44,15 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
     if verbose and msgs.strip():
         print(msgs)
+    # every symbol of the library's own namespace must be defined in it (a
+    # kernel whose host-side launch stub was not emitted links fine and only
+    # fails when the library is loaded)
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    if nm.returncode == 0:
+        missing = [l.split()[-1] for l in nm.stdout.splitlines() if "cider" in l]
+        if missing:
+            os.remove(tmp)
+            raise RuntimeError("libcider.so has undefined symbols of its own: " + ", ".join(missing))
     os.replace(tmp, LIB)
     return LIB
 

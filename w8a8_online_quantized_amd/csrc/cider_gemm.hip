@@ -228,6 +228,13 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// stage_barrier after this wave's LDS writes have landed (lgkmcnt(0)): the
+// barrier alone does not wait for them
+__device__ __forceinline__ void lds_write_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  stage_barrier();
+}
+
 // Address of output (m, n) in a column-split output: the part holding
 // columns n .. n+3 (part widths are multiples of 4), as 16-bit elements.
 __device__ __forceinline__ _Float16* split_dst(const OutSplit& osp, int m, int n) {
@@ -605,7 +612,7 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
             }
           }
         }
-        stage_barrier();
+        lds_write_barrier();
 #pragma unroll
         for (int i = 0; i < kIt; ++i) {
           const int f = (i * NW + wave) * 64 + lane_id();
@@ -668,6 +675,252 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
         }
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Persistent per-channel kernel for launches of more than one round of tiles
+// (int8 weights, fp16 / bf16 output, N % 8 == 0, K % 128 == 0: whole 128-code
+// stages, two in flight). Each block walks its tiles one after another in the same
+// XCD-contiguous order as gemm_dma_kernel, and the tiles overlap at the seam:
+// the last stage of tile t already issues the DMA of tile t+1's first stage
+// and of its scales (into the other of two scale buffers), and tile t's store
+// stage - through LDS, whole 16-byte row chunks, nontemporal, as in
+// gemm_dma_kernel, in slabs that fit the stage buffer nobody reads any more -
+// then runs while that DMA lands, and its global stores drain while tile t+1
+// computes. The waves split the memory work: the upper half issue every DMA
+// and wait for it with s_waitcnt vmcnt, the lower half issue every global
+// store and never wait on vmcnt. (vmcnt counts a wave's loads and stores in
+// one in-order counter, so a wave that stored and then waited for a later
+// load would wait for its stores to drain too.) Stores go through a buffer
+// descriptor spanning the tile's valid rows; a masked lane gets an
+// out-of-range offset, so every storing wave issues the same instructions.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WGM, int WGN, int EPI>
+__global__ void __launch_bounds__(WGM * WGN * 64)
+gemm_persist_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, const int8_t* __restrict__ W,
+                    const float* __restrict__ SW, int M, int N, int K, void* __restrict__ Y) {
+  constexpr int BK = 128, NW = WGM * WGN, NL = NW / 2;   // NL loader waves, NW - NL storer waves
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int TM = WTM / 16, TN = WTN / 16;
+  constexpr int kStageBytes = (BM + BN) * BK;
+  constexpr int kBA = BM * BK / 1024, kBW = BN * BK / 1024;     // 1 KiB DMA blocks per stage
+  constexpr int kIA = kBA / NL, kIW = kBW / NL;                 // per loader wave
+  constexpr int kRowStep = NL * (1024 / BK);                    // tile rows between a wave's blocks
+  constexpr int kScInstr = (BM + BN) / 64;                      // 64 scales per 4-byte DMA instruction
+  constexpr int kScPer = (kScInstr + NL - 1) / NL;
+  constexpr int kScFloats = BM + BN;
+  constexpr int kRowB = BN * 2 + 16;
+  constexpr int R = BM * kRowB <= kStageBytes ? BM : (BM / 2) * kRowB <= kStageBytes ? BM / 2
+                  : (BM / 4) * kRowB <= kStageBytes ? BM / 4 : BM / 8;
+  constexpr int CPR = BN / 8;
+  constexpr int kIt = (R * CPR + (NW - NL) * 64 - 1) / ((NW - NL) * 64);
+  constexpr bool kBF = EPI == kEpiBF16;
+  static_assert(EPI == kEpiF16 || EPI == kEpiBF16, "fp16 / bf16 output");
+  static_assert(kBA % NL == 0 && kBW % NL == 0 && BM % 64 == 0 && BN % 64 == 0, "even DMA split");
+  static_assert(TM * 16 == WTM && TN * 16 == WTN && TM >= 2, "wave tile");
+  static_assert(R % 16 == 0 && R * kRowB <= kStageBytes, "store slab fits one stage");
+
+  // two stages | two scale buffers ([BM] s_a then [BN] s_w) | 1 KiB landing pad for spare DMAs
+  __shared__ __attribute__((aligned(1024))) int8_t smem[2 * kStageBytes + 2 * kScFloats * 4 + 1024];
+  float* const lscb = reinterpret_cast<float*>(smem + 2 * kStageBytes);
+  int8_t* const pad = smem + 2 * kStageBytes + 2 * kScFloats * 4;
+
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = (wave % WGM) * WTM, wn = (wave / WGM) * WTN;
+  const int l16 = lane & 15, l4 = lane >> 4;
+  const bool loader = wave >= NL;
+  const int lw = loader ? wave - NL : 0;
+
+  const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
+  const int units = nbm * nbn;
+  const int KT = (K + BK - 1) / BK;
+  const uint32_t ld = (uint32_t)K;
+
+  // tile of virtual block vb (vb < units): XCD-contiguous ranges, then groups of 8 tile-rows
+  auto tile_origin = [&](int vb, int& m0, int& n0) {
+    const int xcd = vb & 7, idx = vb >> 3;
+    const int per = units >> 3, rem = units & 7;
+    const int tile = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    constexpr int kGroupM = 8;
+    const int first_m = tile / (kGroupM * nbn) * kGroupM;
+    const int gsz = min(nbm - first_m, kGroupM);
+    m0 = (first_m + (tile % (kGroupM * nbn)) % gsz) * BM;
+    n0 = (tile % (kGroupM * nbn)) / gsz * BN;
+  };
+  // descriptors spanning a tile's valid rows (passed by value: a descriptor
+  // held in a struct member and handed to the DMA builtin left the kernel
+  // without its host-side launch stub)
+  auto rsrc_a = [&](int m0) { return make_rsrc(A + (int64_t)m0 * K, (uint32_t)min(BM, M - m0) * ld); };
+  auto rsrc_w = [&](int n0) { return make_rsrc(W + (int64_t)n0 * K, (uint32_t)min(BN, N - n0) * ld); };
+  auto rsrc_sa = [&](int m0) { return make_rsrc(SA + m0, (uint32_t)min(BM, M - m0) * 4); };
+  auto rsrc_sw = [&](int n0) { return make_rsrc(SW + n0, (uint32_t)min(BN, N - n0) * 4); };
+
+  // A loader lane's DMA byte offset at code 0 for its first block; block i of
+  // the wave is kRowStep rows further, which keeps the row's swizzle slot
+  // (kRowStep is a multiple of 16), so its offset is larger by i * kRowStep * K.
+  const int r0 = lw * (1024 / BK) + lane / (BK / 16);
+  const uint32_t off0 = (uint32_t)r0 * ld + (uint32_t)(slot_of<BK>(r0, lane % (BK / 16)) * 16);
+  static_assert(kRowStep % 16 == 0, "uniform block step keeps the swizzle slot");
+  auto issue = [&](__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rw, int kt, int buf) {   // loader waves; K % BK == 0
+    const int kb = kt * BK;
+    {
+      // The whole offset goes in the vector operand (the descriptor's range
+      // check, which zero-fills past the tile's valid rows, applies to it).
+      // `base` is opaque to the optimizer so that the per-block offsets are
+      // formed here, one add each, instead of being hoisted out of the K loop
+      // as kIA + kIW loop-invariant registers.
+      // The same for the LDS destinations (one scalar register each).
+      uint32_t base = off0 + (uint32_t)kb;
+      asm volatile("" : "+v"(base));
+      uint32_t lbase = (uint32_t)buf * kStageBytes + (uint32_t)lw * 1024;
+      asm volatile("" : "+s"(lbase));
+#pragma unroll
+      for (int i = 0; i < kIA; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(smem + lbase + i * NL * 1024), 16,
+                                                 base + (uint32_t)(i * kRowStep) * ld, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < kIW; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(smem + lbase + BM * BK + i * NL * 1024), 16,
+                                                 base + (uint32_t)(i * kRowStep) * ld, 0, 0, 0);
+    }
+  };
+  auto issue_scales = [&](__amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsw, int sb) {   // loader waves; rows past the tile load 0
+    float* dst = lscb + sb * kScFloats;
+    const uint32_t l4b = (uint32_t)lane_id() * 4;   // formed here, not kept across the K loop
+#pragma unroll
+    for (int i = 0; i < kScPer; ++i) {
+      const int j = lw + i * NL;
+      if (j >= kScInstr)   // spare: keeps every loader wave's vmcnt count equal
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_void*)pad, 4, 0x80000000u, 0, 0, 0);
+      else if (j < BM / 64)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(dst + 64 * j), 4, 256u * j + l4b, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_void*)(dst + BM + 64 * (j - BM / 64)), 4,
+                                                 256u * (j - BM / 64) + l4b, 0, 0, 0);
+    }
+  };
+
+  int vb = blockIdx.x;
+  if (vb >= units) return;
+  if (loader) {
+    int m0, n0;
+    tile_origin(vb, m0, n0);
+    issue_scales(rsrc_sa(m0), rsrc_sw(n0), 0);
+    issue(rsrc_a(m0), rsrc_w(n0), 0, 0);
+  }
+  int gs = 0;   // stages this block has consumed: stage kt of the current tile sits in buffer (gs + kt) & 1
+  for (int it = 0;; ++it) {
+    // the current tile's origin and descriptors, and the next tile's origin,
+    // stay live through the K loop; the next tile's descriptors are built at
+    // the last stage
+    int m0, n0;
+    tile_origin(vb, m0, n0);
+    const __amdgpu_buffer_rsrc_t ra = rsrc_a(m0), rw = rsrc_w(n0);
+    const int vbn = vb + (int)gridDim.x;
+    const bool more = vbn < units;
+    int m0n = 0, n0n = 0;   // the next tile's origin (its descriptors are built where used)
+    if (more) tile_origin(vbn, m0n, n0n);
+
+    v4i acc[TN][TM];
+#pragma unroll
+    for (int a = 0; a < TN; ++a)
+#pragma unroll
+      for (int b = 0; b < TM; ++b) acc[a][b] = zero4();
+
+    for (int kt = 0; kt < KT; ++kt) {
+      if (loader) wait_vmcnt<0>();   // stage kt (and, at kt = 0, the tile's scales) landed
+      stage_barrier();
+      const int8_t* sa_ = smem + ((gs + kt) & 1) * kStageBytes;
+      const int8_t* sw_ = sa_ + BM * BK;
+      // two 64-code steps, fragment reads issued ahead of use as in gemm_dma_kernel
+      v4i wf[TN], af[TM], nwf[TN], naf[TM];
+#pragma unroll
+      for (int a = 0; a < TN; ++a)
+        wf[a] = *reinterpret_cast<const v4i*>(sw_ + tile_off<BK>(wn + 16 * a + l16, l4));
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        af[b] = *reinterpret_cast<const v4i*>(sa_ + tile_off<BK>(wm + 16 * b + l16, l4));
+      __builtin_amdgcn_sched_barrier(0);
+      if (loader) {
+        if (kt + 1 < KT) {
+          issue(ra, rw, kt + 1, (gs + kt + 1) & 1);
+        } else if (more) {
+          issue_scales(rsrc_sa(m0n), rsrc_sw(n0n), (it + 1) & 1);
+          issue(rsrc_a(m0n), rsrc_w(n0n), 0, (gs + kt + 1) & 1);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int b = 0; b < TM; ++b) {
+#pragma unroll
+        for (int a = 0; a < TN; ++a)
+          acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[a], af[b], acc[a][b], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (b + 2 < TM) af[b + 2] = *reinterpret_cast<const v4i*>(sa_ + tile_off<BK>(wm + 16 * (b + 2) + l16, l4));
+        naf[b] = *reinterpret_cast<const v4i*>(sa_ + tile_off<BK>(wm + 16 * b + l16, 4 + l4));
+        if (b < TN) nwf[b] = *reinterpret_cast<const v4i*>(sw_ + tile_off<BK>(wn + 16 * b + l16, 4 + l4));
+        if (b == TM - 1) {
+#pragma unroll
+          for (int a = TM; a < TN; ++a)
+            nwf[a] = *reinterpret_cast<const v4i*>(sw_ + tile_off<BK>(wn + 16 * a + l16, 4 + l4));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int b = 0; b < TM; ++b)
+#pragma unroll
+        for (int a = 0; a < TN; ++a)
+          acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(nwf[a], naf[b], acc[a][b], 0, 0, 0);
+    }
+    gs += KT;
+
+    // ---- store stage: slabs of R rows in the buffer of the tile's last stage
+    // (the next tile's first stage lands in the other one)
+    stage_barrier();   // every wave is done reading that buffer
+    int8_t* const slab = smem + ((gs - 1) & 1) * kStageBytes;
+    const float* const lsa = lscb + (it & 1) * kScFloats;
+    const float* const lsw = lsa + BM;
+    const int rows_a = min(BM, M - m0);
+    const __amdgpu_buffer_rsrc_t ry =
+        make_rsrc(static_cast<int8_t*>(Y) + (int64_t)m0 * N * 2, (uint32_t)rows_a * (uint32_t)N * 2);
+    const int s16 = lane_id() & 15, s4 = lane_id() >> 4;
+#pragma unroll
+    for (int p = 0; p < BM / R; ++p) {
+#pragma unroll
+      for (int b = 0; b < TM; ++b) {
+        const int rr = wm + 16 * b - p * R;   // wave-uniform
+        if (rr >= 0 && rr < R) {
+          const float sam = lsa[wm + 16 * b + s16];
+#pragma unroll
+          for (int a = 0; a < TN; ++a) {
+            const int nl = wn + 16 * a + 4 * s4;
+            int8_t* d = slab + (rr + s16) * kRowB + nl * 2;
+            const float4 sw4 = *reinterpret_cast<const float4*>(lsw + nl);   // zero past N
+            if constexpr (kBF)
+              *reinterpret_cast<bf4*>(d) = dequant4_bf(acc[a][b], sam, sw4);
+            else
+              *reinterpret_cast<h4*>(d) = dequant4(acc[a][b], sam, sw4);
+          }
+        }
+      }
+      lds_write_barrier();
+      if (!loader) {
+#pragma unroll
+        for (int i = 0; i < kIt; ++i) {
+          const int f = (i * (NW - NL) + wave) * 64 + lane_id();
+          const int row = min(f / CPR, R - 1), ch = f - (f / CPR) * CPR;
+          const int n = n0 + ch * 8;
+          const bool ok = f < R * CPR && p * R + row < rows_a && n < N;
+          const v4i v = *reinterpret_cast<const v4i*>(slab + row * kRowB + ch * 16);
+          const uint32_t off = ok ? ((uint32_t)(p * R + row) * (uint32_t)N + (uint32_t)n) * 2 : 0x80000000u;
+          __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, 2 /* nontemporal */);
+        }
+      }
+      if (p + 1 < BM / R) stage_barrier();   // the slab is rewritten by the next pass
+    }
+    if (!more) break;
+    vb = vbn;
   }
 }
 
@@ -1555,7 +1808,7 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
             }
           }
         }
-        stage_barrier();
+        lds_write_barrier();
 #pragma unroll
         for (int i = 0; i < kIt; ++i) {
           const int f = (i * NW + wave) * 64 + lane_id();
@@ -1736,6 +1989,22 @@ inline int64_t tiles_of(const GemmArgs& g, int bm, int bn) {
   return ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn);
 }
 
+// The persistent kernel pays off where the one-tile-per-block launch would run
+// more than one round (one block per CU); it takes whole 128-code stages, and
+// its stores need N % 8 == 0 and byte offsets within one tile's rows below 2^31. Same-box A/B (outputs
+// bit-identical): see gemm_persist_kernel's dispatch in launch_pc.
+inline bool persist_fits(const GemmArgs& g, int bm, int bn) {
+  return tiles_of(g, bm, bn) > 256 && (g.N & 7) == 0 && g.K % 128 == 0 &&
+         (int64_t)bm * g.N * 2 < (int64_t(1) << 31);
+}
+
+template <int BM, int BN, int WGM, int WGN, int EPI>
+hipError_t launch_persist(const GemmArgs& g, hipStream_t st) {
+  gemm_persist_kernel<BM, BN, WGM, WGN, EPI><<<dim3(256), dim3(WGM * WGN * 64), 0, st>>>(
+      g.a, g.sa, static_cast<const int8_t*>(g.w), g.sw, (int)g.M, (int)g.N, (int)g.K, g.y);
+  return hipGetLastError();
+}
+
 // Tile choice. A launch of T tiles whose blocks fit `bpc` to a CU (LDS and
 // registers) runs in about ceil(T / (256 * bpc)) rounds, and a round of
 // BM x BN tiles costs about BM * BN * cost, where `cost` (time per output
@@ -1898,7 +2167,10 @@ hipError_t launch_pc(const GemmArgs& g, hipStream_t st) {
     }
   } else {
     switch (cheapest_tile(g, kTilesI8)) {
-      case 0: return launch_dma<256, 320, 2, 4, 128, 2, WK, EPI>(g, st);
+      case 0:
+        if constexpr (EPI == kEpiF16 || EPI == kEpiBF16)
+          if (persist_fits(g, 256, 320)) return launch_persist<256, 320, 2, 4, EPI>(g, st);
+        return launch_dma<256, 320, 2, 4, 128, 2, WK, EPI>(g, st);
       case 1: return launch_dma<128, 320, 2, 4, 128, 2, WK, EPI>(g, st);
       case 2: return launch_dma<128, 256, 2, 4, 128, 2, WK, EPI>(g, st);
       case 3: return launch_dma<128, 128, 2, 2, 64, 3, WK, EPI>(g, st);
