@@ -239,7 +239,7 @@ def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_byte
     ops, gemm_bytes, quant_bytes = algorithmic(mode, M, N, K, gs)
     R = max(2, -(-min_set_bytes // (gemm_bytes + quant_bytes)))
     if mode in ("int8_mv", "w8a8_linear"):
-        return measure_mv(cider, torch, x_h, w_h, M, N, K, gs, steps, warmup, R, ops, gemm_bytes, mode)
+        return measure_mv(cider, torch, x_h, w_h, M, N, K, gs, steps, warmup, R, ops, gemm_bytes, mode, settle_s)
     bits = 4 if mode == "w4a8" else 8
     ags = 0 if mode == "w8a8_tokpg" else gs   # activation group size
     w_dev = w_h.to(dev)
@@ -319,7 +319,7 @@ def measure(cider, torch, inputs, mode, M, N, K, gs, steps, warmup, min_set_byte
             "sclk_mhz": sclk, "settle_steps": settle_steps}
 
 
-def measure_mv(cider, torch, x_h, w_h, M, N, K, gs, steps, warmup, R, ops, nbytes, mode="int8_mv"):
+def measure_mv(cider, torch, x_h, w_h, M, N, K, gs, steps, warmup, R, ops, nbytes, mode="int8_mv", settle_s=0.0):
     """One-launch fp16-in calls, rotating buffer sets: the decode MV (no
     activation quantization) or the one-call linear (quantization inside the
     GEMV kernel)."""
@@ -341,6 +341,13 @@ def measure_mv(cider, torch, x_h, w_h, M, N, K, gs, steps, warmup, R, ops, nbyte
         return cider.prepared("cider_linear_dt", x, 0, wq, sw, M, N, K, 8, gs, ws, need, y, stream)
 
     calls = [prep(*s_) for s_ in sets]
+    if settle_s > 0:
+        t_end, i = time.perf_counter() + settle_s, 0
+        while time.perf_counter() < t_end:
+            for _ in range(64):
+                calls[i % R]()
+                i += 1
+            torch.cuda.synchronize()
     for i in range(warmup):
         calls[i % R]()
     torch.cuda.synchronize()
@@ -530,12 +537,15 @@ def pg_coroof(mode, M, N, K, gs, ops, us):
             "co_roof_us": round(co, 2), "frac_of_co_roof": round(co / us, 4)}
 
 
-def run_sweep(cider, torch, inputs, indices, steps):
-    """Times the selected sweep configurations, each with its own roofline."""
+def run_sweep(cider, torch, inputs, indices, steps, settle_s=0.0):
+    """Times the selected sweep configurations, each with its own roofline
+    (each row first runs settle_s seconds of untimed launches, so that a
+    profiled single-row run sees the same settled clock as the headline)."""
     rows = []
     for i in indices:
         mode, m, n, k, gs = SWEEP[i]
-        rr = measure(cider, torch, inputs, mode, m, n, k, gs, max(10, steps // 2), max(3, steps // 4))
+        rr = measure(cider, torch, inputs, mode, m, n, k, gs, max(10, steps // 2), max(3, steps // 4),
+                     settle_s=settle_s)
         rows.append({"row": i, "mode": mode, "M": m, "N": n, "K": k, "group_size": gs,
                      "gemm_us": round(rr["gemm_ms"] * 1e3, 2), "quant_us": round(rr["quant_ms"] * 1e3, 2),
                      "gemm_roofline": roofline_of(rr["ops"], rr["gemm_bytes"], rr["gemm_ms"]),
@@ -596,7 +606,8 @@ def main():
         sys.exit(3)
 
     if args.sweep_only:
-        rows = run_sweep(cider, torch, inputs, sweep_indices(args.sweep_rows), args.steps)
+        rows = run_sweep(cider, torch, inputs, sweep_indices(args.sweep_rows), args.steps,
+                         settle_s=args.settle_ms * 1e-3)
         res = {"sweep": rows, "kernel_source_sha": kernel_source_sha()}
         if args.read_ceiling:
             res["read_ceiling"] = measure_read_ceiling(cider, torch)
@@ -668,7 +679,8 @@ def main():
         "kernel_source_sha": sha,
     }
     if args.sweep:
-        out["sweep"] = run_sweep(cider, torch, inputs, sweep_indices(args.sweep_rows), args.steps)
+        out["sweep"] = run_sweep(cider, torch, inputs, sweep_indices(args.sweep_rows), args.steps,
+                                 settle_s=args.settle_ms * 1e-3)
     if args.sweep or args.read_ceiling:
         out["read_ceiling"] = measure_read_ceiling(cider, torch)
     if args.vendor:

@@ -767,22 +767,26 @@ gemm_persist_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, 
     {
       // The whole offset goes in the vector operand (the descriptor's range
       // check, which zero-fills past the tile's valid rows, applies to it).
-      // `base` is opaque to the optimizer so that the per-block offsets are
-      // formed here, one add each, instead of being hoisted out of the K loop
-      // as kIA + kIW loop-invariant registers.
-      // The same for the LDS destinations (one scalar register each).
-      uint32_t base = off0 + (uint32_t)kb;
-      asm volatile("" : "+v"(base));
+      // `off` and `lbase` are opaque to the optimizer so that the per-block
+      // offsets and LDS destinations are formed here, one add each, instead
+      // of being hoisted out of the K loop as loop-invariant registers.
+      // Block i of both operands sits at the same offset, and the offset of
+      // block i+1 is one uniform step further: one running register and one
+      // step register, instead of a loop-invariant register per block.
+      uint32_t off = off0 + (uint32_t)kb;
+      asm volatile("" : "+v"(off));
       uint32_t lbase = (uint32_t)buf * kStageBytes + (uint32_t)lw * 1024;
       asm volatile("" : "+s"(lbase));
+      const uint32_t step = (uint32_t)kRowStep * ld;
 #pragma unroll
-      for (int i = 0; i < kIA; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(smem + lbase + i * NL * 1024), 16,
-                                                 base + (uint32_t)(i * kRowStep) * ld, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < kIW; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(smem + lbase + BM * BK + i * NL * 1024), 16,
-                                                 base + (uint32_t)(i * kRowStep) * ld, 0, 0, 0);
+      for (int i = 0; i < (kIA > kIW ? kIA : kIW); ++i) {
+        if (i < kIA)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(smem + lbase + i * NL * 1024), 16, off, 0, 0, 0);
+        if (i < kIW)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(smem + lbase + BM * BK + i * NL * 1024), 16, off,
+                                                   0, 0, 0);
+        off += step;
+      }
     }
   };
   auto issue_scales = [&](__amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsw, int sb) {   // loader waves; rows past the tile load 0
