@@ -2039,7 +2039,11 @@ int cheapest_tile(const GemmArgs& g, const TileCost (&c)[NC], int64_t* est_out =
   return best;
 }
 
-// Per-channel / W4A8 tile tables (costs as described above). 256 x 192 (wave
+// Per-channel / W4A8 tile tables (costs as described above). 128 x 128 keeps
+// three 128-code stages (96 KB of LDS): same-box A/B against three 64-code
+// stages, M=1024 N=4096 K=2048 (the stack's fused q/k/v) 16.5 -> 14.5 us,
+// M=768 16.3 -> 14.1 us, M=1024 N=3072 K=3072 23.2 -> 19.5 us, M=512 N=8192
+// K=4096 29.7 -> 24.3 us; two 128-code stages lost (17.7 us) and four tied. 256 x 192 (wave
 // tiles of 128 x 48) for one round of up to 256 tiles where 128 x 320 or
 // 256 x 320 would leave CUs idle or need a second round; same-box A/B: M=1024
 // N=12288 K=2048 (exactly 256 tiles) 33.4 us against 43.8 us for the 156 tiles
@@ -2155,7 +2159,7 @@ hipError_t launch_pc(const GemmArgs& g, hipStream_t st) {
           return launch_dma_split<128, 320, 2, 4, 128, 2, WK, EPI>(g, p.splits, st);
         } else {
           if (p.tile == 0) return launch_dma_split<64, 160, 2, 2, 128, 4, WK, EPI>(g, p.splits, st);
-          if (p.tile == 1) return launch_dma_split<128, 128, 2, 2, 64, 3, WK, EPI>(g, p.splits, st);
+          if (p.tile == 1) return launch_dma_split<128, 128, 2, 2, 128, 3, WK, EPI>(g, p.splits, st);
           return launch_dma_split<128, 320, 2, 4, 128, 2, WK, EPI>(g, p.splits, st);
         }
       }
@@ -2177,7 +2181,7 @@ hipError_t launch_pc(const GemmArgs& g, hipStream_t st) {
         return launch_dma<256, 320, 2, 4, 128, 2, WK, EPI>(g, st);
       case 1: return launch_dma<128, 320, 2, 4, 128, 2, WK, EPI>(g, st);
       case 2: return launch_dma<128, 256, 2, 4, 128, 2, WK, EPI>(g, st);
-      case 3: return launch_dma<128, 128, 2, 2, 64, 3, WK, EPI>(g, st);
+      case 3: return launch_dma<128, 128, 2, 2, 128, 3, WK, EPI>(g, st);
       case 4: return launch_dma<64, 160, 2, 2, 128, 4, WK, EPI>(g, st);
       case 5: return launch_dma<64, 64, 1, 4, 128, 4, WK, EPI>(g, st);
       case 6: return launch_dma<256, 192, 2, 4, 128, 2, WK, EPI>(g, st);
