@@ -1639,11 +1639,42 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
   const int kc = ((K + nsplit - 1) / nsplit + BK - 1) / BK * BK;
   const int kt0 = split * (kc / BK);
   const int KT = max(0, min((K + BK - 1) / BK, kt0 + kc / BK) - kt0);
+  // A lane's DMA byte offset at code 0 for its first 1 KiB block; block i of
+  // the wave is NW * 8 rows further (a multiple of 16 rows keeps the row's
+  // swizzle slot). A whole stage then costs one add per DMA instruction
+  // instead of dma_stage's per-lane row, slot and range arithmetic, VALU work
+  // that competes with the fold; a stage cut by the end of K still goes
+  // through dma_stage. Same-box A/B (outputs bit-identical), N=2560,
+  // K=10240: gs 64 M=4096 313 -> 304 us, gs 128 M=4096 161.6 -> 160.0 us,
+  // M=2048 102.6 -> 101.1 us. (Interleaving the two operands' blocks ran
+  // slower.)
+  constexpr int kBA = BM * RB / 1024, kBW = BN * RB / 1024;
+  constexpr bool kFastDma = kBA % NW == 0 && kBW % NW == 0 && (NW * (1024 / RB)) % 16 == 0;
+  const int rl0 = wave * (1024 / RB) + lane / (RB / 16);
+  const uint32_t off0 = (uint32_t)rl0 * ld + (uint32_t)(slot_of<RB>(rl0, lane % (RB / 16)) * 16);
   auto issue = [&](int kt) {
     int8_t* st = smem + (kt % NS) * kCodeBytes;
-    dma_stage<BM, RB, NW>(ra, st, pad, wave, lane, ld, (kt0 + kt) * RB, (int)ld);
-    dma_stage<BN, RB, NW>(rw, st + BM * RB, pad, wave, lane, ld, (kt0 + kt) * RB, (int)ld);
+    const int kb = (kt0 + kt) * RB;
+    if (kFastDma && kb + RB <= K) {
+      const uint32_t off = off0 + (uint32_t)kb;
+      const uint32_t step = (uint32_t)(NW * (1024 / RB)) * ld;
+#pragma unroll
+      for (int i = 0; i < kBA / NW; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + (wave + i * NW) * 1024), 16,
+                                                 off + (uint32_t)i * step, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < kBW / NW; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(st + BM * RB + (wave + i * NW) * 1024), 16,
+                                                 off + (uint32_t)i * step, 0, 0, 0);
+    } else {
+      dma_stage<BM, RB, NW>(ra, st, pad, wave, lane, ld, kb, (int)ld);
+      dma_stage<BN, RB, NW>(rw, st + BM * RB, pad, wave, lane, ld, kb, (int)ld);
+    }
     float* slot = ring + (kt % NSR) * kSlotFloats;
+    // the lane's scale-row offset, formed here (opaque to the optimizer): kept
+    // live across the K loop, one register per instruction, it spilled
+    uint32_t lrow = (uint32_t)lane_id() * (uint32_t)G * 4;
+    asm volatile("" : "+v"(lrow));
 #pragma unroll
     for (int i = 0; i < kScalePer; ++i) {
       const int j = wave + i * NW;
@@ -1656,10 +1687,10 @@ gemm_dma_pg_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, c
       float* dst = slot + gi * kSeg + 64 * p;
       // rows past the tile's valid rows are past the descriptor's range: zero
       if (p < BMp / 64) {
-        const uint32_t off = g < G ? ((uint32_t)(64 * p + lane) * G + g) * 4 : 0x80000000u;
+        const uint32_t off = g < G ? lrow + ((uint32_t)(64 * p) * G + g) * 4 : 0x80000000u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)dst, 4, off, 0, 0, 0);
       } else {
-        const uint32_t off = g < G ? ((uint32_t)(64 * (p - BMp / 64) + lane) * G + g) * 4 : 0x80000000u;
+        const uint32_t off = g < G ? lrow + ((uint32_t)(64 * (p - BMp / 64)) * G + g) * 4 : 0x80000000u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_void*)dst, 4, off, 0, 0, 0);
       }
     }
