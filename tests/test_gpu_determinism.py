@@ -25,6 +25,7 @@ FAMILIES = [
     ("256x192 tile", "pc", 1024, 12288, 2048, 0, False),
     ("128x320 tile", "pc", 1024, 10240, 2560, 0, False),
     ("64x80 tile", "pc", 128, 10240, 2560, 0, False),
+    ("64x128 tile", "pc", 1024, 2048, 6144, 0, False),
     ("64x64 four-stage tile", "pc", 1024, 2048, 2560, 0, False),
     ("64x160 tile", "pc", 64, 2560, 10240, 0, False),
     ("per-group gs128 ring", "pg", 1024, 2560, 10240, 128, False),

@@ -203,7 +203,9 @@ def _pc_case(M, N, K, seed=0):
                                    # 256 x 192 tiles with ragged M, N and K; one K stage (full, partial)
                                    (1000, 12200, 320), (1000, 12200, 128), (1000, 12200, 64),
                                    # 64 x 80 tiles (one round where 64 x 64 needs two): exact and ragged
-                                   (128, 10240, 2560), (100, 9990, 2000)])
+                                   (128, 10240, 2560), (100, 9990, 2000),
+                                   # 64 x 128 tiles: exact, and ragged M, N and K
+                                   (768, 2048, 2048), (1000, 1990, 1040)])
 def test_w8a8_per_channel_outputs(M, N, K):
     c = cider()
     x, w = _pc_case(M, N, K)

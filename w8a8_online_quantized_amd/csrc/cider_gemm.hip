@@ -2074,7 +2074,14 @@ int cheapest_tile(const GemmArgs& g, const TileCost (&c)[NC], int64_t* est_out =
 // three 128-code stages (96 KB of LDS): same-box A/B against three 64-code
 // stages, M=1024 N=4096 K=2048 (the stack's fused q/k/v) 16.5 -> 14.5 us,
 // M=768 16.3 -> 14.1 us, M=1024 N=3072 K=3072 23.2 -> 19.5 us, M=512 N=8192
-// K=4096 29.7 -> 24.3 us; two 128-code stages lost (17.7 us) and four tied. 256 x 192 (wave
+// K=4096 29.7 -> 24.3 us; two 128-code stages lost (17.7 us) and four tied.
+// 64 x 128 (four waves of 32 x 64, four 128-code stages, 96 KB): one round
+// where 64 x 64 needs two, with a quarter less DMA per CU than two 64 x 64
+// blocks; it takes over from 64 x 64 wherever the estimate picks it.
+// Same-box A/B on all 11 shapes where the pick changes: M=1024 N=2048
+// K=6144 (the stack's down projection) 26.5 -> 24.6 us, K=2048 10.8 -> 10.4
+// us, M=512 N=4096 K=4096 19.0 -> 17.3 us, M=192 N=8192 K=4096 20.1 -> 18.1
+// us, M=128 N=12288 K=2560 16.3 -> 15.1 us, none slower. 256 x 192 (wave
 // tiles of 128 x 48) for one round of up to 256 tiles where 128 x 320 or
 // 256 x 320 would leave CUs idle or need a second round; same-box A/B: M=1024
 // N=12288 K=2048 (exactly 256 tiles) 33.4 us against 43.8 us for the 156 tiles
@@ -2090,8 +2097,8 @@ int cheapest_tile(const GemmArgs& g, const TileCost (&c)[NC], int64_t* est_out =
 // at M=256 N=4096 K=4096 (19.8 -> 13.2 us) and M=512 (27.8 -> 21.6 us).
 // 64 x 160 (also as the split-K tile) has four stages too (112 KB): M=128
 // N=2560 K=10240 19.4 -> 17.6 us, M=64 18.6 -> 16.5 us.
-constexpr TileCost kTilesI8[] = {{256, 320, 62}, {128, 320, 92}, {128, 256, 102},
-                                 {128, 128, 105}, {64, 160, 167}, {64, 64, 150}, {256, 192, 76}, {64, 80, 185}};
+constexpr TileCost kTilesI8[] = {{256, 320, 62}, {128, 320, 92}, {128, 256, 102}, {128, 128, 105},
+                                 {64, 160, 167}, {64, 64, 150}, {256, 192, 76}, {64, 80, 185}, {64, 128, 139}};
 constexpr TileCost kTilesI4[] = {{256, 320, 62}, {128, 320, 92}, {128, 256, 102}, {128, 128, 105}, {64, 64, 194}};
 
 // Split-K plan for medium M with long K: too few output tiles to fill the
@@ -2216,7 +2223,8 @@ hipError_t launch_pc(const GemmArgs& g, hipStream_t st) {
       case 4: return launch_dma<64, 160, 2, 2, 128, 4, WK, EPI>(g, st);
       case 5: return launch_dma<64, 64, 1, 4, 128, 4, WK, EPI>(g, st);
       case 6: return launch_dma<256, 192, 2, 4, 128, 2, WK, EPI>(g, st);
-      default: return launch_dma<64, 80, 4, 1, 128, 4, WK, EPI>(g, st);
+      case 7: return launch_dma<64, 80, 4, 1, 128, 4, WK, EPI>(g, st);
+      default: return launch_dma<64, 128, 2, 2, 128, 4, WK, EPI>(g, st);
     }
   }
 }
