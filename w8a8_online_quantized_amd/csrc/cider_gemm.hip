@@ -590,26 +590,30 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
       static_assert(R % 16 == 0 && R * kRowB <= kAvail, "store slab fits the operand stages");
       constexpr int CPR = BN / 8;          // 16-byte chunks per tile row
       constexpr int kIt = (R * CPR + NW * 64 - 1) / (NW * 64);
+      // Pass p takes the same TM / NP fragment rows of every wave, so all
+      // waves (and all four SIMDs) share each pass's dequantization; slab
+      // row (i, r) with i = wave % WGM, r < RB is tile row i * WTM + p * RB + r.
+      constexpr int NP = BM / R, RB = 16 * TM / NP;
+      static_assert(TM % NP == 0 && WGM * RB == R, "every wave writes RB rows per pass");
       stage_barrier();                     // every wave is done reading the operand stages
       // lane coordinates recomputed here rather than kept live across the loop
       const int s16 = lane_id() & 15, s4 = lane_id() >> 4;
 #pragma unroll
-      for (int p = 0; p < BM / R; ++p) {
+      for (int p = 0; p < NP; ++p) {
 #pragma unroll
-        for (int b = 0; b < TM; ++b) {
-          const int r0 = wm + 16 * b - p * R;   // wave-uniform
-          if (r0 >= 0 && r0 < R) {
-            const float sam = lsa[wm + 16 * b + s16];
+        for (int bl = 0; bl < TM / NP; ++bl) {
+          const int b = p * (TM / NP) + bl;
+          const int r0 = (wave % WGM) * RB + 16 * bl;   // wave-uniform slab row
+          const float sam = lsa[wm + 16 * b + s16];
 #pragma unroll
-            for (int a = 0; a < TN; ++a) {
-              const int nl = wn + 16 * a + 4 * s4;
-              int8_t* d = smem + (r0 + s16) * kRowB + nl * 2;
-              const float4 sw4 = *reinterpret_cast<const float4*>(lsw + nl);   // zero past N
-              if constexpr (EPI == kEpiBF16 || EPI == kEpiBF16Split)
-                *reinterpret_cast<bf4*>(d) = dequant4_bf(acc[a][b], sam, sw4);
-              else
-                *reinterpret_cast<h4*>(d) = dequant4(acc[a][b], sam, sw4);
-            }
+          for (int a = 0; a < TN; ++a) {
+            const int nl = wn + 16 * a + 4 * s4;
+            int8_t* d = smem + (r0 + s16) * kRowB + nl * 2;
+            const float4 sw4 = *reinterpret_cast<const float4*>(lsw + nl);   // zero past N
+            if constexpr (EPI == kEpiBF16 || EPI == kEpiBF16Split)
+              *reinterpret_cast<bf4*>(d) = dequant4_bf(acc[a][b], sam, sw4);
+            else
+              *reinterpret_cast<h4*>(d) = dequant4(acc[a][b], sam, sw4);
           }
         }
         lds_write_barrier();
@@ -617,7 +621,7 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
         for (int i = 0; i < kIt; ++i) {
           const int f = (i * NW + wave) * 64 + lane_id();
           const int row = f / CPR, ch = f - row * CPR;
-          const int m = m0 + p * R + row, n = n0 + ch * 8;
+          const int m = m0 + (row / RB) * WTM + p * RB + row % RB, n = n0 + ch * 8;
           if (f < R * CPR && m < M && n < N) {
             const v4i v = *reinterpret_cast<const v4i*>(smem + row * kRowB + ch * 16);
             _Float16* dst = Y + (int64_t)m * N + n;
@@ -625,7 +629,7 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
             __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(dst));
           }
         }
-        if (p + 1 < BM / R) stage_barrier();   // the slab is rewritten by the next pass
+        if (p + 1 < NP) stage_barrier();   // the slab is rewritten by the next pass
       }
       return;
     }
@@ -720,6 +724,11 @@ gemm_persist_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, 
   static_assert(kBA % NL == 0 && kBW % NL == 0 && BM % 64 == 0 && BN % 64 == 0, "even DMA split");
   static_assert(TM * 16 == WTM && TN * 16 == WTN && TM >= 2, "wave tile");
   static_assert(R % 16 == 0 && R * kRowB <= kStageBytes, "store slab fits one stage");
+  // pass p of the store stage takes the same TM / NP fragment rows of every
+  // wave (all four SIMDs dequantize in every pass): slab row (i, r) with
+  // i = wave % WGM, r < RB is tile row i * WTM + p * RB + r
+  constexpr int NP = BM / R, RB = 16 * TM / NP;
+  static_assert(TM % NP == 0 && WGM * RB == R, "every wave writes RB rows per pass");
 
   // two stages | two scale buffers ([BM] s_a then [BN] s_w) | 1 KiB landing pad for spare DMAs
   __shared__ __attribute__((aligned(1024))) int8_t smem[2 * kStageBytes + 2 * kScFloats * 4 + 1024];
@@ -890,22 +899,21 @@ gemm_persist_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, 
         make_rsrc(static_cast<int8_t*>(Y) + (int64_t)m0 * N * 2, (uint32_t)rows_a * (uint32_t)N * 2);
     const int s16 = lane_id() & 15, s4 = lane_id() >> 4;
 #pragma unroll
-    for (int p = 0; p < BM / R; ++p) {
+    for (int p = 0; p < NP; ++p) {
 #pragma unroll
-      for (int b = 0; b < TM; ++b) {
-        const int rr = wm + 16 * b - p * R;   // wave-uniform
-        if (rr >= 0 && rr < R) {
-          const float sam = lsa[wm + 16 * b + s16];
+      for (int bl = 0; bl < TM / NP; ++bl) {
+        const int b = p * (TM / NP) + bl;
+        const int rr = (wave % WGM) * RB + 16 * bl;   // wave-uniform slab row
+        const float sam = lsa[wm + 16 * b + s16];
 #pragma unroll
-          for (int a = 0; a < TN; ++a) {
-            const int nl = wn + 16 * a + 4 * s4;
-            int8_t* d = slab + (rr + s16) * kRowB + nl * 2;
-            const float4 sw4 = *reinterpret_cast<const float4*>(lsw + nl);   // zero past N
-            if constexpr (kBF)
-              *reinterpret_cast<bf4*>(d) = dequant4_bf(acc[a][b], sam, sw4);
-            else
-              *reinterpret_cast<h4*>(d) = dequant4(acc[a][b], sam, sw4);
-          }
+        for (int a = 0; a < TN; ++a) {
+          const int nl = wn + 16 * a + 4 * s4;
+          int8_t* d = slab + (rr + s16) * kRowB + nl * 2;
+          const float4 sw4 = *reinterpret_cast<const float4*>(lsw + nl);   // zero past N
+          if constexpr (kBF)
+            *reinterpret_cast<bf4*>(d) = dequant4_bf(acc[a][b], sam, sw4);
+          else
+            *reinterpret_cast<h4*>(d) = dequant4(acc[a][b], sam, sw4);
         }
       }
       lds_write_barrier();
@@ -914,14 +922,15 @@ gemm_persist_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, 
         for (int i = 0; i < kIt; ++i) {
           const int f = (i * (NW - NL) + wave) * 64 + lane_id();
           const int row = min(f / CPR, R - 1), ch = f - (f / CPR) * CPR;
+          const int trow = (row / RB) * WTM + p * RB + row % RB;   // tile row
           const int n = n0 + ch * 8;
-          const bool ok = f < R * CPR && p * R + row < rows_a && n < N;
+          const bool ok = f < R * CPR && trow < rows_a && n < N;
           const v4i v = *reinterpret_cast<const v4i*>(slab + row * kRowB + ch * 16);
-          const uint32_t off = ok ? ((uint32_t)(p * R + row) * (uint32_t)N + (uint32_t)n) * 2 : 0x80000000u;
+          const uint32_t off = ok ? ((uint32_t)trow * (uint32_t)N + (uint32_t)n) * 2 : 0x80000000u;
           __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, 2 /* nontemporal */);
         }
       }
-      if (p + 1 < BM / R) stage_barrier();   // the slab is rewritten by the next pass
+      if (p + 1 < NP) stage_barrier();   // the slab is rewritten by the next pass
     }
     if (!more) break;
     vb = vbn;
