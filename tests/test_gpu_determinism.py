@@ -38,6 +38,7 @@ FAMILIES = [
     ("GEMV W4A8", "w4", 2, 10240, 2560, 0, False),
     ("split-K int32 reduction", "pc", 256, 2560, 10240, 0, True),
     ("split-K fp32 reduction", "pg", 256, 2560, 10240, 128, True),
+    ("split-K 64x160 eight ranges", "pg", 128, 2560, 10240, 64, True),
     ("decode MV", "mv", 1, 10240, 2560, 0, False),
     ("decode MV per-group", "mv", 2, 2560, 10240, 128, False),
 ]

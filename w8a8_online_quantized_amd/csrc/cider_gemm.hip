@@ -2132,7 +2132,7 @@ constexpr TileCost kTilesI4[] = {{256, 320, 62}, {128, 320, 92}, {128, 256, 102}
 // (128x160, 2 ranges). The tile-cost model above mispredicts these
 // launches, hence a table by tile count.
 struct SplitPlan {
-  int tile = -1;     // per-channel 0: 64x160, 1: 128x128, 2: 128x320; per-group 0: 64x64, 1: 128x128, 2: 128x160
+  int tile = -1;     // per-channel 0: 64x160, 1: 128x128, 2: 128x320; per-group 0: 64x64, 1: 128x128, 2: 128x160, 3: 64x160
   int splits = 0;
 };
 
@@ -2140,6 +2140,17 @@ SplitPlan plan_split_pg(const GemmArgs& g) {
   SplitPlan plan;
   if (g.M <= 16 || g.K < 4096) return plan;
   const int64_t t64 = tiles_of(g, 64, 64), t128 = tiles_of(g, 128, 128), t160 = tiles_of(g, 128, 160);
+  // At most 32 tiles of 64 x 160 (M <= 128 at N = 2560) and K >= 8192: eight
+  // K ranges of 64 x 160 (two 128-code stages), 256 units, one per CU.
+  // Same-box A/B at N=2560, K=10240: M=128 31.0 -> 25.3 us (gs 128) and
+  // 32.7 -> 29.1 us (gs 64), M=64 27.4 -> 24.5 us. With four ranges it lost
+  // (M=256 gs 64 41.1 -> 44.9 us; M=128, N=4096, K=4096 19.4 -> 22.0 us),
+  // and three or four stages ran slower than two (27.7 / 26.3 us at M=128).
+  if (tiles_of(g, 64, 160) * 8 <= 256 && g.K / 8 >= 1024) {
+    plan.tile = 3;
+    plan.splits = 8;
+    return plan;
+  }
   if (t64 <= 320) {
     plan.tile = 0;
     plan.splits = t64 <= 160 ? 4 : 2;
@@ -2257,6 +2268,7 @@ hipError_t launch_pg(const GemmArgs& g, hipStream_t st) {
     if (g.ws) {
       const SplitPlan p = plan_split_pg(g);
       if (p.splits && g.ws_bytes >= split_ws_bytes(g.M, g.N, p.splits)) {
+        if (p.tile == 3) return launch_dma_pg_split<64, 160, 2, 2, 2, GS, EPI>(g, p.splits, st);
         if (p.tile == 0) return launch_dma_pg_split<64, 64, 1, 4, 2, GS, EPI>(g, p.splits, st);
         if constexpr (GS == 128) {
           if (p.tile == 2) return launch_dma_pg_split<128, 160, 2, 2, 2, GS, EPI>(g, p.splits, st);
