@@ -204,6 +204,8 @@ def test_split_k_workspace_plan():
     assert g(128, 10240, 2560, 8, 0) == 0                         # short K
     assert g(128, 2560, 10240, 8, 128) == 8 * 128 * 2560 * 4      # per-group: 64x160 tiles, 8 K ranges, fp32
     assert g(256, 2560, 10240, 8, 64) == 4 * 256 * 2560 * 4       # per-group: 64x64 tiles, 4 K ranges
+    assert g(512, 2560, 10240, 8, 128) == 4 * 512 * 2560 * 4      # per-group: 128x128 tiles, 4 K ranges
+    assert g(512, 2048, 4096, 8, 128) == 2 * 512 * 2048 * 4       # per-group, K < 8192: 64x64 tiles, 2 K ranges
     assert g(1024, 2560, 10240, 8, 128) == 3 * 1024 * 2560 * 4    # per-group: 128x128 tiles, 3 K ranges
     assert g(2048, 2560, 10240, 8, 128) == 2 * 2048 * 2560 * 4    # gs 128: 128x160 tiles, 2 K ranges
     assert g(2048, 2560, 10240, 8, 64) == 0                       # gs 64: 320 tiles of 128x128, no split

@@ -92,10 +92,13 @@ from tests.test_gpu_token_group import token_group_bound  # noqa: E402
 
 # 64x160 tiles with 8 K ranges (at most 32 tiles, K >= 8192; ragged M, N and
 # a last range of two stages at K = 8320), 64x64 with 4 / 2 ranges (M = 256,
-# M = 500), 128x128 with 3 (M=1024; ragged at gs 64) and, for gs 128, 128x160
-# with 2 (M=2048; ragged M, N = 2498: scalar stores in the reduction)
+# M = 500 at K = 4096), 128x128 with 4 (161..320 tiles of 64x64 and
+# K >= 8192: M = 500 at K = 8192, ragged M and N) and with 3 (M=1024; ragged
+# at gs 64) and, for gs 128, 128x160 with 2 (M=2048; ragged M, N = 2498:
+# scalar stores in the reduction)
 PG = [(128, 2560, 10240, 128), (128, 2560, 10240, 64), (130, 650, 8192, 128), (64, 1024, 16384, 64),
-      (100, 1990, 8320, 128), (100, 1990, 8320, 64), (256, 2560, 10240, 64), (500, 2000, 8192, 128),
+      (100, 1990, 8320, 128), (100, 1990, 8320, 64), (256, 2560, 10240, 64), (500, 2000, 4096, 128),
+      (500, 2000, 8192, 128), (500, 2000, 8192, 64),
       (1024, 2560, 10240, 128), (1000, 2500, 8192, 64), (2048, 2560, 10240, 128), (1800, 2498, 4096, 128)]
 
 

@@ -1917,6 +1917,11 @@ hipError_t launch_dma_pg(const GemmArgs& g, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Most K ranges of any split-K plan: a reduction thread issues the loads of
+// every range before it adds any (one memory latency instead of one per
+// range; a loop over a run-time count had kept one load batch in flight).
+constexpr int kMaxSplits = 8;
+
 // Split-K reduction of fp32 per-group partial sums P [splits][M][N], added in
 // split order; per-token activation scales multiply the sum (fp32 product,
 // then fp16), as in the unsplit store stage.
@@ -1930,12 +1935,26 @@ splitk_reduce_f32_kernel(const float* __restrict__ P, int splits, int M, int N, 
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
     const int64_t e0 = i * E;
     const int m = (int)(e0 / N);
+    float p[kMaxSplits][E];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+      if (s >= splits) break;
+      if constexpr (VEC) {
+        const float4 v = *reinterpret_cast<const float4*>(P + s * slab + e0);
+        p[s][0] = v.x, p[s][1] = v.y, p[s][2] = v.z, p[s][3] = v.w;
+      } else {
+        p[s][0] = P[s * slab + e0];
+      }
+    }
     float t[E];
 #pragma unroll
-    for (int r = 0; r < E; ++r) t[r] = P[e0 + r];
-    for (int s = 1; s < splits; ++s)
+    for (int r = 0; r < E; ++r) t[r] = p[0][r];
 #pragma unroll
-      for (int r = 0; r < E; ++r) t[r] += P[s * slab + e0 + r];
+    for (int s = 1; s < kMaxSplits; ++s) {
+      if (s >= splits) break;
+#pragma unroll
+      for (int r = 0; r < E; ++r) t[r] += p[s][r];
+    }
 #pragma unroll
     for (int r = 0; r < E; ++r) {
       if constexpr (EPI == kEpiBF16) static_cast<__bf16*>(Y)[e0 + r] = to_bf16(t[r]);
@@ -1949,6 +1968,7 @@ splitk_reduce_f32_kernel(const float* __restrict__ P, int splits, int M, int N, 
 template <int BM, int BN, int WGM, int WGN, int NS, int GS, int EPI>
 hipError_t launch_dma_pg_split(const GemmArgs& g, int splits, hipStream_t st) {
   const int64_t nbm = (g.M + BM - 1) / BM, nbn = (g.N + BN - 1) / BN;
+  if (splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
   float* parts = static_cast<float*>(g.ws);
   gemm_dma_pg_kernel<BM, BN, WGM, WGN, NS, GS, EPI, true>
       <<<dim3((unsigned)(nbm * nbn * splits)), dim3(WGM * WGN * 64), 0, st>>>(
@@ -1990,14 +2010,34 @@ splitk_reduce_kernel(const int32_t* __restrict__ P, int splits, int M, int N, co
     const int64_t e0 = i * E;
     const int m = (int)(e0 / N), n = (int)(e0 % N);
     if constexpr (VEC) {
-      v4i t = *reinterpret_cast<const v4i*>(P + e0);
-      for (int s = 1; s < splits; ++s) t += *reinterpret_cast<const v4i*>(P + s * slab + e0);
+      v4i p[kMaxSplits];
+#pragma unroll
+      for (int s = 0; s < kMaxSplits; ++s) {
+        if (s >= splits) break;
+        p[s] = *reinterpret_cast<const v4i*>(P + s * slab + e0);
+      }
+      v4i t = p[0];
+#pragma unroll
+      for (int s = 1; s < kMaxSplits; ++s) {
+        if (s >= splits) break;
+        t += p[s];
+      }
       const float4 sw = *reinterpret_cast<const float4*>(SW + n);
       if constexpr (EPI == kEpiBF16) *reinterpret_cast<bf4*>(static_cast<__bf16*>(Y) + e0) = dequant4_bf(t, SA[m], sw);
       else *reinterpret_cast<h4*>(static_cast<_Float16*>(Y) + e0) = dequant4(t, SA[m], sw);
     } else {
-      int t = P[e0];
-      for (int s = 1; s < splits; ++s) t += P[s * slab + e0];
+      int p[kMaxSplits];
+#pragma unroll
+      for (int s = 0; s < kMaxSplits; ++s) {
+        if (s >= splits) break;
+        p[s] = P[s * slab + e0];
+      }
+      int t = p[0];
+#pragma unroll
+      for (int s = 1; s < kMaxSplits; ++s) {
+        if (s >= splits) break;
+        t += p[s];
+      }
       if constexpr (EPI == kEpiBF16) static_cast<__bf16*>(Y)[e0] = dequant1_bf(t, SA[m], SW[n]);
       else static_cast<_Float16*>(Y)[e0] = dequant1(t, SA[m], SW[n]);
     }
@@ -2013,6 +2053,7 @@ inline int64_t split_ws_bytes(int64_t M, int64_t N, int splits) { return (int64_
 template <int BM, int BN, int WGM, int WGN, int BK, int NS, int WK, int EPI>
 hipError_t launch_dma_split(const GemmArgs& g, int splits, hipStream_t st) {
   const int64_t nbm = (g.M + BM - 1) / BM, nbn = (g.N + BN - 1) / BN;
+  if (splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
   int32_t* parts = static_cast<int32_t*>(g.ws);
   gemm_dma_kernel<BM, BN, WGM, WGN, BK, NS, WK, kEpiAccI32, true>
       <<<dim3((unsigned)(nbm * nbn * splits)), dim3(WGM * WGN * 64), 0, st>>>(
@@ -2151,7 +2192,15 @@ SplitPlan plan_split_pg(const GemmArgs& g) {
     plan.splits = 8;
     return plan;
   }
-  if (t64 <= 320) {
+  // 161..320 tiles of 64 x 64 with K >= 8192: four K ranges of 128 x 128
+  // rather than two of 64 x 64. Same-box A/B: M=512, N=2560, K=10240 60.4 ->
+  // 51.0 us (gs 128) and 66.2 -> 60.6 us (gs 64), M=500, N=2000, K=8192
+  // 42.2 -> 37.7 us, M=384, N=3072, K=8192 45.5 -> 43.0 us (gs 64: 49.7 ->
+  // 50.3); at K=4096 (M=512, N=2048) it lost, 26.2 -> 26.8 us.
+  if (t64 > 160 && t64 <= 320 && 4 * t128 <= 512 && g.K >= 8192) {
+    plan.tile = 1;
+    plan.splits = 4;
+  } else if (t64 <= 320) {
     plan.tile = 0;
     plan.splits = t64 <= 160 ? 4 : 2;
   } else if (3 * t128 <= 512) {
