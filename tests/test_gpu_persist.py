@@ -1,5 +1,6 @@
 """The persistent per-channel kernel (256 x 320 tiles, more than one round of
-tiles, K % 128 == 0, N % 8 == 0) against the oracle.
+tiles, K % 128 == 0, N % 8 == 0) against the oracle, with int8 weights and
+with packed int4 weights (W4A8).
 
 Its seams are what these shapes aim at: blocks that walk different numbers of
 tiles (tile counts that are not a multiple of 256), tiles cut by the M and N
@@ -95,6 +96,51 @@ def test_persist_repeat_and_neighbours_untouched():
     y0 = y.clone()
     for i in range(20):
         c.cider_w8a8_gemm(xq, sa, wq, sw, 0, y=y)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y0.view(torch.int16)), f"repeat {i}"
+    assert bool((buf[:N] == 12345).all()) and bool((buf[(M + 1) * N:] == 12345).all())
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_persist_w4a8(M, N, K):
+    """Packed int4 weights: sampled rows within one ulp of the oracle's W4A8
+    linear, and the whole output bit-identical to the int8 kernel run on the
+    unpacked codes."""
+    c = cider()
+    x = inputs.activations(M, K, seed=84)
+    w = inputs.weights(N, K, seed=84)
+    wp, sw = c.cider_quant_weight(dev(w), 4, 0)
+    xq, sa = c.cider_quant_act(dev(x), 0)
+    y = host(c.cider_w4a8_gemm(xq, sa, wp, sw))
+    wpo, swo = oracle.quantize_weight(w, 4, 0)
+    assert np.array_equal(host(wp), wpo)
+    rows = rows_for(M, M + N + K + 4)
+    yo, _, _ = oracle.w4a8_linear(x[rows], wpo, swo)
+    assert_y_close(y[rows], yo, 1e-3, max_ulp=1, what=f"persist w4a8 {M}x{N}x{K}")
+    y8 = host(c.cider_w8a8_gemm(xq, sa, dev(oracle.unpack_int4(wpo)), sw, 0))
+    assert np.array_equal(y.view(np.uint16), y8.view(np.uint16))
+
+
+def test_persist_w4a8_bf16_repeat_and_neighbours_untouched():
+    """bf16 output of the W4A8 persistent kernel: bit-identical to the int8
+    kernel on the unpacked codes, 20 repeats bit-identical, and nothing
+    written outside y."""
+    c = cider()
+    M, N, K = 3000, 10248, 1024
+    x = dev(inputs.activations(M, K, seed=85))
+    w = inputs.weights(N, K, seed=85)
+    wp, sw = c.cider_quant_weight(dev(w), 4, 0)
+    xq, sa = c.cider_quant_act(x, 0)
+    buf = torch.full(((M + 2) * N,), 12345, dtype=torch.int16, device="cuda")
+    y = buf[N:(M + 1) * N].view(torch.bfloat16).view(M, N)
+    c.cider_w4a8_gemm(xq, sa, wp, sw, y=y)
+    torch.cuda.synchronize()
+    y8 = c.cider_w8a8_gemm(xq, sa, dev(oracle.unpack_int4(host(wp))), sw, 0, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y8.view(torch.int16))
+    y0 = y.clone()
+    for i in range(20):
+        c.cider_w4a8_gemm(xq, sa, wp, sw, y=y)
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int16), y0.view(torch.int16)), f"repeat {i}"
     assert bool((buf[:N] == 12345).all()) and bool((buf[(M + 1) * N:] == 12345).all())

@@ -684,8 +684,9 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
 
 // ---------------------------------------------------------------------------
 // Persistent per-channel kernel for launches of more than one round of tiles
-// (int8 weights, fp16 / bf16 output, N % 8 == 0, K % 128 == 0: whole 128-code
-// stages, two in flight). Each block walks its tiles one after another in the same
+// (int8 weights, or packed int4 weights unpacked from LDS as in
+// gemm_dma_kernel; fp16 / bf16 output, N % 8 == 0, K % 128 == 0: whole
+// 128-code stages, two in flight). Each block walks its tiles one after another in the same
 // XCD-contiguous order as gemm_dma_kernel, and the tiles overlap at the seam:
 // the last stage of tile t already issues the DMA of tile t+1's first stage
 // and of its scales (into the other of two scale buffers), and tile t's store
@@ -700,17 +701,20 @@ gemm_dma_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, cons
 // descriptor spanning the tile's valid rows; a masked lane gets an
 // out-of-range offset, so every storing wave issues the same instructions.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WGM, int WGN, int EPI>
+template <int BM, int BN, int WGM, int WGN, int EPI, int WK = kWeightI8>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_persist_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, const int8_t* __restrict__ W,
                     const float* __restrict__ SW, int M, int N, int K, void* __restrict__ Y) {
+  constexpr bool kI4 = WK == kWeightI4;
   constexpr int BK = 128, NW = WGM * WGN, NL = NW / 2;   // NL loader waves, NW - NL storer waves
+  constexpr int RBW = kI4 ? BK / 2 : BK;                 // weight bytes per row per stage
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int TM = WTM / 16, TN = WTN / 16;
-  constexpr int kStageBytes = (BM + BN) * BK;
-  constexpr int kBA = BM * BK / 1024, kBW = BN * BK / 1024;     // 1 KiB DMA blocks per stage
+  constexpr int kStageBytes = BM * BK + BN * RBW;
+  constexpr int kBA = BM * BK / 1024, kBW = BN * RBW / 1024;    // 1 KiB DMA blocks per stage
   constexpr int kIA = kBA / NL, kIW = kBW / NL;                 // per loader wave
   constexpr int kRowStep = NL * (1024 / BK);                    // tile rows between a wave's blocks
+  constexpr int kRowStepW = NL * (1024 / RBW);                  // the same for packed weight rows
   constexpr int kScInstr = (BM + BN) / 64;                      // 64 scales per 4-byte DMA instruction
   constexpr int kScPer = (kScInstr + NL - 1) / NL;
   constexpr int kScFloats = BM + BN;
@@ -745,6 +749,7 @@ gemm_persist_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, 
   const int units = nbm * nbn;
   const int KT = (K + BK - 1) / BK;
   const uint32_t ld = (uint32_t)K;
+  const uint32_t ldw = kI4 ? ld / 2 : ld;
 
   // tile of virtual block vb (vb < units): XCD-contiguous ranges, then groups of 8 tile-rows
   auto tile_origin = [&](int vb, int& m0, int& n0) {
@@ -761,7 +766,9 @@ gemm_persist_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, 
   // held in a struct member and handed to the DMA builtin left the kernel
   // without its host-side launch stub)
   auto rsrc_a = [&](int m0) { return make_rsrc(A + (int64_t)m0 * K, (uint32_t)min(BM, M - m0) * ld); };
-  auto rsrc_w = [&](int n0) { return make_rsrc(W + (int64_t)n0 * K, (uint32_t)min(BN, N - n0) * ld); };
+  auto rsrc_w = [&](int n0) {
+    return make_rsrc(W + (int64_t)n0 * (kI4 ? K / 2 : K), (uint32_t)min(BN, N - n0) * ldw);
+  };
   auto rsrc_sa = [&](int m0) { return make_rsrc(SA + m0, (uint32_t)min(BM, M - m0) * 4); };
   auto rsrc_sw = [&](int n0) { return make_rsrc(SW + n0, (uint32_t)min(BN, N - n0) * 4); };
 
@@ -771,6 +778,11 @@ gemm_persist_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, 
   const int r0 = lw * (1024 / BK) + lane / (BK / 16);
   const uint32_t off0 = (uint32_t)r0 * ld + (uint32_t)(slot_of<BK>(r0, lane % (BK / 16)) * 16);
   static_assert(kRowStep % 16 == 0, "uniform block step keeps the swizzle slot");
+  // packed int4 weight rows (64 bytes per stage) have their own lane layout:
+  // 16 rows of 4 chunks per 1 KiB block
+  const int r0w = lw * (1024 / RBW) + lane / (RBW / 16);
+  const uint32_t off0w = kI4 ? (uint32_t)r0w * ldw + (uint32_t)(slot_of<RBW>(r0w, lane % (RBW / 16)) * 16) : 0u;
+  static_assert(kRowStepW % 16 == 0, "uniform block step keeps the swizzle slot");
   auto issue = [&](__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rw, int kt, int buf) {   // loader waves; K % BK == 0
     const int kb = kt * BK;
     {
@@ -787,14 +799,33 @@ gemm_persist_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, 
       uint32_t lbase = (uint32_t)buf * kStageBytes + (uint32_t)lw * 1024;
       asm volatile("" : "+s"(lbase));
       const uint32_t step = (uint32_t)kRowStep * ld;
+      if constexpr (!kI4) {
 #pragma unroll
-      for (int i = 0; i < (kIA > kIW ? kIA : kIW); ++i) {
-        if (i < kIA)
+        for (int i = 0; i < (kIA > kIW ? kIA : kIW); ++i) {
+          if (i < kIA)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(smem + lbase + i * NL * 1024), 16, off, 0, 0, 0);
+          if (i < kIW)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(smem + lbase + BM * BK + i * NL * 1024), 16,
+                                                     off, 0, 0, 0);
+          off += step;
+        }
+      } else {
+        // the two operands' blocks differ in rows per block: a running
+        // offset each
+        uint32_t offw = off0w + (uint32_t)kb / 2;
+        asm volatile("" : "+v"(offw));
+        const uint32_t stepw = (uint32_t)kRowStepW * ldw;
+#pragma unroll
+        for (int i = 0; i < kIA; ++i) {
           __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(smem + lbase + i * NL * 1024), 16, off, 0, 0, 0);
-        if (i < kIW)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(smem + lbase + BM * BK + i * NL * 1024), 16, off,
+          off += step;
+        }
+#pragma unroll
+        for (int i = 0; i < kIW; ++i) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(smem + lbase + BM * BK + i * NL * 1024), 16, offw,
                                                    0, 0, 0);
-        off += step;
+          offw += stepw;
+        }
       }
     }
   };
@@ -846,45 +877,81 @@ gemm_persist_kernel(const int8_t* __restrict__ A, const float* __restrict__ SA, 
       stage_barrier();
       const int8_t* sa_ = smem + ((gs + kt) & 1) * kStageBytes;
       const int8_t* sw_ = sa_ + BM * BK;
-      // two 64-code steps, fragment reads issued ahead of use as in gemm_dma_kernel
-      v4i wf[TN], af[TM], nwf[TN], naf[TM];
-#pragma unroll
-      for (int a = 0; a < TN; ++a)
-        wf[a] = *reinterpret_cast<const v4i*>(sw_ + tile_off<BK>(wn + 16 * a + l16, l4));
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-        af[b] = *reinterpret_cast<const v4i*>(sa_ + tile_off<BK>(wm + 16 * b + l16, l4));
-      __builtin_amdgcn_sched_barrier(0);
-      if (loader) {
-        if (kt + 1 < KT) {
-          issue(ra, rw, kt + 1, (gs + kt + 1) & 1);
-        } else if (more) {
-          issue_scales(rsrc_sa(m0n), rsrc_sw(n0n), (it + 1) & 1);
-          issue(rsrc_a(m0n), rsrc_w(n0n), 0, (gs + kt + 1) & 1);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int b = 0; b < TM; ++b) {
+      if constexpr (kI4) {
+        // lane group g holds packed chunk g of its weight row (codes 32g ..
+        // 32g + 31); half h of it pairs with activation chunk 2g + h, whose
+        // bytes are reordered to the unpacked order (as in gemm_dma_kernel)
+        v4i wraw[TN];
 #pragma unroll
         for (int a = 0; a < TN; ++a)
-          acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[a], af[b], acc[a][b], 0, 0, 0);
+          wraw[a] = *reinterpret_cast<const v4i*>(sw_ + tile_off<RBW>(wn + 16 * a + l16, l4));
         __builtin_amdgcn_sched_barrier(0);
-        if (b + 2 < TM) af[b + 2] = *reinterpret_cast<const v4i*>(sa_ + tile_off<BK>(wm + 16 * (b + 2) + l16, l4));
-        naf[b] = *reinterpret_cast<const v4i*>(sa_ + tile_off<BK>(wm + 16 * b + l16, 4 + l4));
-        if (b < TN) nwf[b] = *reinterpret_cast<const v4i*>(sw_ + tile_off<BK>(wn + 16 * b + l16, 4 + l4));
-        if (b == TM - 1) {
-#pragma unroll
-          for (int a = TM; a < TN; ++a)
-            nwf[a] = *reinterpret_cast<const v4i*>(sw_ + tile_off<BK>(wn + 16 * a + l16, 4 + l4));
+        if (loader) {
+          if (kt + 1 < KT) {
+            issue(ra, rw, kt + 1, (gs + kt + 1) & 1);
+          } else if (more) {
+            issue_scales(rsrc_sa(m0n), rsrc_sw(n0n), (it + 1) & 1);
+            issue(rsrc_a(m0n), rsrc_w(n0n), 0, (gs + kt + 1) & 1);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
-      }
 #pragma unroll
-      for (int b = 0; b < TM; ++b)
+        for (int h = 0; h < 2; ++h) {
+          v4i af[TM];
+#pragma unroll
+          for (int b = 0; b < TM; ++b)
+            af[b] = even_odd_bytes(*reinterpret_cast<const v4i*>(sa_ + tile_off<BK>(wm + 16 * b + l16, 2 * l4 + h)));
+#pragma unroll
+          for (int a = 0; a < TN; ++a) {
+            // unpacked just before its row of MFMAs: one weight fragment live
+            const v4i wf = unpack_int4(h ? make_uint2((uint32_t)wraw[a].z, (uint32_t)wraw[a].w)
+                                         : make_uint2((uint32_t)wraw[a].x, (uint32_t)wraw[a].y));
+#pragma unroll
+            for (int b = 0; b < TM; ++b)
+              acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf, af[b], acc[a][b], 0, 0, 0);
+          }
+        }
+      } else {
+        // two 64-code steps, fragment reads issued ahead of use as in gemm_dma_kernel
+        v4i wf[TN], af[TM], nwf[TN], naf[TM];
 #pragma unroll
         for (int a = 0; a < TN; ++a)
-          acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(nwf[a], naf[b], acc[a][b], 0, 0, 0);
+          wf[a] = *reinterpret_cast<const v4i*>(sw_ + tile_off<BK>(wn + 16 * a + l16, l4));
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          af[b] = *reinterpret_cast<const v4i*>(sa_ + tile_off<BK>(wm + 16 * b + l16, l4));
+        __builtin_amdgcn_sched_barrier(0);
+        if (loader) {
+          if (kt + 1 < KT) {
+            issue(ra, rw, kt + 1, (gs + kt + 1) & 1);
+          } else if (more) {
+            issue_scales(rsrc_sa(m0n), rsrc_sw(n0n), (it + 1) & 1);
+            issue(rsrc_a(m0n), rsrc_w(n0n), 0, (gs + kt + 1) & 1);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < TM; ++b) {
+#pragma unroll
+          for (int a = 0; a < TN; ++a)
+            acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[a], af[b], acc[a][b], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          if (b + 2 < TM) af[b + 2] = *reinterpret_cast<const v4i*>(sa_ + tile_off<BK>(wm + 16 * (b + 2) + l16, l4));
+          naf[b] = *reinterpret_cast<const v4i*>(sa_ + tile_off<BK>(wm + 16 * b + l16, 4 + l4));
+          if (b < TN) nwf[b] = *reinterpret_cast<const v4i*>(sw_ + tile_off<BK>(wn + 16 * b + l16, 4 + l4));
+          if (b == TM - 1) {
+#pragma unroll
+            for (int a = TM; a < TN; ++a)
+              nwf[a] = *reinterpret_cast<const v4i*>(sw_ + tile_off<BK>(wn + 16 * a + l16, 4 + l4));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int b = 0; b < TM; ++b)
+#pragma unroll
+          for (int a = 0; a < TN; ++a)
+            acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(nwf[a], naf[b], acc[a][b], 0, 0, 0);
+      }
     }
     gs += KT;
 
@@ -2083,9 +2150,9 @@ inline bool persist_fits(const GemmArgs& g, int bm, int bn) {
          (int64_t)bm * g.N * 2 < (int64_t(1) << 31);
 }
 
-template <int BM, int BN, int WGM, int WGN, int EPI>
+template <int BM, int BN, int WGM, int WGN, int EPI, int WK = kWeightI8>
 hipError_t launch_persist(const GemmArgs& g, hipStream_t st) {
-  gemm_persist_kernel<BM, BN, WGM, WGN, EPI><<<dim3(256), dim3(WGM * WGN * 64), 0, st>>>(
+  gemm_persist_kernel<BM, BN, WGM, WGN, EPI, WK><<<dim3(256), dim3(WGM * WGN * 64), 0, st>>>(
       g.a, g.sa, static_cast<const int8_t*>(g.w), g.sw, (int)g.M, (int)g.N, (int)g.K, g.y);
   return hipGetLastError();
 }
@@ -2274,7 +2341,10 @@ hipError_t launch_pc(const GemmArgs& g, hipStream_t st) {
   }
   if constexpr (WK == kWeightI4) {
     switch (cheapest_tile(g, kTilesI4)) {
-      case 0: return launch_dma<256, 320, 2, 4, 128, 2, WK, EPI>(g, st);
+      case 0:
+        if constexpr (EPI == kEpiF16 || EPI == kEpiBF16)
+          if (persist_fits(g, 256, 320)) return launch_persist<256, 320, 2, 4, EPI, WK>(g, st);
+        return launch_dma<256, 320, 2, 4, 128, 2, WK, EPI>(g, st);
       case 1: return launch_dma<128, 320, 2, 4, 128, 2, WK, EPI>(g, st);
       case 2: return launch_dma<128, 256, 2, 4, 128, 2, WK, EPI>(g, st);
       case 3: return launch_dma<128, 128, 2, 2, 128, 2, WK, EPI>(g, st);
