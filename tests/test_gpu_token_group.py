@@ -124,7 +124,8 @@ def test_token_group_deterministic_and_stream_ordered():
 
 
 # bf16 rows in, bf16 out (cider_w8a8_gemm_token_group_dt): the skinny kernel,
-# the 64x64 / 128x128 / 128x160 tiles with ragged tails, and both split-K plans
+# the 64x64 / 128x128 / 128x160 tiles with ragged tails, and split-K (64x160
+# in eight K ranges at M=128, 128x128 in three at M=1024)
 @pytest.mark.parametrize("M,N,K,gs,split", [(3, 5, 128, 128, False), (16, 70, 2560, 64, False),
                                             (130, 300, 1152, 64, False), (520, 260, 2560, 128, False),
                                             (4000, 2500, 1280, 128, False), (2000, 2498, 1280, 64, False),
