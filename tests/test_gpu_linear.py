@@ -52,7 +52,7 @@ def test_one_launch_linear(M, N, K, bits):
 
 @pytest.mark.parametrize("M,N,K,bits,gs", [(3, 300, 1056, 8, 0), (4, 130, 16384, 4, 0), (5, 200, 1024, 8, 0), (16, 300, 2560, 4, 0), (70, 260, 1152, 8, 64),
                                            (9, 130, 1024, 8, 128), (300, 650, 2560, 8, 0), (4, 100, 1024, 8, 128),
-                                           (1024, 2560, 10240, 8, 128)])
+                                           (1024, 2560, 10240, 8, 128), (3000, 10248, 1024, 4, 0)])
 def test_workspace_linear(M, N, K, bits, gs):
     c = cider()
     need = c.cider_linear_workspace_size(M, N, K, bits, gs)
